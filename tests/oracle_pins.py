@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each pin takes a loaded oracle library (`oracle._load()` or a deliberately broken build of it)
+and raises AssertionError when the oracle disagrees with brute force, a library routine, a
+published format table, a closed form or an invariant.  tests/test_oracle_pins.py runs them on
+the real oracle; tests/test_oracle_mutants.py checks that every planted mistake trips at least
+one of them.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def _tie_logits(rng, T, E):
+    """Logits from a small integer set so that ties are common, plus a few -inf."""
+    L = rng.integers(-3, 4, size=(T, E)).astype(np.float32) * 0.5
+    L[rng.random((T, E)) < 0.05] = -np.inf
+    L[:, 0] = np.where(rng.random(T) < 0.3, -0.0, L[:, 0])
+    return L
+
+
+def _precedes(a, b, row):
+    """Route order: larger logit first, equal logits by lower expert index (IEEE ==, so -0 == +0)."""
+    return row[a] > row[b] or (row[a] == row[b] and a < b)
+
+
+# ------------------------------------------------------------------------------ route
+
+def pin_route_bruteforce(lib):
+    """ids = the unique k-subset whose members all precede every non-member, ordered by precedence."""
+    rng = np.random.default_rng(11)
+    for E in range(1, 11):
+        for k in range(1, min(4, E) + 1):
+            L = _tie_logits(rng, 24, E)
+            ids, _ = oracle.route(L, k, lib=lib)
+            for t in range(L.shape[0]):
+                row = L[t]
+                winners = [S for S in itertools.combinations(range(E), k)
+                           if all(_precedes(a, b, row) for a in S for b in range(E) if b not in S)]
+                assert len(winners) == 1, (E, k, t)
+                S = list(winners[0])
+                ordered = sorted(S, key=lambda e: (-float(row[e]), e))
+                assert list(ids[t]) == ordered, (E, k, t, row, ids[t], ordered)
+
+
+def pin_route_special_cases(lib):
+    rng = np.random.default_rng(12)
+    # all-equal logits -> ids 0..k-1
+    ids, w = oracle.route(np.full((5, 9), 0.25, np.float32), 4, lib=lib)
+    assert (ids == np.arange(4)).all()
+    assert (w == np.float32(0.25)).all()          # 1/k exactly for a power-of-two k
+    # k = E -> the whole descending order (numpy lexsort as the library cross-check)
+    L = _tie_logits(rng, 16, 7)
+    L[np.isinf(L)] = -5.0
+    ids, _ = oracle.route(L, 7, lib=lib)
+    for t in range(16):
+        assert list(ids[t]) == list(np.lexsort((np.arange(7), -L[t].astype(np.float64))))
+    # adding a constant to a row leaves the ids unchanged
+    L = rng.standard_normal((32, 12)).astype(np.float32)
+    a, _ = oracle.route(L, 3, lib=lib)
+    b, _ = oracle.route(L + np.float32(3.0), 3, lib=lib)
+    assert (a == b).all()
+    # k = 1 -> weight exactly 1
+    _, w = oracle.route(L, 1, lib=lib)
+    assert (w == 1.0).all()
+
+
+def pin_route_weights_float64(lib):
+    """Weights = float64 softmax, restricted to the chosen ids and renormalised, within 1e-6."""
+    rng = np.random.default_rng(13)
+    for E, k, scale in ((8, 2, 1.0), (64, 8, 1.0), (256, 8, 3.0), (5, 5, 1.0)):
+        L = (rng.standard_normal((40, E)) * scale).astype(np.float32)
+        ids, w = oracle.route(L, k, lib=lib)
+        L64 = L.astype(np.float64)
+        p = np.exp(L64 - L64.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+        ref = sel / sel.sum(axis=1, keepdims=True)
+        assert np.abs(w - ref).max() <= 1e-6, np.abs(w - ref).max()
+        assert np.abs(w.astype(np.float64).sum(axis=1) - 1.0).max() <= 1e-6
+        assert (np.diff(w, axis=1) <= 0).all()   # descending logits give non-increasing weights
+
+
+# ------------------------------------------------------------------------------ permute
+
+def pin_permute(lib):
+    rng = np.random.default_rng(14)
+    for T, E, k in ((1, 4, 1), (17, 8, 2), (64, 10, 4), (300, 128, 8), (0, 5, 2)):
+        ids = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+        if T > 5:   # skew: many tokens on expert 0
+            ids[: T // 2, 0] = 0
+            ids[: T // 2, 1:] = np.stack([rng.permutation(np.arange(1, E))[: k - 1] for _ in range(T // 2)])
+        counts, offsets, gather, inv = oracle.permute(ids, E, lib=lib)
+        flat = ids.reshape(-1)
+        assert (counts == np.bincount(flat, minlength=E)).all()
+        assert counts.sum() == T * k and offsets[0] == 0 and offsets[E] == T * k
+        assert (np.diff(offsets) == counts).all()
+        ref = np.argsort(flat, kind="stable")       # library cross-check: stable sort by expert
+        assert (gather == ref).all()
+        assert (np.sort(gather) == np.arange(T * k)).all()   # bijection
+        assert (inv[gather] == np.arange(T * k)).all()
+        for e in range(E):
+            g = gather[offsets[e]:offsets[e + 1]]
+            assert (flat[g] == e).all() and (np.diff(g) > 0).all()
+
+
+# ------------------------------------------------------------------------------ element decoders
+
+def pin_decoder_tables(lib):
+    for code, val in _golden("e2m1_values.txt"):
+        got = oracle.e2m1_value(int(code), lib=lib)
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got)
+    for code, val in _golden("e4m3_special.txt"):
+        got = oracle.e4m3_value(int(code, 16), lib=lib)
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got)
+    # all 256 e4m3 codes against torch's float8_e4m3fn decode (library routine)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle.e4m3_value(c, lib=lib) for c in range(256)], np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)) or \
+        np.array_equal(np.nan_to_num(got, nan=7.0), np.nan_to_num(ref, nan=7.0))
+    # all 65536 fp16 codes against numpy's float16 (library routine), bit for bit (NaN payload aside)
+    bits = np.arange(65536, dtype=np.uint32)
+    ref16 = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    got16 = np.array([oracle.fp16_value(int(b), lib=lib) for b in bits], np.float32)
+    nan = np.isnan(ref16)
+    assert (np.isnan(got16) == nan).all()
+    assert np.array_equal(got16[~nan].view(np.uint32), ref16[~nan].view(np.uint32))
+    # E8M0 = 2^(s-127), 0xFF = NaN; bf16 = upper half of fp32
+    for s in range(255):
+        assert oracle.e8m0_value(s, lib=lib) == 2.0 ** (s - 127), s
+    assert math.isnan(oracle.e8m0_value(255, lib=lib))
+    for b in (0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0x8000):
+        ref = np.array([b << 16], np.uint32).view(np.float32)[0]
+        assert oracle.bf16_value(b, lib=lib) == ref
+
+
+def _exact_q4_0_weights(rng, rows, K):
+    """Weights exactly representable in Q4_0: per block scale s = m * 2^-22 (m odd in [1024, 2048), so s
+    is an exact normal fp16) and integers q-8 in [-8, 7] with the block's extreme value -8 present (so the encoder
+    recovers s exactly)."""
+    nb = K // 32
+    s = (rng.integers(1024, 2048, size=(rows, nb)) | 1).astype(np.float64) * 2.0 ** -22
+    q = rng.integers(-7, 8, size=(rows, nb, 32)).astype(np.float64)
+    q[..., rng.integers(0, 32)] = -8.0
+    return (q * s[..., None]).reshape(rows, K)
+
+
+def pin_dequant_roundtrip(lib):
+    """Encoding exactly representable weights with the input encoders and decoding them with the
+    oracle gives the weights back bit for bit, for every format."""
+    rng = np.random.default_rng(15)
+    rows, K = 256, 256
+    # bf16: any bf16 value
+    w = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32)).to(torch.bfloat16).float()
+    c, _ = synth.encode_bf16(w)
+    assert np.array_equal(oracle.dequant(0, c, None, rows, K, lib=lib), w.numpy())
+    # Q4_0
+    w = _exact_q4_0_weights(rng, rows, K).astype(np.float32)
+    c, _ = synth.encode_q4_0(torch.from_numpy(w))
+    assert np.array_equal(oracle.dequant(1, c, None, rows, K, lib=lib), w)
+    # MXFP4: e2m1 grid values times 2^k, block max magnitude 4 or 6 so the shared exponent is k
+    grid = np.array([float(v) for _, v in _golden("e2m1_values.txt")], np.float64)
+    v = grid[rng.integers(0, 16, size=(rows, K // 32, 32))]
+    v[..., 3] = rng.choice([4.0, 6.0, -4.0, -6.0], size=(rows, K // 32))
+    e = rng.integers(-12, 3, size=(rows, K // 32, 1)).astype(np.float64)
+    w = (v * 2.0 ** e).reshape(rows, K).astype(np.float32)
+    c, s = synth.encode_mxfp4(torch.from_numpy(w))
+    got = oracle.dequant(2, c, s, rows, K, lib=lib)
+    assert np.array_equal(got, w), np.abs(got - w).max()
+    # FP8-B128: e4m3 values times a power-of-two block scale, with +-448 in every block
+    codes = rng.integers(0, 256, size=(rows, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x30
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    vals = vals.reshape(rows // 128, 128, K // 128, 128)
+    vals[:, 5, :, 7] = 448.0
+    sc = 2.0 ** rng.integers(-10, -4, size=(rows // 128, 1, K // 128, 1)).astype(np.float64)
+    w = (vals * sc).reshape(rows, K).astype(np.float32)
+    c, s = synth.encode_fp8_b128(torch.from_numpy(w))
+    got = oracle.dequant(3, c, s, rows, K, lib=lib)
+    assert np.array_equal(got, w), np.abs(got - w).max()
+
+
+def pin_dequant_layouts(lib):
+    """Hand-built blocks with known element positions (GGUF Q4_0 nibble order, OCP MX packing,
+    128x128 FP8 block grid) decode to the values the format definitions give them."""
+    # Q4_0: one row, two blocks; block b has scale 2^-b (fp16), element i gets code (i % 16)
+    blk = np.zeros((1, 2, 18), np.uint8)
+    ref = np.zeros((1, 64), np.float64)
+    for b in range(2):
+        blk[0, b, 0:2] = np.array([2.0 ** -b], np.float16).view(np.uint8)
+        for i in range(32):
+            q = (i * 7 + b) % 16
+            byte = 2 + (i % 16)
+            blk[0, b, byte] |= (q << 4) if i >= 16 else q
+            ref[0, 32 * b + i] = (q - 8) * 2.0 ** -b
+    assert np.array_equal(oracle.dequant(1, blk, None, 1, 64, lib=lib), ref.astype(np.float32))
+    # MXFP4: element j of the row gets code j % 16; scales 2^(s-127) with s = 125, 130
+    codes = np.array([(2 * i % 16) | (((2 * i + 1) % 16) << 4) for i in range(32)], np.uint8)[None]
+    sc = np.array([[125, 130]], np.uint8)
+    grid = np.array([float(v) for _, v in _golden("e2m1_values.txt")])
+    ref = np.array([grid[j % 16] * 2.0 ** (int(sc[0, j // 32]) - 127) for j in range(64)])[None]
+    assert np.array_equal(oracle.dequant(2, codes, sc, 1, 64, lib=lib), ref.astype(np.float32))
+    # FP8-B128: 256x256 of code 0x38 (1.0); block (rb, cb) has scale 1 + rb + 2cb
+    codes = np.full((256, 256), 0x38, np.uint8)
+    sc = np.array([[1.0, 3.0], [2.0, 4.0]], np.float32)
+    got = oracle.dequant(3, codes, sc, 256, 256, lib=lib)
+    ref = np.repeat(np.repeat(sc, 128, axis=0), 128, axis=1)
+    assert np.array_equal(got, ref)
+    # a partial row range decodes the same rows
+    assert np.array_equal(oracle.dequant(3, codes, sc, 256, 256, row0=130, nrows=3, lib=lib), ref[130:133])
+
+
+# ------------------------------------------------------------------------------ FFN and layer
+
+def pin_ffn_float64(lib):
+    """SwiGLU against float64 numpy matmuls on the same fp32 inputs: rel-L2 <= 1e-5."""
+    rng = np.random.default_rng(16)
+    for n, d, I in ((5, 64, 48), (3, 256, 96), (1, 32, 32)):
+        x = rng.standard_normal((n, d)).astype(np.float32)
+        w13 = (rng.standard_normal((2 * I, d)) * 0.05).astype(np.float32)
+        w2 = (rng.standard_normal((d, I)) * 0.05).astype(np.float32)
+        h, y = oracle.swiglu_ffn(x, w13, w2, lib=lib)
+        x64, w64, d64 = x.astype(np.float64), w13.astype(np.float64), w2.astype(np.float64)
+        g = x64 @ w64[:I].T
+        u = x64 @ w64[I:].T
+        h64 = g / (1.0 + np.exp(-g)) * u
+        y64 = h64 @ d64.T
+        assert np.linalg.norm(h - h64) <= 1e-5 * np.linalg.norm(h64)
+        assert np.linalg.norm(y - y64) <= 1e-5 * np.linalg.norm(y64)
+    # x = 0 -> y = 0; W_down = 0 -> y = 0
+    _, y = oracle.swiglu_ffn(np.zeros((2, 64), np.float32),
+                             (rng.standard_normal((64, 64)) * 0.1).astype(np.float32),
+                             (rng.standard_normal((64, 32)) * 0.1).astype(np.float32), lib=lib)
+    assert (y == 0).all()
+    _, y = oracle.swiglu_ffn(rng.standard_normal((2, 64)).astype(np.float32),
+                             (rng.standard_normal((64, 64)) * 0.1).astype(np.float32),
+                             np.zeros((64, 32), np.float32), lib=lib)
+    assert (y == 0).all()
+
+
+def _tiny_layer_inputs(rng, T, d, E, k, I, fmt=0, identical=False):
+    w = synth.Workload("pin", 99, T=T, d=d, E=E, k=k, I=I, fmt=fmt)
+    bank = synth.empty_bank(fmt, E, d, I)
+    w13 = torch.from_numpy((rng.standard_normal((2 * I, d)) * 0.05).astype(np.float32))
+    w2 = torch.from_numpy((rng.standard_normal((d, I)) * 0.05).astype(np.float32))
+    for s in range(E):
+        if not identical:
+            w13 = torch.from_numpy((rng.standard_normal((2 * I, d)) * 0.05).astype(np.float32))
+            w2 = torch.from_numpy((rng.standard_normal((d, I)) * 0.05).astype(np.float32))
+        synth.fill_slot(bank, s, w13, w2)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    return w, bank, L, x
+
+
+def pin_layer_identical_experts(lib):
+    """All experts identical -> the layer equals one dense SwiGLU FFN of x (sum of weights is 1)."""
+    rng = np.random.default_rng(17)
+    for fmt in (0, 1, 2):
+        w, bank, L, x = _tiny_layer_inputs(rng, 12, 64, 6, 3, 64, fmt=fmt, identical=True)
+        r = oracle.layer(L, x, bank, np.arange(6, dtype=np.int32), 3, lib=lib)
+        w13, w2 = oracle.dequant_slot(bank, 0, lib=lib)
+        _, dense = oracle.swiglu_ffn(oracle.bf16_to_f32(x), w13, w2, lib=lib)
+        tol = 8 * 2.0 ** -24 * np.abs(dense).max()
+        assert np.abs(r["out"] - dense).max() <= tol, np.abs(r["out"] - dense).max()
+
+
+def pin_layer_float64(lib):
+    """Whole layer against a float64 numpy evaluation of the same definition (library matmuls,
+    numpy stable sort for the grouping) on fp32-decoded weights: rel-L2 <= 1e-5."""
+    rng = np.random.default_rng(18)
+    T, d, E, k, I = 20, 64, 6, 2, 32
+    w, bank, L, x = _tiny_layer_inputs(rng, T, d, E, k, I, fmt=0)
+    slot_of = np.array([2, -1, 0, 1, 5, 4], np.int32)     # expert 1 not resident
+    r = oracle.layer(L, x, bank, slot_of, k, shared_slot=3, lib=lib)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    W = [[a.astype(np.float64) for a in oracle.dequant_slot(bank, s, lib=lib)] for s in range(E)]
+
+    def ffn(xr, s):
+        w13, w2 = W[s]
+        g = xr @ w13[:I].T
+        return (g / (1 + np.exp(-g)) * (xr @ w13[I:].T)) @ w2.T
+
+    out = ffn(xf, 3)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -L[t].astype(np.float64)))[:k]
+        p = np.exp(L[t].astype(np.float64) - L[t].max())
+        wt = p[order] / p[order].sum()
+        for j, e in enumerate(order):
+            if slot_of[e] >= 0:
+                out[t] += wt[j] * ffn(xf[t:t + 1], slot_of[e])[0]
+        assert r["mask"][t] == sum(1 << j for j, e in enumerate(order) if slot_of[e] < 0)
+    assert np.linalg.norm(r["out"] - out) <= 1e-5 * np.linalg.norm(out)
+
+
+def pin_combine_cases(lib):
+    rng = np.random.default_rng(19)
+    T, d, E, k = 9, 32, 5, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    _, _, _, inv = oracle.permute(ids, E, lib=lib)
+    y = rng.standard_normal((T * k, d)).astype(np.float32)
+    ysh = rng.standard_normal((T, d)).astype(np.float32)
+    # nothing resident: out = y_shared, mask = all k bits
+    out, mask = oracle.combine(y, ysh, ids, w, inv, np.full(E, -1, np.int32), d, lib=lib)
+    assert np.array_equal(out, ysh) and (mask == (1 << k) - 1).all()
+    out, mask = oracle.combine(y, None, ids, w, inv, np.full(E, -1, np.int32), d, lib=lib)
+    assert (out == 0).all()
+    # everything resident: mask 0; one-hot k=1 with weight 1 returns y itself
+    _, mask = oracle.combine(y, None, ids, w, inv, np.arange(E, dtype=np.int32), d, lib=lib)
+    assert (mask == 0).all()
+    ids1 = ids[:, :1].copy()
+    _, _, _, inv1 = oracle.permute(ids1, E, lib=lib)
+    out, _ = oracle.combine(y[:T], None, ids1, np.ones((T, 1), np.float32), inv1,
+                            np.arange(E, dtype=np.int32), d, lib=lib)
+    assert np.array_equal(out, y[:T][inv1])
+    # weighted sum in float64 (two experts resident, one not)
+    slot_of = np.array([0, 1, -1, 3, 4], np.int32)
+    out, mask = oracle.combine(y, None, ids, w, inv, slot_of, d, lib=lib)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            if slot_of[ids[t, j]] >= 0:
+                ref[t] += float(w[t, j]) * y[inv[t * k + j]].astype(np.float64)
+        assert mask[t] == sum(1 << j for j in range(k) if slot_of[ids[t, j]] < 0)
+    assert np.abs(out - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max())
+
+
+ALL_PINS = [pin_route_bruteforce, pin_route_special_cases, pin_route_weights_float64, pin_permute,
+            pin_decoder_tables, pin_dequant_roundtrip, pin_dequant_layouts, pin_ffn_float64,
+            pin_layer_identical_experts, pin_layer_float64, pin_combine_cases]

@@ -1,0 +1,61 @@
+"""Planted mistakes in the oracle must trip at least one pin.
+
+Each case copies ftoracle.c, makes one plausible mistake (a dropped term, a wrong sign or index, a
+swapped operand), builds it with the oracle's own flags and runs every pin against it.  This runs on
+the CPU only; the planted copies live in a temporary directory.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ftoracle.c")
+
+MUTANTS = {
+    "route_ties_to_highest": ("if (best < 0 || L[e] > L[best]) best = e;", "if (best < 0 || L[e] >= L[best]) best = e;"),
+    "route_no_renormalise": ("wt[j] = (p[id[j]] / Z) / S;", "wt[j] = (p[id[j]] / Z);"),
+    "route_softmax_sign": ("p[e] = expf(L[e] - m);", "p[e] = expf(m - L[e]);"),
+    "permute_unstable": ("for (int f = 0; f < n; ++f)\n      if (ids[f] == e) {", "for (int f = n - 1; f >= 0; --f)\n      if (ids[f] == e) {"),
+    "permute_inclusive_offsets": ("offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
+    "permute_inv_dropped": ("inv[f] = pos;", "inv[f] = f;"),
+    "fp16_bias": ("v = ldexpf((float)(1024 + m), e - 25);", "v = ldexpf((float)(1024 + m), e - 24);"),
+    "e2m1_bias": ("ldexpf(1.0f + 0.5f * (float)m, e - 1)", "ldexpf(1.0f + 0.5f * (float)m, e)"),
+    "e2m1_subnormal": ("0.5f * (float)m : ldexpf", "1.0f * (float)m : ldexpf"),
+    "e4m3_subnormal": ("v = ldexpf((float)m, -9);", "v = ldexpf((float)m, -10);"),
+    "e4m3_nan": ("if (e == 15 && m == 7)", "if (e == 15 && m == 8)"),
+    "e8m0_bias": ("ldexpf(1.0f, (int)s - 127)", "ldexpf(1.0f, (int)s - 128)"),
+    "q4_offset": ("o[32 * b + i] = scale * (float)(lo - 8);", "o[32 * b + i] = scale * (float)(lo - 7);"),
+    "q4_nibble_order": ("o[32 * b + i + 16] = scale * (float)(hi - 8);", "o[32 * b + i + 16] = scale * (float)(lo - 8);"),
+    "mx_nibble_order": ("unsigned q = (j & 1) ? (c[j / 2] >> 4) : (c[j / 2] & 15);", "unsigned q = (j & 1) ? (c[j / 2] & 15) : (c[j / 2] >> 4);"),
+    "mx_scale_index": ("ora_e8m0_value(s[j / 32])", "ora_e8m0_value(s[j / 64])"),
+    "fp8_block_row": ("(size_t)(r / 128) * (K / 128)", "(size_t)(r % 2) * (K / 128)"),
+    "fp8_block_col": ("o[j] = s[j / 128] * ora_e4m3_value(c[j]);", "o[j] = s[0] * ora_e4m3_value(c[j]);"),
+    "silu_sign": ("hr[i] = g / (1.0f + expf(-g)) * u;", "hr[i] = g / (1.0f + expf(g)) * u;"),
+    "gate_up_swapped": ("const float* wg = w13 + (size_t)i * d;", "const float* wg = w13 + (size_t)(I + i) * d;"),
+    "down_transposed": ("acc = acc + hr[i] * wd[i];", "acc = acc + hr[i] * w2[(size_t)i * d + c % d];"),
+    "combine_no_weight": ("o[c] = o[c] + wj * yr[c];", "o[c] = o[c] + yr[c];"),
+    "combine_no_shared": ("o[c] = o[c] + ys[c];", "o[c] = o[c];"),
+    "mask_wrong_bit": ("bits |= 1u << j;", "bits |= 1u << (k - 1 - j);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site of {name} not found exactly once"
+    msrc = tmp_path / "ftoracle.c"
+    msrc.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *[f for f in oracle.CFLAGS if f != "-Werror"], str(msrc), "-o", str(so), "-lm"], check=True)
+    lib = oracle._load(str(so))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every pin"
