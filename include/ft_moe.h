@@ -1,0 +1,197 @@
+/*
+ * ft_moe.h -- C ABI of a Mixture-of-Experts layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the hot path of an edge MoE inference engine as described by the FreeToken
+ * pages:
+ *   [walk-through]  "深入FreeToken架构：从HTTP API到CUDA内核的本地MoE推理引擎全链路剖析"
+ *                   (yfxerp.com), sections 一 (request path: ... -> MoE expert dispatch ->
+ *                   kernels) and 五 "MoE 引擎" (expert FFNs held in per-format banks -- BF16,
+ *                   FP8 block, NVFP4, MXFP4, GGUF Q4_0 -- hot experts resident on the GPU,
+ *                   cold ones in host memory, run by a CPU path).
+ *   [article]       zuoshipin.com FreeToken article, sections "一句话看懂 FreeToken" (frequently
+ *                   used expert weights stay in GPU memory) and "为什么 MoE 模型适合做 CPU–GPU
+ *                   协同？" (each token activates only a few experts).
+ *   [summary]       "FreeToken：高效的边缘原生 MoE 服务与带宽自适应执行" (ai-feeds.com), section
+ *                   "方法" (decode-time expert caching, GPU/CPU placement per expert).
+ * The pages give no formulas; the layer computed here is the standard routed-expert layer:
+ * softmax router with top-k and renormalisation, token->expert permutation, SwiGLU expert FFN,
+ * weighted combine.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless the argument says "host".  The caller owns every
+ *     buffer (inputs, outputs and workspace); the library allocates nothing and keeps no device
+ *     state between calls.
+ *   - Calls validate their arguments on the host, then enqueue kernels on `stream` and return
+ *     without waiting: results are valid once the stream reaches that point.  No call
+ *     synchronises the device, so sequences of calls can be captured into a hipGraph.
+ *   - Status: FT_OK (0) or an FT_E_* code.  A non-OK call enqueues nothing and records a message
+ *     readable with ft_moe_last_error() on the same host thread.  No C++ exception crosses the ABI.
+ *   - Every device pointer must be 16-byte aligned; all arrays are dense and row-major.
+ *   - Limits: T >= 0 (T == 0 enqueues nothing), 1 <= E <= 1024, 1 <= k <= min(E, 32).
+ *   - Calls are reentrant; independent calls may run on different streams concurrently.
+ */
+#ifndef FT_MOE_H
+#define FT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FT_MOE_ABI_VERSION 1
+
+enum ft_status {
+  FT_OK = 0,
+  FT_E_INVAL = 1,        /* bad argument (null pointer, size out of range, misalignment) */
+  FT_E_UNSUPPORTED = 2,  /* valid request the library does not implement (format, shape) */
+  FT_E_WORKSPACE = 3,    /* workspace pointer missing or smaller than the size query asked */
+  FT_E_HIP = 4,          /* a HIP call or kernel launch failed; message has hipGetErrorString */
+  FT_E_INTERNAL = 5      /* unexpected internal failure */
+};
+
+/* Expert-bank formats ([walk-through] section 五 lists the bank formats). */
+enum ft_weight_format {
+  FT_W_BF16 = 0,      /* bf16 weights */
+  FT_W_Q4_0 = 1,      /* GGUF Q4_0: blocks of 32 int4 codes along K with one fp16 scale, v = s*(q-8) */
+  FT_W_MXFP4 = 2,     /* OCP MXFP4: e2m1 codes with one E8M0 scale per 32 along K, v = e2m1*2^(s-127) */
+  FT_W_FP8_B128 = 3   /* OCP e4m3fn codes with one fp32 scale per 128x128 (row, K) block, v = s*e4m3 */
+};
+
+/* ft_moe_grouped_ffn flags */
+#define FT_PATH_AUTO 0x0  /* per expert group: few tokens -> streaming GEMV, many -> MFMA GEMM */
+#define FT_PATH_GEMV 0x1  /* every group through the streaming GEMV kernels */
+#define FT_PATH_GEMM 0x2  /* every group through the MFMA GEMM kernels */
+#define FT_PATH_MASK 0x3
+
+/* ft_moe_combine flags */
+#define FT_OUT_BF16 0x4   /* write `out` as bf16 instead of fp32 */
+
+/*
+ * Expert bank in DEVICE layout (passed by host pointer; the struct itself is read on the host).
+ * Slot s holds one expert: W13 = [gate rows 0..I-1 ; up rows I..2I-1] of shape [2I][d] and
+ * W2 of shape [d][I] (the K dimension is contiguous in both).  Per format:
+ *   FT_W_BF16     w13 uint16 [n_slots][2I][d], w2 uint16 [n_slots][d][I]; s13 = s2 = NULL
+ *   FT_W_Q4_0     w13 uint8 [n_slots][2I][d/2], w2 uint8 [n_slots][d][I/2]: the 16 code bytes of each
+ *                 GGUF block in GGUF order (byte i: element i low nibble, element i+16 high nibble);
+ *                 s13 fp16 [n_slots][2I][d/32], s2 fp16 [n_slots][d][I/32].  ft_moe_pack_bank builds
+ *                 this from GGUF's 18-byte blocks.
+ *   FT_W_MXFP4    w13 uint8 [n_slots][2I][d/2] (element 2i low nibble, 2i+1 high), w2 uint8
+ *                 [n_slots][d][I/2]; s13 uint8 E8M0 [n_slots][2I][d/32], s2 [n_slots][d][I/32]
+ *   FT_W_FP8_B128 w13 uint8 [n_slots][2I][d], w2 uint8 [n_slots][d][I]; s13 fp32 [n_slots][2I/128][d/128],
+ *                 s2 fp32 [n_slots][d/128][I/128]
+ * Divisibility: d and I multiples of 8 (bf16), 32 (Q4_0, MXFP4) or 128 (FP8_B128).
+ */
+typedef struct ft_moe_bank {
+  int32_t fmt, n_slots, d, I;
+  const void* w13;
+  const void* w2;
+  const void* s13;
+  const void* s2;
+} ft_moe_bank;
+
+/* FT_MOE_ABI_VERSION of the built library. */
+int ft_moe_abi_version(void);
+
+/* Text of the last non-OK status on this host thread ("" if none).  Owned by the library. */
+const char* ft_moe_last_error(void);
+
+/*
+ * Router: top-k experts per token and their renormalised softmax weights.
+ *   logits fp32 [T][E]  ->  ids int32 [T][k], w fp32 [T][k]
+ * ids[t] lists the k largest logits of row t in descending order; equal logits are taken in
+ * ascending expert order (IEEE comparison, so -0.0 == +0.0).  w[t][j] = p_j / sum_i p_i with
+ * p_j = exp(logit_j - max logit) over the k chosen experts: the softmax over all E experts
+ * restricted to the chosen ones and renormalised (the normaliser over all E cancels).
+ * Logits must be finite or -inf; a row whose k chosen logits are all -inf gets NaN weights.
+ * Sparse activation of a few experts per token: [article] "为什么 MoE 模型适合做 CPU–GPU 协同？".
+ */
+int ft_moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream);
+
+/*
+ * Bytes of workspace ft_moe_permute needs for (T, E, k); 0 when none is needed.
+ */
+size_t ft_moe_permute_workspace(int T, int E, int k);
+
+/*
+ * Token -> expert permutation (the expert-dispatch stage of [walk-through] section 一).
+ *   ids int32 [T][k]  ->  counts int32 [E], offsets int32 [E+1], gather int32 [T*k], inv int32 [T*k]
+ * With flat index f = t*k + j: counts[e] = #{f : ids[f] == e}; offsets = exclusive prefix sum of
+ * counts (offsets[E] = T*k); gather[p] = f lists flat indices grouped by expert id ascending and,
+ * inside a group, by ascending f; inv[gather[p]] = p.  Every id must lie in [0, E).
+ * ws: device workspace of at least ft_moe_permute_workspace(T, E, k) bytes (may be NULL if 0).
+ */
+int ft_moe_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                   int32_t* gather, int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Bytes of workspace ft_moe_grouped_ffn needs.  `bank` is a host pointer.
+ */
+size_t ft_moe_grouped_ffn_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags);
+
+/*
+ * Grouped SwiGLU expert FFN over the resident experts ([walk-through] section 五: expert FFNs in
+ * per-format banks; hot experts resident on the GPU and found through a lookup table).
+ *   bank            host pointer to the bank description (device arrays inside)
+ *   slot_of_expert  int32 [E]: bank slot of each expert, -1 when the expert is not resident
+ *   shared_slot     bank slot of an always-on shared expert applied to every token, or -1
+ *   x               bf16 [T][d] activations
+ *   offsets, gather the permutation of ft_moe_permute for the same routing
+ *   y_sorted        bf16 [T*k][d]: row p = offsets[e] + i receives FFN_e(x[gather[p] / k]) for every
+ *                   resident expert e; rows of non-resident experts are not written
+ *   y_shared        bf16 [T][d]: FFN_shared(x[t]); required iff shared_slot >= 0, else NULL
+ * FFN_s(x) = (SiLU(x Wg^T) * (x Wu^T)) W2^T with Wg = W13[0:I], Wu = W13[I:2I], SiLU(g) = g/(1+e^-g);
+ * products accumulate in fp32; the intermediate h is rounded to bf16 once, y to bf16 once.
+ * flags: FT_PATH_* (which kernels run; results agree within rounding).
+ * ws: device workspace of at least ft_moe_grouped_ffn_workspace(...) bytes.
+ */
+int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
+                       const uint16_t* x, int T, int E, int k, const int32_t* offsets,
+                       const int32_t* gather, uint16_t* y_sorted, uint16_t* y_shared, void* ws,
+                       size_t ws_bytes, int flags, hipStream_t stream);
+
+/*
+ * Weighted combine back to token order, and the residual mask of non-resident experts
+ * ([walk-through] section 五: experts not resident on the GPU are left to another path).
+ *   out[t][c] = sum over j ascending with slot_of_expert[ids[t][j]] >= 0 of
+ *               w[t][j] * y_sorted[inv[t*k+j]][c]   (+ y_shared[t][c] when y_shared != NULL)
+ *   residual_mask[t] bit j = 1 iff expert ids[t][j] is not resident (may be NULL)
+ * Weights are not renormalised over the resident subset: the masked share belongs to the other
+ * path.  out is fp32 [T][d], or bf16 [T][d] with FT_OUT_BF16.
+ */
+int ft_moe_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids,
+                   const float* w, const int32_t* inv, const int32_t* slot_of_expert, int T, int E,
+                   int k, int d, void* out, uint32_t* residual_mask, int flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------ set-up calls */
+
+/*
+ * Bytes of one bank array in device layout: which = 0 w13, 1 w2, 2 s13, 3 s2 (0 if the format has
+ * no such array).  Returns 0 for an invalid request.
+ */
+size_t ft_moe_bank_bytes(int fmt, int n_slots, int d, int I, int which);
+
+/*
+ * Build a device-layout bank from canonical stored bytes (all device pointers).  Canonical is
+ * the device layout for BF16, MXFP4 and FP8_B128 (the call copies), and for Q4_0 GGUF's 18-byte
+ * blocks [n_slots][rows][K/32][18] (fp16 scale, then 16 code bytes) with canon_s13/canon_s2 NULL.
+ * `dst` is a host pointer to a bank whose arrays are already allocated (sizes from
+ * ft_moe_bank_bytes); its fmt/n_slots/d/I must match the arguments.
+ */
+int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, const void* canon_w2,
+                     const void* canon_s13, const void* canon_s2, const ft_moe_bank* dst,
+                     hipStream_t stream);
+
+/*
+ * Decode one bank matrix to fp32 with the same decode routine the FFN kernels use (for checking
+ * the dequantisation bit for bit).  which = 0: W13 of `slot` -> out fp32 [2I][d];
+ * which = 1: W2 of `slot` -> out fp32 [d][I].
+ */
+int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FT_MOE_H */

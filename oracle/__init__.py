@@ -199,12 +199,14 @@ def dequant_slot(bank, slot: int, lib=None):
 
 # ------------------------------------------------------------------------- the layer
 
-def layer(logits, x_bf16, bank, slot_of, k: int, shared_slot: int = -1, tokens=None, lib=None):
+def layer(logits, x_bf16, bank, slot_of, k: int, shared_slot: int = -1, tokens=None, lib=None, workers: int = 1):
     """One MoE layer, optionally only for a sample of tokens.
 
     Returns a dict with ids, w, counts, offsets, gather, inv (whole layer), and for the computed
     tokens: mask [T], out [T][d] (zero rows for tokens not computed), y_pos (sorted positions
     computed), y_rows fp32 [len(y_pos)][d], y_shared fp32 [T][d] or None.
+    `workers` > 1 runs independent expert groups on that many threads (the C calls release the
+    GIL); each group's arithmetic is unchanged.
     """
     lib = lib or _load()
     L = _np(logits, np.float32)
@@ -215,19 +217,29 @@ def layer(logits, x_bf16, bank, slot_of, k: int, shared_slot: int = -1, tokens=N
     counts, offsets, gather, inv = permute(ids, E, lib=lib)
     want = np.ones(T, bool) if tokens is None else np.isin(np.arange(T), np.asarray(tokens))
     xf = bf16_to_f32(x_bf16)
-    y_pos_all, y_rows_all = [], []
+    jobs = []
     for e in range(E):
         s = int(so[e])
         if s < 0 or counts[e] == 0:
             continue
         pos = np.arange(offsets[e], offsets[e + 1])
         pos = pos[want[gather[pos] // k]]
-        if len(pos) == 0:
-            continue
+        if len(pos):
+            jobs.append((s, pos))
+
+    def run(job):
+        s, pos = job
         w13, w2 = dequant_slot(bank, s, lib=lib)
-        _, y = swiglu_ffn(xf[gather[pos] // k], w13, w2, lib=lib)
-        y_pos_all.append(pos)
-        y_rows_all.append(y)
+        return swiglu_ffn(xf[gather[pos] // k], w13, w2, lib=lib)[1]
+
+    if workers > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            ys = list(ex.map(run, jobs))
+    else:
+        ys = [run(j) for j in jobs]
+    y_pos_all = [pos for _, pos in jobs]
+    y_rows_all = ys
     y_pos = np.concatenate(y_pos_all) if y_pos_all else np.zeros(0, np.int64)
     y_rows = np.concatenate(y_rows_all) if y_rows_all else np.zeros((0, d), np.float32)
     y_shared = None

@@ -1,0 +1,251 @@
+"""Python binding of libftmoe.so, the gfx950 HIP library of one Mixture-of-Experts layer.
+
+The functions below carry the C ABI's names (include/ft_moe.h) and only marshal arguments: torch
+tensors provide device memory and the current torch stream provides the HIP stream; every step of
+the layer runs in the library's HIP kernels.  Importing this package fails if the library has not
+been built (python -m routed_expert_ffn_wave_amd.build); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libftmoe.so")
+
+FT_OK, FT_E_INVAL, FT_E_UNSUPPORTED, FT_E_WORKSPACE, FT_E_HIP, FT_E_INTERNAL = range(6)
+FT_W_BF16, FT_W_Q4_0, FT_W_MXFP4, FT_W_FP8_B128 = range(4)
+FT_PATH_AUTO, FT_PATH_GEMV, FT_PATH_GEMM = 0, 1, 2
+FT_OUT_BF16 = 4
+
+STATUS_NAMES = {0: "FT_OK", 1: "FT_E_INVAL", 2: "FT_E_UNSUPPORTED", 3: "FT_E_WORKSPACE", 4: "FT_E_HIP",
+                5: "FT_E_INTERNAL"}
+
+
+class FtError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class ft_moe_bank(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m routed_expert_ffn_wave_amd.build`")
+    # torch is imported first so that the library binds to the HIP runtime torch already loaded
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    BP = ctypes.POINTER(ft_moe_bank)
+    sig = {
+        "ft_moe_abi_version": ([], i),
+        "ft_moe_last_error": ([], ctypes.c_char_p),
+        "ft_moe_route": ([P, i, i, i, P, P, P], i),
+        "ft_moe_permute_workspace": ([i, i, i], sz),
+        "ft_moe_permute": ([P, i, i, i, P, P, P, P, P, sz, P], i),
+        "ft_moe_grouped_ffn_workspace": ([BP, i, i, i, i, i], sz),
+        "ft_moe_grouped_ffn": ([BP, P, i, P, i, i, i, P, P, P, P, P, sz, i, P], i),
+        "ft_moe_combine": ([P, P, P, P, P, P, i, i, i, i, P, P, i, P], i),
+        "ft_moe_bank_bytes": ([i, i, i, i, i], sz),
+        "ft_moe_pack_bank": ([i, i, i, i, P, P, P, P, BP, P], i),
+        "ft_moe_dequant": ([BP, i, i, P, P], i),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_permute_workspace",
+            "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
+            "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != FT_OK:
+        raise FtError(rc, lib.ft_moe_last_error().decode())
+
+
+def ft_moe_abi_version() -> int:
+    return lib.ft_moe_abi_version()
+
+
+def ft_moe_last_error() -> str:
+    return lib.ft_moe_last_error().decode()
+
+
+# ------------------------------------------------------------------------------------- banks
+
+class DeviceBank:
+    """Device-layout expert bank: torch tensors that own the arrays, plus the C description."""
+
+    def __init__(self, fmt: int, n_slots: int, d: int, I: int, w13, w2, s13=None, s2=None):
+        self.fmt, self.n_slots, self.d, self.I = fmt, n_slots, d, I
+        self.w13, self.w2, self.s13, self.s2 = w13, w2, s13, s2
+        self.desc = ft_moe_bank(fmt, n_slots, d, I, w13.data_ptr(), w2.data_ptr(),
+                                None if s13 is None else s13.data_ptr(), None if s2 is None else s2.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.w13, self.w2, self.s13, self.s2) if t is not None)
+
+    @staticmethod
+    def empty(fmt: int, n_slots: int, d: int, I: int, device="cuda") -> "DeviceBank":
+        arrs = []
+        for which in range(4):
+            n = lib.ft_moe_bank_bytes(fmt, n_slots, d, I, which)
+            if n == 0 and which < 2:
+                raise FtError(FT_E_INVAL, f"invalid bank shape fmt={fmt} n_slots={n_slots} d={d} I={I}")
+            arrs.append(torch.empty(n, dtype=torch.uint8, device=device) if n else None)
+        return DeviceBank(fmt, n_slots, d, I, *arrs)
+
+
+def ft_moe_bank_bytes(fmt: int, n_slots: int, d: int, I: int, which: int) -> int:
+    return lib.ft_moe_bank_bytes(fmt, n_slots, d, I, which)
+
+
+def ft_moe_pack_bank(fmt: int, n_slots: int, d: int, I: int, canon_w13, canon_w2, canon_s13=None, canon_s2=None,
+                     dst: DeviceBank | None = None, stream=None) -> DeviceBank:
+    dst = DeviceBank.empty(fmt, n_slots, d, I, device=canon_w13.device) if dst is None else dst
+    _check(lib.ft_moe_pack_bank(fmt, n_slots, d, I, _ptr(canon_w13), _ptr(canon_w2), _ptr(canon_s13),
+                                _ptr(canon_s2), dst.ref, _stream(stream)))
+    return dst
+
+
+def ft_moe_dequant(bank: DeviceBank, slot: int, which: int, out=None, stream=None) -> torch.Tensor:
+    rows, K = (2 * bank.I, bank.d) if which == 0 else (bank.d, bank.I)
+    out = torch.empty(rows, K, dtype=torch.float32, device=bank.w13.device) if out is None else out
+    _check(lib.ft_moe_dequant(bank.ref, slot, which, _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------- the four calls
+
+def ft_moe_route(logits: torch.Tensor, k: int, ids=None, w=None, stream=None):
+    T, E = logits.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device) if ids is None else ids
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device) if w is None else w
+    _check(lib.ft_moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def ft_moe_permute_workspace(T: int, E: int, k: int) -> int:
+    return lib.ft_moe_permute_workspace(T, E, k)
+
+
+def ft_moe_permute(ids: torch.Tensor, E: int, counts=None, offsets=None, gather=None, inv=None, ws=None, stream=None):
+    T, k = ids.shape
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    gather = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev) if gather is None else gather
+    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev) if inv is None else inv
+    need = lib.ft_moe_permute_workspace(T, E, k)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.ft_moe_permute(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets), _ptr(gather), _ptr(inv), _ptr(ws),
+                              ws_bytes, _stream(stream)))
+    return counts, offsets, gather[: T * k], inv[: T * k]
+
+
+def ft_moe_grouped_ffn_workspace(bank: DeviceBank, T: int, E: int, k: int, shared_slot: int = -1, flags: int = 0) -> int:
+    return lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
+
+
+def ft_moe_grouped_ffn(bank: DeviceBank, slot_of_expert, x, k: int, offsets, gather, shared_slot: int = -1,
+                       y_sorted=None, y_shared=None, ws=None, flags: int = FT_PATH_AUTO, stream=None):
+    T, d = x.shape
+    E = slot_of_expert.shape[0]
+    dev = x.device
+    y_sorted = torch.empty(max(T * k, 1), d, dtype=torch.bfloat16, device=dev) if y_sorted is None else y_sorted
+    if shared_slot >= 0 and y_shared is None:
+        y_shared = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    need = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib.ft_moe_grouped_ffn(bank.ref, _ptr(slot_of_expert), shared_slot, _ptr(x), T, E, k, _ptr(offsets),
+                                  _ptr(gather), _ptr(y_sorted), _ptr(y_shared if shared_slot >= 0 else None),
+                                  _ptr(ws), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return y_sorted[: T * k], (y_shared if shared_slot >= 0 else None)
+
+
+def ft_moe_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, d: int, out=None, residual_mask=None,
+                   flags: int = 0, want_mask: bool = True, stream=None):
+    T, k = ids.shape
+    E = slot_of_expert.shape[0]
+    dev = ids.device
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16 if flags & FT_OUT_BF16 else torch.float32, device=dev)
+    if residual_mask is None and want_mask:
+        residual_mask = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    _check(lib.ft_moe_combine(_ptr(y_sorted), _ptr(y_shared), _ptr(ids), _ptr(w), _ptr(inv), _ptr(slot_of_expert), T,
+                              E, k, d, _ptr(out), _ptr(residual_mask), flags, _stream(stream)))
+    return out, (None if residual_mask is None else residual_mask[:T])
+
+
+# ------------------------------------------------------------------------------------- one layer
+
+class MoELayer:
+    """One MoE layer over a device bank with every buffer preallocated for a fixed (T, k).
+
+    forward() enqueues the four calls on the current stream and allocates nothing, so it can be
+    replayed in a loop or captured into a CUDA/HIP graph by the caller."""
+
+    def __init__(self, bank: DeviceBank, slot_of_expert: torch.Tensor, k: int, T: int, shared_slot: int = -1,
+                 flags: int = FT_PATH_AUTO, out_bf16: bool = False):
+        dev = bank.w13.device
+        E = slot_of_expert.shape[0]
+        self.bank, self.slot_of, self.k, self.T, self.E = bank, slot_of_expert, k, T, E
+        self.shared_slot, self.flags, self.out_flags = shared_slot, flags, FT_OUT_BF16 if out_bf16 else 0
+        d = bank.d
+        n = max(T * k, 1)
+        self.ids = torch.empty(max(T, 1), k, dtype=torch.int32, device=dev)
+        self.w = torch.empty(max(T, 1), k, dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.gather = torch.empty(n, dtype=torch.int32, device=dev)
+        self.inv = torch.empty(n, dtype=torch.int32, device=dev)
+        pws = lib.ft_moe_permute_workspace(T, E, k)
+        self.perm_ws = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
+        self.y_sorted = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+        self.y_shared = torch.empty(max(T, 1), d, dtype=torch.bfloat16, device=dev) if shared_slot >= 0 else None
+        fws = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
+        self.ffn_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(max(T, 1), d, dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
+        self.mask = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, stream=None):
+        T, E, k = self.T, self.E, self.k
+        s = _stream(stream)
+        _check(lib.ft_moe_route(_ptr(logits), T, E, k, _ptr(self.ids), _ptr(self.w), s))
+        _check(lib.ft_moe_permute(_ptr(self.ids), T, E, k, _ptr(self.counts), _ptr(self.offsets), _ptr(self.gather),
+                                  _ptr(self.inv), _ptr(self.perm_ws), self.perm_ws.numel(), s))
+        _check(lib.ft_moe_grouped_ffn(self.bank.ref, _ptr(self.slot_of), self.shared_slot, _ptr(x), T, E, k,
+                                      _ptr(self.offsets), _ptr(self.gather), _ptr(self.y_sorted), _ptr(self.y_shared),
+                                      _ptr(self.ffn_ws), self.ffn_ws.numel(), self.flags, s))
+        _check(lib.ft_moe_combine(_ptr(self.y_sorted), _ptr(self.y_shared), _ptr(self.ids), _ptr(self.w),
+                                  _ptr(self.inv), _ptr(self.slot_of), T, E, k, self.bank.d, _ptr(self.out),
+                                  _ptr(self.mask), self.out_flags, s))
+        return self.out[:T], self.mask[:T]

@@ -1,0 +1,370 @@
+// C ABI of the MoE layer (declared in include/ft_moe.h): host-side validation, workspace sizing,
+// path selection and kernel launches on the caller's stream.  No call allocates, synchronises or
+// throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+
+#include "../../include/ft_moe.h"
+#include "ft_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return FT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define CHECK_PTR(p, name) \
+  do {                                                               \
+    if ((p) == nullptr) return fail(FT_E_INVAL, "%s is null", name); \
+    if (!aligned16(p)) return fail(FT_E_INVAL, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+int check_tek(int T, int E, int k) {
+  REQUIRE(T >= 0, FT_E_INVAL, "T must be >= 0 (got %d)", T);
+  REQUIRE(E >= 1 && E <= 1024, FT_E_INVAL, "E must be in [1, 1024] (got %d)", E);
+  REQUIRE(k >= 1 && k <= E && k <= 32, FT_E_INVAL, "k must be in [1, min(E, 32)] (got k=%d, E=%d)", k, E);
+  REQUIRE((long long)T * k <= (1LL << 30), FT_E_INVAL, "T*k too large (%lld)", (long long)T * k);
+  return FT_OK;
+}
+
+
+int check_bank_shape(int fmt, int n_slots, int d, int I) {
+  REQUIRE(fmt >= FT_W_BF16 && fmt <= FT_W_FP8_B128, FT_E_UNSUPPORTED, "unknown weight format %d", fmt);
+  REQUIRE(n_slots >= 1, FT_E_INVAL, "n_slots must be >= 1 (got %d)", n_slots);
+  REQUIRE(d > 0 && I > 0, FT_E_INVAL, "d and I must be positive (got d=%d, I=%d)", d, I);
+  const int m = fmt == FT_W_BF16 ? 8 : fmt == FT_W_FP8_B128 ? 128 : 32;
+  REQUIRE(d % m == 0 && I % m == 0, FT_E_INVAL, "format %d needs d and I to be multiples of %d (got d=%d, I=%d)",
+          fmt, m, d, I);
+  REQUIRE((long long)d * I <= (1LL << 31), FT_E_INVAL, "d*I too large");
+  return FT_OK;
+}
+
+int check_bank(const ft_moe_bank* b) {
+  REQUIRE(b != nullptr, FT_E_INVAL, "bank is null");
+  int rc = check_bank_shape(b->fmt, b->n_slots, b->d, b->I);
+  if (rc) return rc;
+  CHECK_PTR(b->w13, "bank->w13");
+  CHECK_PTR(b->w2, "bank->w2");
+  if (b->fmt != FT_W_BF16) {
+    REQUIRE(b->s13 != nullptr && b->s2 != nullptr, FT_E_INVAL, "format %d needs scale arrays s13 and s2", b->fmt);
+    REQUIRE(aligned16(b->s13) && aligned16(b->s2), FT_E_INVAL, "bank scale arrays must be 16-byte aligned");
+  }
+  return FT_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// groups with at most this many routed rows go through the GEMV kernels when the path is automatic
+constexpr int kGemvMaxRows = 2 * ftk::GEMV_NT;
+
+bool gemm_shape_ok(int d, int I) { return I % 64 == 0 && d % 128 == 0; }
+
+size_t h_bytes(int T, int k, int I, bool shared) {
+  return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ft_moe_abi_version(void) { return FT_MOE_ABI_VERSION; }
+
+const char* ft_moe_last_error(void) { return g_err; }
+
+int ft_moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    if (T == 0) return ok();
+    CHECK_PTR(logits, "logits");
+    CHECK_PTR(ids, "ids");
+    CHECK_PTR(w, "w");
+    return hip_status(ftk::launch_route(logits, T, E, k, ids, w, stream), "ft_moe_route launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_route: unexpected exception");
+  }
+}
+
+size_t ft_moe_permute_workspace(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 32) return 0;
+  return ftk::permute_workspace_bytes(T, E, k);
+}
+
+int ft_moe_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* gather,
+                   int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    CHECK_PTR(counts, "counts");
+    CHECK_PTR(offsets, "offsets");
+    if (T > 0) {
+      CHECK_PTR(ids, "ids");
+      CHECK_PTR(gather, "gather");
+      CHECK_PTR(inv, "inv");
+    }
+    const size_t need = ftk::permute_workspace_bytes(T, E, k);
+    if (need) {
+      REQUIRE(ws != nullptr && ws_bytes >= need, FT_E_WORKSPACE, "permute needs %zu bytes of workspace (got %zu%s)",
+              need, ws_bytes, ws ? "" : ", null pointer");
+      REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
+    }
+    // T == 0 still defines counts = 0 and offsets = 0: the small kernel handles n = 0.
+    return hip_status(ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, ws, stream),
+                      "ft_moe_permute launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_permute: unexpected exception");
+  }
+}
+
+size_t ft_moe_grouped_ffn_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
+  (void)E;
+  (void)flags;
+  if (!bank || T < 0 || k < 1) return 0;
+  return h_bytes(T, k, bank->I, shared_slot >= 0);
+}
+
+int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
+                       int T, int E, int k, const int32_t* offsets, const int32_t* gather, uint16_t* y_sorted,
+                       uint16_t* y_shared, void* ws, size_t ws_bytes, int flags, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    rc = check_bank(bank);
+    if (rc) return rc;
+    REQUIRE((flags & ~FT_PATH_MASK) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+    const int path = flags & FT_PATH_MASK;
+    REQUIRE(path != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
+    REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
+            shared_slot, bank->n_slots);
+    REQUIRE((shared_slot >= 0) == (y_shared != nullptr), FT_E_INVAL,
+            "y_shared must be given exactly when shared_slot >= 0");
+    const bool gemm_ok = gemm_shape_ok(bank->d, bank->I);
+    REQUIRE(path != FT_PATH_GEMM || gemm_ok, FT_E_UNSUPPORTED,
+            "the GEMM path needs I %% 64 == 0 and d %% 128 == 0 (got d=%d, I=%d)", bank->d, bank->I);
+    if (T == 0) return ok();
+    CHECK_PTR(slot_of_expert, "slot_of_expert");
+    CHECK_PTR(x, "x");
+    CHECK_PTR(offsets, "offsets");
+    CHECK_PTR(gather, "gather");
+    CHECK_PTR(y_sorted, "y_sorted");
+    if (y_shared) CHECK_PTR(y_shared, "y_shared");
+    const bool shared = shared_slot >= 0;
+    const size_t need = h_bytes(T, k, bank->I, shared);
+    REQUIRE(ws != nullptr && ws_bytes >= need, FT_E_WORKSPACE, "grouped_ffn needs %zu bytes of workspace (got %zu%s)",
+            need, ws_bytes, ws ? "" : ", null pointer");
+    REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
+
+    ftk::FfnArgs a{};
+    a.fmt = bank->fmt;
+    a.d = bank->d;
+    a.I = bank->I;
+    a.n_slots = bank->n_slots;
+    a.w13 = (const uint8_t*)bank->w13;
+    a.w2 = (const uint8_t*)bank->w2;
+    a.s13 = (const uint8_t*)bank->s13;
+    a.s2 = (const uint8_t*)bank->s2;
+    a.slot_of = slot_of_expert;
+    a.shared_slot = shared_slot;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.offsets = offsets;
+    a.gather = gather;
+    a.h = (uint16_t*)ws;
+    a.y_sorted = y_sorted;
+    a.y_shared = y_shared;
+
+    // Which groups each kernel family takes (by routed-row count).  A group never has more than
+    // T rows (top-k ids of a token are distinct); the shared group has exactly T.
+    const long long TK = (long long)T * k;
+    const long long rows_total = TK + (shared ? T : 0);
+    const long long groups_upper = (long long)(E < TK ? E : TK) + (shared ? 1 : 0);
+    int gemv_max, gemm_min;
+    if (path == FT_PATH_GEMV || (path == FT_PATH_AUTO && !gemm_ok)) {
+      gemv_max = 0x7fffffff;
+      gemm_min = 0x7fffffff;
+    } else if (path == FT_PATH_GEMM) {
+      gemv_max = 0;
+      gemm_min = 1;
+    } else {
+      gemv_max = kGemvMaxRows;
+      gemm_min = kGemvMaxRows + 1;
+    }
+    const int NT = ftk::GEMV_NT, BM = ftk::GEMM_BM;
+    const bool run_gemv = gemv_max > 0;
+    const bool run_gemm = gemm_min <= T;  // no group has more than T rows
+    long long gemv_chunks = 0, gemm_tiles = 0;
+    if (run_gemv) {
+      const long long per_group = (gemv_max >= T) ? (T + NT - 1) / NT : (gemv_max + NT - 1) / NT;
+      const long long a1 = groups_upper * per_group;
+      const long long a2 = (rows_total + NT - 1) / NT + groups_upper;
+      gemv_chunks = a1 < a2 ? a1 : a2;
+    }
+    if (run_gemm) {
+      const long long big_upper = rows_total / gemm_min + 1;
+      const long long g_up = big_upper < groups_upper ? big_upper : groups_upper;
+      gemm_tiles = (rows_total + BM - 1) / BM + g_up;
+    }
+    hipError_t e = hipSuccess;
+    if (run_gemv) {
+      a.min_cnt = 1;
+      a.max_cnt = gemv_max;
+      e = ftk::launch_gemv_gateup(a, (int)gemv_chunks, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv gate/up launch");
+    }
+    if (run_gemm) {
+      a.min_cnt = gemm_min;
+      a.max_cnt = 0x7fffffff;
+      e = ftk::launch_gemm_gateup(a, (int)gemm_tiles, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm gate/up launch");
+    }
+    if (run_gemv) {
+      a.min_cnt = 1;
+      a.max_cnt = gemv_max;
+      e = ftk::launch_gemv_down(a, (int)gemv_chunks, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv down launch");
+    }
+    if (run_gemm) {
+      a.min_cnt = gemm_min;
+      a.max_cnt = 0x7fffffff;
+      e = ftk::launch_gemm_down(a, (int)gemm_tiles, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm down launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_grouped_ffn: unexpected exception");
+  }
+}
+
+int ft_moe_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids, const float* w,
+                   const int32_t* inv, const int32_t* slot_of_expert, int T, int E, int k, int d, void* out,
+                   uint32_t* residual_mask, int flags, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    REQUIRE(d > 0 && d % 8 == 0, FT_E_INVAL, "d must be a positive multiple of 8 (got %d)", d);
+    REQUIRE((flags & ~FT_OUT_BF16) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return ok();
+    CHECK_PTR(y_sorted, "y_sorted");
+    if (y_shared) CHECK_PTR(y_shared, "y_shared");
+    CHECK_PTR(ids, "ids");
+    CHECK_PTR(w, "w");
+    CHECK_PTR(inv, "inv");
+    CHECK_PTR(slot_of_expert, "slot_of_expert");
+    CHECK_PTR(out, "out");
+    if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
+    return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, T, E, k, d, out, residual_mask,
+                                          (flags & FT_OUT_BF16) != 0, stream),
+                      "ft_moe_combine launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_combine: unexpected exception");
+  }
+}
+
+size_t ft_moe_bank_bytes(int fmt, int n_slots, int d, int I, int which) {
+  if (check_bank_shape(fmt, n_slots, d, I) != FT_OK || which < 0 || which > 3) {
+    g_err[0] = 0;
+    return 0;
+  }
+  const size_t n = (size_t)n_slots, r13 = 2 * (size_t)I, r2 = (size_t)d;
+  const size_t K13 = (size_t)d, K2 = (size_t)I;
+  switch (fmt) {
+    case FT_W_BF16:
+      return which == 0 ? n * r13 * K13 * 2 : which == 1 ? n * r2 * K2 * 2 : 0;
+    case FT_W_Q4_0:
+      return which == 0 ? n * r13 * K13 / 2 : which == 1 ? n * r2 * K2 / 2 : which == 2 ? n * r13 * (K13 / 32) * 2
+                                                                                       : n * r2 * (K2 / 32) * 2;
+    case FT_W_MXFP4:
+      return which == 0 ? n * r13 * K13 / 2 : which == 1 ? n * r2 * K2 / 2 : which == 2 ? n * r13 * (K13 / 32)
+                                                                                       : n * r2 * (K2 / 32);
+    default:
+      return which == 0 ? n * r13 * K13 : which == 1 ? n * r2 * K2 : which == 2 ? n * (r13 / 128) * (K13 / 128) * 4
+                                                                               : n * (r2 / 128) * (K2 / 128) * 4;
+  }
+}
+
+int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, const void* canon_w2,
+                     const void* canon_s13, const void* canon_s2, const ft_moe_bank* dst, hipStream_t stream) {
+  try {
+    int rc = check_bank_shape(fmt, n_slots, d, I);
+    if (rc) return rc;
+    rc = check_bank(dst);
+    if (rc) return rc;
+    REQUIRE(dst->fmt == fmt && dst->n_slots == n_slots && dst->d == d && dst->I == I, FT_E_INVAL,
+            "dst bank description does not match (fmt, n_slots, d, I)");
+    REQUIRE(canon_w13 != nullptr && canon_w2 != nullptr, FT_E_INVAL, "canonical weight arrays are null");
+    if (fmt == FT_W_Q4_0) {
+      REQUIRE(((uintptr_t)canon_w13 & 1u) == 0 && ((uintptr_t)canon_w2 & 1u) == 0, FT_E_INVAL,
+              "canonical Q4_0 arrays must be 2-byte aligned");
+      const long long nb13 = (long long)n_slots * 2 * I * (d / 32), nb2 = (long long)n_slots * d * (I / 32);
+      hipError_t e = ftk::launch_pack_q4_0((const uint8_t*)canon_w13, (uint8_t*)dst->w13, (uint16_t*)dst->s13, nb13,
+                                           stream);
+      if (e == hipSuccess)
+        e = ftk::launch_pack_q4_0((const uint8_t*)canon_w2, (uint8_t*)dst->w2, (uint16_t*)dst->s2, nb2, stream);
+      return hip_status(e, "ft_moe_pack_bank (Q4_0) launch");
+    }
+    if (fmt != FT_W_BF16)
+      REQUIRE(canon_s13 != nullptr && canon_s2 != nullptr, FT_E_INVAL, "canonical scale arrays are null");
+    const void* src[4] = {canon_w13, canon_w2, canon_s13, canon_s2};
+    void* dstp[4] = {(void*)dst->w13, (void*)dst->w2, (void*)dst->s13, (void*)dst->s2};
+    for (int i = 0; i < 4; ++i) {
+      const size_t n = ft_moe_bank_bytes(fmt, n_slots, d, I, i);
+      if (n == 0) continue;
+      hipError_t e = hipMemcpyAsync(dstp[i], src[i], n, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return hip_status(e, "ft_moe_pack_bank copy");
+    }
+    return ok();
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_pack_bank: unexpected exception");
+  }
+}
+
+int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hipStream_t stream) {
+  try {
+    int rc = check_bank(bank);
+    if (rc) return rc;
+    REQUIRE(slot >= 0 && slot < bank->n_slots, FT_E_INVAL, "slot %d out of range [0, %d)", slot, bank->n_slots);
+    REQUIRE(which == 0 || which == 1, FT_E_INVAL, "which must be 0 (W13) or 1 (W2), got %d", which);
+    CHECK_PTR(out, "out");
+    const int rows = which == 0 ? 2 * bank->I : bank->d;
+    const int K = which == 0 ? bank->d : bank->I;
+    const size_t per_slot = ft_moe_bank_bytes(bank->fmt, 1, bank->d, bank->I, which);
+    const size_t per_slot_s = ft_moe_bank_bytes(bank->fmt, 1, bank->d, bank->I, which + 2);
+    const uint8_t* codes = (const uint8_t*)(which == 0 ? bank->w13 : bank->w2) + per_slot * slot;
+    const uint8_t* scales = nullptr;
+    if (bank->fmt != FT_W_BF16) scales = (const uint8_t*)(which == 0 ? bank->s13 : bank->s2) + per_slot_s * slot;
+    return hip_status(ftk::launch_dequant(bank->fmt, codes, scales, rows, K, out, stream), "ft_moe_dequant launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_dequant: unexpected exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ftk {
+
+// Everything the grouped FFN kernels read or write, in device memory.
+struct FfnArgs {
+  int fmt, d, I, n_slots;
+  const uint8_t* w13;  // bank arrays (device layout of the public header)
+  const uint8_t* w2;
+  const uint8_t* s13;
+  const uint8_t* s2;
+  const int32_t* slot_of;
+  int shared_slot;
+  const uint16_t* x;   // bf16 [T][d]
+  int T, E, k;
+  const int32_t* offsets;
+  const int32_t* gather;
+  uint16_t* h;         // bf16 [T*k + T][I] workspace (rows T*k.. for the shared expert)
+  uint16_t* y_sorted;  // bf16 [T*k][d]
+  uint16_t* y_shared;  // bf16 [T][d] or null
+  int min_cnt, max_cnt;  // groups this launch handles, by routed-row count
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+size_t permute_workspace_bytes(int T, int E, int k);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids, const float* w,
+                          const int32_t* inv, const int32_t* slot_of, int T, int E, int k, int d, void* out,
+                          uint32_t* mask, bool out_bf16, hipStream_t s);
+
+// Streaming GEMV path (few rows per group).  max_rows_upper: host-side bound on the number of
+// (group, token-chunk) pairs, used to size the grid.
+constexpr int GEMV_NT = 8;  // tokens per pass over the weights
+hipError_t launch_gemv_gateup(const FfnArgs& a, int chunks_upper, hipStream_t s);
+hipError_t launch_gemv_down(const FfnArgs& a, int chunks_upper, hipStream_t s);
+
+// MFMA GEMM path.
+hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s);
+hipError_t launch_gemm_down(const FfnArgs& a, int tiles_upper, hipStream_t s);
+constexpr int GEMM_BM = 128;  // token rows per tile
+
+hipError_t launch_pack_q4_0(const uint8_t* canon, uint8_t* codes, uint16_t* scales, long long nblocks,
+                            hipStream_t s);
+hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, float* out,
+                          hipStream_t s);
+
+}  // namespace ftk

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol the header
+declares, sizes its buffers, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import routed_expert_ffn_wave_amd as ft
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ft_moe.h")
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails before any use
+B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)    # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(ft_moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 11, names
+    out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(names) == set(ft.EXPORTED)
+    for n in names:
+        getattr(ft.lib, n)
+
+
+def test_abi_version():
+    assert ft.ft_moe_abi_version() == 1
+    m = re.search(r"#define FT_MOE_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == 1
+
+
+def _err(rc, code, pattern):
+    assert rc == code, (rc, ft.ft_moe_last_error())
+    assert re.search(pattern, ft.ft_moe_last_error()), ft.ft_moe_last_error()
+
+
+def test_route_validation():
+    L = ft.lib
+    _err(L.ft_moe_route(A, 4, 8, 0, B, B, None), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_route(A, 4, 8, 9, B, B, None), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_route(A, 4, 64, 33, B, B, None), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_route(A, 4, 0, 1, B, B, None), ft.FT_E_INVAL, "E must be")
+    _err(L.ft_moe_route(A, 4, 1025, 1, B, B, None), ft.FT_E_INVAL, "E must be")
+    _err(L.ft_moe_route(A, -1, 8, 2, B, B, None), ft.FT_E_INVAL, "T must be")
+    _err(L.ft_moe_route(None, 4, 8, 2, B, B, None), ft.FT_E_INVAL, "logits is null")
+    _err(L.ft_moe_route(A, 4, 8, 2, None, B, None), ft.FT_E_INVAL, "ids is null")
+    _err(L.ft_moe_route(MIS, 4, 8, 2, B, B, None), ft.FT_E_INVAL, "logits is not 16-byte aligned")
+    # T == 0 is a no-op that succeeds without touching any pointer
+    assert L.ft_moe_route(None, 0, 8, 2, None, None, None) == ft.FT_OK
+    assert ft.ft_moe_last_error() == ""
+
+
+def test_permute_validation_and_workspace():
+    L = ft.lib
+    assert L.ft_moe_permute_workspace(8, 128, 8) == 0           # single-block path
+    assert L.ft_moe_permute_workspace(2048, 128, 8) == 0        # 16384 entries: still one block
+    assert L.ft_moe_permute_workspace(4096, 128, 8) == 32 * 128 * 4
+    assert L.ft_moe_permute_workspace(16384, 256, 8) == 128 * 256 * 4
+    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, None, 0, None), ft.FT_E_WORKSPACE, "needs 16384 bytes")
+    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, A, 100, None), ft.FT_E_WORKSPACE, "needs")
+    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, MIS, 1 << 20, None), ft.FT_E_INVAL, "ws is not")
+    _err(L.ft_moe_permute(A, 4, 8, 2, None, B, B, B, None, 0, None), ft.FT_E_INVAL, "counts is null")
+    _err(L.ft_moe_permute(None, 4, 8, 2, B, B, B, B, None, 0, None), ft.FT_E_INVAL, "ids is null")
+    _err(L.ft_moe_permute(A, 4, 8, 2, B, B, MIS, B, None, 0, None), ft.FT_E_INVAL, "gather is not")
+
+
+def _bank(fmt=ft.FT_W_Q4_0, n=8, d=256, I=512, s=True):
+    return ft.ft_moe_bank(fmt, n, d, I, A.value, B.value, A.value if s else None, B.value if s else None)
+
+
+def test_bank_bytes():
+    L = ft.lib
+    d, I, n = 2048, 768, 128
+    assert L.ft_moe_bank_bytes(ft.FT_W_BF16, n, d, I, 0) == n * 2 * I * d * 2
+    assert L.ft_moe_bank_bytes(ft.FT_W_BF16, n, d, I, 2) == 0
+    assert L.ft_moe_bank_bytes(ft.FT_W_Q4_0, n, d, I, 0) == n * 2 * I * d // 2
+    assert L.ft_moe_bank_bytes(ft.FT_W_Q4_0, n, d, I, 3) == n * d * (I // 32) * 2
+    assert L.ft_moe_bank_bytes(ft.FT_W_MXFP4, n, d, I, 2) == n * 2 * I * (d // 32)
+    assert L.ft_moe_bank_bytes(ft.FT_W_FP8_B128, 96, 7168, 2048, 2) == 96 * 32 * 56 * 4
+    assert L.ft_moe_bank_bytes(ft.FT_W_FP8_B128, 96, 7168, 2000, 0) == 0     # I not a multiple of 128
+    assert L.ft_moe_bank_bytes(7, 1, 256, 256, 0) == 0
+    # per-weight cost of each format: 2, 18/32, 17/32, 1 + 4/16384 bytes
+    for fmt, bpw in ((0, 2.0), (1, 18 / 32), (2, 17 / 32), (3, 1 + 4 / 16384)):
+        tot = sum(L.ft_moe_bank_bytes(fmt, 1, 7168, 2048, w) for w in range(4))
+        assert tot == pytest.approx(3 * 7168 * 2048 * bpw, rel=1e-12)
+
+
+def test_grouped_ffn_validation():
+    L = ft.lib
+    b = _bank()
+    ws = 1 << 20
+    call = lambda **kw: L.ft_moe_grouped_ffn(
+        kw.get("bank", ctypes.byref(b)), kw.get("slot", A), kw.get("shared", -1), kw.get("x", A), kw.get("T", 16),
+        kw.get("E", 8), kw.get("k", 2), kw.get("off", A), kw.get("gather", A), kw.get("y", A), kw.get("ysh", None),
+        kw.get("ws", A), kw.get("ws_bytes", ws), kw.get("flags", 0), None)
+    _err(call(bank=None), ft.FT_E_INVAL, "bank is null")
+    _err(call(ws_bytes=10), ft.FT_E_WORKSPACE, "needs")
+    _err(call(ws=None), ft.FT_E_WORKSPACE, "null pointer")
+    _err(call(flags=3), ft.FT_E_INVAL, "exclusive")
+    _err(call(flags=8), ft.FT_E_INVAL, "unknown flags")
+    _err(call(shared=8), ft.FT_E_INVAL, "shared_slot")
+    _err(call(shared=3), ft.FT_E_INVAL, "y_shared")
+    _err(call(ysh=B), ft.FT_E_INVAL, "y_shared")
+    _err(call(x=None), ft.FT_E_INVAL, "x is null")
+    _err(call(x=MIS), ft.FT_E_INVAL, "x is not 16-byte aligned")
+    _err(call(k=3, E=2), ft.FT_E_INVAL, "k must be")
+    nob = _bank(s=False)
+    _err(call(bank=ctypes.byref(nob)), ft.FT_E_INVAL, "scale arrays")
+    bad = _bank(fmt=9)
+    _err(call(bank=ctypes.byref(bad)), ft.FT_E_UNSUPPORTED, "unknown weight format")
+    odd = _bank(d=48)
+    _err(call(bank=ctypes.byref(odd)), ft.FT_E_INVAL, "multiples of 32")
+    fp8 = _bank(fmt=ft.FT_W_FP8_B128, d=256, I=64)
+    _err(call(bank=ctypes.byref(fp8)), ft.FT_E_INVAL, "multiples of 128")
+    # the MFMA path needs I % 64 == 0 and d % 128 == 0
+    b96 = _bank(fmt=ft.FT_W_BF16, d=96, I=64, s=False)
+    _err(call(bank=ctypes.byref(b96), flags=ft.FT_PATH_GEMM), ft.FT_E_UNSUPPORTED, "GEMM path")
+    # workspace query: bf16 h rows for every routed pair, plus the shared expert's rows
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, -1, 0) == 16 * 2 * 512 * 2
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, 3, 0) == (16 * 2 + 16) * 512 * 2
+    assert call(T=0) == ft.FT_OK
+
+
+def test_combine_validation():
+    L = ft.lib
+    call = lambda **kw: L.ft_moe_combine(kw.get("y", A), kw.get("ysh", None), kw.get("ids", A), kw.get("w", A),
+                                         kw.get("inv", A), kw.get("slot", A), kw.get("T", 4), kw.get("E", 8),
+                                         kw.get("k", 2), kw.get("d", 256), kw.get("out", B), kw.get("mask", None),
+                                         kw.get("flags", 0), None)
+    _err(call(d=250), ft.FT_E_INVAL, "multiple of 8")
+    _err(call(flags=1), ft.FT_E_INVAL, "unknown flags")
+    _err(call(out=None), ft.FT_E_INVAL, "out is null")
+    _err(call(mask=MIS), ft.FT_E_INVAL, "residual_mask is not")
+    _err(call(inv=None), ft.FT_E_INVAL, "inv is null")
+    assert call(T=0) == ft.FT_OK
+
+
+def test_pack_and_dequant_validation():
+    L = ft.lib
+    b = _bank(fmt=ft.FT_W_Q4_0, n=2, d=256, I=256)
+    _err(L.ft_moe_pack_bank(1, 2, 256, 512, A, B, None, None, ctypes.byref(b), None), ft.FT_E_INVAL, "does not match")
+    _err(L.ft_moe_pack_bank(1, 2, 256, 256, None, B, None, None, ctypes.byref(b), None), ft.FT_E_INVAL, "null")
+    _err(L.ft_moe_pack_bank(1, 2, 256, 256, ctypes.c_void_p(0x10001), B, None, None, ctypes.byref(b), None),
+         ft.FT_E_INVAL, "2-byte aligned")
+    _err(L.ft_moe_dequant(ctypes.byref(b), 2, 0, A, None), ft.FT_E_INVAL, "slot 2 out of range")
+    _err(L.ft_moe_dequant(ctypes.byref(b), 0, 2, A, None), ft.FT_E_INVAL, "which must be")
+    _err(L.ft_moe_dequant(ctypes.byref(b), 0, 0, None, None), ft.FT_E_INVAL, "out is null")
+
+
+def test_binding_has_no_oracle_dependency():
+    """The product path must not import the oracle or the input generator."""
+    import sys
+    pkg = os.path.join(ROOT, "routed_expert_ffn_wave_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\b(import|from)\s+(oracle|synth)\b", src), f
+                assert "ftoracle" not in src, f
+    assert "oracle" not in {m.split(".")[0] for m in sys.modules if m.startswith("routed_expert")}

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle on the same seeded
+inputs.  Routing ids, counts, offsets, permutation, residual mask and dequantised weights must match
+bit for bit; routing weights within 1e-6; FFN rows and layer outputs within rel-L2 5e-3 and
+max-abs 3e-2 * max|ref|."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import compare_layer, device_bank, log, run_gpu_layer, WTOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ft():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import routed_expert_ffn_wave_amd as ft
+    return ft
+
+
+def _logits(kind, T, E, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "ties":
+        L = torch.randint(-3, 4, (T, E), generator=g).float() * 0.5
+        L[torch.rand(T, E, generator=g) < 0.05] = float("-inf")
+        L[:, 0] = torch.where(torch.rand(T, generator=g) < 0.3, torch.tensor(-0.0), L[:, 0])
+        # keep at least k finite per row: the first column is finite
+        return L
+    L = torch.randn(T, E, generator=g)
+    if kind == "zipf":
+        L += -1.1 * torch.log(torch.randperm(E, generator=g).double() + 1).float()
+    if kind == "wide":
+        L *= 30.0
+    return L
+
+
+ROUTE_CASES = [(1, 8, 2, "normal"), (37, 8, 2, "ties"), (64, 10, 4, "ties"), (300, 128, 8, "normal"),
+               (513, 256, 8, "zipf"), (64, 1024, 32, "ties"), (5, 32, 32, "normal"), (33, 7, 1, "ties"),
+               (20, 1, 1, "normal"), (100, 65, 8, "wide"), (16384, 256, 8, "zipf")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route(ft, T, E, k, kind):
+    L = _logits(kind, T, E, 1000 + T + E + k)
+    ids, w = ft.ft_moe_route(L.cuda(), k)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(L, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    wg = w.cpu().numpy()
+    finite = np.isfinite(rw)
+    assert np.array_equal(np.isfinite(wg), finite)
+    assert np.abs(wg[finite] - rw[finite]).max(initial=0) <= WTOL
+
+
+PERMUTE_CASES = [(0, 8, 2, "rand"), (1, 8, 2, "rand"), (8, 128, 8, "rand"), (2048, 128, 8, "rand"),
+                 (2049, 128, 8, "rand"), (4096, 128, 8, "skew"), (16384, 256, 8, "skew"), (600, 1024, 32, "rand"),
+                 (5000, 3, 3, "rand"), (3000, 1024, 1, "skew")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", PERMUTE_CASES)
+def test_permute(ft, T, E, k, kind):
+    g = torch.Generator().manual_seed(7 + T + E)
+    if T == 0:
+        ids = torch.zeros(0, k, dtype=torch.int32)
+    else:
+        ids = torch.argsort(torch.rand(T, E, generator=g), dim=1)[:, :k].to(torch.int32)
+        if kind == "skew":
+            hot = torch.arange(k, dtype=torch.int32)
+            ids[: T * 3 // 4] = hot
+    counts, offsets, gather, inv = ft.ft_moe_permute(ids.cuda(), E)
+    torch.cuda.synchronize()
+    rc, ro, rg, ri = oracle.permute(ids.numpy(), E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(gather.cpu().numpy(), rg)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+def _bits_equal_nan_aware(a: np.ndarray, b: np.ndarray):
+    na, nb = np.isnan(a), np.isnan(b)
+    assert np.array_equal(na, nb), "NaN positions differ"
+    assert np.array_equal(a[~na].view(np.uint32), b[~nb].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("content", ["encoded", "random_bytes"])
+def test_dequant_bit_exact(ft, fmt, content):
+    d, I, n = 256, 384, 3
+    if content == "encoded":
+        w = synth.Workload("dq", 50, T=1, d=d, E=n, k=1, I=I, fmt=fmt)
+        canon = synth.make_bank(w)
+    else:  # every code and scale byte random: NaN/inf/subnormal scales, NaN codes, extreme exponents
+        g = torch.Generator().manual_seed(60 + fmt)
+        canon = synth.empty_bank(fmt, n, d, I)
+        for t in (canon.w13, canon.w2):
+            t.view(torch.uint8).copy_(torch.randint(0, 256, t.view(torch.uint8).shape, generator=g, dtype=torch.uint8))
+        if fmt == 3:  # fp32 block scales: random finite positive normals of varied exponent
+            for t in (canon.s13, canon.s2):
+                t.copy_(torch.exp2(torch.randint(-40, 20, t.shape, generator=g).float()) *
+                        (1 + torch.rand(t.shape, generator=g)))
+        elif fmt == 2:
+            for t in (canon.s13, canon.s2):
+                t.copy_(torch.randint(0, 256, t.shape, generator=g, dtype=torch.uint8))
+    bank = device_bank(canon)
+    for slot in range(n):
+        for which, (rows, K) in enumerate(((2 * I, d), (d, I))):
+            got = ft.ft_moe_dequant(bank, slot, which).cpu().numpy()
+            codes = canon.w13[slot] if which == 0 else canon.w2[slot]
+            sc = None if canon.s13 is None else (canon.s13[slot] if which == 0 else canon.s2[slot])
+            ref = oracle.dequant(fmt, codes, sc, rows, K)
+            _bits_equal_nan_aware(got, ref)
+
+
+# ------------------------------------------------------------------------------------- whole layer, reduced sizes
+
+def _small_workloads():
+    W = synth.WORKLOADS
+    return {
+        "tiny_bf16": W["tiny_bf16"],
+        "decode_q4_0": W["decode_q4_0"].replace(layers=1),
+        "prefill_bf16_zipf": W["prefill_bf16_zipf"].replace(T=300, d=512, I=256, E=16, k=4),
+        "mxfp4_shared": W["mxfp4_shared"].replace(T=200, d=512, I=256, E=32, k=4),
+        "fp8_resident": W["fp8_resident"].replace(T=300, d=512, I=256, E=32, k=4, n_resident=12),
+        "q4_0_prefill": W["decode_q4_0"].replace(T=150, d=512, I=256, E=16, k=4, layers=1),
+    }
+
+
+SMALL = _small_workloads()
+
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(ft, name, path):
+    w = SMALL[name]
+    flags = {"auto": 0, "gemv": ft.FT_PATH_GEMV, "gemm": ft.FT_PATH_GEMM}[path]
+    T = w.T if name in ("tiny_bf16", "decode_q4_0") else min(w.T, 40 if path == "gemv" else w.T)
+    log(f"layer {name} T={T} path={path}")
+    li = synth.layer_inputs(w, layer=0, T=T)
+    g = run_gpu_layer(li, device_bank(li.bank), flags=flags)
+    compare_layer(li, g, label=f"{name}/{path}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 37])
+def test_layer_small_sweep_fp8(ft, T):
+    w = SMALL["fp8_resident"]
+    li = synth.layer_inputs(w, layer=1, T=T)
+    g = run_gpu_layer(li, device_bank(li.bank))
+    compare_layer(li, g, label=f"fp8 sweep T={T}")
+
+
+# ------------------------------------------------------------------------------------- degenerate cases
+
+EDGE = synth.Workload("edge", 70, T=33, d=256, E=8, k=2, I=128, fmt=synth.FMT_MXFP4, shared=True)
+
+
+@pytest.mark.parametrize("case", ["all_equal_logits", "k_equals_E", "k1", "T1", "one_expert_takes_all", "x_zero"])
+def test_layer_degenerate(ft, case):
+    w, T = EDGE, EDGE.T
+    if case == "k_equals_E":
+        w = EDGE.replace(k=8)
+    elif case == "k1":
+        w = EDGE.replace(k=1)
+    elif case == "T1":
+        T = 1
+    li = synth.layer_inputs(w, layer=0, T=T)
+    if case == "all_equal_logits":
+        li.logits = torch.zeros(T, w.E)
+    elif case == "one_expert_takes_all":
+        li.logits[:, 3] += 100.0
+    elif case == "x_zero":
+        li.x = torch.zeros_like(li.x)
+    bank = device_bank(li.bank)
+    for flags in (0, ft.FT_PATH_GEMV, ft.FT_PATH_GEMM):
+        g = run_gpu_layer(li, bank, flags=flags)
+        if case == "x_zero":
+            assert (g["out"] == 0).all()
+        compare_layer(li, g, label=f"edge {case} flags={flags}")
+
+
+def test_layer_nothing_resident(ft):
+    """Every routed expert missing from the bank: only the shared expert contributes and every token
+    carries all k mask bits."""
+    li = synth.layer_inputs(EDGE, layer=0)
+    li.bank = li.bank.slot(EDGE.E)                     # a one-slot bank holding the shared expert
+    li.slot_of_expert = torch.full((EDGE.E,), -1, dtype=torch.int32)
+    li.workload = EDGE.replace(E=EDGE.E)               # same shape; shared expert now in slot 0
+    bank = device_bank(li.bank)
+    layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), EDGE.k, EDGE.T, shared_slot=0)
+    out, mask = layer.forward(li.logits.cuda(), li.x.cuda())
+    torch.cuda.synchronize()
+    ora = oracle.layer(li.logits, li.x, li.bank, li.slot_of_expert, EDGE.k, shared_slot=0)
+    assert (ora["mask"] == (1 << EDGE.k) - 1).all()
+    assert np.array_equal(mask.cpu().numpy().astype(np.uint32), ora["mask"])
+    from gpu_util import assert_ffn_close
+    assert_ffn_close(out.cpu().numpy(), ora["out"], "nothing resident: out")
+
+
+def test_t_zero_is_noop(ft):
+    w = SMALL["tiny_bf16"]
+    li = synth.layer_inputs(w, T=4)
+    bank = device_bank(li.bank)
+    layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, 0)
+    out, mask = layer.forward(li.logits[:0].cuda(), li.x[:0].cuda())
+    torch.cuda.synchronize()
+    assert out.shape == (0, w.d) and mask.shape == (0,)
+    assert (layer.counts.cpu() == 0).all() and (layer.offsets.cpu() == 0).all()
+
+
+def test_repeatable_bit_for_bit(ft):
+    w = SMALL["prefill_bf16_zipf"]
+    li = synth.layer_inputs(w, T=300)
+    bank = device_bank(li.bank)
+    a = run_gpu_layer(li, bank)
+    b = run_gpu_layer(li, bank)
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+    assert torch.equal(a["y_sorted"], b["y_sorted"])
+
+
+def test_graph_capture_replays(ft):
+    """The four calls enqueue only, so a graph of one layer replays to the eager result."""
+    w = SMALL["decode_q4_0"]
+    li = synth.layer_inputs(w, T=8)
+    bank = device_bank(li.bank)
+    layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, 8)
+    logits, x = li.logits.cuda(), li.x.cuda()
+    out, _ = layer.forward(logits, x)
+    eager = out.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        layer.forward(logits, x)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            layer.forward(logits, x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        layer.out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager)
