@@ -1,0 +1,252 @@
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_q4_0] [--no-graph]
+
+A step is one pass of the whole layer (route, permute, grouped SwiGLU FFN, combine) over one batch:
+for the default decode workload (T=8, d=2048, E=128, k=8, I=768, Q4_0 banks) a step is 48 independent
+layers run back to back on one stream, captured once into a HIP graph and replayed.  Inputs are seeded
+synthetic tensors already resident in HBM.  Prints one JSON line.
+
+The dominant unit is the grouped-FFN call; its average duration is timed with HIP events on the
+stream it runs on, over timed eager replays of the same steps, and compared with the HBM (decode) or
+MFMA (prefill) roofline of its algorithmic bytes or flops.  The CPU baseline times the scalar oracle
+on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import routed_expert_ffn_wave_amd as ft  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routed_expert_ffn_wave_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def build_layers(w: synth.Workload, T: int, n_layers: int):
+    layers = []
+    for l in range(n_layers):
+        canon = synth.make_bank(w, layer=l, device="cuda")
+        bank = ft.ft_moe_pack_bank(canon.fmt, canon.n_slots, canon.d, canon.I, canon.w13, canon.w2, canon.s13,
+                                   canon.s2)
+        del canon
+        slot = synth.slot_table(w, l).cuda()
+        layer = ft.MoELayer(bank, slot, w.k, T, shared_slot=w.shared_slot)
+        logits = synth.logits(w, l, T, device="cuda")
+        x = synth.activations(w, l, T, device="cuda")
+        layers.append((layer, logits, x))
+        if (l + 1) % 8 == 0 or l + 1 == n_layers:
+            log(f"generated {l + 1}/{n_layers} layers")
+    torch.cuda.synchronize()
+    return layers
+
+
+def run_step(layers):
+    for layer, logits, x in layers:
+        layer.forward(logits, x)
+
+
+def algorithmic_work(w: synth.Workload, layers, T: int):
+    """Per grouped-FFN call, averaged over the layers, from the actual routing:
+    bytes = touched resident experts (+ shared) x stored bytes per expert + x rows + y_sorted rows,
+    flops = 2 * 3 * d * I per computed (token, expert) pair."""
+    per_expert = synth.expert_bytes(w.fmt, w.d, w.I)
+    tot_b, tot_f, tot_pairs, tot_touched = 0.0, 0.0, 0, 0
+    for layer, _, _ in layers:
+        counts = layer.counts.cpu()
+        slot = layer.slot_of.cpu()
+        resident = slot >= 0
+        touched = int(((counts > 0) & resident).sum()) + (1 if w.shared else 0)
+        pairs = int(counts[resident].sum()) + (T if w.shared else 0)
+        tot_touched += touched
+        tot_pairs += pairs
+        tot_b += touched * per_expert + T * w.d * 2 + pairs * w.d * 2
+        tot_f += 2.0 * 3.0 * w.d * w.I * pairs
+    n = len(layers)
+    return tot_b / n, tot_f / n, tot_pairs / n, tot_touched / n
+
+
+def time_ffn_calls(layers, reps: int):
+    """Average duration of one grouped-FFN call, with HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    evs = []
+    for _ in range(reps):
+        for layer, logits, x in layers:
+            T, E, k = layer.T, layer.E, layer.k
+            st = ft._stream(s)
+            ft._check(ft.lib.ft_moe_route(ft._ptr(logits), T, E, k, ft._ptr(layer.ids), ft._ptr(layer.w), st))
+            ft._check(ft.lib.ft_moe_permute(ft._ptr(layer.ids), T, E, k, ft._ptr(layer.counts),
+                                            ft._ptr(layer.offsets), ft._ptr(layer.gather), ft._ptr(layer.inv),
+                                            ft._ptr(layer.perm_ws), layer.perm_ws.numel(), st))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            ft._check(ft.lib.ft_moe_grouped_ffn(layer.bank.ref, ft._ptr(layer.slot_of), layer.shared_slot, ft._ptr(x),
+                                                T, E, k, ft._ptr(layer.offsets), ft._ptr(layer.gather),
+                                                ft._ptr(layer.y_sorted), ft._ptr(layer.y_shared),
+                                                ft._ptr(layer.ffn_ws), layer.ffn_ws.numel(), layer.flags, st))
+            e1.record(s)
+            ft._check(ft.lib.ft_moe_combine(ft._ptr(layer.y_sorted), ft._ptr(layer.y_shared), ft._ptr(layer.ids),
+                                            ft._ptr(layer.w), ft._ptr(layer.inv), ft._ptr(layer.slot_of), T, E, k,
+                                            layer.bank.d, ft._ptr(layer.out), ft._ptr(layer.mask), 0, st))
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return sum(ms) / len(ms) * 1e3  # us
+
+
+def cpu_baseline(w: synth.Workload, T: int, budget_s: float):
+    """Time the scalar oracle on host cores over whole layers of the same workload until the budget
+    is used (at least one layer)."""
+    import oracle
+    t_total, n = 0.0, 0
+    while t_total < budget_s and n < w.layers:
+        li = synth.layer_inputs(w, layer=n, T=T, device="cuda")
+        bank_cpu = li.bank.to("cpu")
+        L, x, so = li.logits.cpu(), li.x.cpu(), li.slot_of_expert.cpu()
+        del li
+        t0 = time.perf_counter()
+        oracle.layer(L, x, bank_cpu, so, w.k, shared_slot=w.shared_slot)
+        t_total += time.perf_counter() - t0
+        n += 1
+    return t_total, n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_q4_0", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's)")
+    ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--ffn-reps", type=int, default=3)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this layer is not sharded across GPUs here "
+              "(see the sharding design); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    T = args.T or w.T
+    n_layers = args.layers or w.layers
+    decode = T <= 64
+    log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}")
+    layers = build_layers(w, T, n_layers)
+
+    for _ in range(max(args.warmup, 1)):
+        run_step(layers)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run_step(layers)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                run_step(layers)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(layers)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    us_per_layer = ms_per_step * 1e3 / n_layers
+    log(f"{ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer")
+
+    # ---- dominant unit: the grouped-FFN call, event-timed on its stream
+    ffn_us = time_ffn_calls(layers, args.ffn_reps)
+    bytes_call, flops_call, pairs, touched = algorithmic_work(w, layers, T)
+    if decode:
+        achieved = bytes_call / (ffn_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops_call / (ffn_us * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS["bf16"]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    roof["traffic"] = None
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    src_hash = kernel_source_hash()
+    if os.path.exists(prof):
+        rec = json.load(open(prof)).get(w.name)
+        if rec and rec.get("source_hash") == src_hash and rec.get("T") == T:
+            roof["traffic"] = rec["bytes_per_call"]
+    roof["kernel"] = "ft_moe_grouped_ffn (gate/up then down, " + ("streaming GEMV" if decode else "MFMA GEMM") + ")"
+    roof["per_call_us"] = round(ffn_us, 3)
+    roof["algorithmic_bytes_per_call"] = round(bytes_call)
+    roof["algorithmic_flops_per_call"] = round(flops_call)
+    log(f"FFN call {ffn_us:.2f} us; {touched:.1f} experts touched, {pairs:.1f} pairs; {roof}")
+
+    # ---- CPU baseline: the oracle on host cores, bounded sample
+    cpu = None
+    if args.cpu_budget > 0:
+        t_cpu, n_cpu = cpu_baseline(w, T, args.cpu_budget)
+        if decode:
+            cpu = {"value": round(t_cpu / n_cpu * 1e6, 1), "unit": "us/layer"}
+        else:
+            cpu = {"value": round(T * n_cpu / t_cpu, 3), "unit": "tokens/s"}
+        cpu.update({"cores": 1, "kind": "oracle",
+                    "sample": f"{n_cpu} whole layer(s) of {w.name} (T={T}), single-threaded scalar C oracle"})
+        log(f"cpu baseline {cpu}")
+
+    if decode:
+        metric, value, unit, hib = "MoE-layer decode latency", us_per_layer, "us/layer", False
+    else:
+        metric, value, unit, hib = "MoE-layer prefill throughput", T / (ms_per_step * 1e-3 / n_layers), "tokens/s", True
+    line = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": hib, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "T": T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
+                   "bank_format": synth.FMT_NAMES[w.fmt], "layers_per_step": n_layers,
+                   "shared_expert": w.shared, "resident_experts": w.n_resident or w.E,
+                   "graph": graph is not None},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

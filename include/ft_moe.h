@@ -72,17 +72,23 @@ enum ft_weight_format {
 /*
  * Expert bank in DEVICE layout (passed by host pointer; the struct itself is read on the host).
  * Slot s holds one expert: W13 = [gate rows 0..I-1 ; up rows I..2I-1] of shape [2I][d] and
- * W2 of shape [d][I] (the K dimension is contiguous in both).  Per format:
- *   FT_W_BF16     w13 uint16 [n_slots][2I][d], w2 uint16 [n_slots][d][I]; s13 = s2 = NULL
- *   FT_W_Q4_0     w13 uint8 [n_slots][2I][d/2], w2 uint8 [n_slots][d][I/2]: the 16 code bytes of each
- *                 GGUF block in GGUF order (byte i: element i low nibble, element i+16 high nibble);
- *                 s13 fp16 [n_slots][2I][d/32], s2 fp16 [n_slots][d][I/32].  ft_moe_pack_bank builds
- *                 this from GGUF's 18-byte blocks.
- *   FT_W_MXFP4    w13 uint8 [n_slots][2I][d/2] (element 2i low nibble, 2i+1 high), w2 uint8
- *                 [n_slots][d][I/2]; s13 uint8 E8M0 [n_slots][2I][d/32], s2 [n_slots][d][I/32]
- *   FT_W_FP8_B128 w13 uint8 [n_slots][2I][d], w2 uint8 [n_slots][d][I]; s13 fp32 [n_slots][2I/128][d/128],
- *                 s2 fp32 [n_slots][d/128][I/128]
- * Divisibility: d and I multiples of 8 (bf16), 32 (Q4_0, MXFP4) or 128 (FP8_B128).
+ * W2 of shape [d][I].  ft_moe_pack_bank builds this layout from the canonical stored formats.
+ *
+ * Each matrix of R rows and K columns is cut into 16-byte code chunks along K (8 bf16, 16 e4m3 or
+ * 32 four-bit codes; nchunk = K / elements-per-chunk) and stored row-interleaved in blocks of 64
+ * rows: chunk c of row r sits at byte ((r/64 * nchunk + c) * 64 + r%64) * 16 of the matrix, so the
+ * same chunk of 64 consecutive rows is 1 KiB of contiguous memory.  Slots are consecutive.
+ *   FT_W_BF16     codes = bf16 in K order; s13 = s2 = NULL
+ *   FT_W_Q4_0     32 codes of one GGUF block per chunk; 32-bit word w of a chunk holds elements
+ *                 8w..8w+7, element 8w+2s in bits 4s..4s+3 and element 8w+2s+1 in bits 16+4s..19+4s;
+ *                 value = scale * (q - 8); scales fp16, one per (row, chunk), same interleave:
+ *                 scale of (r, c) is element (r/64 * nchunk + c) * 64 + r%64
+ *   FT_W_MXFP4    32 e2m1 codes per chunk in K order (element 2i low nibble of byte i, 2i+1 high);
+ *                 E8M0 scales, one byte per (row, chunk), interleaved as for Q4_0
+ *   FT_W_FP8_B128 16 e4m3fn codes per chunk in K order; scales fp32 [rows/128][K/128] per matrix,
+ *                 row-major (not interleaved)
+ * Array sizes per format: ft_moe_bank_bytes.  Divisibility: d a multiple of 128 and I a multiple of 64
+ * (so every matrix has whole 64-row blocks and whole chunks; FP8_B128 also needs I % 128 == 0).
  */
 typedef struct ft_moe_bank {
   int32_t fmt, n_slots, d, I;
@@ -174,20 +180,25 @@ int ft_moe_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int
 size_t ft_moe_bank_bytes(int fmt, int n_slots, int d, int I, int which);
 
 /*
- * Build a device-layout bank from canonical stored bytes (all device pointers).  Canonical is
- * the device layout for BF16, MXFP4 and FP8_B128 (the call copies), and for Q4_0 GGUF's 18-byte
- * blocks [n_slots][rows][K/32][18] (fp16 scale, then 16 code bytes) with canon_s13/canon_s2 NULL.
- * `dst` is a host pointer to a bank whose arrays are already allocated (sizes from
- * ft_moe_bank_bytes); its fmt/n_slots/d/I must match the arguments.
+ * Build a device-layout bank from canonical stored bytes (all pointers are device pointers).
+ * Canonical layouts, per slot, row-major over rows:
+ *   FT_W_BF16     w uint16 [rows][K]
+ *   FT_W_Q4_0     GGUF blocks [rows][K/32][18]: fp16 scale (little endian), then 16 bytes where byte i
+ *                 holds element i (low nibble) and element i+16 (high nibble); canon_s13/s2 NULL
+ *   FT_W_MXFP4    codes uint8 [rows][K/2] (element 2i low nibble), scales uint8 E8M0 [rows][K/32]
+ *   FT_W_FP8_B128 codes uint8 [rows][K], scales fp32 [rows/128][K/128]
+ * `dst` is a host pointer to a bank whose device arrays are already allocated (sizes from
+ * ft_moe_bank_bytes); its fmt/n_slots/d/I must match the arguments.  Source and destination
+ * must not overlap.
  */
 int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, const void* canon_w2,
                      const void* canon_s13, const void* canon_s2, const ft_moe_bank* dst,
                      hipStream_t stream);
 
 /*
- * Decode one bank matrix to fp32 with the same decode routine the FFN kernels use (for checking
- * the dequantisation bit for bit).  which = 0: W13 of `slot` -> out fp32 [2I][d];
- * which = 1: W2 of `slot` -> out fp32 [d][I].
+ * Decode one bank matrix to fp32 with the same per-format decode routine the GEMV kernels use (for
+ * checking the dequantisation bit for bit): which = 0: W13 of `slot` -> out fp32 [2I][d] row-major;
+ * which = 1: W2 of `slot` -> out fp32 [d][I] row-major.
  */
 int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hipStream_t stream);
 

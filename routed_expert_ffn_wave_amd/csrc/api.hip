@@ -59,9 +59,10 @@ int check_bank_shape(int fmt, int n_slots, int d, int I) {
   REQUIRE(fmt >= FT_W_BF16 && fmt <= FT_W_FP8_B128, FT_E_UNSUPPORTED, "unknown weight format %d", fmt);
   REQUIRE(n_slots >= 1, FT_E_INVAL, "n_slots must be >= 1 (got %d)", n_slots);
   REQUIRE(d > 0 && I > 0, FT_E_INVAL, "d and I must be positive (got d=%d, I=%d)", d, I);
-  const int m = fmt == FT_W_BF16 ? 8 : fmt == FT_W_FP8_B128 ? 128 : 32;
-  REQUIRE(d % m == 0 && I % m == 0, FT_E_INVAL, "format %d needs d and I to be multiples of %d (got d=%d, I=%d)",
-          fmt, m, d, I);
+  REQUIRE(d % 128 == 0 && I % 64 == 0, FT_E_INVAL,
+          "d must be a multiple of 128 and I a multiple of 64 (got d=%d, I=%d)", d, I);
+  REQUIRE(fmt != FT_W_FP8_B128 || I % 128 == 0, FT_E_INVAL,
+          "FP8_B128 needs I to be a multiple of 128 (got I=%d)", I);
   REQUIRE((long long)d * I <= (1LL << 31), FT_E_INVAL, "d*I too large");
   return FT_OK;
 }
@@ -83,8 +84,6 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // groups with at most this many routed rows go through the GEMV kernels when the path is automatic
 constexpr int kGemvMaxRows = 2 * ftk::GEMV_NT;
-
-bool gemm_shape_ok(int d, int I) { return I % 64 == 0 && d % 128 == 0; }
 
 size_t h_bytes(int T, int k, int I, bool shared) {
   return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
@@ -165,9 +164,6 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
             shared_slot, bank->n_slots);
     REQUIRE((shared_slot >= 0) == (y_shared != nullptr), FT_E_INVAL,
             "y_shared must be given exactly when shared_slot >= 0");
-    const bool gemm_ok = gemm_shape_ok(bank->d, bank->I);
-    REQUIRE(path != FT_PATH_GEMM || gemm_ok, FT_E_UNSUPPORTED,
-            "the GEMM path needs I %% 64 == 0 and d %% 128 == 0 (got d=%d, I=%d)", bank->d, bank->I);
     if (T == 0) return ok();
     CHECK_PTR(slot_of_expert, "slot_of_expert");
     CHECK_PTR(x, "x");
@@ -208,7 +204,7 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     const long long rows_total = TK + (shared ? T : 0);
     const long long groups_upper = (long long)(E < TK ? E : TK) + (shared ? 1 : 0);
     int gemv_max, gemm_min;
-    if (path == FT_PATH_GEMV || (path == FT_PATH_AUTO && !gemm_ok)) {
+    if (path == FT_PATH_GEMV) {
       gemv_max = 0x7fffffff;
       gemm_min = 0x7fffffff;
     } else if (path == FT_PATH_GEMM) {
@@ -324,23 +320,17 @@ int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, 
     if (fmt == FT_W_Q4_0) {
       REQUIRE(((uintptr_t)canon_w13 & 1u) == 0 && ((uintptr_t)canon_w2 & 1u) == 0, FT_E_INVAL,
               "canonical Q4_0 arrays must be 2-byte aligned");
-      const long long nb13 = (long long)n_slots * 2 * I * (d / 32), nb2 = (long long)n_slots * d * (I / 32);
-      hipError_t e = ftk::launch_pack_q4_0((const uint8_t*)canon_w13, (uint8_t*)dst->w13, (uint16_t*)dst->s13, nb13,
-                                           stream);
-      if (e == hipSuccess)
-        e = ftk::launch_pack_q4_0((const uint8_t*)canon_w2, (uint8_t*)dst->w2, (uint16_t*)dst->s2, nb2, stream);
-      return hip_status(e, "ft_moe_pack_bank (Q4_0) launch");
+    } else {
+      REQUIRE(aligned16(canon_w13) && aligned16(canon_w2), FT_E_INVAL, "canonical code arrays must be 16-byte aligned");
+      if (fmt != FT_W_BF16)
+        REQUIRE(canon_s13 != nullptr && canon_s2 != nullptr, FT_E_INVAL, "canonical scale arrays are null");
     }
-    if (fmt != FT_W_BF16)
-      REQUIRE(canon_s13 != nullptr && canon_s2 != nullptr, FT_E_INVAL, "canonical scale arrays are null");
-    const void* src[4] = {canon_w13, canon_w2, canon_s13, canon_s2};
-    void* dstp[4] = {(void*)dst->w13, (void*)dst->w2, (void*)dst->s13, (void*)dst->s2};
-    for (int i = 0; i < 4; ++i) {
-      const size_t n = ft_moe_bank_bytes(fmt, n_slots, d, I, i);
-      if (n == 0) continue;
-      hipError_t e = hipMemcpyAsync(dstp[i], src[i], n, hipMemcpyDeviceToDevice, stream);
-      if (e != hipSuccess) return hip_status(e, "ft_moe_pack_bank copy");
-    }
+    hipError_t e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w13, (const uint8_t*)canon_s13,
+                                           (uint8_t*)dst->w13, (uint8_t*)dst->s13, (long long)n_slots * 2 * I, d, stream);
+    if (e == hipSuccess)
+      e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w2, (const uint8_t*)canon_s2, (uint8_t*)dst->w2,
+                                  (uint8_t*)dst->s2, (long long)n_slots * d, I, stream);
+    if (e != hipSuccess) return hip_status(e, "ft_moe_pack_bank launch");
     return ok();
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_pack_bank: unexpected exception");

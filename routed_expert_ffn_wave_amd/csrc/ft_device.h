@@ -42,32 +42,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Per-format decode of one lane's code chunk into bf16 pairs.
-//
-// Each format is read as one 16-byte load per row per lane ("chunk"): 8 bf16, 16 e4m3, or 32
-// 4-bit codes (one Q4_0 / MXFP4 block).  decode_chunk() returns the chunk's weights as bf16
-// pairs in "code order"; x_pair_index() gives, for pair p of code order, the index in K order
-// (relative to the chunk start) of its first element; the second element is first + stride.
-//   BF16 / FP8: code order = K order, pairs (2p, 2p+1).
-//   MXFP4: byte i holds elements 2i (low) and 2i+1 (high) -> pairs (2p, 2p+1).
-//   Q4_0 (GGUF): byte i holds element i (low nibble) and element i+16 (high nibble); we form
-//   pairs from the low nibbles of bytes (4w+2c, 4w+2c+1)...  see q4_pairs below.
-// For Q4_0 the decoded bf16 values are (128 + q) (exact; the caller subtracts 136 * sum(x) per block).
+// Per-format decode of one 16-byte code chunk (8 bf16, 16 e4m3 or 32 four-bit codes) into bf16
+// pairs; pair i holds K elements (2i, 2i+1) of the chunk, low half first, so it lines up with the
+// i-th 32-bit word of the matching bf16 activations.  Chunks are in the device layout of the
+// public header (Q4_0 words already hold (2i, 2i+1) pairs in matching nibble positions).
+// Values are exact in bf16: bf16 as stored, e4m3 (3 mantissa bits), e2m1 with unit scale, and for
+// Q4_0 the value 128 + q (bf16 128.0 has ulp 1), from which the caller removes 136 = 128 + 8
+// through the block's activation sum.  Block scales are applied by the caller in fp32.
 
 template <int FMT>
 struct Chunk;
 
 template <>
 struct Chunk<FMT_BF16> {
-  static constexpr int ELEMS = 8;    // K elements per 16-byte chunk
+  static constexpr int ELEMS = 8;  // K elements per 16-byte chunk
   static constexpr int PAIRS = 4;
   __device__ static void decode(const u32x4& c, uint32_t* p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = c[i];
   }
-  // pair i covers K elements (2i, 2i+1)
-  __device__ static int first(int i) { return 2 * i; }
-  static constexpr int SECOND = 1;
 };
 
 template <>
@@ -77,23 +70,16 @@ struct Chunk<FMT_FP8_B128> {
   __device__ static void decode(const u32x4& c, uint32_t* p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // e4m3 -> bf16 is exact (3 mantissa bits, exponent range inside bf16's).
-      bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false);
-      bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true);
-      p[2 * i] = __builtin_bit_cast(uint32_t, lo);
-      p[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+      p[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
+      p[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
     }
   }
-  __device__ static int first(int i) { return 2 * i; }
-  static constexpr int SECOND = 1;
 };
 
 template <>
 struct Chunk<FMT_MXFP4> {
   static constexpr int ELEMS = 32;
   static constexpr int PAIRS = 16;
-  // Decodes e2m1 with unit scale (exact in bf16); the block's E8M0 scale is applied to the
-  // fp32 partial sum.
   __device__ static void decode(const u32x4& c, uint32_t* p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -103,18 +89,13 @@ struct Chunk<FMT_MXFP4> {
       p[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], 1.0f, 3));
     }
   }
-  __device__ static int first(int i) { return 2 * i; }
-  static constexpr int SECOND = 1;
 };
 
 template <>
 struct Chunk<FMT_Q4_0> {
   static constexpr int ELEMS = 32;
   static constexpr int PAIRS = 16;
-  // Dword w (bytes 4w..4w+3) of a block holds, nibble by nibble from bit 0:
-  //   e(4w) e(4w+16) e(4w+1) e(4w+17) e(4w+2) e(4w+18) e(4w+3) e(4w+19).
-  // (d >> 4s) & 0x000F000F picks nibbles s and s+4: elements (4w + s/2 + 16*(s&1)) and
-  // (4w + 2 + s/2 + 16*(s&1)); OR-ing 0x4300 (bf16 128.0, ulp 1) makes each half 128 + q exactly.
+  // word w, shift 4s: nibbles s (low half) and s+4 (high half) = elements 8w+2s and 8w+2s+1
   __device__ static void decode(const u32x4& c, uint32_t* p) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -122,13 +103,21 @@ struct Chunk<FMT_Q4_0> {
       for (int s = 0; s < 4; ++s) p[4 * w + s] = ((c[w] >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
     }
   }
-  // pair 4w+s: first element index (K order inside the block), second = first + 2
-  __device__ static int first(int i) {
-    int w = i >> 2, s = i & 3;
-    return 4 * w + (s >> 1) + 16 * (s & 1);
-  }
-  static constexpr int SECOND = 2;
 };
+
+template <int FMT>
+__host__ __device__ constexpr int chunk_elems() {
+  return FMT == FMT_BF16 ? 8 : FMT == FMT_FP8_B128 ? 16 : 32;
+}
+
+// Byte offset of chunk c of row r in a row-interleaved matrix with nchunk chunks per row.
+__device__ __forceinline__ size_t ilv_chunk_off(int r, int c, int nchunk) {
+  return (((size_t)(r >> 6) * nchunk + c) * 64 + (r & 63)) * 16;
+}
+// Element index of the per-(row, chunk) scale of row r, chunk c (Q4_0, MXFP4).
+__device__ __forceinline__ size_t ilv_scale_idx(int r, int c, int nchunk) {
+  return ((size_t)(r >> 6) * nchunk + c) * 64 + (r & 63);
+}
 
 // ---------------------------------------------------------------------------------------------
 // wave64 reductions

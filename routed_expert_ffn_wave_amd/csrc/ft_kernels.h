@@ -35,7 +35,7 @@ hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, co
                           const int32_t* inv, const int32_t* slot_of, int T, int E, int k, int d, void* out,
                           uint32_t* mask, bool out_bf16, hipStream_t s);
 
-// Streaming GEMV path (few rows per group).  max_rows_upper: host-side bound on the number of
+// Streaming GEMV path (few rows per group).  chunks_upper: host-side bound on the number of
 // (group, token-chunk) pairs, used to size the grid.
 constexpr int GEMV_NT = 8;  // tokens per pass over the weights
 hipError_t launch_gemv_gateup(const FfnArgs& a, int chunks_upper, hipStream_t s);
@@ -46,8 +46,9 @@ hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s);
 hipError_t launch_gemm_down(const FfnArgs& a, int tiles_upper, hipStream_t s);
 constexpr int GEMM_BM = 128;  // token rows per tile
 
-hipError_t launch_pack_q4_0(const uint8_t* canon, uint8_t* codes, uint16_t* scales, long long nblocks,
-                            hipStream_t s);
+// canonical -> row-interleaved device layout for one matrix of `rows` rows (all slots) and K columns
+hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
+                              uint8_t* scales, long long rows, int K, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, float* out,
                           hipStream_t s);
 

@@ -23,31 +23,32 @@ namespace ftk {
 constexpr int BM = GEMM_BM, BN = 128, BK = 32, LDK = BK + 8;  // LDS row stride in bf16 (padded)
 
 template <int FMT>
-__device__ __forceinline__ size_t gemm_code_row_bytes(int K) {
-  return FMT == FMT_BF16 ? (size_t)K * 2 : FMT == FMT_FP8_B128 ? (size_t)K : (size_t)K / 2;
+__device__ __forceinline__ size_t gemm_mat_bytes(int rows, int K) {
+  return FMT == FMT_BF16 ? (size_t)rows * K * 2 : FMT == FMT_FP8_B128 ? (size_t)rows * K : (size_t)rows * K / 2;
 }
 
-// Decode this thread's 16 K-consecutive weights (the half `hf` of row `r` of the K step) into
-// bf16 in K order: out[0..15] = elements [16*hf, 16*hf+16) of the 32-wide K step, except Q4_0
-// whose half-block holds elements {8hf..8hf+7} and {16+8hf..16+8hf+7} (handled by the caller).
+// Decode this thread's 16 K-consecutive weights of K step `ks` (half `hf` = elements 16hf..16hf+15
+// of the 32-wide step) of weight row `r` in a row-interleaved matrix (base `mat`, nchunk chunks
+// per row) into 8 dwords of bf16 pairs in K order.  All element values are exact in bf16; MXFP4's
+// power-of-two scale is folded into the conversion (exact while the product is a normal bf16).
 template <int FMT>
-__device__ __forceinline__ void load_b_half(const uint8_t* rowp, int kstep, int hf, const uint8_t* scales_row,
-                                            uint32_t* out /* 8 dwords = 16 bf16 */) {
-  if constexpr (FMT == FMT_BF16) {
-    const u32x4* p = (const u32x4*)(rowp + (size_t)kstep * BK * 2 + hf * 32);
-    u32x4 a = p[0], b = p[1];
+__device__ __forceinline__ void load_b_half(const uint8_t* mat, int r, int nchunk, int ks, int hf,
+                                            const uint8_t* mx_scales, uint32_t* out) {
+  if constexpr (FMT == FMT_BF16) {  // 8 elements per chunk: chunks 4ks + 2hf, +1
+    const u32x4 a = *(const u32x4*)(mat + ilv_chunk_off(r, 4 * ks + 2 * hf, nchunk));
+    const u32x4 b = *(const u32x4*)(mat + ilv_chunk_off(r, 4 * ks + 2 * hf + 1, nchunk));
     out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
     out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
-  } else if constexpr (FMT == FMT_FP8_B128) {
-    const u32x4 c = *(const u32x4*)(rowp + (size_t)kstep * BK + hf * 16);
+  } else if constexpr (FMT == FMT_FP8_B128) {  // 16 elements per chunk: chunk 2ks + hf
+    const u32x4 c = *(const u32x4*)(mat + ilv_chunk_off(r, 2 * ks + hf, nchunk));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
       out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
     }
-  } else if constexpr (FMT == FMT_MXFP4) {
-    const u32x2 c = *(const u32x2*)(rowp + (size_t)kstep * 16 + hf * 8);
-    const float sc = e8m0_to_f32(scales_row[kstep]);
+  } else if constexpr (FMT == FMT_MXFP4) {  // 32 elements per chunk: half hf = bytes 8hf..8hf+7
+    const u32x2 c = *(const u32x2*)(mat + ilv_chunk_off(r, ks, nchunk) + hf * 8);
+    const float sc = e8m0_to_f32(mx_scales[ilv_scale_idx(r, ks, nchunk)]);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 0));
@@ -55,19 +56,15 @@ __device__ __forceinline__ void load_b_half(const uint8_t* rowp, int kstep, int 
       out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 2));
       out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 3));
     }
-  } else {  // Q4_0: bytes [8hf, 8hf+8) of the block; q - 8 is exact in bf16
-    const u32x2 c = *(const u32x2*)(rowp + (size_t)kstep * 16 + hf * 8);
-    // low nibbles -> out[0..3] (elements 8hf..8hf+7), high nibbles -> out[4..7] (16+8hf..)
+  } else {  // Q4_0: words 2hf, 2hf+1 of the chunk; nibble pair s of word w = elements 8w+2s, 8w+2s+1
+    const u32x2 c = *(const u32x2*)(mat + ilv_chunk_off(r, ks, nchunk) + hf * 8);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t v = c[i];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t b0 = (v >> (16 * j)) & 0xffu, b1 = (v >> (16 * j + 8)) & 0xffu;
-        const float l0 = (float)(int)(b0 & 15u) - 8.0f, l1 = (float)(int)(b1 & 15u) - 8.0f;
-        const float h0 = (float)(int)(b0 >> 4) - 8.0f, h1 = (float)(int)(b1 >> 4) - 8.0f;
-        out[2 * i + j] = (uint32_t)f32_to_bf16_bits(l0) | ((uint32_t)f32_to_bf16_bits(l1) << 16);
-        out[4 + 2 * i + j] = (uint32_t)f32_to_bf16_bits(h0) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t v = (c[i] >> (4 * s)) & 0x000F000Fu;
+        const float lo = (float)(int)(v & 0xffffu) - 8.0f, hi = (float)(int)(v >> 16) - 8.0f;  // q - 8, exact
+        out[4 * i + s] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
       }
     }
   }
@@ -130,9 +127,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
   }
   const uint8_t* codes = GATEUP ? a.w13 : a.w2;
   const uint8_t* scales = GATEUP ? a.s13 : a.s2;
-  const uint8_t* brow = codes + ((size_t)slot * ncols + wrow) * gemm_code_row_bytes<FMT>(K);
-  const uint8_t* bscale_row = nullptr;
-  if constexpr (FMT == FMT_MXFP4) bscale_row = scales + ((size_t)slot * ncols + wrow) * (K / 32);
+  const int nchunk = K / chunk_elems<FMT>();
+  const uint8_t* bmat = codes + (size_t)slot * gemm_mat_bytes<FMT>(ncols, K);
+  const uint8_t* bscales = nullptr;  // per-(row, chunk) scales of this slot (Q4_0, MXFP4)
+  if constexpr (FMT == FMT_Q4_0) bscales = scales + (size_t)slot * ncols * (size_t)nchunk * 2;
+  if constexpr (FMT == FMT_MXFP4) bscales = scales + (size_t)slot * ncols * (size_t)nchunk;
   __syncthreads();
   const uint16_t* arow = s_arow[ln];
 
@@ -157,13 +156,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
       av1 = p[1];
     }
     uint32_t bw[8];
-    load_b_half<FMT>(brow, ks, half_id, bscale_row, bw);
+    load_b_half<FMT>(bmat, wrow, nchunk, ks, half_id, bscales, bw);
     float bsc = 1.0f;
     if constexpr (PARTIAL) {
       if ((ks % SCALE_STEPS) == 0) {
         if constexpr (FMT == FMT_Q4_0) {
-          const uint16_t* s16 = (const uint16_t*)scales;
-          bsc = fp16_bits_to_f32(s16[((size_t)slot * ncols + wrow) * (K / 32) + ks]);
+          bsc = fp16_bits_to_f32(((const uint16_t*)bscales)[ilv_scale_idx(wrow, ks, nchunk)]);
         } else {
           const float* s32 = (const float*)scales;
           bsc = s32[((size_t)slot * (ncols / 128) + wrow / 128) * (K / 128) + ks / 4];
@@ -176,13 +174,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
     }
     *(u32x4*)&As[ln * LDK + half_id * 16] = av0;
     *(u32x4*)&As[ln * LDK + half_id * 16 + 8] = av1;
-    if constexpr (FMT == FMT_Q4_0) {
-      *(u32x4*)&Bs[ln * LDK + half_id * 8] = u32x4{bw[0], bw[1], bw[2], bw[3]};
-      *(u32x4*)&Bs[ln * LDK + 16 + half_id * 8] = u32x4{bw[4], bw[5], bw[6], bw[7]};
-    } else {
-      *(u32x4*)&Bs[ln * LDK + half_id * 16] = u32x4{bw[0], bw[1], bw[2], bw[3]};
-      *(u32x4*)&Bs[ln * LDK + half_id * 16 + 8] = u32x4{bw[4], bw[5], bw[6], bw[7]};
-    }
+    *(u32x4*)&Bs[ln * LDK + half_id * 16] = u32x4{bw[0], bw[1], bw[2], bw[3]};
+    *(u32x4*)&Bs[ln * LDK + half_id * 16 + 8] = u32x4{bw[4], bw[5], bw[6], bw[7]};
     __syncthreads();
 
     // ---- MFMA: two K sub-steps of 16

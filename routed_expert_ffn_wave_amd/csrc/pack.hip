@@ -1,57 +1,113 @@
-// Bank set-up kernels: GGUF Q4_0 repack into the device layout, and the dequantisation export
-// that decodes bank matrices to fp32 with the same per-format decode routine the FFN kernels use.
+// Bank set-up kernels: canonical stored formats -> the row-interleaved device layout, and the
+// dequantisation export that decodes device-layout bank matrices to fp32 with the same per-format
+// chunk decode the GEMV kernels use.
 //
 // Bank formats: FreeToken walk-through "深入FreeToken架构…全链路剖析", section 五 (per-format expert
-// banks, each with its own schema).
+// banks, each with its own schema).  Element encodings: GGUF Q4_0, OCP MXFP4 (E8M0 scales), OCP
+// e4m3fn.  All slots of a bank are treated as one matrix of n_slots * R rows: with R a multiple of
+// 64, the interleave of that matrix equals the per-slot interleave with slots laid end to end.
 #include "ft_device.h"
 #include "ft_kernels.h"
 
 namespace ftk {
 
-// canonical block: fp16 scale (little endian) then 16 code bytes -> codes[16], scale
-__global__ __launch_bounds__(256) void pack_q4_0_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ codes,
-                                                        uint16_t* __restrict__ scales, long long nblocks) {
-  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint8_t* src = canon + b * 18;
-  const uint16_t* s16 = (const uint16_t*)src;  // 18 * b is even: 2-byte aligned
-  u32x4 c;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t lo = s16[1 + 2 * i], hi = s16[2 + 2 * i];
-    c[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-  }
-  *(u32x4*)(codes + b * 16) = c;
-  scales[b] = s16[0];
+// 16-byte code chunks: canonical row-major [rows][nchunk][16] -> interleaved.
+__global__ __launch_bounds__(256) void interleave_chunks_kernel(const u32x4* __restrict__ src, uint8_t* __restrict__ dst,
+                                                                long long rows, int nchunk) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nchunk) return;
+  const long long r = i / nchunk;
+  const int c = (int)(i % nchunk);
+  *(u32x4*)(dst + ilv_chunk_off((int)r, c, nchunk)) = src[i];
 }
 
-hipError_t launch_pack_q4_0(const uint8_t* canon, uint8_t* codes, uint16_t* scales, long long nblocks, hipStream_t s) {
-  const long long grid = (nblocks + 255) / 256;
-  hipLaunchKernelGGL(pack_q4_0_kernel, dim3((unsigned)grid), dim3(256), 0, s, canon, codes, scales, nblocks);
+// one scale element per (row, chunk): canonical [rows][nchunk] -> interleaved.
+template <typename T>
+__global__ __launch_bounds__(256) void interleave_scales_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                                long long rows, int nchunk) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nchunk) return;
+  const long long r = i / nchunk;
+  const int c = (int)(i % nchunk);
+  dst[ilv_scale_idx((int)r, c, nchunk)] = src[i];
+}
+
+// GGUF Q4_0 block (fp16 scale, then byte i = element i | element i+16 << 4) -> device chunk whose
+// word w holds elements 8w+2s in bits 4s.. and 8w+2s+1 in bits 16+4s.., plus the interleaved scale.
+__global__ __launch_bounds__(256) void pack_q4_0_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales, long long rows, int nchunk) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nchunk) return;
+  const long long r = i / nchunk;
+  const int c = (int)(i % nchunk);
+  const uint8_t* blk = canon + i * 18;
+  const uint16_t* s16 = (const uint16_t*)blk;  // 18 * i is even: 2-byte aligned
+  uint32_t q[32];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint16_t two = s16[1 + b];  // code bytes 2b, 2b+1
+    const uint32_t b0 = two & 0xffu, b1 = two >> 8;
+    q[2 * b] = b0 & 15u;
+    q[2 * b + 16] = b0 >> 4;
+    q[2 * b + 1] = b1 & 15u;
+    q[2 * b + 17] = b1 >> 4;
+  }
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v |= (q[8 * w + 2 * s] << (4 * s)) | (q[8 * w + 2 * s + 1] << (16 + 4 * s));
+    o[w] = v;
+  }
+  *(u32x4*)(codes + ilv_chunk_off((int)r, c, nchunk)) = o;
+  scales[ilv_scale_idx((int)r, c, nchunk)] = s16[0];
+}
+
+static unsigned grid_for(long long n) { return (unsigned)((n + 255) / 256); }
+
+// Pack one matrix (all slots): rows = n_slots * R, K columns.
+hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
+                              uint8_t* scales, long long rows, int K, hipStream_t s) {
+  const int nchunk = K / (fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32);
+  const long long n = rows * nchunk;
+  if (n == 0) return hipSuccess;
+  if (fmt == FMT_Q4_0) {
+    hipLaunchKernelGGL(pack_q4_0_kernel, dim3(grid_for(n)), dim3(256), 0, s, canon_codes, codes, (uint16_t*)scales,
+                       rows, nchunk);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(interleave_chunks_kernel, dim3(grid_for(n)), dim3(256), 0, s, (const u32x4*)canon_codes, codes,
+                     rows, nchunk);
+  if (fmt == FMT_MXFP4)
+    hipLaunchKernelGGL(interleave_scales_kernel<uint8_t>, dim3(grid_for(n)), dim3(256), 0, s, canon_scales, scales,
+                       rows, nchunk);
+  if (fmt == FMT_FP8_B128) {
+    hipError_t e = hipMemcpyAsync(scales, canon_scales, (size_t)(rows / 128) * (K / 128) * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
-// One thread per 16-byte chunk of codes.  Values are formed exactly as the GEMV kernel forms them:
-// Chunk<FMT>::decode to bf16 pairs, then the chunk's scale applied in fp32.
+// One thread per 16-byte chunk: Chunk<FMT>::decode to bf16 pairs, then the chunk's scale applied
+// in fp32, written row-major.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                       int rows, int K, float* __restrict__ out) {
 #pragma clang fp contract(off)
   using C = Chunk<FMT>;
-  const int per_row = K / C::ELEMS;
+  const int nchunk = K / C::ELEMS;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)rows * per_row) return;
-  const int r = (int)(idx / per_row), ch = (int)(idx % per_row);
-  const size_t rbytes = FMT == FMT_BF16 ? (size_t)K * 2 : FMT == FMT_FP8_B128 ? (size_t)K : (size_t)K / 2;
-  const u32x4 c = *(const u32x4*)(codes + (size_t)r * rbytes + (size_t)ch * 16);
+  if (idx >= (long long)rows * nchunk) return;
+  const int r = (int)(idx / nchunk), c = (int)(idx % nchunk);
+  const u32x4 v = *(const u32x4*)(codes + ilv_chunk_off(r, c, nchunk));
   uint32_t p[C::PAIRS];
-  C::decode(c, p);
+  C::decode(v, p);
   float sc = 1.0f;
-  if constexpr (FMT == FMT_Q4_0) sc = fp16_bits_to_f32(((const uint16_t*)scales)[(size_t)r * (K / 32) + ch]);
-  if constexpr (FMT == FMT_MXFP4) sc = e8m0_to_f32(scales[(size_t)r * (K / 32) + ch]);
-  if constexpr (FMT == FMT_FP8_B128)
-    sc = ((const float*)scales)[(size_t)(r / 128) * (K / 128) + (ch * C::ELEMS) / 128];
-  float* o = out + (size_t)r * K + (size_t)ch * C::ELEMS;
+  if constexpr (FMT == FMT_Q4_0) sc = fp16_bits_to_f32(((const uint16_t*)scales)[ilv_scale_idx(r, c, nchunk)]);
+  if constexpr (FMT == FMT_MXFP4) sc = e8m0_to_f32(scales[ilv_scale_idx(r, c, nchunk)]);
+  if constexpr (FMT == FMT_FP8_B128) sc = ((const float*)scales)[(size_t)(r / 128) * (K / 128) + (c * C::ELEMS) / 128];
+  float* o = out + (size_t)r * K + (size_t)c * C::ELEMS;
 #pragma unroll
   for (int i = 0; i < C::PAIRS; ++i) {
     float v0 = bf16_bits_to_f32(p[i] & 0xffffu), v1 = bf16_bits_to_f32(p[i] >> 16);
@@ -63,8 +119,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       v0 = v0 * sc;
       v1 = v1 * sc;
     }
-    o[C::first(i)] = v0;
-    o[C::first(i) + C::SECOND] = v1;
+    o[2 * i] = v0;
+    o[2 * i + 1] = v1;
   }
 }
 
@@ -72,7 +128,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, 
                           hipStream_t s) {
   const int elems = fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32;
   const long long n = (long long)rows * (K / elems);
-  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  dim3 grid(grid_for(n)), block(256);
   switch (fmt) {
     case FMT_BF16: hipLaunchKernelGGL(dequant_kernel<FMT_BF16>, grid, block, 0, s, codes, scales, rows, K, out); break;
     case FMT_Q4_0: hipLaunchKernelGGL(dequant_kernel<FMT_Q4_0>, grid, block, 0, s, codes, scales, rows, K, out); break;

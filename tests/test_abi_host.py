@@ -119,13 +119,12 @@ def test_grouped_ffn_validation():
     _err(call(bank=ctypes.byref(nob)), ft.FT_E_INVAL, "scale arrays")
     bad = _bank(fmt=9)
     _err(call(bank=ctypes.byref(bad)), ft.FT_E_UNSUPPORTED, "unknown weight format")
-    odd = _bank(d=48)
-    _err(call(bank=ctypes.byref(odd)), ft.FT_E_INVAL, "multiples of 32")
+    odd = _bank(d=192)
+    _err(call(bank=ctypes.byref(odd)), ft.FT_E_INVAL, "multiple of 128")
+    odd_i = _bank(d=256, I=96)
+    _err(call(bank=ctypes.byref(odd_i)), ft.FT_E_INVAL, "multiple of 64")
     fp8 = _bank(fmt=ft.FT_W_FP8_B128, d=256, I=64)
-    _err(call(bank=ctypes.byref(fp8)), ft.FT_E_INVAL, "multiples of 128")
-    # the MFMA path needs I % 64 == 0 and d % 128 == 0
-    b96 = _bank(fmt=ft.FT_W_BF16, d=96, I=64, s=False)
-    _err(call(bank=ctypes.byref(b96), flags=ft.FT_PATH_GEMM), ft.FT_E_UNSUPPORTED, "GEMM path")
+    _err(call(bank=ctypes.byref(fp8)), ft.FT_E_INVAL, "FP8_B128 needs I")
     # workspace query: bf16 h rows for every routed pair, plus the shared expert's rows
     assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, -1, 0) == 16 * 2 * 512 * 2
     assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, 3, 0) == (16 * 2 + 16) * 512 * 2
