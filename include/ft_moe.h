@@ -78,6 +78,9 @@ enum ft_weight_format {
  * 32 four-bit codes; nchunk = K / elements-per-chunk) and stored row-interleaved in blocks of 64
  * rows: chunk c of row r sits at byte ((r/64 * nchunk + c) * 64 + r%64) * 16 of the matrix, so the
  * same chunk of 64 consecutive rows is 1 KiB of contiguous memory.  Slots are consecutive.
+ * W13 rows are stored in gate/up blocks: device row 64b + j is gate row 32b + j for j < 32 and up
+ * row I + 32b + (j - 32) for j >= 32, so every 64-row block yields 32 columns of SiLU(g) * u.
+ * W2 rows keep their order.
  *   FT_W_BF16     codes = bf16 in K order; s13 = s2 = NULL
  *   FT_W_Q4_0     32 codes of one GGUF block per chunk; 32-bit word w of a chunk holds elements
  *                 8w..8w+7, element 8w+2s in bits 4s..4s+3 and element 8w+2s+1 in bits 16+4s..19+4s;
@@ -86,7 +89,7 @@ enum ft_weight_format {
  *   FT_W_MXFP4    32 e2m1 codes per chunk in K order (element 2i low nibble of byte i, 2i+1 high);
  *                 E8M0 scales, one byte per (row, chunk), interleaved as for Q4_0
  *   FT_W_FP8_B128 16 e4m3fn codes per chunk in K order; scales fp32 [rows/128][K/128] per matrix,
- *                 row-major (not interleaved)
+ *                 row-major over logical rows (not interleaved, not reordered)
  * Array sizes per format: ft_moe_bank_bytes.  Divisibility: d a multiple of 128 and I a multiple of 64
  * (so every matrix has whole 64-row blocks and whole chunks; FP8_B128 also needs I % 128 == 0).
  */

@@ -83,7 +83,7 @@ int check_bank(const ft_moe_bank* b) {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // groups with at most this many routed rows go through the GEMV kernels when the path is automatic
-constexpr int kGemvMaxRows = 2 * ftk::GEMV_NT;
+constexpr int kGemvMaxRows = ftk::GEMV_MAX_ROWS;
 
 size_t h_bytes(int T, int k, int I, bool shared) {
   return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
@@ -214,16 +214,10 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
       gemv_max = kGemvMaxRows;
       gemm_min = kGemvMaxRows + 1;
     }
-    const int NT = ftk::GEMV_NT, BM = ftk::GEMM_BM;
+    const int BM = ftk::GEMM_BM;
     const bool run_gemv = gemv_max > 0;
     const bool run_gemm = gemm_min <= T;  // no group has more than T rows
-    long long gemv_chunks = 0, gemm_tiles = 0;
-    if (run_gemv) {
-      const long long per_group = (gemv_max >= T) ? (T + NT - 1) / NT : (gemv_max + NT - 1) / NT;
-      const long long a1 = groups_upper * per_group;
-      const long long a2 = (rows_total + NT - 1) / NT + groups_upper;
-      gemv_chunks = a1 < a2 ? a1 : a2;
-    }
+    long long gemm_tiles = 0;
     if (run_gemm) {
       const long long big_upper = rows_total / gemm_min + 1;
       const long long g_up = big_upper < groups_upper ? big_upper : groups_upper;
@@ -233,7 +227,7 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     if (run_gemv) {
       a.min_cnt = 1;
       a.max_cnt = gemv_max;
-      e = ftk::launch_gemv_gateup(a, (int)gemv_chunks, stream);
+      e = ftk::launch_gemv_gateup(a, (int)groups_upper, rows_total, stream);
       if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv gate/up launch");
     }
     if (run_gemm) {
@@ -245,7 +239,7 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     if (run_gemv) {
       a.min_cnt = 1;
       a.max_cnt = gemv_max;
-      e = ftk::launch_gemv_down(a, (int)gemv_chunks, stream);
+      e = ftk::launch_gemv_down(a, (int)groups_upper, rows_total, stream);
       if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv down launch");
     }
     if (run_gemm) {
@@ -326,10 +320,10 @@ int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, 
         REQUIRE(canon_s13 != nullptr && canon_s2 != nullptr, FT_E_INVAL, "canonical scale arrays are null");
     }
     hipError_t e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w13, (const uint8_t*)canon_s13,
-                                           (uint8_t*)dst->w13, (uint8_t*)dst->s13, (long long)n_slots * 2 * I, d, stream);
+                                           (uint8_t*)dst->w13, (uint8_t*)dst->s13, (long long)n_slots * 2 * I, d, I, stream);
     if (e == hipSuccess)
       e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w2, (const uint8_t*)canon_s2, (uint8_t*)dst->w2,
-                                  (uint8_t*)dst->s2, (long long)n_slots * d, I, stream);
+                                  (uint8_t*)dst->s2, (long long)n_slots * d, I, 0, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_pack_bank launch");
     return ok();
   } catch (...) {
@@ -351,7 +345,8 @@ int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hip
     const uint8_t* codes = (const uint8_t*)(which == 0 ? bank->w13 : bank->w2) + per_slot * slot;
     const uint8_t* scales = nullptr;
     if (bank->fmt != FT_W_BF16) scales = (const uint8_t*)(which == 0 ? bank->s13 : bank->s2) + per_slot_s * slot;
-    return hip_status(ftk::launch_dequant(bank->fmt, codes, scales, rows, K, out, stream), "ft_moe_dequant launch");
+    return hip_status(ftk::launch_dequant(bank->fmt, codes, scales, rows, K, which == 0 ? bank->I : 0, out, stream),
+                      "ft_moe_dequant launch");
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_dequant: unexpected exception");
   }

@@ -110,6 +110,15 @@ __host__ __device__ constexpr int chunk_elems() {
   return FMT == FMT_BF16 ? 8 : FMT == FMT_FP8_B128 ? 16 : 32;
 }
 
+// W13 device row order: each 64-row block holds 32 gate rows then the 32 matching up rows, so one
+// block produces 32 columns of h.  Logical row L (gate 0..I-1, up I..2I-1) <-> device row.
+__host__ __device__ __forceinline__ int w13_device_row(int L, int I) {
+  return L < I ? 64 * (L >> 5) + (L & 31) : 64 * ((L - I) >> 5) + 32 + ((L - I) & 31);
+}
+__host__ __device__ __forceinline__ int w13_logical_row(int r, int I) {
+  return (r & 63) < 32 ? 32 * (r >> 6) + (r & 31) : I + 32 * (r >> 6) + (r & 31);
+}
+
 // Byte offset of chunk c of row r in a row-interleaved matrix with nchunk chunks per row.
 __device__ __forceinline__ size_t ilv_chunk_off(int r, int c, int nchunk) {
   return (((size_t)(r >> 6) * nchunk + c) * 64 + (r & 63)) * 16;

@@ -35,11 +35,11 @@ hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, co
                           const int32_t* inv, const int32_t* slot_of, int T, int E, int k, int d, void* out,
                           uint32_t* mask, bool out_bf16, hipStream_t s);
 
-// Streaming GEMV path (few rows per group).  chunks_upper: host-side bound on the number of
-// (group, token-chunk) pairs, used to size the grid.
-constexpr int GEMV_NT = 8;  // tokens per pass over the weights
-hipError_t launch_gemv_gateup(const FfnArgs& a, int chunks_upper, hipStream_t s);
-hipError_t launch_gemv_down(const FfnArgs& a, int chunks_upper, hipStream_t s);
+// Streaming GEMV path (few rows per group).  groups_upper / rows_upper: host-side bounds on the
+// number of groups and of rows (tokens) the launch may see, used to size the grid.
+hipError_t launch_gemv_gateup(const FfnArgs& a, int groups_upper, long long rows_upper, hipStream_t s);
+hipError_t launch_gemv_down(const FfnArgs& a, int groups_upper, long long rows_upper, hipStream_t s);
+constexpr int GEMV_MAX_ROWS = 16;  // largest group the automatic path sends to the GEMV kernels
 
 // MFMA GEMM path.
 hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s);
@@ -47,9 +47,10 @@ hipError_t launch_gemm_down(const FfnArgs& a, int tiles_upper, hipStream_t s);
 constexpr int GEMM_BM = 128;  // token rows per tile
 
 // canonical -> row-interleaved device layout for one matrix of `rows` rows (all slots) and K columns
+// (perm_I > 0: W13 of expert intermediate size perm_I, whose rows are reordered into gate/up blocks)
 hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
-                              uint8_t* scales, long long rows, int K, hipStream_t s);
-hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, float* out,
-                          hipStream_t s);
+                              uint8_t* scales, long long rows, int K, int perm_I, hipStream_t s);
+hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, int perm_I,
+                          float* out, hipStream_t s);
 
 }  // namespace ftk

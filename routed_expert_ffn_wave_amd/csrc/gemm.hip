@@ -117,14 +117,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
   // weight row of local column n
   const int half_id = tid & 1;
   const int ln = tid >> 1;  // 0..127: the A row and the B row this thread stages
-  int wrow;
-  if (GATEUP) {
-    const int j = ln >> 5, c = ln & 31;
-    const int i = nt * 64 + (j >> 1) * 32 + c;
-    wrow = (j & 1) ? a.I + i : i;
-  } else {
-    wrow = nt * BN + ln;
-  }
+  // device row of the B-tile row ln (W13 device blocks already hold 32 gate then 32 up rows, so
+  // tile nt's 128 device rows are gate i0..i0+31, up i0.., gate i0+32.., up i0+32.. with i0 = 64nt)
+  // and its logical row (for the FP8 scale grid, which is indexed by logical rows)
+  const int drow = nt * BN + ln;
+  const int wrow = GATEUP ? w13_logical_row(drow, a.I) : drow;
   const uint8_t* codes = GATEUP ? a.w13 : a.w2;
   const uint8_t* scales = GATEUP ? a.s13 : a.s2;
   const int nchunk = K / chunk_elems<FMT>();
@@ -156,12 +153,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
       av1 = p[1];
     }
     uint32_t bw[8];
-    load_b_half<FMT>(bmat, wrow, nchunk, ks, half_id, bscales, bw);
+    load_b_half<FMT>(bmat, drow, nchunk, ks, half_id, bscales, bw);
     float bsc = 1.0f;
     if constexpr (PARTIAL) {
       if ((ks % SCALE_STEPS) == 0) {
         if constexpr (FMT == FMT_Q4_0) {
-          bsc = fp16_bits_to_f32(((const uint16_t*)bscales)[ilv_scale_idx(wrow, ks, nchunk)]);
+          bsc = fp16_bits_to_f32(((const uint16_t*)bscales)[ilv_scale_idx(drow, ks, nchunk)]);
         } else {
           const float* s32 = (const float*)scales;
           bsc = s32[((size_t)slot * (ncols / 128) + wrow / 128) * (K / 128) + ks / 4];

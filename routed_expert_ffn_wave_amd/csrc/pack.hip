@@ -11,34 +11,43 @@
 
 namespace ftk {
 
+// Device row of canonical row r (all slots stacked): W13 matrices (perm_I > 0) reorder the rows of
+// each slot into gate/up blocks, W2 keeps the order.
+__device__ __forceinline__ long long device_row(long long r, int perm_I) {
+  if (perm_I == 0) return r;
+  const long long per = 2LL * perm_I, s = r / per;
+  return s * per + w13_device_row((int)(r % per), perm_I);
+}
+
 // 16-byte code chunks: canonical row-major [rows][nchunk][16] -> interleaved.
 __global__ __launch_bounds__(256) void interleave_chunks_kernel(const u32x4* __restrict__ src, uint8_t* __restrict__ dst,
-                                                                long long rows, int nchunk) {
+                                                                long long rows, int nchunk, int perm_I) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * nchunk) return;
   const long long r = i / nchunk;
   const int c = (int)(i % nchunk);
-  *(u32x4*)(dst + ilv_chunk_off((int)r, c, nchunk)) = src[i];
+  *(u32x4*)(dst + ilv_chunk_off((int)device_row(r, perm_I), c, nchunk)) = src[i];
 }
 
 // one scale element per (row, chunk): canonical [rows][nchunk] -> interleaved.
 template <typename T>
 __global__ __launch_bounds__(256) void interleave_scales_kernel(const T* __restrict__ src, T* __restrict__ dst,
-                                                                long long rows, int nchunk) {
+                                                                long long rows, int nchunk, int perm_I) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * nchunk) return;
   const long long r = i / nchunk;
   const int c = (int)(i % nchunk);
-  dst[ilv_scale_idx((int)r, c, nchunk)] = src[i];
+  dst[ilv_scale_idx((int)device_row(r, perm_I), c, nchunk)] = src[i];
 }
 
 // GGUF Q4_0 block (fp16 scale, then byte i = element i | element i+16 << 4) -> device chunk whose
 // word w holds elements 8w+2s in bits 4s.. and 8w+2s+1 in bits 16+4s.., plus the interleaved scale.
 __global__ __launch_bounds__(256) void pack_q4_0_kernel(const uint8_t* __restrict__ canon, uint8_t* __restrict__ codes,
-                                                        uint16_t* __restrict__ scales, long long rows, int nchunk) {
+                                                        uint16_t* __restrict__ scales, long long rows, int nchunk,
+                                                        int perm_I) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * nchunk) return;
-  const long long r = i / nchunk;
+  const long long r = device_row(i / nchunk, perm_I);
   const int c = (int)(i % nchunk);
   const uint8_t* blk = canon + i * 18;
   const uint16_t* s16 = (const uint16_t*)blk;  // 18 * i is even: 2-byte aligned
@@ -68,20 +77,20 @@ static unsigned grid_for(long long n) { return (unsigned)((n + 255) / 256); }
 
 // Pack one matrix (all slots): rows = n_slots * R, K columns.
 hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
-                              uint8_t* scales, long long rows, int K, hipStream_t s) {
+                              uint8_t* scales, long long rows, int K, int perm_I, hipStream_t s) {
   const int nchunk = K / (fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32);
   const long long n = rows * nchunk;
   if (n == 0) return hipSuccess;
   if (fmt == FMT_Q4_0) {
     hipLaunchKernelGGL(pack_q4_0_kernel, dim3(grid_for(n)), dim3(256), 0, s, canon_codes, codes, (uint16_t*)scales,
-                       rows, nchunk);
+                       rows, nchunk, perm_I);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(interleave_chunks_kernel, dim3(grid_for(n)), dim3(256), 0, s, (const u32x4*)canon_codes, codes,
-                     rows, nchunk);
+                     rows, nchunk, perm_I);
   if (fmt == FMT_MXFP4)
     hipLaunchKernelGGL(interleave_scales_kernel<uint8_t>, dim3(grid_for(n)), dim3(256), 0, s, canon_scales, scales,
-                       rows, nchunk);
+                       rows, nchunk, perm_I);
   if (fmt == FMT_FP8_B128) {
     hipError_t e = hipMemcpyAsync(scales, canon_scales, (size_t)(rows / 128) * (K / 128) * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
@@ -93,19 +102,20 @@ hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t
 // in fp32, written row-major.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                      int rows, int K, float* __restrict__ out) {
+                                                      int rows, int K, int perm_I, float* __restrict__ out) {
 #pragma clang fp contract(off)
   using C = Chunk<FMT>;
   const int nchunk = K / C::ELEMS;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)rows * nchunk) return;
-  const int r = (int)(idx / nchunk), c = (int)(idx % nchunk);
-  const u32x4 v = *(const u32x4*)(codes + ilv_chunk_off(r, c, nchunk));
+  const int r = (int)(idx / nchunk), c = (int)(idx % nchunk);  // logical row
+  const int dr = perm_I ? w13_device_row(r, perm_I) : r;          // its device row
+  const u32x4 v = *(const u32x4*)(codes + ilv_chunk_off(dr, c, nchunk));
   uint32_t p[C::PAIRS];
   C::decode(v, p);
   float sc = 1.0f;
-  if constexpr (FMT == FMT_Q4_0) sc = fp16_bits_to_f32(((const uint16_t*)scales)[ilv_scale_idx(r, c, nchunk)]);
-  if constexpr (FMT == FMT_MXFP4) sc = e8m0_to_f32(scales[ilv_scale_idx(r, c, nchunk)]);
+  if constexpr (FMT == FMT_Q4_0) sc = fp16_bits_to_f32(((const uint16_t*)scales)[ilv_scale_idx(dr, c, nchunk)]);
+  if constexpr (FMT == FMT_MXFP4) sc = e8m0_to_f32(scales[ilv_scale_idx(dr, c, nchunk)]);
   if constexpr (FMT == FMT_FP8_B128) sc = ((const float*)scales)[(size_t)(r / 128) * (K / 128) + (c * C::ELEMS) / 128];
   float* o = out + (size_t)r * K + (size_t)c * C::ELEMS;
 #pragma unroll
@@ -124,16 +134,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
-hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, float* out,
-                          hipStream_t s) {
+hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, int perm_I,
+                          float* out, hipStream_t s) {
   const int elems = fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32;
   const long long n = (long long)rows * (K / elems);
   dim3 grid(grid_for(n)), block(256);
   switch (fmt) {
-    case FMT_BF16: hipLaunchKernelGGL(dequant_kernel<FMT_BF16>, grid, block, 0, s, codes, scales, rows, K, out); break;
-    case FMT_Q4_0: hipLaunchKernelGGL(dequant_kernel<FMT_Q4_0>, grid, block, 0, s, codes, scales, rows, K, out); break;
-    case FMT_MXFP4: hipLaunchKernelGGL(dequant_kernel<FMT_MXFP4>, grid, block, 0, s, codes, scales, rows, K, out); break;
-    default: hipLaunchKernelGGL(dequant_kernel<FMT_FP8_B128>, grid, block, 0, s, codes, scales, rows, K, out); break;
+    case FMT_BF16: hipLaunchKernelGGL(dequant_kernel<FMT_BF16>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
+    case FMT_Q4_0: hipLaunchKernelGGL(dequant_kernel<FMT_Q4_0>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
+    case FMT_MXFP4: hipLaunchKernelGGL(dequant_kernel<FMT_MXFP4>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
+    default: hipLaunchKernelGGL(dequant_kernel<FMT_FP8_B128>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
   }
   return hipGetLastError();
 }
