@@ -135,6 +135,62 @@ def cpu_baseline(w: synth.Workload, T: int, budget_s: float):
     return t_total, n
 
 
+def copy_probe(nbytes: int, reps: int = 5):
+    """A plain elementwise copy of known size (fp32 negation: reads and writes `nbytes` each),
+    the calibration kernel for the HBM byte counters."""
+    src = torch.randn(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} x neg over {nbytes} bytes")
+
+
+def _pmc_per_kernel(path: str, counter: str):
+    """Average value of one counter per dispatch, by kernel name, from a rocprofv3 counter CSV."""
+    import csv
+    acc = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            a = acc.setdefault(row["Kernel_Name"], [0.0, 0])
+            a[0] += float(row["Counter_Value"])
+            a[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
+
+
+def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str):
+    """HBM bytes per grouped-FFN call from two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the counter reads for the copy probe of known size.  Every FFN
+    call launches one dispatch of each FFN kernel, so per-call bytes sum the kernels' averages."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "neg_kernel" in k]
+    copy_w = [v for k, v in write.items() if "neg_kernel" in k]
+    assert copy_f and copy_w, "the copy probe was not profiled"
+    kib = copy_bytes / 1024.0
+    f_fetch, f_write = kib / copy_f[0][0], kib / copy_w[0][0]
+    kernels = {}
+    for name, (v, n) in fetch.items():
+        if "ftk::" not in name or "gemv" not in name and "gemm" not in name and "ffn" not in name:
+            continue
+        wv = write.get(name, (0.0, 0))[0]
+        kernels[name] = {"dispatches": n, "fetch_kib": round(v, 1), "write_kib": round(wv, 1),
+                         "fetch_bytes": round(v * 1024 * f_fetch), "write_bytes": round(wv * 1024 * f_write)}
+    rec = {"T": T, "source_hash": kernel_source_hash(), "copy_probe_bytes": copy_bytes,
+           "copy_factor_fetch": round(f_fetch, 5), "copy_factor_write": round(f_write, 5), "kernels": kernels,
+           "fetch_bytes_per_call": sum(k["fetch_bytes"] for k in kernels.values()),
+           "write_bytes_per_call": sum(k["write_bytes"] for k in kernels.values())}
+    rec["bytes_per_call"] = rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"]
+    db = json.load(open(out_json)) if os.path.exists(out_json) else {}
+    db[workload] = rec
+    with open(out_json, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +202,16 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--ffn-reps", type=int, default=3)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="first run the counter-calibration copy kernel over BYTES")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        w = synth.WORKLOADS[args.workload]
+        pmc_summary(w.name, args.T or w.T, args.pmc_summary[0], args.pmc_summary[1], args.copy_probe,
+                    os.path.join(ROOT, "profiles", "traffic.json"))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this layer is not sharded across GPUs here "
@@ -157,6 +222,8 @@ def main():
     T = args.T or w.T
     n_layers = args.layers or w.layers
     decode = T <= 64
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}")
     layers = build_layers(w, T, n_layers)
 

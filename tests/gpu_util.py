@@ -91,3 +91,54 @@ def compare_layer(li: synth.LayerInputs, g: dict, tokens=None, label=""):
     log(f"{label}: ok; oracle {t_ora:.1f}s on {len(tok)} tokens; errors " +
         ", ".join(f"{k} rel-L2 {v[0]:.2e} max {v[1]:.2e}" for k, v in errs.items()))
     return ora, errs
+
+
+def run_gpu_layer_graph(li: synth.LayerInputs, bank_dev, replays: int = 2):
+    """The benchmark's launch configuration: MoELayer's four calls captured once into a HIP graph
+    on a side stream and replayed; every replay must reproduce the eager result bit for bit.
+    `li` may hold device tensors (inputs generated on the GPU)."""
+    import routed_expert_ffn_wave_amd as ft
+    w = li.workload
+    T = li.T
+    layer = ft.MoELayer(bank_dev, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot)
+    logits, x = li.logits.cuda(), li.x.cuda()
+    out, mask = layer.forward(logits, x)
+    eager = out.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        layer.forward(logits, x)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            layer.forward(logits, x)
+    torch.cuda.synchronize()
+    for _ in range(replays):
+        layer.out.zero_()
+        layer.y_sorted.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out[:T], eager), "graph replay differs from the eager layer"
+    n = T * w.k
+    return dict(ids=layer.ids[:T].cpu().numpy(), w=layer.w[:T].cpu().numpy(), counts=layer.counts.cpu().numpy(),
+                offsets=layer.offsets.cpu().numpy(), gather=layer.gather[:n].cpu().numpy(),
+                inv=layer.inv[:n].cpu().numpy(), y_sorted=layer.y_sorted[:n],
+                y_shared=None if layer.y_shared is None else layer.y_shared[:T],
+                out=layer.out[:T].float().cpu().numpy(), mask=layer.mask[:T].cpu().numpy().astype(np.uint32))
+
+
+def host_inputs(li: synth.LayerInputs) -> synth.LayerInputs:
+    """Host copy of device-generated inputs, for the oracle."""
+    return synth.LayerInputs(li.workload, li.layer, li.T, li.logits.cpu(), li.x.cpu(), li.slot_of_expert.cpu(),
+                             li.bank.to("cpu"))
+
+
+def sample_tokens(T: int, n: int, seed: int):
+    """A seeded sample of n tokens that always holds the first and the last token."""
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.unique(np.concatenate([[0, T - 1], mid]))

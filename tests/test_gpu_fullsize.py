@@ -1,0 +1,106 @@
+"""GPU parity at the workloads' full sizes, in the benchmark's launch configuration: MoELayer's four
+calls captured into a HIP graph and replayed.  Inputs follow the seeded recipe, generated on the GPU
+(large banks) and copied to the host for the oracle.  Routing, permutation and mask are compared
+bit for bit over the whole layer; FFN rows and outputs over every token where the oracle finishes
+in seconds, else over a seeded token sample that holds the first and last token."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import synth
+from gpu_util import compare_layer, device_bank, host_inputs, log, run_gpu_layer_graph, sample_tokens
+
+pytestmark = pytest.mark.gpu
+W = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def ft():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import routed_expert_ffn_wave_amd as ft
+    return ft
+
+
+def _inputs(w: synth.Workload, layer: int, T: int, bank=None):
+    """Device inputs of one layer; `bank` reuses an already generated (canonical, host) bank."""
+    L = synth.logits(w, layer, T, device="cuda")
+    x = synth.activations(w, layer, T, device="cuda")
+    slot = synth.slot_table(w, layer)
+    if bank is None:
+        bank = synth.make_bank(w, layer, device="cuda").to("cpu")
+    return synth.LayerInputs(w, layer, T, L, x, slot, bank)
+
+
+def _make_bank(w: synth.Workload, layer: int):
+    """synth.make_bank on the GPU, slot by slot with progress lines."""
+    experts = synth.slot_experts(w, layer)
+    bank = synth.empty_bank(w.fmt, len(experts), w.d, w.I, device="cuda")
+    for s, e in enumerate(experts):
+        w13, w2 = synth.expert_weights(w, layer, e, device="cuda")
+        synth.fill_slot(bank, s, w13, w2)
+        if (s + 1) % 32 == 0 or s + 1 == len(experts):
+            torch.cuda.synchronize()
+            log(f"{w.name}: {s + 1}/{len(experts)} slots generated")
+    return bank
+
+
+def _check(ft, li, bank_dev, n_sample: int, label: str):
+    log(f"{label}: T={li.T} d={li.workload.d} E={li.workload.E} k={li.workload.k} I={li.workload.I}")
+    g = run_gpu_layer_graph(li, bank_dev)
+    host = host_inputs(li)
+    tokens = None if li.T <= n_sample else sample_tokens(li.T, n_sample, seed=li.T + 17 * li.layer)
+    compare_layer(host, g, tokens=tokens, label=label)
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_decode_q4_0_full(ft, layer):
+    w = W["decode_q4_0"]
+    li = _inputs(w, layer, w.T)
+    _check(ft, li, device_bank(li.bank), n_sample=w.T, label=f"decode_q4_0 layer {layer}")
+
+
+def test_prefill_bf16_zipf_full(ft):
+    w = W["prefill_bf16_zipf"]
+    li = _inputs(w, 0, w.T)
+    _check(ft, li, device_bank(li.bank), n_sample=12, label="prefill_bf16_zipf")
+
+
+@pytest.fixture(scope="module")
+def mxfp4_bank(ft):
+    w = W["mxfp4_shared"]
+    log("generating the mxfp4_shared bank (257 slots)")
+    canon = _make_bank(w, 0)
+    host = canon.to("cpu")
+    dev = device_bank(canon)
+    del canon
+    torch.cuda.empty_cache()
+    return host, dev
+
+
+@pytest.mark.parametrize("T,n_sample", [(16, 16), (8192, 8)])
+def test_mxfp4_shared_full(ft, mxfp4_bank, T, n_sample):
+    w = W["mxfp4_shared"]
+    host, dev = mxfp4_bank
+    li = _inputs(w, 0, T, bank=host)
+    _check(ft, li, dev, n_sample=n_sample, label=f"mxfp4_shared T={T}")
+
+
+@pytest.fixture(scope="module")
+def fp8_bank(ft):
+    w = W["fp8_resident"]
+    log("generating the fp8_resident bank (96 resident slots)")
+    canon = _make_bank(w, 0)
+    host = canon.to("cpu")
+    dev = device_bank(canon)
+    del canon
+    torch.cuda.empty_cache()
+    return host, dev
+
+
+@pytest.mark.parametrize("T,n_sample", [(1, 1), (16, 16), (256, 8), (4096, 8), (16384, 8)])
+def test_fp8_resident_full(ft, fp8_bank, T, n_sample):
+    w = W["fp8_resident"]
+    host, dev = fp8_bank
+    li = _inputs(w, 0, T, bank=host)
+    _check(ft, li, dev, n_sample=n_sample, label=f"fp8_resident T={T}")
