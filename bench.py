@@ -70,8 +70,8 @@ def run_step(layers):
 
 
 def algorithmic_work(w: synth.Workload, layers, T: int):
-    """Per grouped-FFN call, averaged over the layers, from the actual routing:
-    bytes = touched resident experts (+ shared) x stored bytes per expert + x rows + y_sorted rows,
+    """Per layer call, averaged over the layers, from the actual routing of each layer:
+    bytes = touched resident experts (+ shared) x stored bytes per expert + x + logits + out,
     flops = 2 * 3 * d * I per computed (token, expert) pair."""
     per_expert = synth.expert_bytes(w.fmt, w.d, w.I)
     tot_b, tot_f, tot_pairs, tot_touched = 0.0, 0.0, 0, 0
@@ -83,35 +83,24 @@ def algorithmic_work(w: synth.Workload, layers, T: int):
         pairs = int(counts[resident].sum()) + (T if w.shared else 0)
         tot_touched += touched
         tot_pairs += pairs
-        tot_b += touched * per_expert + T * w.d * 2 + pairs * w.d * 2
+        tot_b += touched * per_expert + T * w.d * 2 + T * w.E * 4 + T * w.d * layer.out.element_size()
         tot_f += 2.0 * 3.0 * w.d * w.I * pairs
     n = len(layers)
     return tot_b / n, tot_f / n, tot_pairs / n, tot_touched / n
 
 
-def time_ffn_calls(layers, reps: int):
-    """Average duration of one grouped-FFN call, with HIP events on the current stream."""
+def time_layer_calls(layers, reps: int):
+    """Average duration of one layer call (ft_moe_layer: its kernels back to back), with HIP events
+    recorded on the stream the kernels run on, over eager passes through the layers."""
     s = torch.cuda.current_stream()
     evs = []
     for _ in range(reps):
         for layer, logits, x in layers:
-            T, E, k = layer.T, layer.E, layer.k
-            st = ft._stream(s)
-            ft._check(ft.lib.ft_moe_route(ft._ptr(logits), T, E, k, ft._ptr(layer.ids), ft._ptr(layer.w), st))
-            ft._check(ft.lib.ft_moe_permute(ft._ptr(layer.ids), T, E, k, ft._ptr(layer.counts),
-                                            ft._ptr(layer.offsets), ft._ptr(layer.gather), ft._ptr(layer.inv),
-                                            ft._ptr(layer.perm_ws), layer.perm_ws.numel(), st))
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(s)
-            ft._check(ft.lib.ft_moe_grouped_ffn(layer.bank.ref, ft._ptr(layer.slot_of), layer.shared_slot, ft._ptr(x),
-                                                T, E, k, ft._ptr(layer.offsets), ft._ptr(layer.gather),
-                                                ft._ptr(layer.y_sorted), ft._ptr(layer.y_shared),
-                                                ft._ptr(layer.ffn_ws), layer.ffn_ws.numel(), layer.flags, st))
+            layer.forward(logits, x, stream=s)
             e1.record(s)
-            ft._check(ft.lib.ft_moe_combine(ft._ptr(layer.y_sorted), ft._ptr(layer.y_shared), ft._ptr(layer.ids),
-                                            ft._ptr(layer.w), ft._ptr(layer.inv), ft._ptr(layer.slot_of), T, E, k,
-                                            layer.bank.d, ft._ptr(layer.out), ft._ptr(layer.mask), 0, st))
             evs.append((e0, e1))
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in evs]
@@ -161,9 +150,9 @@ def _pmc_per_kernel(path: str, counter: str):
 
 
 def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str):
-    """HBM bytes per grouped-FFN call from two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch), each scaled by what the counter reads for the copy probe of known size.  Every FFN
-    call launches one dispatch of each FFN kernel, so per-call bytes sum the kernels' averages."""
+    """HBM bytes per layer call from two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the counter reads for the copy probe of known size: the bytes of
+    every dispatch of the layer's kernels divided by the number of layer calls."""
     fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
     copy_f = [v for k, v in fetch.items() if "neg_kernel" in k]
@@ -173,15 +162,19 @@ def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_byte
     f_fetch, f_write = kib / copy_f[0][0], kib / copy_w[0][0]
     kernels = {}
     for name, (v, n) in fetch.items():
-        if "ftk::" not in name or "gemv" not in name and "gemm" not in name and "ffn" not in name:
+        if "ftk::" not in name or "pack" in name or "dequant" in name or "interleave" in name:
             continue
         wv = write.get(name, (0.0, 0))[0]
         kernels[name] = {"dispatches": n, "fetch_kib": round(v, 1), "write_kib": round(wv, 1),
                          "fetch_bytes": round(v * 1024 * f_fetch), "write_bytes": round(wv * 1024 * f_write)}
+    # every layer call launches exactly one routing kernel
+    calls = sum(k["dispatches"] for name, k in kernels.items() if "route" in name)
+    assert calls > 0, "no routing kernel in the counter run"
+    per_call = lambda key: round(sum(k[key] * k["dispatches"] for k in kernels.values()) / calls)
     rec = {"T": T, "source_hash": kernel_source_hash(), "copy_probe_bytes": copy_bytes,
            "copy_factor_fetch": round(f_fetch, 5), "copy_factor_write": round(f_write, 5), "kernels": kernels,
-           "fetch_bytes_per_call": sum(k["fetch_bytes"] for k in kernels.values()),
-           "write_bytes_per_call": sum(k["write_bytes"] for k in kernels.values())}
+           "layer_calls": calls, "fetch_bytes_per_call": per_call("fetch_bytes"),
+           "write_bytes_per_call": per_call("write_bytes")}
     rec["bytes_per_call"] = rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"]
     db = json.load(open(out_json)) if os.path.exists(out_json) else {}
     db[workload] = rec
@@ -259,8 +252,8 @@ def main():
     us_per_layer = ms_per_step * 1e3 / n_layers
     log(f"{ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer")
 
-    # ---- dominant unit: the grouped-FFN call, event-timed on its stream
-    ffn_us = time_ffn_calls(layers, args.ffn_reps)
+    # ---- dominant unit: the layer call, event-timed on its stream
+    ffn_us = time_layer_calls(layers, args.ffn_reps)
     bytes_call, flops_call, pairs, touched = algorithmic_work(w, layers, T)
     if decode:
         achieved = bytes_call / (ffn_us * 1e-6) / 1e9
@@ -278,11 +271,12 @@ def main():
         rec = json.load(open(prof)).get(w.name)
         if rec and rec.get("source_hash") == src_hash and rec.get("T") == T:
             roof["traffic"] = rec["bytes_per_call"]
-    roof["kernel"] = "ft_moe_grouped_ffn (gate/up then down, " + ("streaming GEMV" if decode else "MFMA GEMM") + ")"
+    roof["kernel"] = ("ft_moe_layer: route_permute_kernel + ffn_combine_kernel (streaming GEMV, fused combine)"
+                      if T <= 16 else "ft_moe_layer: route, permute, grouped FFN (MFMA GEMM + GEMV), combine")
     roof["per_call_us"] = round(ffn_us, 3)
     roof["algorithmic_bytes_per_call"] = round(bytes_call)
     roof["algorithmic_flops_per_call"] = round(flops_call)
-    log(f"FFN call {ffn_us:.2f} us; {touched:.1f} experts touched, {pairs:.1f} pairs; {roof}")
+    log(f"layer call {ffn_us:.2f} us; {touched:.1f} experts touched, {pairs:.1f} pairs; {roof}")
 
     # ---- CPU baseline: the oracle on host cores, bounded sample
     cpu = None

@@ -66,8 +66,11 @@ enum ft_weight_format {
 #define FT_PATH_GEMM 0x2  /* every group through the MFMA GEMM kernels */
 #define FT_PATH_MASK 0x3
 
-/* ft_moe_combine flags */
+/* ft_moe_combine / ft_moe_layer flags */
 #define FT_OUT_BF16 0x4   /* write `out` as bf16 instead of fp32 */
+
+/* ft_moe_layer flags */
+#define FT_LAYER_UNFUSED 0x8  /* always run the four calls' kernels, never the fused decode kernels */
 
 /*
  * Expert bank in DEVICE layout (passed by host pointer; the struct itself is read on the host).
@@ -173,6 +176,35 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
 int ft_moe_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids,
                    const float* w, const int32_t* inv, const int32_t* slot_of_expert, int T, int E,
                    int k, int d, void* out, uint32_t* residual_mask, int flags, hipStream_t stream);
+
+/*
+ * Bytes of workspace ft_moe_layer needs (0 for invalid arguments).  `bank` is a host pointer.
+ */
+size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags);
+
+/*
+ * The whole layer in one call: exactly ft_moe_route, ft_moe_permute, ft_moe_grouped_ffn and
+ * ft_moe_combine on the same arguments, with every intermediate result written to the caller's
+ * buffers (ids, w, counts, offsets, gather, inv, y_sorted, y_shared) and the same definitions.
+ * For decode batches (1 <= T <= 16, path not FT_PATH_GEMM, no FT_LAYER_UNFUSED) it runs two
+ * kernels instead of the calls' five or more: a one-block route + permute prologue, then one kernel
+ * that runs every gate/up item, every down item and the combine, ordered by device-side dependency
+ * counters (no host synchronisation; the sequence is graph-capturable).  Its results
+ * equal the four calls' within rounding (the partial sums of a row may be added in another
+ * grouping); here a slot_of_expert entry outside [0, n_slots) counts as not resident everywhere.
+ * Dispatch and combine follow [walk-through] sections 一 and 五.
+ * ws: device workspace of ft_moe_layer_workspace(...) bytes, zero-filled by the caller before its
+ * first use; every call leaves it ready for the next one (the fused kernel returns its counters to
+ * zero).  Its first int32 is a status word that the fused kernel sets non-zero if an internal
+ * dependency wait gave up (results are then invalid); the library never clears it, and it stays 0
+ * in every correct run.  Calls that may overlap need separate workspaces.
+ * flags: FT_PATH_*, FT_OUT_BF16, FT_LAYER_UNFUSED.  T == 0 only writes counts = offsets = 0.
+ */
+int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
+                 const float* logits, const uint16_t* x, int T, int E, int k, int32_t* ids, float* w,
+                 int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* inv, uint16_t* y_sorted,
+                 uint16_t* y_shared, void* out, uint32_t* residual_mask, void* ws, size_t ws_bytes,
+                 int flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------ set-up calls */
 

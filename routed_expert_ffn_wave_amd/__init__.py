@@ -19,6 +19,9 @@ FT_OK, FT_E_INVAL, FT_E_UNSUPPORTED, FT_E_WORKSPACE, FT_E_HIP, FT_E_INTERNAL = r
 FT_W_BF16, FT_W_Q4_0, FT_W_MXFP4, FT_W_FP8_B128 = range(4)
 FT_PATH_AUTO, FT_PATH_GEMV, FT_PATH_GEMM = 0, 1, 2
 FT_OUT_BF16 = 4
+FT_LAYER_UNFUSED = 8
+FT_PATH_MASK = 3
+LAYER_MAX_T = 16   # largest T of the fused decode kernels
 
 STATUS_NAMES = {0: "FT_OK", 1: "FT_E_INVAL", 2: "FT_E_UNSUPPORTED", 3: "FT_E_WORKSPACE", 4: "FT_E_HIP",
                 5: "FT_E_INTERNAL"}
@@ -55,6 +58,8 @@ def _load():
         "ft_moe_bank_bytes": ([i, i, i, i, i], sz),
         "ft_moe_pack_bank": ([i, i, i, i, P, P, P, P, BP, P], i),
         "ft_moe_dequant": ([BP, i, i, P, P], i),
+        "ft_moe_layer_workspace": ([BP, i, i, i, i, i], sz),
+        "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -67,7 +72,7 @@ lib = _load()
 
 EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
-            "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant")
+            "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -210,14 +215,17 @@ def ft_moe_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, d: int, out=
 class MoELayer:
     """One MoE layer over a device bank with every buffer preallocated for a fixed (T, k).
 
-    forward() enqueues the four calls on the current stream and allocates nothing, so it can be
-    replayed in a loop or captured into a CUDA/HIP graph by the caller."""
+    forward() enqueues the layer on the current stream and allocates nothing, so it can be replayed
+    in a loop or captured into a CUDA/HIP graph by the caller.  mode "layer" makes one ft_moe_layer
+    call (the fused decode kernels where they apply); mode "calls" makes the four separate calls."""
 
     def __init__(self, bank: DeviceBank, slot_of_expert: torch.Tensor, k: int, T: int, shared_slot: int = -1,
-                 flags: int = FT_PATH_AUTO, out_bf16: bool = False):
+                 flags: int = FT_PATH_AUTO, out_bf16: bool = False, mode: str = "layer"):
+        if mode not in ("layer", "calls"):
+            raise ValueError(f"mode must be 'layer' or 'calls', not {mode!r}")
         dev = bank.w13.device
         E = slot_of_expert.shape[0]
-        self.bank, self.slot_of, self.k, self.T, self.E = bank, slot_of_expert, k, T, E
+        self.bank, self.slot_of, self.k, self.T, self.E, self.mode = bank, slot_of_expert, k, T, E, mode
         self.shared_slot, self.flags, self.out_flags = shared_slot, flags, FT_OUT_BF16 if out_bf16 else 0
         d = bank.d
         n = max(T * k, 1)
@@ -227,18 +235,39 @@ class MoELayer:
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.gather = torch.empty(n, dtype=torch.int32, device=dev)
         self.inv = torch.empty(n, dtype=torch.int32, device=dev)
-        pws = lib.ft_moe_permute_workspace(T, E, k)
-        self.perm_ws = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
         self.y_sorted = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
         self.y_shared = torch.empty(max(T, 1), d, dtype=torch.bfloat16, device=dev) if shared_slot >= 0 else None
-        fws = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
-        self.ffn_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
         self.out = torch.empty(max(T, 1), d, dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
         self.mask = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+        if mode == "layer":
+            lws = lib.ft_moe_layer_workspace(bank.ref, T, E, k, shared_slot, flags | self.out_flags)
+            if lws == 0:
+                raise FtError(FT_E_INVAL, f"invalid layer shape T={T} E={E} k={k}")
+            self.ws = torch.zeros(lws, dtype=torch.uint8, device=dev)
+        else:
+            pws = lib.ft_moe_permute_workspace(T, E, k)
+            self.perm_ws = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
+            fws = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
+            self.ffn_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
+
+        # the header's rule for the fused decode kernels
+        self.fused = (mode == "layer" and 1 <= T <= LAYER_MAX_T and (flags & FT_PATH_MASK) != FT_PATH_GEMM
+                      and not flags & FT_LAYER_UNFUSED)
+
+    def status_word(self) -> int:
+        """The fused path's status word (non-zero: an internal wait gave up).  Synchronises."""
+        return int(self.ws[:4].view(torch.int32).item()) if self.fused else 0
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, stream=None):
         T, E, k = self.T, self.E, self.k
         s = _stream(stream)
+        if self.mode == "layer":
+            _check(lib.ft_moe_layer(self.bank.ref, _ptr(self.slot_of), self.shared_slot, _ptr(logits), _ptr(x), T, E,
+                                    k, _ptr(self.ids), _ptr(self.w), _ptr(self.counts), _ptr(self.offsets),
+                                    _ptr(self.gather), _ptr(self.inv), _ptr(self.y_sorted), _ptr(self.y_shared),
+                                    _ptr(self.out), _ptr(self.mask), _ptr(self.ws), self.ws.numel(),
+                                    self.flags | self.out_flags, s))
+            return self.out[:T], self.mask[:T]
         _check(lib.ft_moe_route(_ptr(logits), T, E, k, _ptr(self.ids), _ptr(self.w), s))
         _check(lib.ft_moe_permute(_ptr(self.ids), T, E, k, _ptr(self.counts), _ptr(self.offsets), _ptr(self.gather),
                                   _ptr(self.inv), _ptr(self.perm_ws), self.perm_ws.numel(), s))

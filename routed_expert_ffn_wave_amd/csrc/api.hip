@@ -89,6 +89,122 @@ size_t h_bytes(int T, int k, int I, bool shared) {
   return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
 }
 
+// FfnArgs for one grouped-FFN call and its launches (arguments already validated).
+int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
+                       int T, int E, int k, const int32_t* offsets, const int32_t* gather, uint16_t* y_sorted,
+                       uint16_t* y_shared, uint16_t* h, int flags, hipStream_t stream) {
+  const int path = flags & FT_PATH_MASK;
+  const bool shared = shared_slot >= 0;
+  ftk::FfnArgs a{};
+  a.fmt = bank->fmt;
+  a.d = bank->d;
+  a.I = bank->I;
+  a.n_slots = bank->n_slots;
+  a.w13 = (const uint8_t*)bank->w13;
+  a.w2 = (const uint8_t*)bank->w2;
+  a.s13 = (const uint8_t*)bank->s13;
+  a.s2 = (const uint8_t*)bank->s2;
+  a.slot_of = slot_of_expert;
+  a.shared_slot = shared_slot;
+  a.x = x;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.offsets = offsets;
+  a.gather = gather;
+  a.h = h;
+  a.y_sorted = y_sorted;
+  a.y_shared = y_shared;
+
+  // Which groups each kernel family takes (by routed-row count).  A group never has more than
+  // T rows (top-k ids of a token are distinct); the shared group has exactly T.
+  const long long TK = (long long)T * k;
+  const long long rows_total = TK + (shared ? T : 0);
+  const long long groups_upper = (long long)(E < TK ? E : TK) + (shared ? 1 : 0);
+  int gemv_max, gemm_min;
+  if (path == FT_PATH_GEMV) {
+    gemv_max = 0x7fffffff;
+    gemm_min = 0x7fffffff;
+  } else if (path == FT_PATH_GEMM) {
+    gemv_max = 0;
+    gemm_min = 1;
+  } else {
+    gemv_max = kGemvMaxRows;
+    gemm_min = kGemvMaxRows + 1;
+  }
+  const int BM = ftk::GEMM_BM;
+  const bool run_gemv = gemv_max > 0;
+  const bool run_gemm = gemm_min <= T;  // no group has more than T rows
+  long long gemm_tiles = 0;
+  if (run_gemm) {
+    const long long big_upper = rows_total / gemm_min + 1;
+    const long long g_up = big_upper < groups_upper ? big_upper : groups_upper;
+    gemm_tiles = (rows_total + BM - 1) / BM + g_up;
+  }
+  hipError_t e = hipSuccess;
+  if (run_gemv) {
+    a.min_cnt = 1;
+    a.max_cnt = gemv_max;
+    e = ftk::launch_gemv_gateup(a, (int)groups_upper, rows_total, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv gate/up launch");
+  }
+  if (run_gemm) {
+    a.min_cnt = gemm_min;
+    a.max_cnt = 0x7fffffff;
+    e = ftk::launch_gemm_gateup(a, (int)gemm_tiles, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm gate/up launch");
+  }
+  if (run_gemv) {
+    a.min_cnt = 1;
+    a.max_cnt = gemv_max;
+    e = ftk::launch_gemv_down(a, (int)groups_upper, rows_total, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv down launch");
+  }
+  if (run_gemm) {
+    a.min_cnt = gemm_min;
+    a.max_cnt = 0x7fffffff;
+    e = ftk::launch_gemm_down(a, (int)gemm_tiles, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm down launch");
+  }
+  return ok();
+}
+
+// Workspace of ft_moe_layer: control words and the fused path's counters, then the h rows and the
+// permutation workspace of the unfused path.
+struct LayerWs {
+  size_t ctl, done13, cdone, h, perm, total;
+  int n_rc;
+};
+
+bool layer_fused(int T, int flags) {
+  return T >= 1 && T <= ftk::LAYER_MAX_T && (flags & FT_LAYER_UNFUSED) == 0 &&
+         (flags & FT_PATH_MASK) != FT_PATH_GEMM;
+}
+
+LayerWs layer_ws(int d, int I, int T, int E, int k, bool shared, bool fused) {
+  LayerWs L{};
+  size_t o = 0;
+  L.ctl = o;
+  o += round256((size_t)ftk::CTL_INTS * 4);
+  L.n_rc = fused ? ftk::layer_decode_rowchunks_upper(T, E, k, shared) : 0;
+  L.done13 = o;
+  o += round256((size_t)L.n_rc * ftk::CNT_STRIDE * 4);
+  L.cdone = o;
+  o += fused ? round256((size_t)T * (d / 64) * ftk::CNT_STRIDE * 4) : 0;
+  L.h = o;
+  o += h_bytes(T, k, I, shared);
+  L.perm = o;
+  o += round256(ftk::permute_workspace_bytes(T, E, k));
+  L.total = o;
+  return L;
+}
+
+int id_bits_of(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,78 +293,8 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
             need, ws_bytes, ws ? "" : ", null pointer");
     REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
 
-    ftk::FfnArgs a{};
-    a.fmt = bank->fmt;
-    a.d = bank->d;
-    a.I = bank->I;
-    a.n_slots = bank->n_slots;
-    a.w13 = (const uint8_t*)bank->w13;
-    a.w2 = (const uint8_t*)bank->w2;
-    a.s13 = (const uint8_t*)bank->s13;
-    a.s2 = (const uint8_t*)bank->s2;
-    a.slot_of = slot_of_expert;
-    a.shared_slot = shared_slot;
-    a.x = x;
-    a.T = T;
-    a.E = E;
-    a.k = k;
-    a.offsets = offsets;
-    a.gather = gather;
-    a.h = (uint16_t*)ws;
-    a.y_sorted = y_sorted;
-    a.y_shared = y_shared;
-
-    // Which groups each kernel family takes (by routed-row count).  A group never has more than
-    // T rows (top-k ids of a token are distinct); the shared group has exactly T.
-    const long long TK = (long long)T * k;
-    const long long rows_total = TK + (shared ? T : 0);
-    const long long groups_upper = (long long)(E < TK ? E : TK) + (shared ? 1 : 0);
-    int gemv_max, gemm_min;
-    if (path == FT_PATH_GEMV) {
-      gemv_max = 0x7fffffff;
-      gemm_min = 0x7fffffff;
-    } else if (path == FT_PATH_GEMM) {
-      gemv_max = 0;
-      gemm_min = 1;
-    } else {
-      gemv_max = kGemvMaxRows;
-      gemm_min = kGemvMaxRows + 1;
-    }
-    const int BM = ftk::GEMM_BM;
-    const bool run_gemv = gemv_max > 0;
-    const bool run_gemm = gemm_min <= T;  // no group has more than T rows
-    long long gemm_tiles = 0;
-    if (run_gemm) {
-      const long long big_upper = rows_total / gemm_min + 1;
-      const long long g_up = big_upper < groups_upper ? big_upper : groups_upper;
-      gemm_tiles = (rows_total + BM - 1) / BM + g_up;
-    }
-    hipError_t e = hipSuccess;
-    if (run_gemv) {
-      a.min_cnt = 1;
-      a.max_cnt = gemv_max;
-      e = ftk::launch_gemv_gateup(a, (int)groups_upper, rows_total, stream);
-      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv gate/up launch");
-    }
-    if (run_gemm) {
-      a.min_cnt = gemm_min;
-      a.max_cnt = 0x7fffffff;
-      e = ftk::launch_gemm_gateup(a, (int)gemm_tiles, stream);
-      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm gate/up launch");
-    }
-    if (run_gemv) {
-      a.min_cnt = 1;
-      a.max_cnt = gemv_max;
-      e = ftk::launch_gemv_down(a, (int)groups_upper, rows_total, stream);
-      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv down launch");
-    }
-    if (run_gemm) {
-      a.min_cnt = gemm_min;
-      a.max_cnt = 0x7fffffff;
-      e = ftk::launch_gemm_down(a, (int)gemm_tiles, stream);
-      if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm down launch");
-    }
-    return ok();
+    return launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
+                              (uint16_t*)ws, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_grouped_ffn: unexpected exception");
   }
@@ -349,6 +395,109 @@ int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hip
                       "ft_moe_dequant launch");
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_dequant: unexpected exception");
+  }
+}
+
+size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
+  if (bank == nullptr || check_tek(T, E, k) != FT_OK || check_bank_shape(bank->fmt, bank->n_slots, bank->d, bank->I)) {
+    g_err[0] = 0;
+    return 0;
+  }
+  return layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(T, flags)).total;
+}
+
+int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
+                 const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                 int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
+                 uint32_t* residual_mask, void* ws, size_t ws_bytes, int flags, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    rc = check_bank(bank);
+    if (rc) return rc;
+    REQUIRE((flags & ~(FT_PATH_MASK | FT_OUT_BF16 | FT_LAYER_UNFUSED)) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+    REQUIRE((flags & FT_PATH_MASK) != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
+    REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
+            shared_slot, bank->n_slots);
+    REQUIRE((shared_slot >= 0) == (y_shared != nullptr), FT_E_INVAL,
+            "y_shared must be given exactly when shared_slot >= 0");
+    CHECK_PTR(counts, "counts");
+    CHECK_PTR(offsets, "offsets");
+    const bool shared = shared_slot >= 0;
+    const bool fused = layer_fused(T, flags);
+    const LayerWs W = layer_ws(bank->d, bank->I, T, E, k, shared, fused);
+    REQUIRE(ws != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
+            W.total, ws_bytes, ws ? "" : ", null pointer");
+    REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
+    uint8_t* wsb = (uint8_t*)ws;
+    if (T == 0)  // counts and offsets are still defined (all zero)
+      return hip_status(ftk::launch_permute(ids, 0, E, k, counts, offsets, gather, inv, wsb + W.perm, stream),
+                        "ft_moe_layer permute launch");
+    CHECK_PTR(slot_of_expert, "slot_of_expert");
+    CHECK_PTR(logits, "logits");
+    CHECK_PTR(x, "x");
+    CHECK_PTR(ids, "ids");
+    CHECK_PTR(w, "w");
+    CHECK_PTR(gather, "gather");
+    CHECK_PTR(inv, "inv");
+    CHECK_PTR(y_sorted, "y_sorted");
+    if (y_shared) CHECK_PTR(y_shared, "y_shared");
+    CHECK_PTR(out, "out");
+    if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
+    const bool out_bf16 = (flags & FT_OUT_BF16) != 0;
+    if (!fused) {
+      hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
+      if (e != hipSuccess) return hip_status(e, "ft_moe_layer route launch");
+      e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
+      if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
+      rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
+                              (uint16_t*)(wsb + W.h), flags & FT_PATH_MASK, stream);
+      if (rc) return rc;
+      return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, T, E, k, bank->d, out,
+                                            residual_mask, out_bf16, stream),
+                        "ft_moe_layer combine launch");
+    }
+    ftk::LayerArgs L{};
+    ftk::FfnArgs& a = L.f;
+    a.fmt = bank->fmt;
+    a.d = bank->d;
+    a.I = bank->I;
+    a.n_slots = bank->n_slots;
+    a.w13 = (const uint8_t*)bank->w13;
+    a.w2 = (const uint8_t*)bank->w2;
+    a.s13 = (const uint8_t*)bank->s13;
+    a.s2 = (const uint8_t*)bank->s2;
+    a.slot_of = slot_of_expert;
+    a.shared_slot = shared_slot;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.offsets = offsets;
+    a.gather = gather;
+    a.h = (uint16_t*)(wsb + W.h);
+    a.y_sorted = y_sorted;
+    a.y_shared = y_shared;
+    a.min_cnt = 1;
+    a.max_cnt = 0x7fffffff;
+    L.logits = logits;
+    L.ids = ids;
+    L.w = w;
+    L.counts = counts;
+    L.offsets = offsets;
+    L.gather = gather;
+    L.inv = inv;
+    L.mask = residual_mask;
+    L.out = out;
+    L.out_bf16 = out_bf16 ? 1 : 0;
+    L.id_bits = id_bits_of(E);
+    L.ctl = (int32_t*)(wsb + W.ctl);
+    L.done13 = (int32_t*)(wsb + W.done13);
+    L.n_rc = W.n_rc;
+    L.cdone = (int32_t*)(wsb + W.cdone);
+    return hip_status(ftk::launch_layer_decode(L, stream), "ft_moe_layer fused launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_layer: unexpected exception");
   }
 }
 

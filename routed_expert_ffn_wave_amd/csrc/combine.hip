@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       const float wj = s_w[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wj * bf16_bits_to_f32(v[i] & 0xffffu);
-        acc[2 * i + 1] += wj * bf16_bits_to_f32(v[i] >> 16);
+        acc[2 * i] = fmaf(wj, bf16_bits_to_f32(v[i] & 0xffffu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj, bf16_bits_to_f32(v[i] >> 16), acc[2 * i + 1]);
       }
     }
     if (y_shared) {

@@ -46,6 +46,44 @@ hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s);
 hipError_t launch_gemm_down(const FfnArgs& a, int tiles_upper, hipStream_t s);
 constexpr int GEMM_BM = 128;  // token rows per tile
 
+// ---- fused decode layer: one kernel whose blocks each route and permute the (few) tokens in LDS,
+// then share one list of gate/up and down items through per-XCD work queues, and combine.  Its
+// counters start at zero and the last block to finish returns them to zero.
+constexpr int LAYER_MAX_T = 16;   // tokens per call on the fused path (one routing wave per token)
+constexpr int LAYER_NT = 4;       // tokens per GEMV pass on the fused path
+constexpr int CNT_STRIDE = 64;    // ints between two counters: one 256-byte line each, so polls and
+                                  // updates of different counters never share a line
+constexpr int LAYER_NQ = 8;       // work queues of the fused FFN kernel (one per XCD)
+constexpr int CTL_ERR = 0;        // control word: non-zero when a dependency wait gave up
+constexpr int CTL_QUEUE = CNT_STRIDE;  // queue q's next position at CTL_QUEUE + q * CNT_STRIDE
+constexpr int CTL_EXIT = CTL_QUEUE + LAYER_NQ * CNT_STRIDE;  // blocks that have finished
+constexpr int CTL_INTS = CNT_STRIDE * (2 + LAYER_NQ);
+
+struct LayerArgs {
+  FfnArgs f;                 // the grouped FFN (offsets/gather from the prologue)
+  const float* logits;       // fp32 [T][E]
+  int32_t* ids;              // [T][k]
+  float* w;                  // [T][k]
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E+1]
+  int32_t* gather;           // [T*k]
+  int32_t* inv;              // [T*k]
+  uint32_t* mask;            // [T] or null
+  void* out;                 // fp32 or bf16 [T][d]
+  int out_bf16;
+  int id_bits;
+  int32_t* ctl;              // [CTL_INTS] control words
+  int32_t* done13;           // [n_rc][CNT_STRIDE] finished gate/up items per row chunk
+  int n_rc;                  // upper bound on row chunks (groups x token chunks)
+  int32_t* cdone;            // [T][d/64][CNT_STRIDE] contributions made per (token, 64-column block)
+};
+hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s);
+// upper bound on the row chunks (groups x chunks of LAYER_NT tokens) of a fused call
+inline int layer_decode_rowchunks_upper(int T, int E, int k, bool shared) {
+  const int groups = (E < T * k ? E : T * k) + (shared ? 1 : 0);
+  return groups + (T * k + (shared ? T : 0)) / LAYER_NT;
+}
+
 // canonical -> row-interleaved device layout for one matrix of `rows` rows (all slots) and K columns
 // (perm_I > 0: W13 of expert intermediate size perm_I, whose rows are reordered into gate/up blocks)
 hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,

@@ -15,57 +15,17 @@
 // and a workspace of per-(expert, segment) counts.
 #include "ft_device.h"
 #include "ft_kernels.h"
+#include "ft_permute.h"
 
 namespace ftk {
 
-constexpr int SEG = 1024;
 
-__device__ __forceinline__ uint64_t peers_of(int e, bool active, int id_bits) {
-  uint64_t m = __ballot(active);
-  for (int b = 0; b < id_bits; ++b) {
-    uint64_t bal = __ballot(active && ((e >> b) & 1));
-    m &= ((e >> b) & 1) ? bal : ~bal;
-  }
-  return m;
+// dynamic LDS above the default 64 KiB has to be granted per kernel
+static hipError_t allow_lds(const void* kern, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-// Walk one segment in order and scatter; `base` (LDS, length E) holds this segment's next sorted
-// position per expert and is advanced in place.  Only this wave touches `base`.
-__device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids, int n, int E, int seg_begin,
-                                                int id_bits, int* base, int32_t* __restrict__ gather,
-                                                int32_t* __restrict__ inv) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int seg_end = min(seg_begin + SEG, n);
-  for (int f0 = seg_begin; f0 < seg_end; f0 += 64) {
-    const int f = f0 + lane;
-    const int e_raw = f < seg_end ? ids[f] : 0;
-    const bool active = f < seg_end && (unsigned)e_raw < (unsigned)E;  // invalid ids get no position
-    const int e = active ? e_raw : 0;
-    const uint64_t peers = peers_of(e, active, id_bits);
-    int pos = 0;
-    if (active) {
-      pos = base[e] + __popcll(peers & lt);
-      gather[pos] = f;
-      inv[f] = pos;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // the highest lane of each peer set advances the running base
-    if (active && (peers >> lane) == 1ull) base[e] = pos + 1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-__device__ __forceinline__ void count_segment(const int32_t* __restrict__ ids, int n, int E, int seg_begin,
-                                              int* hist) {
-  const int lane = threadIdx.x & 63;
-  const int seg_end = min(seg_begin + SEG, n);
-  for (int f = seg_begin + lane; f < seg_end; f += 64) {
-    const int e = ids[f];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // ids outside [0, E) are skipped
-  }
-}
 
 // Block-wide exclusive scan, in place, of a[0..E) in LDS (E <= 16 * blockDim.x).  tmp: LDS, >= 32 ints.
 // Returns the total to every thread.  All threads of the block must call it.
@@ -107,13 +67,11 @@ __device__ int block_exclusive_scan(int* a, int E, int* tmp) {
   return total;
 }
 
-// Single block, 1024 threads (16 waves), n <= 16 * SEG.
-__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                              int id_bits, int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ gather,
-                                                              int32_t* __restrict__ inv) {
-  extern __shared__ int lds[];
+// One block of 1024 threads (16 waves), n <= 16 * SEG; ids may live in LDS or global memory.
+// lds: at least 17 * E + 32 ints.
+__device__ void permute_block(const int32_t* ids, int n, int E, int id_bits, int* lds, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ gather,
+                              int32_t* __restrict__ inv) {
   int* hist = lds;            // [16][E]: per-wave counts, then per-wave bases
   int* off = lds + 16 * E;    // [E]
   int* tmp = off + E;         // [32]
@@ -139,6 +97,15 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   for (int i = tid; i < 16 * E; i += 1024) hist[i] += off[i % E];
   __syncthreads();
   scatter_segment(ids, n, E, wv * SEG, id_bits, hist + wv * E, gather, inv);
+}
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                              int id_bits, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ gather,
+                                                              int32_t* __restrict__ inv) {
+  extern __shared__ int lds[];
+  permute_block(ids, n, E, id_bits, lds, counts, offsets, gather, inv);
 }
 
 // ---- large path: blocks of 256 threads (4 waves), one segment per wave.
@@ -228,6 +195,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
   const int bits = id_bits_for(E);
   if (n <= 16 * SEG) {
     size_t lds = (size_t)(17 * E + 32) * sizeof(int);
+    hipError_t e = allow_lds((const void*)permute_small_kernel, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, ids, n, E, bits, counts, offsets,
                        gather, inv);
     return hipGetLastError();

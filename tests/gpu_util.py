@@ -46,16 +46,18 @@ def assert_ffn_close(got, ref, what: str):
     return rel, mx
 
 
-def run_gpu_layer(li: synth.LayerInputs, bank_dev, flags=0):
-    """Run the four calls through MoELayer (the benchmark's launch configuration)."""
+def run_gpu_layer(li: synth.LayerInputs, bank_dev, flags=0, mode="layer"):
+    """Run the layer through MoELayer: one ft_moe_layer call ("layer", the benchmark's launch
+    configuration) or the four separate calls ("calls")."""
     import routed_expert_ffn_wave_amd as ft
     w = li.workload
     T = li.T
-    layer = ft.MoELayer(bank_dev, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot, flags=flags)
+    layer = ft.MoELayer(bank_dev, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot, flags=flags, mode=mode)
     logits = li.logits.cuda()
     x = li.x.cuda()
     out, mask = layer.forward(logits, x)
     torch.cuda.synchronize()
+    assert layer.status_word() == 0, "a dependency wait of the fused kernel gave up"
     n = T * w.k
     return dict(ids=layer.ids[:T].cpu().numpy(), w=layer.w[:T].cpu().numpy(), counts=layer.counts.cpu().numpy(),
                 offsets=layer.offsets.cpu().numpy(), gather=layer.gather[:n].cpu().numpy(),
@@ -121,6 +123,7 @@ def run_gpu_layer_graph(li: synth.LayerInputs, bank_dev, replays: int = 2):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out[:T], eager), "graph replay differs from the eager layer"
+        assert layer.status_word() == 0, "a dependency wait of the fused kernel gave up"
     n = T * w.k
     return dict(ids=layer.ids[:T].cpu().numpy(), w=layer.w[:T].cpu().numpy(), counts=layer.counts.cpu().numpy(),
                 offsets=layer.offsets.cpu().numpy(), gather=layer.gather[:n].cpu().numpy(),

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -129,6 +129,43 @@ def test_grouped_ffn_validation():
     assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, -1, 0) == 16 * 2 * 512 * 2
     assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, 3, 0) == (16 * 2 + 16) * 512 * 2
     assert call(T=0) == ft.FT_OK
+
+
+def test_layer_validation_and_workspace():
+    L = ft.lib
+    b = _bank(fmt=ft.FT_W_Q4_0, n=8, d=256, I=512)
+    ws = 1 << 22
+
+    def call(**kw):
+        return L.ft_moe_layer(kw.get("bank", ctypes.byref(b)), kw.get("slot", A), kw.get("shared", -1),
+                              kw.get("logits", A), kw.get("x", A), kw.get("T", 8), kw.get("E", 8), kw.get("k", 2),
+                              kw.get("ids", A), kw.get("w", A), kw.get("counts", A), kw.get("offsets", A),
+                              kw.get("gather", A), kw.get("inv", A), kw.get("y", A), kw.get("ysh", None),
+                              kw.get("out", B), kw.get("mask", None), kw.get("ws", A), kw.get("ws_bytes", ws),
+                              kw.get("flags", 0), None)
+    _err(call(bank=None), ft.FT_E_INVAL, "bank is null")
+    _err(call(flags=16), ft.FT_E_INVAL, "unknown flags")
+    _err(call(flags=3), ft.FT_E_INVAL, "exclusive")
+    _err(call(k=9), ft.FT_E_INVAL, "k must be")
+    _err(call(shared=3), ft.FT_E_INVAL, "y_shared")
+    _err(call(ws_bytes=100), ft.FT_E_WORKSPACE, "needs")
+    _err(call(ws=MIS), ft.FT_E_INVAL, "ws is not")
+    _err(call(logits=None), ft.FT_E_INVAL, "logits is null")
+    _err(call(out=MIS), ft.FT_E_INVAL, "out is not 16-byte aligned")
+    _err(call(inv=None), ft.FT_E_INVAL, "inv is null")
+    _err(call(counts=None), ft.FT_E_INVAL, "counts is null")
+    # workspace: control words, fused counters and h rows for decode sizes; h rows and the
+    # permutation's workspace otherwise
+    fused = L.ft_moe_layer_workspace(ctypes.byref(b), 8, 8, 2, -1, 0)
+    unfused = L.ft_moe_layer_workspace(ctypes.byref(b), 8, 8, 2, -1, ft.FT_LAYER_UNFUSED)
+    h = 8 * 2 * 512 * 2
+    ctl = 10 * 64 * 4   # status word, a work-queue counter per XCD and the exit counter, each on its own line
+    assert unfused == ctl + h
+    assert fused > unfused
+    big = L.ft_moe_layer_workspace(ctypes.byref(b), 4096, 8, 2, -1, 0)
+    assert big == ctl + 4096 * 2 * 512 * 2
+    assert L.ft_moe_layer_workspace(ctypes.byref(b), 16, 8, 9, -1, 0) == 0
+    assert L.ft_moe_layer_workspace(None, 16, 8, 2, -1, 0) == 0
 
 
 def test_combine_validation():

@@ -57,7 +57,7 @@ def test_route(ft, T, E, k, kind):
 
 
 PERMUTE_CASES = [(0, 8, 2, "rand"), (1, 8, 2, "rand"), (8, 128, 8, "rand"), (2048, 128, 8, "rand"),
-                 (2049, 128, 8, "rand"), (4096, 128, 8, "skew"), (16384, 256, 8, "skew"), (600, 1024, 32, "rand"),
+                 (2049, 128, 8, "rand"), (4096, 128, 8, "skew"), (16384, 256, 8, "skew"), (600, 1024, 32, "rand"), (400, 1024, 32, "rand"),
                  (5000, 3, 3, "rand"), (3000, 1024, 1, "skew")]
 
 
@@ -132,16 +132,72 @@ def _small_workloads():
 SMALL = _small_workloads()
 
 
-@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"])
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm", "calls"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_small(ft, name, path):
+    """ft_moe_layer with each FFN path (fused decode kernels where T <= 16), and the four calls."""
     w = SMALL[name]
-    flags = {"auto": 0, "gemv": ft.FT_PATH_GEMV, "gemm": ft.FT_PATH_GEMM}[path]
+    flags = {"auto": 0, "gemv": ft.FT_PATH_GEMV, "gemm": ft.FT_PATH_GEMM, "calls": 0}[path]
     T = w.T if name in ("tiny_bf16", "decode_q4_0") else min(w.T, 40 if path == "gemv" else w.T)
     log(f"layer {name} T={T} path={path}")
     li = synth.layer_inputs(w, layer=0, T=T)
-    g = run_gpu_layer(li, device_bank(li.bank), flags=flags)
+    g = run_gpu_layer(li, device_bank(li.bank), flags=flags, mode="calls" if path == "calls" else "layer")
     compare_layer(li, g, label=f"{name}/{path}")
+
+
+FUSED_T = [1, 3, 8, 13, 16]
+
+
+@pytest.mark.parametrize("T", FUSED_T)
+def test_fused_layer_equals_calls_bit_for_bit(ft, T):
+    """On the decode shape both routes run the same GEMV items and the same combine arithmetic, so
+    the fused kernels must reproduce the four calls bit for bit."""
+    w = SMALL["decode_q4_0"].replace(T=16)
+    li = synth.layer_inputs(w, layer=3, T=T)
+    bank = device_bank(li.bank)
+    a = run_gpu_layer(li, bank, flags=ft.FT_PATH_GEMV, mode="layer")
+    b = run_gpu_layer(li, bank, flags=ft.FT_PATH_GEMV, mode="calls")
+    for key in ("ids", "counts", "offsets", "gather", "inv", "mask"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["w"].view(np.uint32), b["w"].view(np.uint32))
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+    assert torch.equal(a["y_sorted"], b["y_sorted"])
+    compare_layer(li, a, label=f"fused T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("case", ["mxfp4_shared", "partial_residency", "one_expert_takes_all", "k_equals_E",
+                                  "bf16_out", "tokens_with_nothing_resident"])
+def test_fused_layer_cases(ft, case, T):
+    w = EDGE.replace(T=16)
+    flags = 0
+    if case == "k_equals_E":
+        w = w.replace(k=8)
+    if case == "tokens_with_nothing_resident":
+        w = w.replace(shared=False)
+    li = synth.layer_inputs(w, layer=2, T=T)
+    if case == "tokens_with_nothing_resident":
+        # only experts 6 and 7 stay: tokens routed elsewhere combine nothing and get zero rows
+        li.slot_of_expert = li.slot_of_expert.clone()
+        li.slot_of_expert[:6] = -1
+    if case == "one_expert_takes_all":
+        li.logits[:, 5] += 100.0
+    if case == "partial_residency":
+        # experts 1, 4 and 6 leave the bank: their pairs go to the mask, the rest still combine
+        li.slot_of_expert = li.slot_of_expert.clone()
+        li.slot_of_expert[[1, 4, 6]] = -1
+    bank = device_bank(li.bank)
+    if case == "bf16_out":
+        layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot, out_bf16=True)
+        out, _ = layer.forward(li.logits.cuda(), li.x.cuda())
+        torch.cuda.synchronize()
+        assert layer.status_word() == 0
+        ref = run_gpu_layer(li, bank, mode="calls")
+        ref_bf16 = torch.from_numpy(ref["out"]).to(torch.bfloat16)
+        assert torch.equal(out.cpu(), ref_bf16)
+        return
+    g = run_gpu_layer(li, bank, flags=flags)
+    compare_layer(li, g, label=f"fused {case} T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 5, 16, 37])
