@@ -186,10 +186,11 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
  * The whole layer in one call: exactly ft_moe_route, ft_moe_permute, ft_moe_grouped_ffn and
  * ft_moe_combine on the same arguments, with every intermediate result written to the caller's
  * buffers (ids, w, counts, offsets, gather, inv, y_sorted, y_shared) and the same definitions.
- * For decode batches (1 <= T <= 16, path not FT_PATH_GEMM, no FT_LAYER_UNFUSED) it runs two
- * kernels instead of the calls' five or more: a one-block route + permute prologue, then one kernel
- * that runs every gate/up item, every down item and the combine, ordered by device-side dependency
- * counters (no host synchronisation; the sequence is graph-capturable).  Its results
+ * For decode batches (1 <= T <= 16, path not FT_PATH_GEMM, no FT_LAYER_UNFUSED, and a shape whose
+ * per-block working set fits the 160 KiB LDS of a CU) it runs one kernel instead of the calls' five
+ * or more: every block routes and permutes the tokens itself, then takes gate/up and down work
+ * items from device queues, ordered by device-side dependency counters, and combines (no host
+ * synchronisation; graph-capturable).  Its results
  * equal the four calls' within rounding (the partial sums of a row may be added in another
  * grouping); here a slot_of_expert entry outside [0, n_slots) counts as not resident everywhere.
  * Dispatch and combine follow [walk-through] sections 一 and 五.

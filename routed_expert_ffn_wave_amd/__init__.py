@@ -250,13 +250,10 @@ class MoELayer:
             fws = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
             self.ffn_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
 
-        # the header's rule for the fused decode kernels
-        self.fused = (mode == "layer" and 1 <= T <= LAYER_MAX_T and (flags & FT_PATH_MASK) != FT_PATH_GEMM
-                      and not flags & FT_LAYER_UNFUSED)
-
     def status_word(self) -> int:
-        """The fused path's status word (non-zero: an internal wait gave up).  Synchronises."""
-        return int(self.ws[:4].view(torch.int32).item()) if self.fused else 0
+        """The layer workspace's status word (non-zero: a wait of the fused kernel gave up; the
+        unfused path never writes it).  Synchronises."""
+        return int(self.ws[:4].view(torch.int32).item()) if self.mode == "layer" else 0
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, stream=None):
         T, E, k = self.T, self.E, self.k

@@ -176,9 +176,9 @@ struct LayerWs {
   int n_rc;
 };
 
-bool layer_fused(int T, int flags) {
+bool layer_fused(const ft_moe_bank* b, int T, int E, int k, int flags) {
   return T >= 1 && T <= ftk::LAYER_MAX_T && (flags & FT_LAYER_UNFUSED) == 0 &&
-         (flags & FT_PATH_MASK) != FT_PATH_GEMM;
+         (flags & FT_PATH_MASK) != FT_PATH_GEMM && ftk::layer_decode_fits(b->fmt, T, E, k, b->d, b->I);
 }
 
 LayerWs layer_ws(int d, int I, int T, int E, int k, bool shared, bool fused) {
@@ -403,7 +403,7 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
     g_err[0] = 0;
     return 0;
   }
-  return layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(T, flags)).total;
+  return layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags)).total;
 }
 
 int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
@@ -424,7 +424,7 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
     CHECK_PTR(counts, "counts");
     CHECK_PTR(offsets, "offsets");
     const bool shared = shared_slot >= 0;
-    const bool fused = layer_fused(T, flags);
+    const bool fused = layer_fused(bank, T, E, k, flags);
     const LayerWs W = layer_ws(bank->d, bank->I, T, E, k, shared, fused);
     REQUIRE(ws != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
             W.total, ws_bytes, ws ? "" : ", null pointer");

@@ -78,6 +78,7 @@ struct LayerArgs {
   int32_t* cdone;            // [T][d/64][CNT_STRIDE] contributions made per (token, 64-column block)
 };
 hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s);
+bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I);  // its LDS fits one CU
 // upper bound on the row chunks (groups x chunks of LAYER_NT tokens) of a fused call
 inline int layer_decode_rowchunks_upper(int T, int E, int k, bool shared) {
   const int groups = (E < T * k ? E : T * k) + (shared ? 1 : 0);

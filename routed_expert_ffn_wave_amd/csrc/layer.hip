@@ -295,6 +295,13 @@ static hipError_t launch_layer_fmt(const LayerArgs& L, hipStream_t s) {
   return launch_layer_vpl<FMT, 8, false>(L, s);
 }
 
+bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I) {
+  const int WPB = (d > I ? d : I) <= 2048 ? 4 : 8;
+  const size_t lds = ((layer_meta_ints(T, E, k, LAYER_NT) * 4 + 15) & ~(size_t)15) +
+                     gv_union_bytes(fmt, d > I ? d : I, LAYER_NT, WPB);
+  return lds <= 160 * 1024;
+}
+
 hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s) {
   switch (L.f.fmt) {
     case FMT_BF16: return launch_layer_fmt<FMT_BF16>(L, s);

@@ -149,9 +149,11 @@ FUSED_T = [1, 3, 8, 13, 16]
 
 
 @pytest.mark.parametrize("T", FUSED_T)
-def test_fused_layer_equals_calls_bit_for_bit(ft, T):
-    """On the decode shape both routes run the same GEMV items and the same combine arithmetic, so
-    the fused kernels must reproduce the four calls bit for bit."""
+def test_fused_layer_matches_calls(ft, T):
+    """The fused kernel routes with the router kernel's routine, so routing, permutation and mask
+    match the four calls bit for bit; its FFN sums run in another grouping, so FFN rows and outputs
+    match within the FFN tolerance (and the oracle's).  A second fused run repeats every bit."""
+    from gpu_util import assert_ffn_close
     w = SMALL["decode_q4_0"].replace(T=16)
     li = synth.layer_inputs(w, layer=3, T=T)
     bank = device_bank(li.bank)
@@ -160,8 +162,11 @@ def test_fused_layer_equals_calls_bit_for_bit(ft, T):
     for key in ("ids", "counts", "offsets", "gather", "inv", "mask"):
         assert np.array_equal(a[key], b[key]), key
     assert np.array_equal(a["w"].view(np.uint32), b["w"].view(np.uint32))
-    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
-    assert torch.equal(a["y_sorted"], b["y_sorted"])
+    assert_ffn_close(a["out"], b["out"], f"fused vs calls T={T}: out")
+    assert_ffn_close(a["y_sorted"].float().cpu().numpy(), b["y_sorted"].float().cpu().numpy(),
+                     f"fused vs calls T={T}: y_sorted")
+    again = run_gpu_layer(li, bank, flags=ft.FT_PATH_GEMV, mode="layer")
+    assert np.array_equal(a["out"].view(np.uint32), again["out"].view(np.uint32))
     compare_layer(li, a, label=f"fused T={T}")
 
 
@@ -188,11 +193,12 @@ def test_fused_layer_cases(ft, case, T):
         li.slot_of_expert[[1, 4, 6]] = -1
     bank = device_bank(li.bank)
     if case == "bf16_out":
+        # the same fp32 sums as the fp32 output, rounded to nearest even
         layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot, out_bf16=True)
         out, _ = layer.forward(li.logits.cuda(), li.x.cuda())
         torch.cuda.synchronize()
         assert layer.status_word() == 0
-        ref = run_gpu_layer(li, bank, mode="calls")
+        ref = run_gpu_layer(li, bank, mode="layer")
         ref_bf16 = torch.from_numpy(ref["out"]).to(torch.bfloat16)
         assert torch.equal(out.cpu(), ref_bf16)
         return
