@@ -28,7 +28,6 @@
 
 namespace ftk {
 
-constexpr int GV_RPL = 1;  // row blocks per item (one row of each per lane)
 constexpr int GV_PF = 6;   // chunks of weights in flight per lane (prefetch ring)
 
 typedef const __attribute__((address_space(4))) uint32_t* scalar_u32p;  // read through the scalar cache
@@ -48,9 +47,9 @@ __host__ __device__ inline size_t gv_scale_bytes(int fmt, int K) {
 __host__ __device__ inline size_t gv_xsum_bytes(int fmt, int K, int NT) {
   return fmt == FMT_Q4_0 ? (size_t)NT * (K / 32) * 4 : 0;
 }
-__host__ __device__ inline size_t gv_union_bytes(int fmt, int K, int NT, int WPB) {
-  const size_t xb = (size_t)NT * K * 2 + gv_scale_bytes(fmt, K) + gv_xsum_bytes(fmt, K, NT);
-  const size_t rb = (size_t)WPB * GV_RPL * NT * 64 * 4;
+__host__ __device__ inline size_t gv_union_bytes(int fmt, int K, int NT, int WPB, int RPL = 1) {
+  const size_t xb = (size_t)NT * K * 2 + RPL * gv_scale_bytes(fmt, K) + gv_xsum_bytes(fmt, K, NT);
+  const size_t rb = (size_t)WPB * RPL * NT * 64 * 4;
   return xb > rb ? xb : rb;
 }
 
@@ -70,22 +69,22 @@ __device__ __forceinline__ u32x4 load_u32x4_agent(const uint16_t* p) {
 // Wait until this wave's stores have completed (a compiler barrier too).
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One work item: rows of 64-row device block `cb` of bank slot `slot` against the nt (<= NT) token
-// rows t0.. of a group whose sorted rows start at row0 (`shared`: the shared expert's group).
-// Writes 32 columns of h (gate/up) or 64 columns of y (down).  All threads of the block call it;
+// One work item: the RPL 64-row device blocks RPL*cb .. RPL*cb+RPL-1 of bank slot `slot` against the
+// nt (<= NT) token rows t0.. of a group whose sorted rows start at row0 (`shared`: the shared
+// expert's group).  Writes 32 columns of h per row block (gate/up) or 64 columns of y (down).  All threads of the block call it;
 // it ends with a block barrier, after which the LDS union may be reused.  COH: h rows are read and
 // h / y rows written with agent-scope atomic accesses (other blocks of the launch use them).
 // s_tok: token of each sorted row in LDS, or null to read a.gather through the scalar cache.
-template <int FMT, bool GATEUP, int WPB, int NT, bool COH = false>
+template <int FMT, bool GATEUP, int WPB, int NT, bool COH = false, int RPL = 1>
 __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, int slot, int row0, int t0, int nt,
                                           int cb, bool shared, const int* s_tok = nullptr) {
   using C = Chunk<FMT>;
-  constexpr int RPL = GV_RPL, PF = GV_PF, NTHR = WPB * 64;
+  constexpr int PF = GV_PF / RPL, NTHR = WPB * 64;  // the same bytes in flight for any RPL
   const int K = GATEUP ? a.d : a.I;
   const int nrows = GATEUP ? 2 * a.I : a.d;
   uint16_t* s_x = (uint16_t*)s_union;                                // [NT][K] activation rows of the item
-  uint8_t* s_sc = s_union + (size_t)NT * K * 2;                      // [nchunk][64] scales of the item's rows
-  float* s_xsum = (float*)(s_sc + gv_scale_bytes(FMT, K));           // [NT][K/32] (Q4_0)
+  uint8_t* s_sc = s_union + (size_t)NT * K * 2;                      // [RPL][nchunk][64] scales of the item's rows
+  float* s_xsum = (float*)(s_sc + RPL * gv_scale_bytes(FMT, K));     // [NT][K/32] (Q4_0)
   float* s_red = (float*)s_union;                                    // [WPB][RPL][NT][64] partial sums
 
   const int lane = threadIdx.x & 63;
@@ -98,8 +97,11 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   const uint8_t* scales = GATEUP ? a.s13 : a.s2;
   constexpr size_t CSTRIDE = 64 * 16;  // consecutive chunks of one row block are 1 KiB apart
   // the RPL rows of this lane
+  // row block RPL*cb + q of the matrix for each q: device row (gate/up: lanes 0-31 gate rows,
+  // lanes 32-63 the matching up rows)
   int rowq[RPL];
-  rowq[0] = 64 * cb + lane;  // device row (gate/up: lanes 0-31 gate 32cb+l, lanes 32-63 up 32cb+l-32)
+#pragma unroll
+  for (int q = 0; q < RPL; ++q) rowq[q] = 64 * (RPL * cb + q) + lane;
   auto chunk_of = [&](int j) { return WPB * j + w; };  // this wave's j-th chunk
   const uint8_t* mat = codes + (size_t)slot * mbytes;
   const uint8_t* rowp[RPL];
@@ -116,8 +118,8 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   constexpr int SB = FMT == FMT_Q4_0 ? 2 : 1;
   constexpr bool STAGE_SCALES = FMT == FMT_Q4_0 || FMT == FMT_MXFP4;
   const int nx8 = K / 8;
-  const int nsv = STAGE_SCALES ? nchunk * 64 * SB / 16 : 0;
-  const uint8_t* ssrc = scales + ((size_t)slot * nrows * nchunk + (size_t)cb * nchunk * 64) * SB;
+  const int nsv = STAGE_SCALES ? RPL * nchunk * 64 * SB / 16 : 0;  // the RPL row blocks' scales are one run
+  const uint8_t* ssrc = scales + ((size_t)slot * nrows * nchunk + (size_t)RPL * cb * nchunk * 64) * SB;
   const uint16_t* xr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -156,7 +158,8 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   auto issue = [&](u32x4* b, int j) {
     const int c = chunk_of(j);
 #pragma unroll
-    for (int q = 0; q < RPL; ++q) b[q] = *(const u32x4*)(rowp[q] + (size_t)c * CSTRIDE);
+    for (int q = 0; q < RPL; ++q)  // streamed once: non-temporal, so they do not evict what is reused
+      b[q] = __builtin_nontemporal_load((const u32x4*)(rowp[q] + (size_t)c * CSTRIDE));
   };
   if (niter > 0) {
 #pragma unroll
@@ -217,41 +220,40 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
             // one fp32 scale per 128x128 block of logical rows (a gate/up device block holds 32 gate
             // rows in lanes 0-31 and the matching 32 up rows in lanes 32-63)
             const float* s32 = (const float*)scales + (size_t)slot * (size_t)(nrows / 128) * (K / 128);
-            const int rb = (GATEUP ? 32 * cb + (lane >= 32 ? a.I : 0) : 64 * cb) / 128;
+            const int rb = (GATEUP ? 32 * (RPL * cb + q) + (lane >= 32 ? a.I : 0) : 64 * (RPL * cb + q)) / 128;
             fsc[q] = s32[(size_t)rb * (K / 128) + (c * 16) / 128];
           } else if constexpr (FMT == FMT_Q4_0) {
-            fsc[q] = fp16_bits_to_f32(((const uint16_t*)s_sc)[c * 64 + lane]);
+            fsc[q] = fp16_bits_to_f32(((const uint16_t*)s_sc)[(q * nchunk + c) * 64 + lane]);
           } else if constexpr (FMT == FMT_MXFP4) {
-            fsc[q] = e8m0_to_f32(s_sc[c * 64 + lane]);
+            fsc[q] = e8m0_to_f32(s_sc[(q * nchunk + c) * 64 + lane]);
           } else {
             fsc[q] = 1.0f;
           }
         }
-        uint32_t wp[RPL][C::PAIRS];  // decoded once, used for every token
+        // one row block at a time: its chunk is decoded once and used for every token (the token
+        // rows are read again from LDS for the next row block rather than held in registers)
 #pragma unroll
-        for (int q = 0; q < RPL; ++q) C::decode(buf[p][q], wp[q]);
+        for (int q = 0; q < RPL; ++q) {
+          uint32_t wp[C::PAIRS];
+          C::decode(buf[p][q], wp);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < nt) {
-            uint32_t xw[C::PAIRS];
-            const u32x4* xs = (const u32x4*)(s_x + (size_t)t * K + (size_t)c * C::ELEMS);
+          for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+              uint32_t xw[C::PAIRS];
+              const u32x4* xs = (const u32x4*)(s_x + (size_t)t * K + (size_t)c * C::ELEMS);
 #pragma unroll
-            for (int i = 0; i < C::PAIRS / 4; ++i) {
-              const u32x4 v = xs[i];
-              xw[4 * i] = v[0];
-              xw[4 * i + 1] = v[1];
-              xw[4 * i + 2] = v[2];
-              xw[4 * i + 3] = v[3];
-            }
-            float xsum = 0.0f;
-            if constexpr (FMT == FMT_Q4_0) xsum = s_xsum[t * (K / 32) + c];
-#pragma unroll
-            for (int q = 0; q < RPL; ++q) {
+              for (int i = 0; i < C::PAIRS / 4; ++i) {
+                const u32x4 v = xs[i];
+                xw[4 * i] = v[0];
+                xw[4 * i + 1] = v[1];
+                xw[4 * i + 2] = v[2];
+                xw[4 * i + 3] = v[3];
+              }
               float part = 0.0f;
 #pragma unroll
-              for (int i = 0; i < C::PAIRS; ++i) part = dot2_bf16(wp[q][i], xw[i], part);
+              for (int i = 0; i < C::PAIRS; ++i) part = dot2_bf16(wp[i], xw[i], part);
               if constexpr (FMT == FMT_Q4_0)
-                acc[q][t] = fmaf(fsc[q], fmaf(-136.0f, xsum, part), acc[q][t]);  // decoded as 128 + q
+                acc[q][t] = fmaf(fsc[q], fmaf(-136.0f, s_xsum[t * (K / 32) + c], part), acc[q][t]);  // 128 + q
               else if constexpr (FMT == FMT_BF16)
                 acc[q][t] += part;
               else
@@ -271,19 +273,20 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
     for (int t = 0; t < NT; ++t)
       if (t < nt) s_red[((w * RPL + q) * NT + t) * 64 + lane] = acc[q][t];
   __syncthreads();
-  for (int t = w; t < nt; t += WPB) {
+  for (int tq = w; tq < nt * RPL; tq += WPB) {
+    const int t = tq / RPL, q = tq % RPL, cbq = RPL * cb + q;
     const int orow = row0 + t0 + t;  // h row, or y_sorted row
     if (GATEUP) {
       float g = 0.0f, u = 0.0f;
       if (lane < 32) {
 #pragma unroll
         for (int ww = 0; ww < WPB; ++ww) {
-          g += s_red[(ww * NT + t) * 64 + lane];
-          u += s_red[(ww * NT + t) * 64 + lane + 32];
+          g += s_red[((ww * RPL + q) * NT + t) * 64 + lane];
+          u += s_red[((ww * RPL + q) * NT + t) * 64 + lane + 32];
         }
       }
       const uint32_t hb = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
-      uint16_t* hp = a.h + (size_t)orow * a.I + 32 * cb + lane;
+      uint16_t* hp = a.h + (size_t)orow * a.I + 32 * cbq + lane;
       if constexpr (COH) {
         const uint32_t nb = __shfl_down(hb, 1, 64);  // pairs of columns as one 32-bit store
         if (lane < 32 && (lane & 1) == 0) store_u32_agent(hp, hb | (nb << 16));
@@ -293,14 +296,14 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
     } else {
       float v = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < WPB; ++ww) v += s_red[(ww * NT + t) * 64 + lane];
+      for (int ww = 0; ww < WPB; ++ww) v += s_red[((ww * RPL + q) * NT + t) * 64 + lane];
       uint16_t* yrow = shared ? a.y_shared + (size_t)(t0 + t) * a.d : a.y_sorted + (size_t)orow * a.d;
       const uint32_t yb = f32_to_bf16_bits(v);
       if constexpr (COH) {
         const uint32_t nb = __shfl_down(yb, 1, 64);
-        if ((lane & 1) == 0) store_u32_agent(yrow + 64 * cb + lane, yb | (nb << 16));
+        if ((lane & 1) == 0) store_u32_agent(yrow + 64 * cbq + lane, yb | (nb << 16));
       } else {
-        yrow[64 * cb + lane] = (uint16_t)yb;
+        yrow[64 * cbq + lane] = (uint16_t)yb;
       }
     }
   }

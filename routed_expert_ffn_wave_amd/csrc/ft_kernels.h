@@ -51,6 +51,7 @@ constexpr int GEMM_BM = 128;  // token rows per tile
 // counters start at zero and the last block to finish returns them to zero.
 constexpr int LAYER_MAX_T = 16;   // tokens per call on the fused path (one routing wave per token)
 constexpr int LAYER_NT = 4;       // tokens per GEMV pass on the fused path
+constexpr int LAYER_RPL2 = 2;     // 64-row blocks per down item on the fused path (d % 128 == 0)
 constexpr int CNT_STRIDE = 64;    // ints between two counters: one 256-byte line each, so polls and
                                   // updates of different counters never share a line
 constexpr int LAYER_NQ = 8;       // work queues of the fused FFN kernel (one per XCD)

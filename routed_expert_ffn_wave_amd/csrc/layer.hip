@@ -52,7 +52,13 @@ __host__ __device__ inline size_t layer_meta_ints(int T, int E, int k, int NT) {
          + 3 * (size_t)E + 1       // counts, offsets (E+1), running bases
          + (size_t)T               // contributions expected per token
          + 4 * (size_t)(E + 2) + 4 // groups
-         + 2 + NT;                 // control
+         + 2 + NT * LAYER_RPL2;    // control
+}
+
+// LDS of the GEMV items: gate/up items over d, down items (LAYER_RPL2 row blocks) over I
+__host__ __device__ inline size_t layer_union_bytes(int fmt, int d, int I, int NT, int WPB) {
+  const size_t u13 = gv_union_bytes(fmt, d, NT, WPB, 1), u2 = gv_union_bytes(fmt, I, NT, WPB, LAYER_RPL2);
+  return u13 > u2 ? u13 : u2;
 }
 
 template <int FMT, int WPB, int NT, int VPL, bool OUT_BF16>
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   int* g_cnt = g_row0 + E + 2;
   int* g_rc0 = g_cnt + E + 2;
   int* g_tmp = g_rc0 + E + 2;     // [4]
-  int* s_ctl = g_tmp + 4;         // [0]: claimed position, [1]: last block, [2..2+NT): tokens to combine
+  int* s_ctl = g_tmp + 4;         // [0]: claimed position, [1]: last block, [2..): (token, column block)s to combine
   uint8_t* s_union = lds + ((layer_meta_ints(T, E, k, NT) * 4 + 15) & ~(size_t)15);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -158,9 +164,10 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   GroupSrc src{s_slot, s_off, E, T, k, a.shared_slot, 1, 0x7fffffff, a.n_slots};
   GroupList gl{g_slot, g_row0, g_cnt, g_rc0, 0};
   build_groups(src, gl, g_tmp, [&](int cnt) { return (cnt + NT - 1) / NT; });  // ends with a barrier
-  const int ncb13 = 2 * a.I / 64, ncb2 = a.d / 64;
+  constexpr int RPL2 = LAYER_RPL2;
+  const int ncb13 = 2 * a.I / 64, ncb2 = a.d / 64, nit2 = ncb2 / RPL2;  // down items: RPL2 row blocks each
   const int nrc = g_rc0[gl.n];
-  const int n13 = nrc * ncb13, total = n13 + nrc * ncb2;
+  const int n13 = nrc * ncb13, total = n13 + nrc * nit2;
 
   int pos = blockIdx.x / nq;
   for (int it = pos * nq + qx; it < total; it = pos * nq + qx) {
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
     if (tid == 0) next = nb_q + atomic_add_agent(queue, 1);  // claim ahead
     const bool gateup = it < n13;
     const int local = gateup ? it : it - n13;
-    const int ncb = gateup ? ncb13 : ncb2;
+    const int ncb = gateup ? ncb13 : nit2;
     const int rc = local / ncb, cb = local % ncb;
     const int g = find_group(g_rc0, gl.n, rc);
     const int row0 = g_row0[g], slot = g_slot[g];
@@ -194,20 +201,22 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
         }
       }
       __syncthreads();  // the row chunk's h is complete: read it below with agent-scope loads
-      gemv_item<FMT, false, WPB, NT, true>(a, s_union, slot, row0, t0, nt, cb, shared, s_gather);
+      gemv_item<FMT, false, WPB, NT, true, RPL2>(a, s_union, slot, row0, t0, nt, cb, shared, s_gather);
       wait_stores();  // this wave's y stores have completed before the counts move
       __syncthreads();
-      if (tid < nt) {
-        const int tok = shared ? t0 + tid : s_gather[row0 + t0 + tid];
-        const int done = atomic_add_agent(L.cdone + (tok * ncb2 + cb) * CNT_STRIDE, 1);
-        s_ctl[2 + tid] = done + 1 == s_tgt[tok] ? tok : -1;  // the last contribution: combine here
+      if (tid < nt * RPL2) {  // one contribution per (token, 64-column block) of the item
+        const int t = tid / RPL2, cbq = RPL2 * cb + tid % RPL2;
+        const int tok = shared ? t0 + t : s_gather[row0 + t0 + t];
+        const int done = atomic_add_agent(L.cdone + (tok * ncb2 + cbq) * CNT_STRIDE, 1);
+        s_ctl[2 + tid] = done + 1 == s_tgt[tok] ? tok * ncb2 + cbq : -1;  // the last one: combine here
       }
       __syncthreads();
-      for (int t = w; t < nt; t += WPB) {
-        const int tok = s_ctl[2 + t];
-        if (tok < 0) continue;
+      for (int i = w; i < nt * RPL2; i += WPB) {
+        const int v = s_ctl[2 + i];
+        if (v < 0) continue;
+        const int tok = v / ncb2, cbq = v % ncb2;
         // every contribution's y rows are complete: agent-scope loads of column pairs
-        const int col = 64 * cb + lane, pcol = col & ~1, hi = (lane & 1) * 16;
+        const int col = 64 * cbq + lane, pcol = col & ~1, hi = (lane & 1) * 16;
         float acc = 0.0f;
         for (int j = 0; j < k; ++j) {
           const int r = s_crow[tok * k + j];
@@ -250,7 +259,8 @@ static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   auto kern = layer_decode_kernel<FMT, WPB, NT, VPL, OUT_BF16>;
   const FfnArgs& a = L.f;
   const int K = a.d > a.I ? a.d : a.I;
-  const size_t lds = ((layer_meta_ints(a.T, a.E, a.k, NT) * 4 + 15) & ~(size_t)15) + gv_union_bytes(FMT, K, NT, WPB);
+  const size_t lds = ((layer_meta_ints(a.T, a.E, a.k, NT) * 4 + 15) & ~(size_t)15) +
+                     layer_union_bytes(FMT, a.d, a.I, NT, WPB);
   static int resident_per_cu = -1;
   static size_t resident_lds = 0;
   if (resident_per_cu < 0 || lds > resident_lds) {
@@ -266,7 +276,7 @@ static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
   // at most the blocks the device holds at once (every block runs, so every queue advances)
-  const long long items = (long long)L.n_rc * (2 * a.I / 64 + a.d / 64);
+  const long long items = (long long)L.n_rc * (2 * a.I / 64 + a.d / (64 * LAYER_RPL2));
   long long blocks = (long long)resident_per_cu * cus;
   if (blocks > items) blocks = items;
   if (blocks < 1) blocks = 1;
@@ -298,7 +308,7 @@ static hipError_t launch_layer_fmt(const LayerArgs& L, hipStream_t s) {
 bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I) {
   const int WPB = (d > I ? d : I) <= 2048 ? 4 : 8;
   const size_t lds = ((layer_meta_ints(T, E, k, LAYER_NT) * 4 + 15) & ~(size_t)15) +
-                     gv_union_bytes(fmt, d > I ? d : I, LAYER_NT, WPB);
+                     layer_union_bytes(fmt, d, I, LAYER_NT, WPB);
   return lds <= 160 * 1024;
 }
 
