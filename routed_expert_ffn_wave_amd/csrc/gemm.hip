@@ -8,77 +8,96 @@
 // representable in bf16 (Q4_0's fp16 per 32, FP8's fp32 per 128x128) multiply fp32 partial sums of
 // their K block, so each weight is used exactly as its format defines it.
 //
-// Work item = (group, tile of BM=128 tokens, tile of 128 weight rows), one block of 4 waves each;
-// wave (wm, wn) computes 64x64 of the output as 2x2 MFMA tiles of 32x32.
-//   gate/up: the 128 weight rows of a tile are 64 intermediate columns i, laid out as
-//            [gate i0..i0+31 | up i0..i0+31 | gate i0+32.. | up i0+32..], so each wave holds the gate
-//            and up sums of the same (token, i) in the same lane and applies SiLU(g)*u in registers.
-//   down:    128 rows of W2 = 128 output columns.
+// Tile = (group, BM=128 tokens, BN weight rows), K in steps of BK=64; one block of 4 waves, wave
+// (wm, wn) computes 64 x (BN/2) of the tile as 2 x WN MFMA tiles of 32x32.  BN = 256 (WN = 4) for
+// bf16 and MXFP4 banks; Q4_0 and FP8 banks, which also keep per-scale-block partial sums, use
+// BN = 128 (WN = 2).  The step s+1 operands are loaded into registers while the MFMAs of step s run
+// from LDS, then written to LDS (decoded) between two barriers.  Blocks are persistent: the grid
+// is what the device holds at once and blocks stride over the tile list, which is built on the
+// device (groups from the permutation, row chunk major), so skewed groups need no host round trip.
+//   gate/up: W13 device blocks of 64 rows hold 32 gate rows then the matching 32 up rows, so MFMA
+//            column tiles 2p and 2p+1 of a wave are the gate and up sums of the same (token, i) in
+//            the same lane, and SiLU(g)*u is applied in registers.
+//   down:    BN rows of W2 = BN output columns.
 #include "ft_device.h"
 #include "ft_groups.h"
 #include "ft_kernels.h"
 
 namespace ftk {
 
-constexpr int BM = GEMM_BM, BN = 128, BK = 32, LDK = BK + 8;  // LDS row stride in bf16 (padded)
+constexpr int BM = GEMM_BM, BK = 64, LDK = BK + 8;  // LDS row stride in bf16 (padded)
 
 template <int FMT>
 __device__ __forceinline__ size_t gemm_mat_bytes(int rows, int K) {
   return FMT == FMT_BF16 ? (size_t)rows * K * 2 : FMT == FMT_FP8_B128 ? (size_t)rows * K : (size_t)rows * K / 2;
 }
+template <int FMT, int WN_>
+struct GemmCfg {
+  static constexpr int WN = WN_;                                            // MFMA column tiles per wave
+  static constexpr int BN = 64 * WN;                                        // weight rows per tile
+  static constexpr bool PARTIAL = FMT == FMT_Q4_0 || FMT == FMT_FP8_B128;   // scale per K block
+  // raw 16-byte code chunks per thread and step (B tile: BN rows x BK; 256 threads)
+  static constexpr int BCH = (BN * BK / chunk_elems<FMT>()) / 256;
+};
 
-// Decode this thread's 16 K-consecutive weights of K step `ks` (half `hf` = elements 16hf..16hf+15
-// of the 32-wide step) of weight row `r` in a row-interleaved matrix (base `mat`, nchunk chunks
-// per row) into 8 dwords of bf16 pairs in K order.  All element values are exact in bf16; MXFP4's
-// power-of-two scale is folded into the conversion (exact while the product is a normal bf16).
+// dynamic LDS: [groups 4 x (E+2) ints + tmp][A: BM x LDK][B: BN x LDK][row pointers BM][scales BN]
+__host__ __device__ inline size_t gemm_group_bytes(int E) { return (((size_t)4 * (E + 2) + 4) * 4 + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t gemm_lds_bytes(int E, int BN) {
+  return gemm_group_bytes(E) + (size_t)(BM + BN) * LDK * 2 + (size_t)BM * 8 + (size_t)BN * 4 * 2;
+}
+
+// Decode one raw chunk of the B tile into bf16 pairs in K order (pairs per chunk: 4 bf16, 8 e4m3,
+// 16 four-bit); MXFP4's power-of-two scale is folded into the conversion (exact while the product
+// is a normal bf16), Q4_0 gives q - 8.
 template <int FMT>
-__device__ __forceinline__ void load_b_half(const uint8_t* mat, int r, int nchunk, int ks, int hf,
-                                            const uint8_t* mx_scales, uint32_t* out) {
-  if constexpr (FMT == FMT_BF16) {  // 8 elements per chunk: chunks 4ks + 2hf, +1
-    const u32x4 a = *(const u32x4*)(mat + ilv_chunk_off(r, 4 * ks + 2 * hf, nchunk));
-    const u32x4 b = *(const u32x4*)(mat + ilv_chunk_off(r, 4 * ks + 2 * hf + 1, nchunk));
-    out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
-    out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
-  } else if constexpr (FMT == FMT_FP8_B128) {  // 16 elements per chunk: chunk 2ks + hf
-    const u32x4 c = *(const u32x4*)(mat + ilv_chunk_off(r, 2 * ks + hf, nchunk));
+__device__ __forceinline__ void decode_b(const u32x4& c, float mx_scale, uint32_t* out) {
+  if constexpr (FMT == FMT_BF16) {
+    out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
+  } else if constexpr (FMT == FMT_FP8_B128) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
       out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
     }
-  } else if constexpr (FMT == FMT_MXFP4) {  // 32 elements per chunk: half hf = bytes 8hf..8hf+7
-    const u32x2 c = *(const u32x2*)(mat + ilv_chunk_off(r, ks, nchunk) + hf * 8);
-    const float sc = e8m0_to_f32(mx_scales[ilv_scale_idx(r, ks, nchunk)]);
+  } else if constexpr (FMT == FMT_MXFP4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 0));
-      out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 1));
-      out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 2));
-      out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 3));
+    for (int i = 0; i < 4; ++i) {
+      out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], mx_scale, 0));
+      out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], mx_scale, 1));
+      out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], mx_scale, 2));
+      out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], mx_scale, 3));
     }
-  } else {  // Q4_0: words 2hf, 2hf+1 of the chunk; nibble pair s of word w = elements 8w+2s, 8w+2s+1
-    const u32x2 c = *(const u32x2*)(mat + ilv_chunk_off(r, ks, nchunk) + hf * 8);
+  } else {  // Q4_0: nibble pair s of word w = elements 8w+2s, 8w+2s+1 -> bf16 (q - 8), exact
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int w = 0; w < 4; ++w) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t v = (c[i] >> (4 * s)) & 0x000F000Fu;
-        const float lo = (float)(int)(v & 0xffffu) - 8.0f, hi = (float)(int)(v >> 16) - 8.0f;  // q - 8, exact
-        out[4 * i + s] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+        const uint32_t v = (c[w] >> (4 * s)) & 0x000F000Fu;
+        const float lo = (float)(int)(v & 0xffffu) - 8.0f, hi = (float)(int)(v >> 16) - 8.0f;
+        out[4 * w + s] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
       }
     }
   }
 }
 
-template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
-  constexpr bool PARTIAL = (FMT == FMT_Q4_0 || FMT == FMT_FP8_B128);
-  constexpr int SCALE_STEPS = (FMT == FMT_FP8_B128) ? 4 : 1;  // K steps per scale block
-  __shared__ int s_slot[1025], s_row0[1025], s_cnt[1025], s_item0[1026], s_tmp[4];
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
-  __shared__ float s_bscale[BN];   // per weight row scale of the current scale block
-  __shared__ const uint16_t* s_arow[BM];
+template <int FMT, bool GATEUP, int WN_>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
+  using G = GemmCfg<FMT, WN_>;
+  constexpr int WN = G::WN, BN = G::BN, BCH = G::BCH;
+  constexpr int EPC = chunk_elems<FMT>();          // K elements per 16-byte chunk
+  constexpr int CPR = BK / EPC;                     // chunks per B row and step
+  constexpr int SCALE_STEPS = FMT == FMT_FP8_B128 ? 2 : 1;  // K steps per scale block (FP8: 128 = 2 x 64)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int E2 = a.E + 2;
+  int* s_slot = (int*)lds;
+  int* s_row0 = s_slot + E2;
+  int* s_cnt = s_row0 + E2;
+  int* s_item0 = s_cnt + E2;
+  int* s_tmp = s_item0 + E2;
+  uint16_t* As = (uint16_t*)(lds + gemm_group_bytes(a.E));
+  uint16_t* Bs = As + BM * LDK;
+  const uint16_t** s_arow = (const uint16_t**)(Bs + BN * LDK);
+  float* s_bscale = (float*)(s_arow + BM);  // [2][BN]: Q4_0 scales of the step's two 32-blocks, or FP8's
 
   const int K = GATEUP ? a.d : a.I;
   const int ncols = GATEUP ? 2 * a.I : a.d;  // weight rows
@@ -86,172 +105,250 @@ __global__ __launch_bounds__(256) void gemm_kernel(FfnArgs a) {
   GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
   GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
   build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + BM - 1) / BM) * ntiles; });
-  const int it = blockIdx.x;
-  if (it >= s_item0[gl.n]) return;
+  const int nitems = s_item0[gl.n];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int g = find_group(s_item0, gl.n, it);
-  const int local = it - s_item0[g];
-  const int mt = local / ntiles, nt = local % ntiles;
-  const int slot = s_slot[g], row0 = s_row0[g], cnt = s_cnt[g];
   const int TK = a.T * a.k;
-  const bool shared = row0 >= TK;
-  const int m0 = mt * BM;
-  const int mrows = min(BM, cnt - m0);
-
-  // activation row pointers of the tile (null past the group's end)
-  if (tid < BM) {
-    const uint16_t* p = nullptr;
-    if (tid < mrows) {
-      if (GATEUP) {
-        const int tok = shared ? (m0 + tid) : (a.gather[row0 + m0 + tid] / a.k);
-        p = a.x + (size_t)tok * a.d;
-      } else {
-        p = a.h + (size_t)(row0 + m0 + tid) * a.I;
-      }
-    }
-    s_arow[tid] = p;
-  }
-
-  // weight row of local column n
-  const int half_id = tid & 1;
-  const int ln = tid >> 1;  // 0..127: the A row and the B row this thread stages
-  // device row of the B-tile row ln (W13 device blocks already hold 32 gate then 32 up rows, so
-  // tile nt's 128 device rows are gate i0..i0+31, up i0.., gate i0+32.., up i0+32.. with i0 = 64nt)
-  // and its logical row (for the FP8 scale grid, which is indexed by logical rows)
-  const int drow = nt * BN + ln;
-  const int wrow = GATEUP ? w13_logical_row(drow, a.I) : drow;
+  const int nchunk = K / EPC;
   const uint8_t* codes = GATEUP ? a.w13 : a.w2;
   const uint8_t* scales = GATEUP ? a.s13 : a.s2;
-  const int nchunk = K / chunk_elems<FMT>();
-  const uint8_t* bmat = codes + (size_t)slot * gemm_mat_bytes<FMT>(ncols, K);
-  const uint8_t* bscales = nullptr;  // per-(row, chunk) scales of this slot (Q4_0, MXFP4)
-  if constexpr (FMT == FMT_Q4_0) bscales = scales + (size_t)slot * ncols * (size_t)nchunk * 2;
-  if constexpr (FMT == FMT_MXFP4) bscales = scales + (size_t)slot * ncols * (size_t)nchunk;
-  __syncthreads();
-  const uint16_t* arow = s_arow[ln];
+  const int nsteps = K / BK;
+  // A staging: thread -> row tid/2, K half (tid&1)*32 of the step: 4 x 16 bytes
+  const int ar = tid >> 1, ah = tid & 1;
 
-  f32x16 acc[2][2], part[2][2];
+  // Blocks are placed on the 8 XCDs round-robin (block b on XCD b % 8).  Give each XCD a contiguous
+  // run of each round's tiles, so that the tiles running at once on one XCD share their activation
+  // rows (same token tile, neighbouring weight tiles) and weight tiles through its L2.
+  const int NB = gridDim.x;
+  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int it = lb; it < nitems; it += NB) {
+    const int g = find_group(s_item0, gl.n, it);
+    const int local = it - s_item0[g];
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int slot = s_slot[g], row0 = s_row0[g], cnt = s_cnt[g];
+    const bool shared = row0 >= TK;
+    const int m0 = mt * BM;
+    const int mrows = min(BM, cnt - m0);
+    if (tid < BM) {  // activation rows of the tile (null past the group's end)
+      const uint16_t* p = nullptr;
+      if (tid < mrows) {
+        if (GATEUP) {
+          const int tok = shared ? (m0 + tid) : (a.gather[row0 + m0 + tid] / a.k);
+          p = a.x + (size_t)tok * a.d;
+        } else {
+          p = a.h + (size_t)(row0 + m0 + tid) * a.I;
+        }
+      }
+      s_arow[tid] = p;
+    }
+    __syncthreads();
+    const uint16_t* arow = s_arow[ar];
+    const uint8_t* bmat = codes + (size_t)slot * gemm_mat_bytes<FMT>(ncols, K);
+    // B staging: thread -> (row, chunk) pairs of the BN x BK tile, rows fastest so that 64 lanes
+    // read one 1 KiB run of the row-interleaved layout
+    auto b_row = [&](int i) { return (tid + 256 * i) % BN; };
+    auto b_chk = [&](int i) { return (tid + 256 * i) / BN; };
+
+    u32x4 ra[4], rb[BCH];
+    float rsc[2] = {1.0f, 1.0f};  // this thread's B-row scales for the step (Q4_0: two 32-blocks)
+    float rmx[BCH];               // MXFP4 scale of each staged chunk
+    auto load_step = [&](int s) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i) ra[i] = arow ? *(const u32x4*)(arow + (size_t)s * BK + ah * 32 + 8 * i) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < BCH; ++i) {
+        const int r = nt * BN + b_row(i), c = s * CPR + b_chk(i);
+        rb[i] = *(const u32x4*)(bmat + ilv_chunk_off(r, c, nchunk));
+        if constexpr (FMT == FMT_MXFP4)
+          rmx[i] = e8m0_to_f32(scales[(size_t)slot * ncols * nchunk + ilv_scale_idx(r, c, nchunk)]);
+      }
+      if constexpr (FMT == FMT_Q4_0) {  // rows tid < BN: the scales of the step's two 32-blocks
+        if (tid < BN) {
+          const int r = nt * BN + tid;
+          const uint16_t* s16 = (const uint16_t*)scales + (size_t)slot * ncols * nchunk;
+          rsc[0] = fp16_bits_to_f32(s16[ilv_scale_idx(r, 2 * s, nchunk)]);
+          rsc[1] = fp16_bits_to_f32(s16[ilv_scale_idx(r, 2 * s + 1, nchunk)]);
+        }
+      }
+      if constexpr (FMT == FMT_FP8_B128) {
+        if (tid < BN && (s % SCALE_STEPS) == 0) {
+          const int r = nt * BN + tid;
+          const int lr = GATEUP ? w13_logical_row(r, a.I) : r;
+          rsc[0] = ((const float*)scales)[((size_t)slot * (ncols / 128) + lr / 128) * (K / 128) + s / SCALE_STEPS];
+        }
+      }
+    };
+    auto store_step = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4*)&As[ar * LDK + ah * 32 + 8 * i] = ra[i];
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        uint32_t w[EPC / 2];
+        decode_b<FMT>(rb[i], FMT == FMT_MXFP4 ? rmx[i] : 1.0f, w);
+        uint32_t* dst = (uint32_t*)&Bs[b_row(i) * LDK + b_chk(i) * EPC];
+#pragma unroll
+        for (int q = 0; q < EPC / 8; ++q)
+          *(u32x4*)(dst + 4 * q) = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+      }
+      if constexpr (FMT == FMT_Q4_0) {
+        if (tid < BN) {
+          s_bscale[tid] = rsc[0];
+          s_bscale[BN + tid] = rsc[1];
+        }
+      }
+      if constexpr (FMT == FMT_FP8_B128) {
+        if (tid < BN && (s % SCALE_STEPS) == 0) s_bscale[tid] = rsc[0];
+      }
+    };
+
+    f32x16 acc[2][WN], part[2][G::PARTIAL ? WN : 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < (G::PARTIAL ? WN : 1); ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[i][j][r] = 0.0f;
+    }
+
+    load_step(0);
+    for (int s = 0; s < nsteps; ++s) {
+      __syncthreads();  // every wave is done with the previous step's LDS tiles
+      store_step(s);
+      __syncthreads();
+      if (s + 1 < nsteps) load_step(s + 1);  // in flight during this step's MFMAs
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 16) {
+        bf16x8 af[2], bf[WN];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = wm * 64 + i * 32 + (lane & 31);
+          af[i] = *(const bf16x8*)&As[r * LDK + kk + 8 * (lane >> 5)];
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int c = wn * (BN / 2) + j * 32 + (lane & 31);
+          bf[j] = *(const bf16x8*)&Bs[c * LDK + kk + 8 * (lane >> 5)];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            if constexpr (G::PARTIAL)
+              part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], part[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          }
+        if constexpr (FMT == FMT_Q4_0) {  // a 32-block ends every second K sub-step
+          if ((kk & 16) != 0) {
+#pragma unroll
+            for (int j = 0; j < WN; ++j) {
+              const float sc = s_bscale[(kk >> 5) * BN + wn * (BN / 2) + j * 32 + (lane & 31)];
+#pragma unroll
+              for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
+                  part[i][j][r] = 0.0f;
+                }
+            }
+          }
+        }
+      }
+      if constexpr (FMT == FMT_FP8_B128) {  // a 128-block ends every second step
+        if ((s % SCALE_STEPS) == SCALE_STEPS - 1) {
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const float sc = s_bscale[wn * (BN / 2) + j * 32 + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
+                part[i][j][r] = 0.0f;
+              }
+          }
+        }
+      }
+    }
+
+    // ---- epilogue.  Lane holds, for tile (i, j), rows wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4
+    // and column wn*(BN/2) + j*32 + lane%32.
+    const int col = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        acc[i][j][r] = 0.0f;
-        part[i][j][r] = 0.0f;
-      }
-
-  const int nsteps = K / BK;
-  for (int ks = 0; ks < nsteps; ++ks) {
-    // ---- stage A (16 bf16 per thread) and B (16 decoded weights per thread) into LDS
-    u32x4 av0 = {0, 0, 0, 0}, av1 = {0, 0, 0, 0};
-    if (arow) {
-      const u32x4* p = (const u32x4*)(arow + (size_t)ks * BK + half_id * 16);
-      av0 = p[0];
-      av1 = p[1];
-    }
-    uint32_t bw[8];
-    load_b_half<FMT>(bmat, drow, nchunk, ks, half_id, bscales, bw);
-    float bsc = 1.0f;
-    if constexpr (PARTIAL) {
-      if ((ks % SCALE_STEPS) == 0) {
-        if constexpr (FMT == FMT_Q4_0) {
-          bsc = fp16_bits_to_f32(((const uint16_t*)bscales)[ilv_scale_idx(drow, ks, nchunk)]);
+        const int m = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m >= mrows) continue;
+        if (GATEUP) {
+#pragma unroll
+          for (int p = 0; p < WN / 2; ++p) {
+            const float gte = acc[i][2 * p][r], up = acc[i][2 * p + 1][r];
+            const float hv = gte / (1.0f + expf(-gte)) * up;
+            // device block (nt*BN + wn*BN/2)/64 + p holds intermediate columns 32 * that + 0..31
+            const int icol = 32 * ((nt * BN + wn * (BN / 2)) / 64 + p) + col;
+            a.h[(size_t)(row0 + m0 + m) * a.I + icol] = f32_to_bf16_bits(hv);
+          }
         } else {
-          const float* s32 = (const float*)scales;
-          bsc = s32[((size_t)slot * (ncols / 128) + wrow / 128) * (K / 128) + ks / 4];
+          uint16_t* yrow = shared ? a.y_shared + (size_t)(m0 + m) * a.d : a.y_sorted + (size_t)(row0 + m0 + m) * a.d;
+#pragma unroll
+          for (int j = 0; j < WN; ++j) yrow[nt * BN + wn * (BN / 2) + j * 32 + col] = f32_to_bf16_bits(acc[i][j][r]);
         }
       }
     }
-    __syncthreads();  // every wave is done with the previous step's As, Bs and s_bscale
-    if constexpr (PARTIAL) {
-      if (half_id == 0 && (ks % SCALE_STEPS) == 0) s_bscale[ln] = bsc;
-    }
-    *(u32x4*)&As[ln * LDK + half_id * 16] = av0;
-    *(u32x4*)&As[ln * LDK + half_id * 16 + 8] = av1;
-    *(u32x4*)&Bs[ln * LDK + half_id * 16] = u32x4{bw[0], bw[1], bw[2], bw[3]};
-    *(u32x4*)&Bs[ln * LDK + half_id * 16 + 8] = u32x4{bw[4], bw[5], bw[6], bw[7]};
-    __syncthreads();
-
-    // ---- MFMA: two K sub-steps of 16
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8*)&As[r * LDK + kk + 8 * (lane >> 5)];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = wn * 64 + j * 32 + (lane & 31);
-        bf[j] = *(const bf16x8*)&Bs[c * LDK + kk + 8 * (lane >> 5)];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if constexpr (PARTIAL)
-            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], part[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-    }
-    if constexpr (PARTIAL) {
-      if ((ks % SCALE_STEPS) == SCALE_STEPS - 1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float sc = s_bscale[wn * 64 + j * 32 + (lane & 31)];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
-              part[i][j][r] = 0.0f;
-            }
-        }
-      }
-    }
+    __syncthreads();  // s_arow and the LDS tiles are rewritten by the next tile
   }
+}
 
-  // ---- epilogue.  Lane holds, for tile (i, j), rows wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4 and
-  // column wn*64 + j*32 + lane%32.
-  const int col = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      if (m >= mrows) continue;
-      if (GATEUP) {
-        const float gte = acc[i][0][r], up = acc[i][1][r];
-        const float hv = gte / (1.0f + expf(-gte)) * up;
-        const int icol = nt * 64 + wn * 32 + col;
-        a.h[(size_t)(row0 + m0 + m) * a.I + icol] = f32_to_bf16_bits(hv);
-      } else {
-        uint16_t* yrow = shared ? a.y_shared + (size_t)(m0 + m) * a.d : a.y_sorted + (size_t)(row0 + m0 + m) * a.d;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) yrow[nt * BN + wn * 64 + j * 32 + col] = f32_to_bf16_bits(acc[i][j][r]);
-      }
-    }
+template <int FMT, bool GATEUP, int WN>
+static hipError_t launch_gemm_cfg(const FfnArgs& a, int tiles_upper, hipStream_t s) {
+  auto kern = gemm_kernel<FMT, GATEUP, WN>;
+  const size_t lds = gemm_lds_bytes(a.E, 64 * WN);
+  static int resident_per_cu = -1;
+  static size_t resident_lds = 0;
+  if (resident_per_cu < 0 || lds > resident_lds) {
+    int per_cu = 0;
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipGetLastError();
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) return hipGetLastError();
+    resident_per_cu = per_cu > 0 ? per_cu : 1;
+    resident_lds = lds;
   }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+  const int ntiles = (GATEUP ? 2 * a.I : a.d) / (64 * WN);
+  long long blocks = (long long)tiles_upper * ntiles;
+  const long long cap = (long long)resident_per_cu * cus;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+// 256-row weight tiles for bf16 and MXFP4 when the matrix divides into them; 128-row tiles otherwise
+// and for the formats that keep per-scale-block partial sums
+template <int FMT, bool GATEUP>
+static hipError_t launch_gemm_fmt(const FfnArgs& a, int tiles_upper, hipStream_t s) {
+  const int rows = GATEUP ? 2 * a.I : a.d;
+  if constexpr (FMT == FMT_BF16 || FMT == FMT_MXFP4)
+    if (rows % 256 == 0) return launch_gemm_cfg<FMT, GATEUP, 4>(a, tiles_upper, s);
+  return launch_gemm_cfg<FMT, GATEUP, 2>(a, tiles_upper, s);
 }
 
 template <bool GATEUP>
 static hipError_t launch_gemm(const FfnArgs& a, int tiles_upper, hipStream_t s) {
-  const int ntiles = GATEUP ? (2 * a.I) / BN : a.d / BN;
-  long long blocks = (long long)tiles_upper * ntiles;
-  if (blocks < 1) blocks = 1;
-  dim3 grid((unsigned)blocks), block(256);
   switch (a.fmt) {
-    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<FMT_BF16, GATEUP>), grid, block, 0, s, a); break;
-    case FMT_Q4_0: hipLaunchKernelGGL((gemm_kernel<FMT_Q4_0, GATEUP>), grid, block, 0, s, a); break;
-    case FMT_MXFP4: hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, GATEUP>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<FMT_FP8_B128, GATEUP>), grid, block, 0, s, a); break;
+    case FMT_BF16: return launch_gemm_fmt<FMT_BF16, GATEUP>(a, tiles_upper, s);
+    case FMT_Q4_0: return launch_gemm_fmt<FMT_Q4_0, GATEUP>(a, tiles_upper, s);
+    case FMT_MXFP4: return launch_gemm_fmt<FMT_MXFP4, GATEUP>(a, tiles_upper, s);
+    default: return launch_gemm_fmt<FMT_FP8_B128, GATEUP>(a, tiles_upper, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s) {
