@@ -167,8 +167,8 @@ def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_byte
         wv = write.get(name, (0.0, 0))[0]
         kernels[name] = {"dispatches": n, "fetch_kib": round(v, 1), "write_kib": round(wv, 1),
                          "fetch_bytes": round(v * 1024 * f_fetch), "write_bytes": round(wv * 1024 * f_write)}
-    # every layer call launches exactly one routing kernel
-    calls = sum(k["dispatches"] for name, k in kernels.items() if "route" in name)
+    # every layer call launches exactly one routing kernel or one fused decode-layer kernel
+    calls = sum(k["dispatches"] for name, k in kernels.items() if "route_kernel" in name or "layer_decode" in name)
     assert calls > 0, "no routing kernel in the counter run"
     per_call = lambda key: round(sum(k[key] * k["dispatches"] for k in kernels.values()) / calls)
     rec = {"T": T, "source_hash": kernel_source_hash(), "copy_probe_bytes": copy_bytes,
@@ -271,8 +271,9 @@ def main():
         rec = json.load(open(prof)).get(w.name)
         if rec and rec.get("source_hash") == src_hash and rec.get("T") == T:
             roof["traffic"] = rec["bytes_per_call"]
-    roof["kernel"] = ("ft_moe_layer: route_permute_kernel + ffn_combine_kernel (streaming GEMV, fused combine)"
-                      if T <= 16 else "ft_moe_layer: route, permute, grouped FFN (MFMA GEMM + GEMV), combine")
+    roof["kernel"] = ("ft_moe_layer: layer_decode_kernel (one launch: routing, permutation, streaming GEMV, "
+                      "combine)" if T <= 16 else
+                      "ft_moe_layer: route, permute, grouped FFN (MFMA GEMM + GEMV), combine kernels")
     roof["per_call_us"] = round(ffn_us, 3)
     roof["algorithmic_bytes_per_call"] = round(bytes_call)
     roof["algorithmic_flops_per_call"] = round(flops_call)
