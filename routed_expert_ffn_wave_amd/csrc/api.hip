@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <exception>
 
@@ -317,7 +318,8 @@ int ft_moe_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int
     CHECK_PTR(slot_of_expert, "slot_of_expert");
     CHECK_PTR(out, "out");
     if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
-    return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, T, E, k, d, out, residual_mask,
+    return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, INT_MAX, T, E, k, d, out,
+                                          residual_mask,
                                           (flags & FT_OUT_BF16) != 0, stream),
                       "ft_moe_combine launch");
   } catch (...) {
@@ -453,7 +455,8 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
       rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
                               (uint16_t*)(wsb + W.h), flags & FT_PATH_MASK, stream);
       if (rc) return rc;
-      return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, T, E, k, bank->d, out,
+      return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
+                                            bank->d, out,
                                             residual_mask, out_bf16, stream),
                         "ft_moe_layer combine launch");
     }

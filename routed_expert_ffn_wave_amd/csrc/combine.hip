@@ -15,7 +15,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ y_shared,
                                                       const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
-                                                      const int32_t* __restrict__ slot_of, int E, int k, int d,
+                                                      const int32_t* __restrict__ slot_of, int n_slots, int E,
+                                                      int k, int d,
                                                       void* __restrict__ out, uint32_t* __restrict__ mask) {
   const int t = blockIdx.x;
   __shared__ int s_row[32];
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     bool nonres = false;
     if (j < k) {
       const int e = ids[(size_t)t * k + j];
-      nonres = (unsigned)e >= (unsigned)E || slot_of[e] < 0;  // an invalid id counts as not resident
+      // an invalid id, or a slot outside [0, n_slots), counts as not resident
+      nonres = (unsigned)e >= (unsigned)E || (unsigned)slot_of[e] >= (unsigned)n_slots;
       s_row[j] = nonres ? -1 : inv[(size_t)t * k + j];
       s_w[j] = w[(size_t)t * k + j];
     }
@@ -71,14 +73,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids, const float* w,
-                          const int32_t* inv, const int32_t* slot_of, int T, int E, int k, int d, void* out,
-                          uint32_t* mask, bool out_bf16, hipStream_t s) {
+                          const int32_t* inv, const int32_t* slot_of, int n_slots, int T, int E, int k, int d,
+                          void* out, uint32_t* mask, bool out_bf16, hipStream_t s) {
   if (out_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, y_sorted, y_shared, ids, w, inv, slot_of, E, k,
-                       d, out, mask);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, y_sorted, y_shared, ids, w, inv, slot_of, n_slots,
+                       E, k, d, out, mask);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, y_sorted, y_shared, ids, w, inv, slot_of,
-                       E, k, d, out, mask);
+                       n_slots, E, k, d, out, mask);
   return hipGetLastError();
 }
 

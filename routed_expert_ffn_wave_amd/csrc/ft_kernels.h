@@ -32,8 +32,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids, const float* w,
-                          const int32_t* inv, const int32_t* slot_of, int T, int E, int k, int d, void* out,
-                          uint32_t* mask, bool out_bf16, hipStream_t s);
+                          const int32_t* inv, const int32_t* slot_of, int n_slots, int T, int E, int k, int d,
+                          void* out, uint32_t* mask, bool out_bf16, hipStream_t s);
 
 // Streaming GEMV path (few rows per group).  groups_upper / rows_upper: host-side bounds on the
 // number of groups and of rows (tokens) the launch may see, used to size the grid.

@@ -206,6 +206,25 @@ def test_fused_layer_cases(ft, case, T):
     compare_layer(li, g, label=f"fused {case} T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("unfused", [False, True])
+def test_layer_slots_beyond_bank(ft, T, unfused):
+    """Slot-table entries at or past the bank's n_slots count as not resident on both paths of
+    ft_moe_layer: the result equals the oracle's with those entries set to -1."""
+    w = EDGE.replace(T=16, shared=False)
+    li = synth.layer_inputs(w, layer=4, T=T)
+    bank = device_bank(li.bank)
+    n_slots = li.bank.n_slots
+    ref_slots = li.slot_of_expert.clone()
+    ref_slots[[2, 5]] = -1
+    li.slot_of_expert = li.slot_of_expert.clone()
+    li.slot_of_expert[2] = n_slots
+    li.slot_of_expert[5] = n_slots + 7
+    g = run_gpu_layer(li, bank, flags=ft.FT_LAYER_UNFUSED if unfused else 0)
+    li.slot_of_expert = ref_slots
+    compare_layer(li, g, label=f"slots beyond bank T={T} unfused={unfused}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 37])
 def test_layer_small_sweep_fp8(ft, T):
     w = SMALL["fp8_resident"]
