@@ -37,6 +37,13 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s << 23);
 }
 
+// (v & m) | o in one instruction: m is uniform (an SGPR), o is kept in a VGPR
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(m), "v"(o));
+  return r;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
@@ -98,10 +105,13 @@ struct Chunk<FMT_Q4_0> {
   // word w, shift 4s: nibbles s (low half) and s+4 (high half) = elements 8w+2s and 8w+2s+1
   __device__ static void decode(const u32x4& c, uint32_t* p) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 4; ++w) decode_word(c[w], p + 4 * w);
+  }
+  // (v >> 4s) & 0x000F000F | 0x43004300 as one shift and one v_and_or_b32 (the compiler would
+  // otherwise emit an AND and an OR, each with a literal operand)
+  __device__ static void decode_word(uint32_t v, uint32_t* p) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) p[4 * w + s] = ((c[w] >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
-    }
+    for (int s = 0; s < 4; ++s) p[s] = and_or(s == 0 ? v : v >> (4 * s), 0x000F000Fu, 0x43004300u);
   }
 };
 
