@@ -149,4 +149,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Inclusive prefix sum over the 64 lanes with DPP (gfx9): shifts within each row of 16 lanes, then
+// the row totals broadcast to the rows above.  Lanes whose source is outside the pattern add 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_or_zero<0x111>(x);        // row_shr:1
+  x += dpp_or_zero<0x112>(x);        // row_shr:2
+  x += dpp_or_zero<0x114>(x);        // row_shr:4
+  x += dpp_or_zero<0x118>(x);        // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 }  // namespace ftk

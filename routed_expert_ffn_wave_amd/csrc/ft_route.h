@@ -143,11 +143,11 @@ __device__ __forceinline__ void route_rows(const float* __restrict__ logits, int
     for (int i = 1; i < VPR; ++i) best = max(best, key[i]);
     const int m = row_max_i(best);
     if (j == 0) key0 = m;  // the row's largest logit, in every lane
+    // lowest index holding m in this lane: a min over independent selects, not a chain
     int cand = INT_MAX;
 #pragma unroll
-    for (int i = VPR - 1; i >= 0; --i)
-      if (key[i] == m) cand = 16 * i + l16;  // lowest i wins: scanned last
-    if (m == INT_MIN) cand = INT_MAX;        // nothing left (a missing token)
+    for (int i = 0; i < VPR; ++i) cand = min(cand, key[i] == m ? 16 * i + l16 : INT_MAX);
+    if (m == INT_MIN) cand = INT_MAX;  // nothing left (a missing token)
     const int e = row_min_i(cand);
 #pragma unroll
     for (int i = 0; i < VPR; ++i)

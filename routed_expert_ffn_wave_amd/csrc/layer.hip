@@ -27,7 +27,6 @@
 #include "ft_gemv.h"
 #include "ft_groups.h"
 #include "ft_kernels.h"
-#include "ft_permute.h"
 #include "ft_route.h"
 
 namespace ftk {
@@ -44,15 +43,19 @@ __device__ __forceinline__ void atomic_zero_agent(int32_t* p) {
   __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Groups a fused call can have: one per routed (token, slot) pair at most, one per expert at
+// most, plus the shared expert.
+__host__ __device__ inline int layer_group_cap(int T, int E, int k) { return (T * k < E ? T * k : E) + 1; }
+
 // LDS of the routing / permutation / group part, in ints (the GEMV union follows, 16-aligned)
 __host__ __device__ inline size_t layer_meta_ints(int T, int E, int k, int NT) {
   const int n = T * k;
-  return (size_t)E                 // slot table
-         + 5 * (size_t)n           // ids, w, gather, inv, crow
-         + 3 * (size_t)E + 1       // counts, offsets (E+1), running bases
-         + (size_t)T               // contributions expected per token
-         + 4 * (size_t)(E + 2) + 4 // groups
-         + 2 + NT * LAYER_RPL2;    // control
+  return (size_t)E                                // slot table
+         + 4 * (size_t)n                          // ids, w, gather, crow
+         + (size_t)T                              // contributions expected per token
+         + 4 * (size_t)(layer_group_cap(T, E, k) + 1) + 4  // groups
+         + 1 + 16                                 // resident ballots (8 x 64 bits, 8-aligned)
+         + 2 + NT * LAYER_RPL2;                   // control
 }
 
 // LDS of the GEMV items: gate/up items over d, down items (LAYER_RPL2 row blocks) over I
@@ -61,27 +64,169 @@ __host__ __device__ inline size_t layer_union_bytes(int fmt, int d, int I, int N
   return u13 > u2 ? u13 : u2;
 }
 
+// Permutation, group list and per-pair / per-token bookkeeping of a decode layer, by one wave and
+// without LDS round trips between the steps (FreeToken walk-through "深入FreeToken架构…全链路剖析",
+// section 一: expert dispatch).  Pair f = t*k + j with expert e_f takes sorted position
+//   pos(f) = #{g : e_g < e_f} + #{g < f : e_g == e_f},
+// which is the stable order by expert; both counts come from ballots of the experts' bits in
+// segments of 64 pairs (an MSB-first comparison of every lane's value against all 64 at once), and
+// the same comparison against expert index e gives offsets[e] = #{g : e_g < e} and counts[e].
+// Writes: s_gtok[pos] = token, s_crow[f] = pos or -1 (expert not resident), s_tgt[t] = number of
+// contributions token t's combine waits for, the groups (resident experts with tokens in
+// ascending expert order, then the shared expert) with their first row chunk, g_tmp[0] = number
+// of groups; block 0 also writes gather, inv, counts, offsets and the residual mask.
+template <int NT, int VPL>
+__device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int* s_slot, const int* s_ids, int* s_gtok,
+                                                   int* s_crow, int* s_tgt, int* g_slot, int* g_row0, int* g_cnt,
+                                                   int* g_rc0, int* g_tmp, uint64_t* s_resb) {
+  const FfnArgs& a = L.f;
+  const int T = a.T, E = a.E, k = a.k, n = T * k, nseg = (n + 63) / 64;
+  // expert ids are below E <= 64 * VPL, so IDB bits order them
+  constexpr int IDB = VPL <= 1 ? 6 : VPL <= 2 ? 7 : VPL <= 4 ? 8 : VPL <= 8 ? 9 : 10;
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const bool out = blockIdx.x == 0;
+  auto resident = [&](int slot) { return slot >= 0 && slot < a.n_slots; };
+
+  // ballots of the expert-id bits of segment s (pairs 64s .. 64s+63); returns the valid lanes
+  uint64_t bits[IDB];
+  auto segment = [&](int s) {
+    const int f = lane + 64 * s;
+    const int e = f < n ? s_ids[f] : -1;
+    const bool ok = f < n && (unsigned)e < (unsigned)E;
+#pragma unroll
+    for (int b = 0; b < IDB; ++b) bits[b] = __ballot(ok && ((e >> b) & 1));
+    return __ballot(ok);
+  };
+  // lanes of the current segment with expert < x (returned) and == x (eq), most significant bit
+  // first, without branches: sel is all ones where bit b of x is set
+  auto compare = [&](int x, uint64_t valid, uint64_t& eq) {
+    uint64_t lt = 0;
+    eq = valid;
+#pragma unroll
+    for (int b = IDB - 1; b >= 0; --b) {
+      const uint64_t m = bits[b];
+      const uint64_t sel = 0ull - (uint64_t)((x >> b) & 1);
+      lt |= eq & ~m & sel;
+      eq &= ~(m ^ sel);
+    }
+    return lt;
+  };
+
+  // per pair: sorted position -> token, and the row its y will be in; s_resb[r]: which pairs of
+  // segment r have a resident expert
+  for (int r = 0; r < nseg; ++r) {
+    const int f = lane + 64 * r;
+    const int e = f < n ? s_ids[f] : -1;
+    const bool ok = f < n && (unsigned)e < (unsigned)E;
+    int p = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const uint64_t valid = segment(s);
+      uint64_t eq;
+      const uint64_t lt = compare(ok ? e : 0, valid, eq);
+      p += __popcll(lt) + (s < r ? __popcll(eq) : s == r ? __popcll(eq & below) : 0);
+    }
+    const bool res = ok && resident(s_slot[e]);
+    const uint64_t rb = __ballot(res);
+    if (lane == 0) s_resb[r] = rb;
+    if (ok) {
+      s_gtok[p] = f / k;
+      s_crow[f] = res ? p : -1;
+      if (out) {
+        L.gather[p] = f;
+        L.inv[f] = p;
+      }
+    }
+  }
+  int ex_lt[VPL], ex_eq[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) ex_lt[u] = ex_eq[u] = 0;
+  int total = 0;
+  for (int s = 0; s < nseg; ++s) {
+    const uint64_t valid = segment(s);
+    total += __popcll(valid);
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      uint64_t eq;
+      const uint64_t lt = compare(lane + 64 * u, valid, eq);
+      ex_lt[u] += __popcll(lt);
+      ex_eq[u] += __popcll(eq);
+    }
+  }
+  // per expert: counts, offsets; groups in ascending expert order with their first row chunk
+  int ng = 0, nrc = 0;
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    const int e = lane + 64 * u;
+    if (64 * u >= E) break;
+    const int cnt = ex_eq[u], off = ex_lt[u];
+    if (out && e < E) {
+      L.counts[e] = cnt;
+      L.offsets[e] = off;
+    }
+    const int slot = e < E ? s_slot[e] : -1;
+    const bool keep = e < E && cnt > 0 && resident(slot);
+    const int items = keep ? (cnt + NT - 1) / NT : 0;
+    const uint64_t kb = __ballot(keep);
+    const int incl = wave_incl_scan(items);
+    if (keep) {
+      const int gi = ng + __popcll(kb & below);
+      g_slot[gi] = slot;
+      g_row0[gi] = off;
+      g_cnt[gi] = cnt;
+      g_rc0[gi] = nrc + incl - items;
+    }
+    ng += __popcll(kb);
+    nrc += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (lane == 0) {
+    if (out) L.offsets[E] = total;
+    if (resident(a.shared_slot)) {  // the shared expert: every token, rows T*k.. of h
+      g_slot[ng] = a.shared_slot;
+      g_row0[ng] = n;
+      g_cnt[ng] = T;
+      g_rc0[ng] = nrc;
+      nrc += (T + NT - 1) / NT;
+      ++ng;
+    }
+    g_rc0[ng] = nrc;
+    g_tmp[0] = ng;
+  }
+  // per token: the residual mask and the contributions its combine waits for, from the resident
+  // ballots (token t's k <= 32 pairs start at bit t*k and span at most two segments)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (lane < T) {
+    const int b0 = lane * k, s0 = b0 >> 6, sh = b0 & 63;
+    uint64_t v = s_resb[s0] >> sh;
+    if (sh + k > 64) v |= s_resb[s0 + 1] << (64 - sh);
+    const uint32_t kmask = k == 32 ? 0xffffffffu : (1u << k) - 1u;
+    const uint32_t res = (uint32_t)v & kmask;
+    s_tgt[lane] = __popc(res) + (a.shared_slot >= 0 ? 1 : 0);
+    if (out && L.mask) L.mask[lane] = ~res & kmask;
+  }
+}
+
 template <int FMT, int WPB, int NT, int VPL, bool OUT_BF16>
 __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   const FfnArgs& a = L.f;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int T = a.T, E = a.E, k = a.k, n = T * k;
-  int* s_slot = (int*)lds;        // [E]
-  int* s_ids = s_slot + E;        // [n]
+  int* s_slot = (int*)lds;           // [E]
+  int* s_ids = s_slot + E;           // [n]
   float* s_w = (float*)(s_ids + n);  // [n]
-  int* s_gather = (int*)(s_w + n);   // [n] sorted position -> flat index; then -> token
-  int* s_inv = s_gather + n;      // [n]
-  int* s_crow = s_inv + n;        // [n] sorted row a (token, slot) pair's y sits in, -1 if not computed
-  int* s_cnt = s_crow + n;        // [E]
-  int* s_off = s_cnt + E;         // [E+1]
-  int* s_base = s_off + E + 1;    // [E]
-  int* s_tgt = s_base + E;        // [T]
-  int* g_slot = s_tgt + T;        // groups: [E+2] each
-  int* g_row0 = g_slot + E + 2;
-  int* g_cnt = g_row0 + E + 2;
-  int* g_rc0 = g_cnt + E + 2;
-  int* g_tmp = g_rc0 + E + 2;     // [4]
-  int* s_ctl = g_tmp + 4;         // [0]: claimed position, [1]: last block, [2..): (token, column block)s to combine
+  int* s_gather = (int*)(s_w + n);   // [n] sorted position -> token
+  int* s_crow = s_gather + n;        // [n] sorted row a (token, slot) pair's y sits in, -1 if not computed
+  int* s_tgt = s_crow + n;           // [T]
+  const int gcap = layer_group_cap(T, E, k);
+  int* g_slot = s_tgt + T;           // groups: [gcap + 1] each
+  int* g_row0 = g_slot + gcap + 1;
+  int* g_cnt = g_row0 + gcap + 1;
+  int* g_rc0 = g_cnt + gcap + 1;
+  int* g_tmp = g_rc0 + gcap + 1;     // [4]
+  // [8] resident-pair ballots per segment of 64 pairs, at an even int offset (8-byte aligned)
+  uint64_t* s_resb = (uint64_t*)(s_slot + (((int)(g_tmp + 4 - s_slot) + 1) & ~1));
+  int* s_ctl = (int*)(s_resb + 8);         // [0]: claimed position, [1]: last block, [2..): (token, column block)s to combine
   uint8_t* s_union = lds + ((layer_meta_ints(T, E, k, NT) * 4 + 15) & ~(size_t)15);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -90,10 +235,7 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   const int nq = min((int)gridDim.x, LAYER_NQ), qx = blockIdx.x % nq;
   const int nb_q = ((int)gridDim.x - qx + nq - 1) / nq;
   int32_t* queue = L.ctl + CTL_QUEUE + qx * CNT_STRIDE;
-  for (int i = tid; i < E; i += WPB * 64) {
-    s_slot[i] = a.slot_of[i];
-    s_cnt[i] = 0;
-  }
+  for (int i = tid; i < E; i += WPB * 64) s_slot[i] = a.slot_of[i];
 
   // ---- route (the same routine as the router kernel, so both give the same bits)
   route_tokens<VPL>(L.logits, T, E, k, w, WPB, [&](int t, int j, int e, float wt) {
@@ -102,52 +244,16 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   });
   __syncthreads();
 
-  // ---- permute (wave 0): histogram, offsets, stable positions
-  if (w == 0) {
-    count_segment(s_ids, n, E, 0, s_cnt);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    wave_exclusive_scan(s_cnt, E, s_off);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < E; i += 64) s_base[i] = s_off[i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    scatter_segment(s_ids, n, E, 0, L.id_bits, s_base, s_gather, s_inv);
-  }
+  // ---- permutation, groups, per-pair rows and per-token counts: wave 0, in registers
+  if (w == 0)
+    decode_bookkeeping<NT, VPL>(L, s_slot, s_ids, s_gather, s_crow, s_tgt, g_slot, g_row0, g_cnt, g_rc0, g_tmp, s_resb);
   __syncthreads();
-
-  // ---- per pair: the row its y will be in (or -1: expert not resident); per token: the mask and
-  // the number of contributions its combine waits for
-  const bool shared_on = a.shared_slot >= 0;
-  for (int f = tid; f < n; f += WPB * 64) {
-    const int slot = s_slot[s_ids[f]];
-    s_crow[f] = (slot >= 0 && slot < a.n_slots) ? s_inv[f] : -1;
-  }
-  if (tid < T) {
-    uint32_t bits = 0;
-    int cnt = 0;
-    for (int j = 0; j < k; ++j) {
-      const int slot = s_slot[s_ids[tid * k + j]];
-      if (slot >= 0 && slot < a.n_slots)
-        ++cnt;
-      else
-        bits |= 1u << j;
-    }
-    s_tgt[tid] = cnt + (shared_on ? 1 : 0);
-    if (blockIdx.x == 0 && L.mask) L.mask[tid] = bits;
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) {  // the routing and permutation outputs of the call
+  if (blockIdx.x == 0) {  // the routing outputs of the call, and zero rows for tokens with nothing to combine
     for (int f = tid; f < n; f += WPB * 64) {
       L.ids[f] = s_ids[f];
       L.w[f] = s_w[f];
-      L.gather[f] = s_gather[f];
-      L.inv[f] = s_inv[f];
     }
-    for (int e = tid; e < E; e += WPB * 64) L.counts[e] = s_cnt[e];
-    for (int e = tid; e <= E; e += WPB * 64) L.offsets[e] = s_off[e];
-    for (int t = 0; t < T; ++t) {  // tokens with nothing to combine
+    for (int t = 0; t < T; ++t) {
       if (s_tgt[t] != 0) continue;
       for (int c = tid; c < a.d; c += WPB * 64) {
         if (OUT_BF16)
@@ -157,13 +263,7 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
       }
     }
   }
-  // sorted row -> token, in place (block 0's thread stored the flat index above, same element)
-  for (int p = tid; p < n; p += WPB * 64) s_gather[p] = s_gather[p] / k;
-
-  // ---- groups, then the items
-  GroupSrc src{s_slot, s_off, E, T, k, a.shared_slot, 1, 0x7fffffff, a.n_slots};
-  GroupList gl{g_slot, g_row0, g_cnt, g_rc0, 0};
-  build_groups(src, gl, g_tmp, [&](int cnt) { return (cnt + NT - 1) / NT; });  // ends with a barrier
+  GroupList gl{g_slot, g_row0, g_cnt, g_rc0, g_tmp[0]};
   constexpr int RPL2 = LAYER_RPL2;
   const int ncb13 = 2 * a.I / 64, ncb2 = a.d / 64, nit2 = ncb2 / RPL2;  // down items: RPL2 row blocks each
   const int nrc = g_rc0[gl.n];
