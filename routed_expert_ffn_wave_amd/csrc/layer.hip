@@ -235,13 +235,25 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
   const int nq = min((int)gridDim.x, LAYER_NQ), qx = blockIdx.x % nq;
   const int nb_q = ((int)gridDim.x - qx + nq - 1) / nq;
   int32_t* queue = L.ctl + CTL_QUEUE + qx * CNT_STRIDE;
-  for (int i = tid; i < E; i += WPB * 64) s_slot[i] = a.slot_of[i];
+  // the slot table is loaded into registers first, so that its round trip overlaps the logits'
+  constexpr int SLOTS_PER_THREAD = (64 * VPL + WPB * 64 - 1) / (WPB * 64);  // E <= 64 * VPL
+  int slot_reg[SLOTS_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < SLOTS_PER_THREAD; ++i) {
+    const int e = tid + i * WPB * 64;
+    slot_reg[i] = e < E ? a.slot_of[e] : -1;
+  }
 
   // ---- route (the same routine as the router kernel, so both give the same bits)
   route_tokens<VPL>(L.logits, T, E, k, w, WPB, [&](int t, int j, int e, float wt) {
     s_ids[t * k + j] = e;
     s_w[t * k + j] = wt;
   });
+#pragma unroll
+  for (int i = 0; i < SLOTS_PER_THREAD; ++i) {
+    const int e = tid + i * WPB * 64;
+    if (e < E) s_slot[e] = slot_reg[i];
+  }
   __syncthreads();
 
   // ---- permutation, groups, per-pair rows and per-token counts: wave 0, in registers
