@@ -115,34 +115,51 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   // come through the scalar cache.
   constexpr int XMAX = WPB <= 4 ? 1 : 2;  // 16-byte activation loads per thread and token in the batch
   constexpr int SMAX = WPB <= 4 ? 2 : 4;  // 16-byte scale loads per thread in the batch
+  // With more than 4 tokens per item the rows are staged as one flat list of 16-byte pieces
+  // (piece v = token v / (K/8), column piece v % (K/8)), XB pieces per thread and batch.
+  constexpr bool FLAT = NT > 4;
+  constexpr int XB = 4;
   constexpr int SB = FMT == FMT_Q4_0 ? 2 : 1;
   constexpr bool STAGE_SCALES = FMT == FMT_Q4_0 || FMT == FMT_MXFP4;
   const int nx8 = K / 8;
   const int nsv = STAGE_SCALES ? RPL * nchunk * 64 * SB / 16 : 0;  // the RPL row blocks' scales are one run
   const uint8_t* ssrc = scales + ((size_t)slot * nrows * nchunk + (size_t)RPL * cb * nchunk * 64) * SB;
-  const uint16_t* xr[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tt = t < nt ? t : nt - 1;
+  auto row_of = [&](int tt) -> const uint16_t* {  // activation row of the item's token tt
     if (GATEUP) {
       const int tok = shared ? t0 + tt
                       : s_tok ? s_tok[row0 + t0 + tt]
                               : (int)((scalar_u32p)(uintptr_t)a.gather)[row0 + t0 + tt] / a.k;
-      xr[t] = a.x + (size_t)tok * a.d;
-    } else {
-      xr[t] = a.h + (size_t)(row0 + t0 + tt) * a.I;
+      return a.x + (size_t)tok * a.d;
     }
+    return a.h + (size_t)(row0 + t0 + tt) * a.I;
+  };
+  constexpr int NXR = FLAT ? 1 : NT;
+  const uint16_t* xr[NXR];
+  if constexpr (!FLAT) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xr[t] = row_of(t < nt ? t : nt - 1);
   }
   auto load_x = [&](const uint16_t* p) -> u32x4 {
     return (COH && !GATEUP) ? load_u32x4_agent(p) : *(const u32x4*)p;
   };
-  u32x4 xv[XMAX][NT];
+  const int nx = nt * nx8;
+  auto load_piece = [&](int v) { return load_x(row_of(v / nx8) + 8 * (v % nx8)); };
+  u32x4 xv[FLAT ? 1 : XMAX][NXR];
+  u32x4 xf[FLAT ? XB : 1];
+  if constexpr (FLAT) {
 #pragma unroll
-  for (int i = 0; i < XMAX; ++i) {
-    const int e8 = threadIdx.x + i * NTHR;
+    for (int i = 0; i < XB; ++i) {
+      const int v = threadIdx.x + i * NTHR;
+      if (v < nx) xf[i] = load_piece(v);
+    }
+  } else {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (t < nt && e8 < nx8) xv[i][t] = load_x(xr[t] + 8 * e8);
+    for (int i = 0; i < XMAX; ++i) {
+      const int e8 = threadIdx.x + i * NTHR;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t < nt && e8 < nx8) xv[i][t] = load_x(xr[t] + 8 * e8);
+    }
   }
   u32x4 sv[SMAX];
 #pragma unroll
@@ -180,12 +197,32 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
       if ((e8 & 3) == 0) s_xsum[t * (K / 32) + (e8 >> 2)] = sum;
     }
   };
+  if constexpr (FLAT) {
 #pragma unroll
-  for (int i = 0; i < XMAX; ++i) {
-    const int e8 = threadIdx.x + i * NTHR;
+    for (int i = 0; i < XB; ++i) {
+      const int v = threadIdx.x + i * NTHR;
+      if (v < nx) put_x(v / nx8, v % nx8, xf[i]);
+    }
+    for (int v0 = XB * NTHR; v0 < nx; v0 += XB * NTHR) {  // further batches (the weights are in flight)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (t < nt && e8 < nx8) put_x(t, e8, xv[i][t]);
+      for (int i = 0; i < XB; ++i) {
+        const int v = v0 + threadIdx.x + i * NTHR;
+        if (v < nx) xf[i] = load_piece(v);
+      }
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        const int v = v0 + threadIdx.x + i * NTHR;
+        if (v < nx) put_x(v / nx8, v % nx8, xf[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < XMAX; ++i) {
+      const int e8 = threadIdx.x + i * NTHR;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t < nt && e8 < nx8) put_x(t, e8, xv[i][t]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < SMAX; ++i) {
@@ -193,8 +230,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
     if (v < nsv) *(u32x4*)(s_sc + 16 * (size_t)v) = sv[i];
   }
   // rows longer than the batch (not reached by the shapes the launch pairs with WPB)
-  for (int e8 = threadIdx.x + XMAX * NTHR; e8 < nx8; e8 += NTHR)
-    for (int t = 0; t < nt; ++t) put_x(t, e8, load_x(xr[t] + 8 * e8));
+  if constexpr (!FLAT) {
+    for (int e8 = threadIdx.x + XMAX * NTHR; e8 < nx8; e8 += NTHR)
+      for (int t = 0; t < nt; ++t) put_x(t, e8, load_x(xr[t] + 8 * e8));
+  }
   for (int v = threadIdx.x + SMAX * NTHR; v < nsv; v += NTHR)
     *(u32x4*)(s_sc + 16 * (size_t)v) = *(const u32x4*)(ssrc + 16 * (size_t)v);
 

@@ -30,7 +30,7 @@
 namespace ftk {
 
 template <int FMT, bool GATEUP, int WPB, int NT>
-__global__ __launch_bounds__(WPB * 64) void gemv_kernel(FfnArgs a) {
+__global__ __launch_bounds__(WPB * 64, 4) void gemv_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int E2 = a.E + 2;
   int* s_slot = (int*)lds;
@@ -86,10 +86,15 @@ static hipError_t launch_cfg(const FfnArgs& a, int groups_upper, long long rows_
   return hipGetLastError();
 }
 
+// Groups reach this kernel with up to GEMV_MAX_ROWS tokens; an item carries up to NT of them, and
+// every further row chunk of a group reads the expert's weights again.  So short rows take 16
+// tokens per item (one pass over the weights per group), longer rows 8 or 4 (their activation rows
+// must fit in LDS); eight waves per block keep enough loads in flight with two blocks per CU.
 template <int FMT, bool GATEUP>
 static hipError_t launch_fmt(const FfnArgs& a, int groups_upper, long long rows_upper, hipStream_t s) {
   const int K = GATEUP ? a.d : a.I;
-  if (K <= 2048) return launch_cfg<FMT, GATEUP, 4, 4>(a, groups_upper, rows_upper, s);
+  if (K <= 2048) return launch_cfg<FMT, GATEUP, 8, 16>(a, groups_upper, rows_upper, s);
+  if (K <= 4096) return launch_cfg<FMT, GATEUP, 8, 8>(a, groups_upper, rows_upper, s);
   return launch_cfg<FMT, GATEUP, 8, 4>(a, groups_upper, rows_upper, s);
 }
 
