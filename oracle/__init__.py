@@ -24,7 +24,7 @@ _LIB = os.path.join(_HERE, "libftoracle.so")
 CFLAGS = ["-O2", "-fno-tree-vectorize", "-fno-tree-slp-vectorize", "-ffp-contract=off", "-fno-fast-math",
           "-std=c11", "-fPIC", "-shared", "-Wall", "-Werror"]
 
-FMT_BF16, FMT_Q4_0, FMT_MXFP4, FMT_FP8_B128 = 0, 1, 2, 3
+FMT_BF16, FMT_Q4_0, FMT_MXFP4, FMT_FP8_B128, FMT_NVFP4 = 0, 1, 2, 3, 4
 
 
 def build(extra_flags=(), out=_LIB) -> str:

@@ -5,7 +5,7 @@
  *
  * What it computes.  The FreeToken architecture walk-through ("深入FreeToken架构
  * …全链路剖析", section 五 "MoE 引擎") fixes the structure: expert FFNs live in
- * per-format quantised banks (BF16, FP8 block, MXFP4, GGUF Q4_0), GPU-resident
+ * per-format quantised banks (BF16, FP8 block, NVFP4, MXFP4, GGUF Q4_0), GPU-resident
  * ("hot") experts are found by lookup, and cold experts are computed elsewhere.
  * Section 一 names "MoE 专家调度" (expert dispatch) as a stage of the request
  * path.  The pages give no formula for the gate, the top-k rule, the FFN or the
@@ -30,7 +30,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORA_BF16 = 0, ORA_Q4_0 = 1, ORA_MXFP4 = 2, ORA_FP8_B128 = 3 };
+enum { ORA_BF16 = 0, ORA_Q4_0 = 1, ORA_MXFP4 = 2, ORA_FP8_B128 = 3, ORA_NVFP4 = 4 };
 
 int ora_version(void) { return 1; }
 
@@ -89,6 +89,9 @@ float ora_e8m0_value(unsigned s) { return s == 255 ? NAN : ldexpf(1.0f, (int)s -
  *   MXFP4    codes uint8 [rows][K/2] (element 2i low nibble, 2i+1 high), scales uint8 [rows][K/32];
  *            v = e2m1(q) * 2^(s-127)
  *   FP8_B128 codes uint8 [rows][K], scales fp32 [rows/128][K/128]; v = fl32(scale * e4m3(q))
+ *   NVFP4    codes uint8 [rows][K/2] as MXFP4; scales uint8 [rows][K/16] e4m3 (one per 16 along K)
+ *            followed by one fp32 tensor scale t (little endian, 4-byte aligned);
+ *            v = fl32(t * (e2m1(q) * e4m3(s)))  (the inner product is exact in fp32)
  * Returns 0, or -1 for a bad format or shape.
  */
 int ora_dequant(int fmt, const void* codes, const void* scales, int rows, int K, int row0, int nrows,
@@ -117,6 +120,16 @@ int ora_dequant(int fmt, const void* codes, const void* scales, int rows, int K,
       for (int j = 0; j < K; ++j) {
         unsigned q = (j & 1) ? (c[j / 2] >> 4) : (c[j / 2] & 15);
         o[j] = ora_e2m1_value(q) * ora_e8m0_value(s[j / 32]);
+      }
+    } else if (fmt == ORA_NVFP4) {
+      if (K % 32) return -1;
+      const uint8_t* c = (const uint8_t*)codes + (size_t)r * (K / 2);
+      const uint8_t* s = (const uint8_t*)scales + (size_t)r * (K / 16);
+      float t;
+      memcpy(&t, (const uint8_t*)scales + (size_t)rows * (K / 16), 4);
+      for (int j = 0; j < K; ++j) {
+        const unsigned q = (c[j >> 1] >> (4 * (j & 1))) & 15u; /* element 2i low nibble, 2i+1 high */
+        o[j] = t * (ora_e2m1_value(q) * ora_e4m3_value(s[j / 16]));
       }
     } else if (fmt == ORA_FP8_B128) {
       if (K % 128 || rows % 128) return -1;

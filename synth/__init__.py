@@ -4,10 +4,10 @@ This module draws and encodes inputs only.  It holds none of the layer's
 arithmetic (no routing, no dequantisation, no FFN): it is shared by the CPU
 oracle and the HIP path so that both see the same bytes, and nothing else is.
 
-Workloads are five MoE-layer shapes, with their sizes written out below.
+Workloads are six MoE-layer shapes, with their sizes written out below.
 The expert-bank formats are the ones the FreeToken
 architecture walk-through lists for its expert banks ("深入FreeToken架构…全链路
-剖析", section 五 "MoE 引擎": BF16 / FP8 block / MXFP4 / GGUF Q4_0 each with its
+剖析", section 五 "MoE 引擎": BF16 / FP8 block / NVFP4 / MXFP4 / GGUF Q4_0 each with its
 own bank schema).  Encodings follow the public format definitions:
 
 * Q4_0 (GGUF): blocks of 32 weights along K, 18 bytes each: an fp16 scale
@@ -18,6 +18,9 @@ own bank schema).  Encodings follow the public format definitions:
   along K, stored in a separate [rows][K/32] array.
 * FP8-B128: OCP e4m3fn elements with one fp32 scale per 128x128 block of
   (output row, K), stored as [rows/128][K/128].
+* NVFP4: e2m1 elements packed as for MXFP4, one e4m3fn scale byte per 16
+  elements along K ([rows][K/16]) and one fp32 scale for the whole matrix,
+  stored after the block scales; value = tensor scale * e2m1 * e4m3.
 * BF16: plain bf16, row-major.
 
 Random numbers: each tensor has its own torch generator seeded from
@@ -34,8 +37,9 @@ import dataclasses
 import numpy as np
 import torch
 
-FMT_BF16, FMT_Q4_0, FMT_MXFP4, FMT_FP8_B128 = 0, 1, 2, 3
-FMT_NAMES = {FMT_BF16: "bf16", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_FP8_B128: "fp8_b128"}
+FMT_BF16, FMT_Q4_0, FMT_MXFP4, FMT_FP8_B128, FMT_NVFP4 = 0, 1, 2, 3, 4
+FMT_NAMES = {FMT_BF16: "bf16", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_FP8_B128: "fp8_b128",
+             FMT_NVFP4: "nvfp4"}
 
 STREAM_LOGITS, STREAM_X, STREAM_RANK, STREAM_SLOTS, STREAM_GATE, STREAM_UP, STREAM_DOWN = range(7)
 
@@ -87,6 +91,8 @@ WORKLOADS = {
     # Resident-bank layer: FP8-B128 banks, 96 of 256 experts resident, residual mask, T sweep.
     "fp8_resident": Workload("fp8_resident", 4, T=16384, d=7168, E=256, k=8, I=2048, fmt=FMT_FP8_B128,
                              zipf=True, n_resident=96, t_sweep=(1, 16, 256, 4096, 16384)),
+    # The decode shape above with NVFP4 banks (the fifth bank format of the walk-through).
+    "nvfp4_decode": Workload("nvfp4_decode", 5, T=8, d=2048, E=128, k=8, I=768, fmt=FMT_NVFP4, layers=48),
 }
 
 
@@ -239,8 +245,45 @@ def encode_fp8_b128(wt: torch.Tensor):
     return q.reshape(rows, K).contiguous(), scale.reshape(rows // 128, K // 128).contiguous()
 
 
+def _e2m1_codes(v: torch.Tensor) -> torch.Tensor:
+    """Nearest e2m1 code of each value (ties to the even code), saturating at 6; sign in bit 3."""
+    a = v.abs()
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float32, device=v.device)
+    dist = (a.unsqueeze(-1) - grid).abs()
+    best = dist.amin(dim=-1, keepdim=True)
+    codes = torch.arange(8, device=v.device)
+    score = (dist == best).to(torch.int32) * (2 - (codes & 1))
+    mag = score.argmax(dim=-1).to(torch.uint8)
+    return mag | (((v < 0) & (mag != 0)).to(torch.uint8) << 3)
+
+
+def encode_nvfp4(wt: torch.Tensor):
+    """NVFP4: codes [rows][K/2] uint8 (element 2i low nibble), scales uint8 [rows*K/16 + 4]: one
+    e4m3fn scale per 16 elements along K, then the matrix's fp32 scale (4 bytes, little endian).
+
+    tensor scale t = amax / (448 * 6), so that block scales fit e4m3; block scale
+    s = e4m3(block amax / 6 / t) (round to nearest even, saturating at 448); elements are the
+    nearest e2m1 values of w / (t * s) (ties to the even code, saturating at 6)."""
+    rows, K = wt.shape
+    assert K % 32 == 0
+    amax = wt.abs().amax()
+    t = (amax / (448.0 * 6.0)).float() if amax > 0 else torch.tensor(1.0, device=wt.device)
+    b = wt.reshape(rows, K // 16, 16)
+    bmax = b.abs().amax(dim=-1, keepdim=True)
+    sq = (bmax / 6.0 / t).clamp(max=448.0).to(torch.float8_e4m3fn)
+    s = sq.float()
+    denom = torch.where(s > 0, s * t, torch.ones_like(s))
+    v = torch.where(s > 0, b / denom, torch.zeros_like(b))
+    c = _e2m1_codes(v).reshape(rows, K)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).contiguous()
+    scales = torch.empty(rows * (K // 16) + 4, dtype=torch.uint8, device=wt.device)
+    scales[: rows * (K // 16)] = sq.view(torch.uint8).reshape(-1)
+    scales[rows * (K // 16):] = t.reshape(1).view(torch.uint8)
+    return packed, scales
+
+
 ENCODERS = {FMT_BF16: encode_bf16, FMT_Q4_0: encode_q4_0, FMT_MXFP4: encode_mxfp4,
-            FMT_FP8_B128: encode_fp8_b128}
+            FMT_FP8_B128: encode_fp8_b128, FMT_NVFP4: encode_nvfp4}
 
 
 def code_shape(fmt: int, rows: int, K: int):
@@ -249,7 +292,7 @@ def code_shape(fmt: int, rows: int, K: int):
         return (rows, K), torch.int16
     if fmt == FMT_Q4_0:
         return (rows, K // 32, 18), torch.uint8
-    if fmt == FMT_MXFP4:
+    if fmt in (FMT_MXFP4, FMT_NVFP4):
         return (rows, K // 2), torch.uint8
     if fmt == FMT_FP8_B128:
         return (rows, K), torch.uint8
@@ -261,6 +304,8 @@ def scale_shape(fmt: int, rows: int, K: int):
         return (rows, K // 32), torch.uint8
     if fmt == FMT_FP8_B128:
         return (rows // 128, K // 128), torch.float32
+    if fmt == FMT_NVFP4:
+        return (rows * (K // 16) + 4,), torch.uint8
     return None, None
 
 
@@ -343,7 +388,7 @@ def layer_inputs(w: Workload, layer: int = 0, T: int | None = None, device="cpu"
 def bytes_per_weight(fmt: int) -> float:
     """Stored bytes per weight including scales."""
     return {FMT_BF16: 2.0, FMT_Q4_0: 18.0 / 32.0, FMT_MXFP4: 17.0 / 32.0,
-            FMT_FP8_B128: 1.0 + 4.0 / (128 * 128)}[fmt]
+            FMT_FP8_B128: 1.0 + 4.0 / (128 * 128), FMT_NVFP4: 9.0 / 16.0}[fmt]
 
 
 def expert_bytes(fmt: int, d: int, I: int) -> float:

@@ -201,6 +201,19 @@ def pin_dequant_roundtrip(lib):
     c, s = synth.encode_fp8_b128(torch.from_numpy(w))
     got = oracle.dequant(3, c, s, rows, K, lib=lib)
     assert np.array_equal(got, w), np.abs(got - w).max()
+    # NVFP4: e2m1 grid values times an e4m3 block scale times a tensor scale t.  With +-6 in every
+    # 16-block and amax = 6 * 448 * t in the matrix, the encoder recovers t and every block scale
+    # (t a power of two so that amax / (448 * 6) is t exactly; block scales e4m3 values in [1, 448])
+    t = 2.0 ** -9
+    v = grid[rng.integers(0, 16, size=(rows, K // 16, 16))]
+    v[..., 5] = rng.choice([6.0, -6.0], size=(rows, K // 16))
+    sc_codes = rng.integers(0x38, 0x7F, size=(rows, K // 16, 1)).astype(np.uint8)  # e4m3 1.0 .. 448
+    sc_codes[0, 0, 0] = 0x7E                                                       # 448 somewhere
+    bs = torch.from_numpy(sc_codes).view(torch.float8_e4m3fn).double().numpy()
+    w = (v * bs * t).reshape(rows, K).astype(np.float32)
+    c, s = synth.encode_nvfp4(torch.from_numpy(w))
+    got = oracle.dequant(4, c, s, rows, K, lib=lib)
+    assert np.array_equal(got, w), np.abs(got - w).max()
 
 
 def pin_dequant_layouts(lib):
@@ -223,6 +236,14 @@ def pin_dequant_layouts(lib):
     grid = np.array([float(v) for _, v in _golden("e2m1_values.txt")])
     ref = np.array([grid[j % 16] * 2.0 ** (int(sc[0, j // 32]) - 127) for j in range(64)])[None]
     assert np.array_equal(oracle.dequant(2, codes, sc, 1, 64, lib=lib), ref.astype(np.float32))
+    # NVFP4: same code layout as MXFP4; 16-element blocks with e4m3 scales 0x30 (0.5), 0x40 (2.0),
+    # 0x3C (1.5), 0x44 (3.0); tensor scale 0.25 stored after the block scales
+    bsc = np.array([[0x30, 0x40, 0x3C, 0x44]], np.uint8)
+    tail = np.array([0.25], np.float32).view(np.uint8)
+    ns = np.concatenate([bsc.reshape(-1), tail])
+    bval = [0.5, 2.0, 1.5, 3.0]
+    ref = np.array([0.25 * grid[j % 16] * bval[j // 16] for j in range(64)])[None]
+    assert np.array_equal(oracle.dequant(4, codes, ns, 1, 64, lib=lib), ref.astype(np.float32))
     # FP8-B128: 256x256 of code 0x38 (1.0); block (rb, cb) has scale 1 + rb + 2cb
     codes = np.full((256, 256), 0x38, np.uint8)
     sc = np.array([[1.0, 3.0], [2.0, 4.0]], np.float32)

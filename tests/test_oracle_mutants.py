@@ -31,6 +31,9 @@ MUTANTS = {
     "q4_nibble_order": ("o[32 * b + i + 16] = scale * (float)(hi - 8);", "o[32 * b + i + 16] = scale * (float)(lo - 8);"),
     "mx_nibble_order": ("unsigned q = (j & 1) ? (c[j / 2] >> 4) : (c[j / 2] & 15);", "unsigned q = (j & 1) ? (c[j / 2] & 15) : (c[j / 2] >> 4);"),
     "mx_scale_index": ("ora_e8m0_value(s[j / 32])", "ora_e8m0_value(s[j / 64])"),
+    "nv_nibble_order": ("(c[j >> 1] >> (4 * (j & 1))) & 15u", "(c[j >> 1] >> (4 * (1 - (j & 1)))) & 15u"),
+    "nv_scale_index": ("ora_e4m3_value(s[j / 16])", "ora_e4m3_value(s[j / 32])"),
+    "nv_tensor_scale_dropped": ("o[j] = t * (ora_e2m1_value(q) * ora_e4m3_value(s[j / 16]));", "o[j] = ora_e2m1_value(q) * ora_e4m3_value(s[j / 16]);"),
     "fp8_block_row": ("(size_t)(r / 128) * (K / 128)", "(size_t)(r % 2) * (K / 128)"),
     "fp8_block_col": ("o[j] = s[j / 128] * ora_e4m3_value(c[j]);", "o[j] = s[0] * ora_e4m3_value(c[j]);"),
     "silu_sign": ("hr[i] = g / (1.0f + expf(-g)) * u;", "hr[i] = g / (1.0f + expf(g)) * u;"),
