@@ -57,7 +57,9 @@ enum ft_weight_format {
   FT_W_BF16 = 0,      /* bf16 weights */
   FT_W_Q4_0 = 1,      /* GGUF Q4_0: blocks of 32 int4 codes along K with one fp16 scale, v = s*(q-8) */
   FT_W_MXFP4 = 2,     /* OCP MXFP4: e2m1 codes with one E8M0 scale per 32 along K, v = e2m1*2^(s-127) */
-  FT_W_FP8_B128 = 3   /* OCP e4m3fn codes with one fp32 scale per 128x128 (row, K) block, v = s*e4m3 */
+  FT_W_FP8_B128 = 3,  /* OCP e4m3fn codes with one fp32 scale per 128x128 (row, K) block, v = s*e4m3 */
+  FT_W_NVFP4 = 4      /* NVFP4: e2m1 codes, one e4m3fn scale per 16 along K and one fp32 scale t per
+                         matrix, v = t * (e2m1 * e4m3) */
 };
 
 /* ft_moe_grouped_ffn flags */
@@ -93,6 +95,9 @@ enum ft_weight_format {
  *                 E8M0 scales, one byte per (row, chunk), interleaved as for Q4_0
  *   FT_W_FP8_B128 16 e4m3fn codes per chunk in K order; scales fp32 [rows/128][K/128] per matrix,
  *                 row-major over logical rows (not interleaved, not reordered)
+ *   FT_W_NVFP4    codes as FT_W_MXFP4; block scales two e4m3fn bytes per (row, chunk) (low byte:
+ *                 elements 0-15 of the chunk, high byte: 16-31), one 16-bit pair per (row, chunk)
+ *                 interleaved as for Q4_0, for all slots; then the fp32 matrix scales, one per slot
  * Array sizes per format: ft_moe_bank_bytes.  Divisibility: d a multiple of 128 and I a multiple of 64
  * (so every matrix has whole 64-row blocks and whole chunks; FP8_B128 also needs I % 128 == 0).
  */
@@ -223,6 +228,8 @@ size_t ft_moe_bank_bytes(int fmt, int n_slots, int d, int I, int which);
  *                 holds element i (low nibble) and element i+16 (high nibble); canon_s13/s2 NULL
  *   FT_W_MXFP4    codes uint8 [rows][K/2] (element 2i low nibble), scales uint8 E8M0 [rows][K/32]
  *   FT_W_FP8_B128 codes uint8 [rows][K], scales fp32 [rows/128][K/128]
+ *   FT_W_NVFP4    codes uint8 [rows][K/2] (element 2i low nibble), scales uint8 [rows*K/16 + 4]:
+ *                 e4m3fn scales [rows][K/16], then the matrix's fp32 scale (little endian)
  * `dst` is a host pointer to a bank whose device arrays are already allocated (sizes from
  * ft_moe_bank_bytes); its fmt/n_slots/d/I must match the arguments.  Source and destination
  * must not overlap.

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libftmoe.so")
 
 FT_OK, FT_E_INVAL, FT_E_UNSUPPORTED, FT_E_WORKSPACE, FT_E_HIP, FT_E_INTERNAL = range(6)
-FT_W_BF16, FT_W_Q4_0, FT_W_MXFP4, FT_W_FP8_B128 = range(4)
+FT_W_BF16, FT_W_Q4_0, FT_W_MXFP4, FT_W_FP8_B128, FT_W_NVFP4 = range(5)
 FT_PATH_AUTO, FT_PATH_GEMV, FT_PATH_GEMM = 0, 1, 2
 FT_OUT_BF16 = 4
 FT_LAYER_UNFUSED = 8

@@ -57,7 +57,7 @@ int check_tek(int T, int E, int k) {
 
 
 int check_bank_shape(int fmt, int n_slots, int d, int I) {
-  REQUIRE(fmt >= FT_W_BF16 && fmt <= FT_W_FP8_B128, FT_E_UNSUPPORTED, "unknown weight format %d", fmt);
+  REQUIRE(fmt >= FT_W_BF16 && fmt <= FT_W_NVFP4, FT_E_UNSUPPORTED, "unknown weight format %d", fmt);
   REQUIRE(n_slots >= 1, FT_E_INVAL, "n_slots must be >= 1 (got %d)", n_slots);
   REQUIRE(d > 0 && I > 0, FT_E_INVAL, "d and I must be positive (got d=%d, I=%d)", d, I);
   REQUIRE(d % 128 == 0 && I % 64 == 0, FT_E_INVAL,
@@ -343,6 +343,9 @@ size_t ft_moe_bank_bytes(int fmt, int n_slots, int d, int I, int which) {
     case FT_W_MXFP4:
       return which == 0 ? n * r13 * K13 / 2 : which == 1 ? n * r2 * K2 / 2 : which == 2 ? n * r13 * (K13 / 32)
                                                                                        : n * r2 * (K2 / 32);
+    case FT_W_NVFP4:  // two e4m3 bytes per (row, chunk), then one fp32 matrix scale per slot
+      return which == 0 ? n * r13 * K13 / 2 : which == 1 ? n * r2 * K2 / 2 : which == 2 ? n * r13 * (K13 / 32) * 2 + n * 4
+                                                                                       : n * r2 * (K2 / 32) * 2 + n * 4;
     default:
       return which == 0 ? n * r13 * K13 : which == 1 ? n * r2 * K2 : which == 2 ? n * (r13 / 128) * (K13 / 128) * 4
                                                                                : n * (r2 / 128) * (K2 / 128) * 4;
@@ -368,10 +371,11 @@ int ft_moe_pack_bank(int fmt, int n_slots, int d, int I, const void* canon_w13, 
         REQUIRE(canon_s13 != nullptr && canon_s2 != nullptr, FT_E_INVAL, "canonical scale arrays are null");
     }
     hipError_t e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w13, (const uint8_t*)canon_s13,
-                                           (uint8_t*)dst->w13, (uint8_t*)dst->s13, (long long)n_slots * 2 * I, d, I, stream);
+                                           (uint8_t*)dst->w13, (uint8_t*)dst->s13, (long long)n_slots * 2 * I, d, I,
+                                           2 * I, stream);
     if (e == hipSuccess)
       e = ftk::launch_pack_matrix(fmt, (const uint8_t*)canon_w2, (const uint8_t*)canon_s2, (uint8_t*)dst->w2,
-                                  (uint8_t*)dst->s2, (long long)n_slots * d, I, 0, stream);
+                                  (uint8_t*)dst->s2, (long long)n_slots * d, I, 0, d, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_pack_bank launch");
     return ok();
   } catch (...) {
@@ -392,8 +396,17 @@ int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hip
     const size_t per_slot_s = ft_moe_bank_bytes(bank->fmt, 1, bank->d, bank->I, which + 2);
     const uint8_t* codes = (const uint8_t*)(which == 0 ? bank->w13 : bank->w2) + per_slot * slot;
     const uint8_t* scales = nullptr;
-    if (bank->fmt != FT_W_BF16) scales = (const uint8_t*)(which == 0 ? bank->s13 : bank->s2) + per_slot_s * slot;
-    return hip_status(ftk::launch_dequant(bank->fmt, codes, scales, rows, K, which == 0 ? bank->I : 0, out, stream),
+    const float* tscale = nullptr;
+    if (bank->fmt == FT_W_NVFP4) {  // block scales of every slot, then the slots' matrix scales
+      const uint8_t* base = (const uint8_t*)(which == 0 ? bank->s13 : bank->s2);
+      const size_t blk = (size_t)rows * (K / 32) * 2;
+      scales = base + blk * slot;
+      tscale = (const float*)(base + blk * bank->n_slots) + slot;
+    } else if (bank->fmt != FT_W_BF16) {
+      scales = (const uint8_t*)(which == 0 ? bank->s13 : bank->s2) + per_slot_s * slot;
+    }
+    return hip_status(ftk::launch_dequant(bank->fmt, codes, scales, rows, K, which == 0 ? bank->I : 0, tscale, out,
+                                          stream),
                       "ft_moe_dequant launch");
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_dequant: unexpected exception");

@@ -18,7 +18,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
-enum { FMT_BF16 = 0, FMT_Q4_0 = 1, FMT_MXFP4 = 2, FMT_FP8_B128 = 3 };
+enum { FMT_BF16 = 0, FMT_Q4_0 = 1, FMT_MXFP4 = 2, FMT_FP8_B128 = 3, FMT_NVFP4 = 4 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 __device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// OCP e4m3fn byte as fp32 (exact): bias 7, subnormal below exponent 1, S.1111.111 is NaN, no inf.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u, sign = (b & 0x80u) << 24;
+  if (e == 15u && m == 7u) return __uint_as_float(0x7fc00000u | sign);
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
 
 // E8M0 scale 2^(s-127) as fp32 (s = 255 is NaN).  2^-127 is an fp32 subnormal and is kept exactly.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
@@ -115,9 +123,21 @@ struct Chunk<FMT_Q4_0> {
   }
 };
 
+// NVFP4: codes as MXFP4; the two 16-element halves of a chunk (words 0-1 and 2-3) have their own
+// e4m3 scales, which the caller applies to fp32 partial sums (or, for the MFMA tiles, to each
+// decoded value: e2m1 * e4m3 has at most 6 significant bits, so that bf16 product is exact).  The
+// conversion instruction's scale operand contributes only its power of two (checked on the
+// device), so it is given 1.0 here.
+template <>
+struct Chunk<FMT_NVFP4> {
+  static constexpr int ELEMS = 32;
+  static constexpr int PAIRS = 16;
+  __device__ static void decode(const u32x4& c, uint32_t* p) { Chunk<FMT_MXFP4>::decode(c, p); }
+};
+
 template <int FMT>
 __host__ __device__ constexpr int chunk_elems() {
-  return FMT == FMT_BF16 ? 8 : FMT == FMT_FP8_B128 ? 16 : 32;
+  return FMT == FMT_BF16 ? 8 : FMT == FMT_FP8_B128 ? 16 : 32;  // four-bit formats: 32
 }
 
 // W13 device row order: each 64-row block holds 32 gate rows then the 32 matching up rows, so one

@@ -39,9 +39,10 @@ __device__ __forceinline__ size_t mat_bytes(int rows, int K) {
 
 // dynamic LDS: [groups: 4 x (E+2) ints][tmp: 4 ints][x rows NT x K bf16, item scales | partial sums]
 __host__ __device__ inline size_t gv_group_bytes(int E) { return ((size_t)4 * (E + 2) * 4 + 16 + 15) & ~(size_t)15; }
-// per-(row, chunk) scale bytes of one 64-row block (Q4_0: fp16, MXFP4: E8M0; none otherwise)
+// per-(row, chunk) scale bytes of one 64-row block (Q4_0: fp16, MXFP4: E8M0, NVFP4: two e4m3;
+// none otherwise)
 __host__ __device__ inline size_t gv_scale_bytes(int fmt, int K) {
-  return fmt == FMT_Q4_0 ? (size_t)64 * (K / 32) * 2 : fmt == FMT_MXFP4 ? (size_t)64 * (K / 32) : 0;
+  return (fmt == FMT_Q4_0 || fmt == FMT_NVFP4) ? (size_t)64 * (K / 32) * 2 : fmt == FMT_MXFP4 ? (size_t)64 * (K / 32) : 0;
 }
 // Q4_0: per-(token, 32-element block) activation sums, fp32
 __host__ __device__ inline size_t gv_xsum_bytes(int fmt, int K, int NT) {
@@ -119,8 +120,8 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   // (piece v = token v / (K/8), column piece v % (K/8)), XB pieces per thread and batch.
   constexpr bool FLAT = NT > 4;
   constexpr int XB = 4;
-  constexpr int SB = FMT == FMT_Q4_0 ? 2 : 1;
-  constexpr bool STAGE_SCALES = FMT == FMT_Q4_0 || FMT == FMT_MXFP4;
+  constexpr int SB = (FMT == FMT_Q4_0 || FMT == FMT_NVFP4) ? 2 : 1;
+  constexpr bool STAGE_SCALES = FMT == FMT_Q4_0 || FMT == FMT_MXFP4 || FMT == FMT_NVFP4;
   const int nx8 = K / 8;
   const int nsv = STAGE_SCALES ? RPL * nchunk * 64 * SB / 16 : 0;  // the RPL row blocks' scales are one run
   const uint8_t* ssrc = scales + ((size_t)slot * nrows * nchunk + (size_t)RPL * cb * nchunk * 64) * SB;
@@ -252,9 +253,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
       issue(buf[(p + PF - 1) % PF], min(j + PF - 1, jlast));
       if (j < niter) {
         const int c = chunk_of(j);
-        float fsc[RPL];
+        float fsc[RPL], fsc_hi[RPL];
 #pragma unroll
         for (int q = 0; q < RPL; ++q) {
+          fsc_hi[q] = 1.0f;
           if constexpr (FMT == FMT_FP8_B128) {
             // one fp32 scale per 128x128 block of logical rows (a gate/up device block holds 32 gate
             // rows in lanes 0-31 and the matching 32 up rows in lanes 32-63)
@@ -265,6 +267,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
             fsc[q] = fp16_bits_to_f32(((const uint16_t*)s_sc)[(q * nchunk + c) * 64 + lane]);
           } else if constexpr (FMT == FMT_MXFP4) {
             fsc[q] = e8m0_to_f32(s_sc[(q * nchunk + c) * 64 + lane]);
+          } else if constexpr (FMT == FMT_NVFP4) {  // e4m3 scales of the chunk's two 16-element halves
+            const uint32_t two = ((const uint16_t*)s_sc)[(q * nchunk + c) * 64 + lane];
+            fsc[q] = e4m3_to_f32(two & 0xffu);
+            fsc_hi[q] = e4m3_to_f32(two >> 8);
           } else {
             fsc[q] = 1.0f;
           }
@@ -287,6 +293,15 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
                 xw[4 * i + 1] = v[1];
                 xw[4 * i + 2] = v[2];
                 xw[4 * i + 3] = v[3];
+              }
+              if constexpr (FMT == FMT_NVFP4) {  // each half's scale on its own fp32 partial sum
+                float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+                for (int i = 0; i < C::PAIRS / 2; ++i) lo = dot2_bf16(wp[i], xw[i], lo);
+#pragma unroll
+                for (int i = C::PAIRS / 2; i < C::PAIRS; ++i) hi = dot2_bf16(wp[i], xw[i], hi);
+                acc[q][t] = fmaf(hi, fsc_hi[q], fmaf(lo, fsc[q], acc[q][t]));
+                continue;
               }
               float part = 0.0f;
 #pragma unroll
@@ -312,6 +327,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
     for (int t = 0; t < NT; ++t)
       if (t < nt) s_red[((w * RPL + q) * NT + t) * 64 + lane] = acc[q][t];
   __syncthreads();
+  // NVFP4: the matrix's fp32 scale, stored after every slot's block scales
+  float tsc = 1.0f;
+  if constexpr (FMT == FMT_NVFP4)
+    tsc = ((const float*)(scales + (size_t)a.n_slots * nrows * nchunk * 2))[slot];
   for (int tq = w; tq < nt * RPL; tq += WPB) {
     const int t = tq / RPL, q = tq % RPL, cbq = RPL * cb + q;
     const int orow = row0 + t0 + t;  // h row, or y_sorted row
@@ -323,6 +342,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
           g += s_red[((ww * RPL + q) * NT + t) * 64 + lane];
           u += s_red[((ww * RPL + q) * NT + t) * 64 + lane + 32];
         }
+      }
+      if constexpr (FMT == FMT_NVFP4) {
+        g *= tsc;
+        u *= tsc;
       }
       const uint32_t hb = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
       uint16_t* hp = a.h + (size_t)orow * a.I + 32 * cbq + lane;
@@ -336,6 +359,7 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
       float v = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < WPB; ++ww) v += s_red[((ww * RPL + q) * NT + t) * 64 + lane];
+      if constexpr (FMT == FMT_NVFP4) v *= tsc;
       uint16_t* yrow = shared ? a.y_shared + (size_t)(t0 + t) * a.d : a.y_sorted + (size_t)orow * a.d;
       const uint32_t yb = f32_to_bf16_bits(v);
       if constexpr (COH) {

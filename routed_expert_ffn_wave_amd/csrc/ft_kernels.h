@@ -87,10 +87,12 @@ inline int layer_decode_rowchunks_upper(int T, int E, int k, bool shared) {
 }
 
 // canonical -> row-interleaved device layout for one matrix of `rows` rows (all slots) and K columns
-// (perm_I > 0: W13 of expert intermediate size perm_I, whose rows are reordered into gate/up blocks)
+// (perm_I > 0: W13 of expert intermediate size perm_I, whose rows are reordered into gate/up blocks;
+// R: rows per slot)
 hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
-                              uint8_t* scales, long long rows, int K, int perm_I, hipStream_t s);
+                              uint8_t* scales, long long rows, int K, int perm_I, int R, hipStream_t s);
+// tscale: the matrix scale of an NVFP4 matrix (device pointer), else unused
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, int perm_I,
-                          float* out, hipStream_t s);
+                          const float* tscale, float* out, hipStream_t s);
 
 }  // namespace ftk

@@ -50,7 +50,8 @@ __host__ __device__ inline size_t gemm_lds_bytes(int E, int BN) {
 // 16 four-bit); MXFP4's power-of-two scale is folded into the conversion (exact while the product
 // is a normal bf16), Q4_0 gives q - 8.
 template <int FMT>
-__device__ __forceinline__ void decode_b(const u32x4& c, float mx_scale, uint32_t* out) {
+__device__ __forceinline__ void decode_b(const u32x4& c, float mx_scale, uint32_t* out, float nv_lo = 1.0f,
+                                         float nv_hi = 1.0f) {
   if constexpr (FMT == FMT_BF16) {
     out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
   } else if constexpr (FMT == FMT_FP8_B128) {
@@ -58,6 +59,21 @@ __device__ __forceinline__ void decode_b(const u32x4& c, float mx_scale, uint32_
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
       out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
+    }
+  } else if constexpr (FMT == FMT_NVFP4) {  // exact e2m1, then each value times its half's e4m3 scale
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = i < 2 ? nv_lo : nv_hi;
+      uint32_t p[4];
+      p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], 1.0f, 0));
+      p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], 1.0f, 1));
+      p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], 1.0f, 2));
+      p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], 1.0f, 3));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float lo = bf16_bits_to_f32(p[b] & 0xffffu) * s, hi = bf16_bits_to_f32(p[b] >> 16) * s;
+        out[4 * i + b] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+      }
     }
   } else if constexpr (FMT == FMT_MXFP4) {
 #pragma unroll
@@ -152,7 +168,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
 
     u32x4 ra[4], rb[BCH];
     float rsc[2] = {1.0f, 1.0f};  // this thread's B-row scales for the step (Q4_0: two 32-blocks)
-    float rmx[BCH];               // MXFP4 scale of each staged chunk
+    float rmx[BCH];               // MXFP4 scale of each staged chunk (NVFP4: scale of its low half)
+    float rnv[BCH];               // NVFP4: scale of the chunk's high half
     auto load_step = [&](int s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ra[i] = arow ? *(const u32x4*)(arow + (size_t)s * BK + ah * 32 + 8 * i) : u32x4{0, 0, 0, 0};
@@ -162,6 +179,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
         rb[i] = *(const u32x4*)(bmat + ilv_chunk_off(r, c, nchunk));
         if constexpr (FMT == FMT_MXFP4)
           rmx[i] = e8m0_to_f32(scales[(size_t)slot * ncols * nchunk + ilv_scale_idx(r, c, nchunk)]);
+        if constexpr (FMT == FMT_NVFP4) {
+          const uint32_t two = ((const uint16_t*)scales)[(size_t)slot * ncols * nchunk + ilv_scale_idx(r, c, nchunk)];
+          rmx[i] = e4m3_to_f32(two & 0xffu);
+          rnv[i] = e4m3_to_f32(two >> 8);
+        }
       }
       if constexpr (FMT == FMT_Q4_0) {  // rows tid < BN: the scales of the step's two 32-blocks
         if (tid < BN) {
@@ -185,7 +207,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
 #pragma unroll
       for (int i = 0; i < BCH; ++i) {
         uint32_t w[EPC / 2];
-        decode_b<FMT>(rb[i], FMT == FMT_MXFP4 ? rmx[i] : 1.0f, w);
+        if constexpr (FMT == FMT_NVFP4)
+          decode_b<FMT>(rb[i], 1.0f, w, rmx[i], rnv[i]);
+        else
+          decode_b<FMT>(rb[i], FMT == FMT_MXFP4 ? rmx[i] : 1.0f, w);
         uint32_t* dst = (uint32_t*)&Bs[b_row(i) * LDK + b_chk(i) * EPC];
 #pragma unroll
         for (int q = 0; q < EPC / 8; ++q)
@@ -279,6 +304,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
     // ---- epilogue.  Lane holds, for tile (i, j), rows wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4
     // and column wn*(BN/2) + j*32 + lane%32.
     const int col = lane & 31;
+    float tsc = 1.0f;  // NVFP4: the matrix's fp32 scale, stored after every slot's block scales
+    if constexpr (FMT == FMT_NVFP4) tsc = ((const float*)(scales + (size_t)a.n_slots * ncols * nchunk * 2))[slot];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -288,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
         if (GATEUP) {
 #pragma unroll
           for (int p = 0; p < WN / 2; ++p) {
-            const float gte = acc[i][2 * p][r], up = acc[i][2 * p + 1][r];
+            const float gte = acc[i][2 * p][r] * tsc, up = acc[i][2 * p + 1][r] * tsc;
             const float hv = gte / (1.0f + expf(-gte)) * up;
             // device block (nt*BN + wn*BN/2)/64 + p holds intermediate columns 32 * that + 0..31
             const int icol = 32 * ((nt * BN + wn * (BN / 2)) / 64 + p) + col;
@@ -297,7 +324,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
         } else {
           uint16_t* yrow = shared ? a.y_shared + (size_t)(m0 + m) * a.d : a.y_sorted + (size_t)(row0 + m0 + m) * a.d;
 #pragma unroll
-          for (int j = 0; j < WN; ++j) yrow[nt * BN + wn * (BN / 2) + j * 32 + col] = f32_to_bf16_bits(acc[i][j][r]);
+          for (int j = 0; j < WN; ++j)
+            yrow[nt * BN + wn * (BN / 2) + j * 32 + col] = f32_to_bf16_bits(acc[i][j][r] * tsc);
         }
       }
     }
@@ -336,7 +364,7 @@ static hipError_t launch_gemm_cfg(const FfnArgs& a, int tiles_upper, hipStream_t
 template <int FMT, bool GATEUP>
 static hipError_t launch_gemm_fmt(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   const int rows = GATEUP ? 2 * a.I : a.d;
-  if constexpr (FMT == FMT_BF16 || FMT == FMT_MXFP4)
+  if constexpr (FMT == FMT_BF16 || FMT == FMT_MXFP4 || FMT == FMT_NVFP4)
     if (rows % 256 == 0) return launch_gemm_cfg<FMT, GATEUP, 4>(a, tiles_upper, s);
   return launch_gemm_cfg<FMT, GATEUP, 2>(a, tiles_upper, s);
 }
@@ -347,6 +375,7 @@ static hipError_t launch_gemm(const FfnArgs& a, int tiles_upper, hipStream_t s) 
     case FMT_BF16: return launch_gemm_fmt<FMT_BF16, GATEUP>(a, tiles_upper, s);
     case FMT_Q4_0: return launch_gemm_fmt<FMT_Q4_0, GATEUP>(a, tiles_upper, s);
     case FMT_MXFP4: return launch_gemm_fmt<FMT_MXFP4, GATEUP>(a, tiles_upper, s);
+    case FMT_NVFP4: return launch_gemm_fmt<FMT_NVFP4, GATEUP>(a, tiles_upper, s);
     default: return launch_gemm_fmt<FMT_FP8_B128, GATEUP>(a, tiles_upper, s);
   }
 }

@@ -104,6 +104,7 @@ static hipError_t launch_gemv(const FfnArgs& a, int groups_upper, long long rows
     case FMT_BF16: return launch_fmt<FMT_BF16, GATEUP>(a, groups_upper, rows_upper, s);
     case FMT_Q4_0: return launch_fmt<FMT_Q4_0, GATEUP>(a, groups_upper, rows_upper, s);
     case FMT_MXFP4: return launch_fmt<FMT_MXFP4, GATEUP>(a, groups_upper, rows_upper, s);
+    case FMT_NVFP4: return launch_fmt<FMT_NVFP4, GATEUP>(a, groups_upper, rows_upper, s);
     default: return launch_fmt<FMT_FP8_B128, GATEUP>(a, groups_upper, rows_upper, s);
   }
 }

@@ -429,6 +429,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s) {
     case FMT_BF16: return launch_layer_fmt<FMT_BF16>(L, s);
     case FMT_Q4_0: return launch_layer_fmt<FMT_Q4_0>(L, s);
     case FMT_MXFP4: return launch_layer_fmt<FMT_MXFP4>(L, s);
+    case FMT_NVFP4: return launch_layer_fmt<FMT_NVFP4>(L, s);
     default: return launch_layer_fmt<FMT_FP8_B128>(L, s);
   }
 }

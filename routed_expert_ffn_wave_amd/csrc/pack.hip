@@ -4,7 +4,7 @@
 //
 // Bank formats: FreeToken walk-through "深入FreeToken架构…全链路剖析", section 五 (per-format expert
 // banks, each with its own schema).  Element encodings: GGUF Q4_0, OCP MXFP4 (E8M0 scales), OCP
-// e4m3fn.  All slots of a bank are treated as one matrix of n_slots * R rows: with R a multiple of
+// e4m3fn, NVFP4 (e2m1 with e4m3 scales per 16 and an fp32 matrix scale).  All slots of a bank are treated as one matrix of n_slots * R rows: with R a multiple of
 // 64, the interleave of that matrix equals the per-slot interleave with slots laid end to end.
 #include "ft_device.h"
 #include "ft_kernels.h"
@@ -73,11 +73,33 @@ __global__ __launch_bounds__(256) void pack_q4_0_kernel(const uint8_t* __restric
   scales[ilv_scale_idx((int)r, c, nchunk)] = s16[0];
 }
 
+// NVFP4 scales: canonical per slot [R][K/16] e4m3 bytes then the fp32 matrix scale; device: the
+// two e4m3 bytes of (row, chunk) as one 16-bit pair, interleaved over all slots' rows, then the
+// n_slots matrix scales.
+__global__ __launch_bounds__(256) void pack_nvfp4_scales_kernel(const uint8_t* __restrict__ canon,
+                                                                uint16_t* __restrict__ dst, long long rows, int R,
+                                                                int nchunk, int perm_I) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nchunk) return;
+  const long long r = i / nchunk;
+  const int c = (int)(i % nchunk);
+  const long long slot = r / R, rr = r % R;
+  const size_t stride = (size_t)R * nchunk * 2 + 4;  // canonical bytes per slot
+  const uint16_t* src = (const uint16_t*)(canon + slot * stride + (size_t)rr * nchunk * 2);  // even offsets
+  dst[ilv_scale_idx((int)device_row(r, perm_I), c, nchunk)] = src[c];
+  if (rr == 0 && c == 0) {  // the slot's matrix scale
+    float t;
+    const uint8_t* ts = canon + slot * stride + (size_t)R * nchunk * 2;
+    __builtin_memcpy(&t, ts, 4);
+    ((float*)(dst + rows * nchunk))[slot] = t;
+  }
+}
+
 static unsigned grid_for(long long n) { return (unsigned)((n + 255) / 256); }
 
 // Pack one matrix (all slots): rows = n_slots * R, K columns.
 hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t* canon_scales, uint8_t* codes,
-                              uint8_t* scales, long long rows, int K, int perm_I, hipStream_t s) {
+                              uint8_t* scales, long long rows, int K, int perm_I, int R, hipStream_t s) {
   const int nchunk = K / (fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32);
   const long long n = rows * nchunk;
   if (n == 0) return hipSuccess;
@@ -91,6 +113,9 @@ hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t
   if (fmt == FMT_MXFP4)
     hipLaunchKernelGGL(interleave_scales_kernel<uint8_t>, dim3(grid_for(n)), dim3(256), 0, s, canon_scales, scales,
                        rows, nchunk, perm_I);
+  if (fmt == FMT_NVFP4)
+    hipLaunchKernelGGL(pack_nvfp4_scales_kernel, dim3(grid_for(n)), dim3(256), 0, s, canon_scales, (uint16_t*)scales,
+                       rows, R, nchunk, perm_I);
   if (fmt == FMT_FP8_B128) {
     hipError_t e = hipMemcpyAsync(scales, canon_scales, (size_t)(rows / 128) * (K / 128) * 4, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
@@ -102,7 +127,8 @@ hipError_t launch_pack_matrix(int fmt, const uint8_t* canon_codes, const uint8_t
 // in fp32, written row-major.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                      int rows, int K, int perm_I, float* __restrict__ out) {
+                                                      int rows, int K, int perm_I, const float* __restrict__ tscale,
+                                                      float* __restrict__ out) {
 #pragma clang fp contract(off)
   using C = Chunk<FMT>;
   const int nchunk = K / C::ELEMS;
@@ -117,6 +143,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   if constexpr (FMT == FMT_Q4_0) sc = fp16_bits_to_f32(((const uint16_t*)scales)[ilv_scale_idx(dr, c, nchunk)]);
   if constexpr (FMT == FMT_MXFP4) sc = e8m0_to_f32(scales[ilv_scale_idx(dr, c, nchunk)]);
   if constexpr (FMT == FMT_FP8_B128) sc = ((const float*)scales)[(size_t)(r / 128) * (K / 128) + (c * C::ELEMS) / 128];
+  float sc_hi = sc, ts = 1.0f;
+  if constexpr (FMT == FMT_NVFP4) {  // e4m3 scales of the chunk's two halves, and the matrix scale
+    const uint32_t two = ((const uint16_t*)scales)[ilv_scale_idx(dr, c, nchunk)];
+    sc = e4m3_to_f32(two & 0xffu);
+    sc_hi = e4m3_to_f32(two >> 8);
+    ts = *tscale;
+  }
   float* o = out + (size_t)r * K + (size_t)c * C::ELEMS;
 #pragma unroll
   for (int i = 0; i < C::PAIRS; ++i) {
@@ -125,7 +158,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       v0 = v0 - 136.0f;  // decode gives 128 + q; the weight is scale * (q - 8)
       v1 = v1 - 136.0f;
     }
-    if constexpr (FMT != FMT_BF16) {
+    if constexpr (FMT == FMT_NVFP4) {  // t * (e2m1 * e4m3): the inner product is exact
+      const float s = i < C::PAIRS / 2 ? sc : sc_hi;
+      v0 = ts * (v0 * s);
+      v1 = ts * (v1 * s);
+    } else if constexpr (FMT != FMT_BF16) {
       v0 = v0 * sc;
       v1 = v1 * sc;
     }
@@ -135,15 +172,18 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }
 
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int rows, int K, int perm_I,
-                          float* out, hipStream_t s) {
+                          const float* tscale, float* out, hipStream_t s) {
   const int elems = fmt == FMT_BF16 ? 8 : fmt == FMT_FP8_B128 ? 16 : 32;
   const long long n = (long long)rows * (K / elems);
   dim3 grid(grid_for(n)), block(256);
   switch (fmt) {
-    case FMT_BF16: hipLaunchKernelGGL(dequant_kernel<FMT_BF16>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
-    case FMT_Q4_0: hipLaunchKernelGGL(dequant_kernel<FMT_Q4_0>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
-    case FMT_MXFP4: hipLaunchKernelGGL(dequant_kernel<FMT_MXFP4>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
-    default: hipLaunchKernelGGL(dequant_kernel<FMT_FP8_B128>, grid, block, 0, s, codes, scales, rows, K, perm_I, out); break;
+#define FT_DQ(F) hipLaunchKernelGGL(dequant_kernel<F>, grid, block, 0, s, codes, scales, rows, K, perm_I, tscale, out)
+    case FMT_BF16: FT_DQ(FMT_BF16); break;
+    case FMT_Q4_0: FT_DQ(FMT_Q4_0); break;
+    case FMT_MXFP4: FT_DQ(FMT_MXFP4); break;
+    case FMT_NVFP4: FT_DQ(FMT_NVFP4); break;
+    default: FT_DQ(FMT_FP8_B128); break;
+#undef FT_DQ
   }
   return hipGetLastError();
 }

@@ -90,10 +90,14 @@ def test_bank_bytes():
     assert L.ft_moe_bank_bytes(ft.FT_W_FP8_B128, 96, 7168, 2048, 2) == 96 * 32 * 56 * 4
     assert L.ft_moe_bank_bytes(ft.FT_W_FP8_B128, 96, 7168, 2000, 0) == 0     # I not a multiple of 128
     assert L.ft_moe_bank_bytes(7, 1, 256, 256, 0) == 0
-    # per-weight cost of each format: 2, 18/32, 17/32, 1 + 4/16384 bytes
-    for fmt, bpw in ((0, 2.0), (1, 18 / 32), (2, 17 / 32), (3, 1 + 4 / 16384)):
+    # NVFP4: codes as MXFP4; two e4m3 bytes per (row, chunk), then one fp32 matrix scale per slot
+    assert L.ft_moe_bank_bytes(ft.FT_W_NVFP4, n, d, I, 0) == n * 2 * I * d // 2
+    assert L.ft_moe_bank_bytes(ft.FT_W_NVFP4, n, d, I, 2) == n * 2 * I * (d // 32) * 2 + n * 4
+    assert L.ft_moe_bank_bytes(ft.FT_W_NVFP4, n, d, I, 3) == n * d * (I // 32) * 2 + n * 4
+    # per-weight cost of each format: 2, 18/32, 17/32, 1 + 4/16384, 9/16 (+ two fp32 per slot) bytes
+    for fmt, bpw, extra in ((0, 2.0, 0), (1, 18 / 32, 0), (2, 17 / 32, 0), (3, 1 + 4 / 16384, 0), (4, 9 / 16, 8)):
         tot = sum(L.ft_moe_bank_bytes(fmt, 1, 7168, 2048, w) for w in range(4))
-        assert tot == pytest.approx(3 * 7168 * 2048 * bpw, rel=1e-12)
+        assert tot - extra == pytest.approx(3 * 7168 * 2048 * bpw, rel=1e-12)
 
 
 def test_grouped_ffn_validation():

@@ -86,7 +86,7 @@ def _bits_equal_nan_aware(a: np.ndarray, b: np.ndarray):
     assert np.array_equal(a[~na].view(np.uint32), b[~nb].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("content", ["encoded", "random_bytes"])
 def test_dequant_bit_exact(ft, fmt, content):
     d, I, n = 256, 384, 3
@@ -102,7 +102,7 @@ def test_dequant_bit_exact(ft, fmt, content):
             for t in (canon.s13, canon.s2):
                 t.copy_(torch.exp2(torch.randint(-40, 20, t.shape, generator=g).float()) *
                         (1 + torch.rand(t.shape, generator=g)))
-        elif fmt == 2:
+        elif fmt in (2, 4):  # E8M0 bytes; NVFP4 e4m3 bytes and the fp32 matrix scale's bytes
             for t in (canon.s13, canon.s2):
                 t.copy_(torch.randint(0, 256, t.shape, generator=g, dtype=torch.uint8))
     bank = device_bank(canon)
@@ -126,6 +126,8 @@ def _small_workloads():
         "mxfp4_shared": W["mxfp4_shared"].replace(T=200, d=512, I=256, E=32, k=4),
         "fp8_resident": W["fp8_resident"].replace(T=300, d=512, I=256, E=32, k=4, n_resident=12),
         "q4_0_prefill": W["decode_q4_0"].replace(T=150, d=512, I=256, E=16, k=4, layers=1),
+        "nvfp4_decode": W["nvfp4_decode"].replace(layers=1),
+        "nvfp4_prefill": W["nvfp4_decode"].replace(T=150, d=512, I=256, E=16, k=4, layers=1),
     }
 
 
