@@ -27,6 +27,10 @@ struct GroupList {
   int n;
 };
 
+// LDS bytes of a group list for E experts: slot, row0, cnt and item0 arrays of E + 2 ints each, and
+// a few ints of scratch, rounded up to 16 bytes.
+__host__ __device__ inline size_t group_lds_bytes(int E) { return (((size_t)4 * (E + 2) + 4) * 4 + 15) & ~(size_t)15; }
+
 // Build the group list in LDS with wave 0 (ascending expert order, shared group last).
 // items_of(cnt) gives the number of work items of a group with `cnt` rows.  Every thread of the
 // block must call this; it ends with a block barrier.

@@ -41,9 +41,8 @@ struct GemmCfg {
 };
 
 // dynamic LDS: [groups 4 x (E+2) ints + tmp][A: BM x LDK][B: BN x LDK][row pointers BM][scales BN]
-__host__ __device__ inline size_t gemm_group_bytes(int E) { return (((size_t)4 * (E + 2) + 4) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t gemm_lds_bytes(int E, int BN) {
-  return gemm_group_bytes(E) + (size_t)(BM + BN) * LDK * 2 + (size_t)BM * 8 + (size_t)BN * 4 * 2;
+  return group_lds_bytes(E) + (size_t)(BM + BN) * LDK * 2 + (size_t)BM * 8 + (size_t)BN * 4 * 2;
 }
 
 // Decode one raw chunk of the B tile into bf16 pairs in K order (pairs per chunk: 4 bf16, 8 e4m3,
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(FfnArgs a) {
   int* s_cnt = s_row0 + E2;
   int* s_item0 = s_cnt + E2;
   int* s_tmp = s_item0 + E2;
-  uint16_t* As = (uint16_t*)(lds + gemm_group_bytes(a.E));
+  uint16_t* As = (uint16_t*)(lds + group_lds_bytes(a.E));
   uint16_t* Bs = As + BM * LDK;
   const uint16_t** s_arow = (const uint16_t**)(Bs + BN * LDK);
   float* s_bscale = (float*)(s_arow + BM);  // [2][BN]: Q4_0 scales of the step's two 32-blocks, or FP8's
@@ -364,6 +363,7 @@ static hipError_t launch_gemm_cfg(const FfnArgs& a, int tiles_upper, hipStream_t
 template <int FMT, bool GATEUP>
 static hipError_t launch_gemm_fmt(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   const int rows = GATEUP ? 2 * a.I : a.d;
+  if (gemm_wide_fits(FMT, rows, a.E)) return launch_gemm_wide(a, GATEUP, tiles_upper, s);
   if constexpr (FMT == FMT_BF16 || FMT == FMT_MXFP4 || FMT == FMT_NVFP4)
     if (rows % 256 == 0) return launch_gemm_cfg<FMT, GATEUP, 4>(a, tiles_upper, s);
   return launch_gemm_cfg<FMT, GATEUP, 2>(a, tiles_upper, s);

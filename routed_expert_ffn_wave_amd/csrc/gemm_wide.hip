@@ -1,0 +1,328 @@
+// Grouped expert GEMM on MFMA with wide wave tiles and a direct-to-LDS operand ring (bf16 banks).
+//
+// Expert FFNs are read from per-format banks (FreeToken walk-through "深入FreeToken架构…全链路剖析",
+// section 五); with many tokens per expert, each group is a dense bf16 contraction on the matrix cores.
+//
+// Tile = 128 token rows x 512 weight rows, one block of 4 waves per CU.  Wave w computes the 128
+// rows times weight rows 128w .. 128w+127 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32
+// accumulators per lane), so each K step of 16 reads 8 fragments from LDS for 16 MFMAs: half the LDS
+// traffic per flop of a 64 x 128 wave tile.
+//
+// Operands go from global memory straight into LDS (global_load_lds_dwordx4: 64 lanes x 16 bytes
+// to consecutive LDS bytes) through a ring of WNS stages of 32 K columns.  The stage for step
+// s + WNS is issued at step s, once every wave has finished reading step s, so each load has
+// WNS - 1 steps of MFMA work to arrive.  The loads are issued from inline assembly: the compiler
+// then puts no full vmcnt wait in front of the LDS reads; the kernel waits for exactly the stage
+// it needs (vmcnt counts one wave's own loads, which complete in issue order) and meets the other
+// waves at a barrier that does not drain the memory counters.
+//
+// LDS stage layout:
+//   A: 128 rows x 64 bytes; row r keeps its 16-byte K chunk c in slot c ^ f(r), with
+//      f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the fragment reads (32 rows at one chunk) touch each
+//      bank once per 8 lanes (32 banks) or per 16 lanes (64 banks).
+//   B: the bank's row-interleaved layout keeps one chunk of 64 rows in 1 KiB; a stage holds
+//      8 row blocks x 4 chunks of them, [block][chunk][64 rows][16 bytes], read without conflicts.
+#include <type_traits>
+
+#include "ft_device.h"
+#include "ft_groups.h"
+#include "ft_kernels.h"
+
+namespace ftk {
+namespace {
+
+constexpr int WBM = GEMM_BM;                 // token rows per tile
+constexpr int WBN = 512;                     // weight rows per tile (4 waves x 128)
+constexpr int WBK = 32;                      // K columns per ring stage
+constexpr int WNS = 3;                       // ring stages
+constexpr int A_BYTES = WBM * WBK * 2;       // 8 KiB
+constexpr int B_BYTES = WBN * WBK * 2;       // 32 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int DMA_A = A_BYTES / 1024 / 4;    // 1 KiB loads per wave and stage
+constexpr int DMA_B = B_BYTES / 1024 / 4;
+constexpr int DMA_STAGE = DMA_A + DMA_B;
+static_assert(WBM == 128 && DMA_A == 2 && DMA_B == 8, "stage shape");
+static_assert(WNS >= 2 && WNS <= 3, "wait_newer covers up to two newer stages");
+
+__host__ __device__ inline size_t wide_ring_off(int E) { return (group_lds_bytes(E) + 1023) & ~(size_t)1023; }
+__host__ __device__ inline size_t wide_lds_bytes(int E) { return wide_ring_off(E) + (size_t)WNS * STAGE_BYTES; }
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave: lane l's 16 bytes at base + voff are written to LDS bytes lds + 16 l .. + 15.  M0
+// carries the LDS address (one wait state after writing it) and gets its old value back.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+// Four loads of 1 KiB: global base + voff + 1024 t to LDS lds + 1024 t (t = 0..3; the immediate
+// offset applies to both addresses).
+__device__ __forceinline__ void dma16x4(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+// Wait until this wave's loads of a stage have landed, `newer` (0..2, wave-uniform) stages having
+// been issued after it.
+__device__ __forceinline__ void wait_newer(int newer) {
+  if (newer >= 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_STAGE) : "memory");
+  else if (newer == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_STAGE) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// Own LDS reads complete, then the block barrier; memory operations do not move across it.
+__device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int E2 = a.E + 2;
+  int* s_slot = (int*)lds;
+  int* s_row0 = s_slot + E2;
+  int* s_cnt = s_row0 + E2;
+  int* s_item0 = s_cnt + E2;
+  int* s_tmp = s_item0 + E2;
+  uint8_t* ring = lds + wide_ring_off(a.E);
+  const uint32_t ring_m0 = lds_u32(ring);
+
+  const int K = GATEUP ? a.d : a.I;
+  const int ncols = GATEUP ? 2 * a.I : a.d;  // weight rows
+  const int ntiles = ncols / WBN;
+  const int nchunk = K / 8;                  // 16-byte chunks per weight row
+  GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
+  GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
+  build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + WBM - 1) / WBM) * ntiles; });
+  const int nitems = s_item0[gl.n];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int TK = a.T * a.k;
+  const int nsteps = K / WBK;
+  const uint8_t* abase = GATEUP ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+  const uint32_t arow_bytes = (uint32_t)K * 2;
+
+  // Fragment reads, byte offsets inside a stage.  A fragment i of substep u: rows 32 i + l32, chunk
+  // 2 u + hi.  B fragment j of substep u: row block 2 wv + j / 2, rows 32 (j % 2) + l32, chunk 2 u + hi.
+  const int xo = ((l32 >> 1) ^ (l32 >> 2)) & 3;
+  const int a_rd0 = l32 * 64 + ((hi ^ xo) << 4);
+  const int a_rd1 = l32 * 64 + (((2 + hi) ^ xo) << 4);
+  const int b_rd = A_BYTES + (8 * wv + hi) * 1024 + l32 * 16;
+
+  // Blocks are placed on the 8 XCDs round-robin: give each XCD a contiguous run of the tile list so
+  // that tiles running at once on one XCD share activation rows and weight tiles through its L2.
+  const int NB = gridDim.x;
+  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int it = lb; it < nitems; it += NB) {
+    const int g = find_group(s_item0, gl.n, it);
+    const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int slot = __builtin_amdgcn_readfirstlane(s_slot[g]);
+    const int row0 = __builtin_amdgcn_readfirstlane(s_row0[g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[g]);
+    const bool shared = row0 >= TK;
+    const int m0 = mt * WBM;
+    const int mrows = min(WBM, cnt - m0);
+
+    // This lane's two A rows (rows past the group's end repeat its last row; their results are
+    // never stored) and the chunk its LDS slot holds.
+    uint32_t aoff[DMA_A];
+#pragma unroll
+    for (int q = 0; q < DMA_A; ++q) {
+      const int r = 16 * (DMA_A * wv + q) + (lane >> 2);
+      const int m = min(r, mrows - 1);
+      int src_row;
+      if (GATEUP)
+        src_row = shared ? (m0 + m) : a.gather[row0 + m0 + m] / a.k;
+      else
+        src_row = row0 + m0 + m;
+      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+      aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
+    }
+    // this wave's two 64-row blocks of the weight tile
+    const uint8_t* bt = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K * 2 + (size_t)(8 * nt + 2 * wv) * nchunk * 1024;
+    // Load unit q (0..3) of this wave's share of stage s into the ring buffer at LDS byte `buf`:
+    // q = 0, 1: 16 A rows each; q = 2, 3: one 64-row block of the weight tile, its 4 chunks.
+    const uint32_t bvoff = (uint32_t)lane * 16;
+    auto issue_unit = [&](uint32_t buf, int s, int q) {
+      if (q < DMA_A) {
+        dma16(abase + (size_t)s * (WBK * 2), aoff[q], buf + (DMA_A * wv + q) * 1024);
+      } else {
+        const int rb = q - DMA_A;
+        dma16x4(bt + ((size_t)rb * nchunk + 4 * s) * 1024, bvoff, buf + A_BYTES + (2 * wv + rb) * 4096);
+      }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    bf16x8 f0[8], f1[8];  // fragments of substeps 0 and 1: A rows 0..3, then B columns 0..3
+    // fragment n of substep u of the stage at `st`
+    auto frag = [&](const uint8_t* st, int u, int n) -> bf16x8 {
+      if (n < 4) return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + n * 2048);
+      return *(const bf16x8*)(st + b_rd + u * 2048 + ((n - 4) >> 1) * 4096 + ((n - 4) & 1) * 512);
+    };
+
+    const int pre = min(WNS, nsteps);
+    for (int s = 0; s < pre; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) issue_unit(ring_m0 + (uint32_t)s * STAGE_BYTES, s, q);
+    wait_newer(pre - 1);
+    lds_reads_done_barrier();
+#pragma unroll
+    for (int n = 0; n < 8; ++n) f0[n] = frag(ring, 0, n);
+    int cb = 0;  // ring buffer of step s
+    // One step: 16 MFMAs on substep 0 with substep 1's fragment reads between them; the wait for
+    // stage s + 1 and the barrier; 16 MFMAs on substep 1 with the next stage's substep-0 reads and
+    // (while stages remain) this wave's loads of stage s + WNS, into the buffer just released,
+    // between them.  The scheduling barriers keep that order, so reads and loads issue in the
+    // MFMAs' shadow.
+    auto step = [&](int s, auto load_ahead) {
+      const uint8_t* st = ring + cb * STAGE_BYTES;
+      const int nb = (cb + 1 == WNS) ? 0 : cb + 1;
+      const uint8_t* nst = ring + nb * STAGE_BYTES;  // past the last step: read but unused
+      const uint32_t dbuf = ring_m0 + (uint32_t)cb * STAGE_BYTES;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[n >> 2], f0[4 + (n & 3)], acc[n >> 2][n & 3], 0, 0, 0);
+        if (n < 8) f1[n] = frag(st, 1, n);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // every wave is done reading stage s and has stage s + 1 in LDS
+      if (s + 1 < nsteps) wait_newer(min(WNS - 2, nsteps - 2 - s));
+      lds_reads_done_barrier();
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[n >> 2], f1[4 + (n & 3)], acc[n >> 2][n & 3], 0, 0, 0);
+        if (n < 8) f0[n] = frag(nst, 0, n);
+        if constexpr (decltype(load_ahead)::value) {
+          if (n == 2 || n == 4 || n == 6 || n == 8) issue_unit(dbuf, s + WNS, (n - 2) >> 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cb = nb;
+    };
+    int s = 0;
+    for (; s < nsteps - WNS; ++s) step(s, std::true_type{});
+    for (; s < nsteps; ++s) step(s, std::false_type{});
+
+    // ---- epilogue.  Lane holds, for tile (i, j), rows 32 i + (r/4)*8 + hi*4 + r%4 and weight
+    // row 128 wv + 32 j + l32 of the tile.  Each wave stages its bf16 results for 64 rows at a time
+    // in its own slice of the ring (free now: every stage has been read), two columns per dword:
+    // lanes 2c and 2c + 1 swap one value of rows (a, a + 1), so lane 2c holds row a and lane 2c + 1
+    // row a + 1, each for columns 2c, 2c + 1.  The slice is then stored as whole row segments.
+    //   gate/up: SiLU(g) * u; device row block 8 nt + 2 wv + p holds 32 gate rows, then the 32 up
+    //            rows of intermediate columns 32 * (8 nt + 2 wv + p) + 0..31: 64 columns per wave.
+    //   down:    128 output columns per wave.
+    constexpr int OCOLS = GATEUP ? 64 : 128;      // bf16 output columns per wave
+    constexpr int PITCH = OCOLS * 2 + 16;         // staging row pitch in bytes
+    constexpr int LPR = OCOLS * 2 / 16;           // lanes per row segment (16 bytes each)
+    constexpr int RPI = 64 / LPR;                 // rows per store instruction
+    static_assert(4 * 64 * PITCH <= WNS * STAGE_BYTES, "staging fits in the ring");
+    uint8_t* stg = ring + wv * (64 * PITCH);
+    // lane index laundered through an empty asm, so that the epilogue's per-lane offsets are
+    // computed here and not hoisted out of the tile loop (where they would only take registers)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int el32 = ln & 31, ehi = ln >> 5;
+    const bool odd = ln & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // byte selectors of the pair swap
+    uint16_t* ocol0 = GATEUP ? a.h + 32 * (8 * nt + 2 * wv) : (shared ? a.y_shared : a.y_sorted) + WBN * nt + 128 * wv;
+    const size_t opitch = GATEUP ? (size_t)a.I : (size_t)a.d;
+    const int orow0 = (GATEUP || !shared) ? row0 + m0 : m0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * hh + ii;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = 32 * ii + (r >> 2) * 8 + ehi * 4 + (r & 3) + (odd ? 1 : 0);  // in the half
+#pragma unroll
+          for (int jj = 0; jj < OCOLS / 32; ++jj) {
+            float v0, v1;  // rows r, r + 1 of this lane's column
+            if (GATEUP) {
+              // SiLU(g) * u with the hardware exp and reciprocal (about 1 ulp each, far below the
+              // bf16 rounding of h)
+              const float g0 = acc[i][2 * jj][r], u0 = acc[i][2 * jj + 1][r];
+              const float g1 = acc[i][2 * jj][r + 1], u1 = acc[i][2 * jj + 1][r + 1];
+              v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
+              v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
+            } else {
+              v0 = acc[i][jj][r];
+              v1 = acc[i][jj][r + 1];
+            }
+            const bf16x2 pv = {(__bf16)v0, (__bf16)v1};
+            const uint32_t pk = __builtin_bit_cast(uint32_t, pv);
+            const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pk, 0xB1, 0xf, 0xf, false);
+            // even lane: (own row r, partner row r); odd lane: (partner row r + 1, own row r + 1)
+            const uint32_t word = __builtin_amdgcn_perm(other, pk, sel);
+            *(uint32_t*)(stg + row * PITCH + (32 * jj + (el32 & ~1)) * 2) = word;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 64 / RPI; ++q) {
+        const int row = q * RPI + ln / LPR, seg = ln % LPR;
+        const u32x4 v = *(const u32x4*)(stg + row * PITCH + seg * 16);
+        const int m = 64 * hh + row;
+        if (m < mrows) *(u32x4*)(ocol0 + (size_t)(orow0 + m) * opitch + seg * 8) = v;
+      }
+    }
+    lds_reads_done_barrier();  // the next tile's loads overwrite the staging slices
+  }
+}
+
+template <bool GATEUP>
+hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
+  auto kern = gemm_wide_kernel<GATEUP>;
+  static bool attr_set = false;
+  static int cus = 0;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wide_lds_bytes(512)) !=
+        hipSuccess)
+      return hipGetLastError();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+    attr_set = true;
+  }
+  const int ntiles = (GATEUP ? 2 * a.I : a.d) / WBN;
+  long long blocks = (long long)tiles_upper * ntiles;
+  if (blocks > cus) blocks = cus;  // one block per CU (the ring takes most of its LDS)
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), wide_lds_bytes(a.E), s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_wide_fits(int fmt, int rows, int E) {
+  return fmt == FMT_BF16 && rows % WBN == 0 && E <= 512 && wide_lds_bytes(E) <= 160 * 1024;
+}
+
+hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s) {
+  return gateup ? launch_wide<true>(a, tiles_upper, s) : launch_wide<false>(a, tiles_upper, s);
+}
+
+}  // namespace ftk
