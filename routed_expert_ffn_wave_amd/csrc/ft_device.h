@@ -39,10 +39,11 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 }
 
 // E8M0 scale 2^(s-127) as fp32 (s = 255 is NaN).  2^-127 is an fp32 subnormal and is kept exactly.
+// Plain integer arithmetic (no compare, no branch): s << 23 is 2^(s-127) for s = 1..254; the max
+// turns s = 0 into the subnormal 0x00400000, and (s + 1) >> 8 sets the quiet-NaN bit for s = 255.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  if (s == 255u) return __uint_as_float(0x7fc00000u);
-  if (s == 0u) return __uint_as_float(0x00400000u);
-  return __uint_as_float(s << 23);
+  const uint32_t b = max(s << 23, 0x00400000u) | (((s + 1u) >> 8) << 22);
+  return __uint_as_float(b);
 }
 
 // (v & m) | o in one instruction: m is uniform (an SGPR), o is kept in a VGPR

@@ -363,7 +363,7 @@ static hipError_t launch_gemm_cfg(const FfnArgs& a, int tiles_upper, hipStream_t
 template <int FMT, bool GATEUP>
 static hipError_t launch_gemm_fmt(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   const int rows = GATEUP ? 2 * a.I : a.d;
-  if (gemm_wide_fits(FMT, rows, a.E)) return launch_gemm_wide(a, GATEUP, tiles_upper, s);
+  if (gemm_wide_fits(FMT, rows, GATEUP ? a.d : a.I, a.E)) return launch_gemm_wide(a, GATEUP, tiles_upper, s);
   if constexpr (FMT == FMT_BF16 || FMT == FMT_MXFP4 || FMT == FMT_NVFP4)
     if (rows % 256 == 0) return launch_gemm_cfg<FMT, GATEUP, 4>(a, tiles_upper, s);
   return launch_gemm_cfg<FMT, GATEUP, 2>(a, tiles_upper, s);

@@ -1,7 +1,8 @@
-// Grouped expert GEMM on MFMA with wide wave tiles and a direct-to-LDS operand ring (bf16 banks).
+// Grouped expert GEMM on MFMA with wide wave tiles and a direct-to-LDS operand ring (bf16 and MXFP4
+// banks).
 //
 // Expert FFNs are read from per-format banks (FreeToken walk-through "深入FreeToken架构…全链路剖析",
-// section 五); with many tokens per expert, each group is a dense bf16 contraction on the matrix cores.
+// section 五); with many tokens per expert, each group is a dense contraction on the matrix cores.
 //
 // Tile = 128 token rows x 512 weight rows, one block of 4 waves per CU.  Wave w computes the 128
 // rows times weight rows 128w .. 128w+127 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32
@@ -9,19 +10,22 @@
 // traffic per flop of a 64 x 128 wave tile.
 //
 // Operands go from global memory straight into LDS (global_load_lds_dwordx4: 64 lanes x 16 bytes
-// to consecutive LDS bytes) through a ring of WNS stages of 32 K columns.  The stage for step
-// s + WNS is issued at step s, once every wave has finished reading step s, so each load has
-// WNS - 1 steps of MFMA work to arrive.  The loads are issued from inline assembly: the compiler
-// then puts no full vmcnt wait in front of the LDS reads; the kernel waits for exactly the stage
-// it needs (vmcnt counts one wave's own loads, which complete in issue order) and meets the other
-// waves at a barrier that does not drain the memory counters.
+// to consecutive LDS bytes) through a ring of NS stages of 32 K columns.  The stage for step s + NS
+// is issued at step s, once every wave has finished reading step s, so each load has NS - 1 steps
+// of MFMA work to arrive.  The loads are issued from inline assembly: the compiler then puts no
+// full vmcnt wait in front of the LDS reads; the kernel waits for exactly the stage it needs (vmcnt
+// counts one wave's own loads, which complete in issue order) and meets the other waves at a
+// barrier that does not drain the memory counters.
 //
 // LDS stage layout:
 //   A: 128 rows x 64 bytes; row r keeps its 16-byte K chunk c in slot c ^ f(r), with
 //      f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the fragment reads (32 rows at one chunk) touch each
 //      bank once per 8 lanes (32 banks) or per 16 lanes (64 banks).
-//   B: the bank's row-interleaved layout keeps one chunk of 64 rows in 1 KiB; a stage holds
-//      8 row blocks x 4 chunks of them, [block][chunk][64 rows][16 bytes], read without conflicts.
+//   B: the bank's row-interleaved layout keeps one chunk of 64 rows in 1 KiB; a stage holds the 8
+//      row blocks of the tile, [block][chunk][64 rows][16 bytes]: 4 chunks of 8 bf16, or one chunk
+//      of 32 MXFP4 codes, whose E8M0 scales follow (256 bytes per wave: its two blocks' 64-byte
+//      runs).  MXFP4 fragments are decoded to bf16 in registers (e2m1 times a power of two is exact
+//      in bf16), so every format runs the bf16 MFMA.
 #include <type_traits>
 
 #include "ft_device.h"
@@ -34,18 +38,32 @@ namespace {
 constexpr int WBM = GEMM_BM;                 // token rows per tile
 constexpr int WBN = 512;                     // weight rows per tile (4 waves x 128)
 constexpr int WBK = 32;                      // K columns per ring stage
-constexpr int WNS = 3;                       // ring stages
-constexpr int A_BYTES = WBM * WBK * 2;       // 8 KiB
-constexpr int B_BYTES = WBN * WBK * 2;       // 32 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int DMA_A = A_BYTES / 1024 / 4;    // 1 KiB loads per wave and stage
-constexpr int DMA_B = B_BYTES / 1024 / 4;
-constexpr int DMA_STAGE = DMA_A + DMA_B;
-static_assert(WBM == 128 && DMA_A == 2 && DMA_B == 8, "stage shape");
-static_assert(WNS >= 2 && WNS <= 3, "wait_newer covers up to two newer stages");
+constexpr int A_BYTES = WBM * WBK * 2;       // 8 KiB of activations per stage
+constexpr int DMA_A = A_BYTES / 1024 / 4;    // A loads (1 KiB) per wave and stage
+static_assert(WBM == 128 && DMA_A == 2, "stage shape");
+
+template <int FMT>
+struct WideCfg;
+template <>
+struct WideCfg<FMT_BF16> {
+  static constexpr int NS = 3;                   // ring stages
+  static constexpr int B_BYTES = WBN * WBK * 2;  // 4 chunks of 8 bf16 per row
+  static constexpr int S_BYTES = 0;
+  static constexpr int DMA = DMA_A + 8;          // loads per wave and stage
+};
+template <>
+struct WideCfg<FMT_MXFP4> {
+  static constexpr int NS = 5;
+  static constexpr int B_BYTES = WBN * 16;       // one chunk of 32 codes per row
+  static constexpr int S_BYTES = 4 * 256;        // E8M0 scales, 256 bytes per wave
+  static constexpr int DMA = DMA_A + 3;
+};
+template <int FMT>
+constexpr int stage_bytes() { return A_BYTES + WideCfg<FMT>::B_BYTES + WideCfg<FMT>::S_BYTES; }
 
 __host__ __device__ inline size_t wide_ring_off(int E) { return (group_lds_bytes(E) + 1023) & ~(size_t)1023; }
-__host__ __device__ inline size_t wide_lds_bytes(int E) { return wide_ring_off(E) + (size_t)WNS * STAGE_BYTES; }
+template <int FMT>
+__host__ __device__ inline size_t wide_lds_bytes(int E) { return wide_ring_off(E) + (size_t)WideCfg<FMT>::NS * stage_bytes<FMT>(); }
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -76,21 +94,40 @@ __device__ __forceinline__ void dma16x4(const uint8_t* base, uint32_t voff, uint
       : "v"(voff), "s"(base), "s"(lds)
       : "memory");
 }
-// Wait until this wave's loads of a stage have landed, `newer` (0..2, wave-uniform) stages having
-// been issued after it.
+// One wave: lane l's 4 bytes at base + voff are written to LDS bytes lds + 4 l .. + 3.
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+// Wait until this wave's loads of a stage have landed, `newer` (0..4, wave-uniform) stages of U
+// loads each having been issued after it.
+template <int U>
 __device__ __forceinline__ void wait_newer(int newer) {
-  if (newer >= 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_STAGE) : "memory");
+  static_assert(4 * U <= 63, "vmcnt range");
+  if (newer >= 4)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * U) : "memory");
+  else if (newer == 3)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * U) : "memory");
+  else if (newer == 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * U) : "memory");
   else if (newer == 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_STAGE) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(U) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 // Own LDS reads complete, then the block barrier; memory operations do not move across it.
 __device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool GATEUP>
+template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
+  using C = WideCfg<FMT>;
+  constexpr bool MX = FMT == FMT_MXFP4;
+  constexpr int NS = C::NS, STAGE = stage_bytes<FMT>();
+  constexpr int EPC = MX ? 32 : 8;  // K elements per 16-byte chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int E2 = a.E + 2;
   int* s_slot = (int*)lds;
@@ -104,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
   const int K = GATEUP ? a.d : a.I;
   const int ncols = GATEUP ? 2 * a.I : a.d;  // weight rows
   const int ntiles = ncols / WBN;
-  const int nchunk = K / 8;                  // 16-byte chunks per weight row
+  const int nchunk = K / EPC;                // 16-byte chunks per weight row
   GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
   GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
   build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + WBM - 1) / WBM) * ntiles; });
@@ -121,9 +158,16 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
   // Fragment reads, byte offsets inside a stage.  A fragment i of substep u: rows 32 i + l32, chunk
   // 2 u + hi.  B fragment j of substep u: row block 2 wv + j / 2, rows 32 (j % 2) + l32, chunk 2 u + hi.
   const int xo = ((l32 >> 1) ^ (l32 >> 2)) & 3;
-  const int a_rd0 = l32 * 64 + ((hi ^ xo) << 4);
-  const int a_rd1 = l32 * 64 + (((2 + hi) ^ xo) << 4);
+  // (MXFP4 pairs substep u and half hi with chunk 2 hi + u instead of 2 u + hi: any order of the
+  // K sum is the same contraction, and this one gives each lane both substeps' B codes as one
+  // 8-byte read, dwords 2 hi and 2 hi + 1 of the row's 16-byte chunk.)
+  const int a_rd0 = l32 * 64 + (((MX ? 2 * hi : hi) ^ xo) << 4);
+  const int a_rd1 = l32 * 64 + (((MX ? 2 * hi + 1 : 2 + hi) ^ xo) << 4);
   const int b_rd = A_BYTES + (8 * wv + hi) * 1024 + l32 * 16;
+  // MXFP4: this lane's 8 code bytes of B row 32 (j % 2) + l32 of block 2 wv + j / 2 (both
+  // substeps), and the row's scale byte in this wave's scale run
+  const int bx_rd = A_BYTES + (2 * wv * 64 + l32) * 16 + 8 * hi;
+  const int sx_rd = A_BYTES + C::B_BYTES + wv * 256 + l32;
 
   // Blocks are placed on the 8 XCDs round-robin: give each XCD a contiguous run of the tile list so
   // that tiles running at once on one XCD share activation rows and weight tiles through its L2.
@@ -155,19 +199,34 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
       const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
       aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
     }
-    // this wave's two 64-row blocks of the weight tile
-    const uint8_t* bt = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K * 2 + (size_t)(8 * nt + 2 * wv) * nchunk * 1024;
-    // Load unit q (0..3) of this wave's share of stage s into the ring buffer at LDS byte `buf`:
-    // q = 0, 1: 16 A rows each; q = 2, 3: one 64-row block of the weight tile, its 4 chunks.
+    // this wave's two 64-row blocks of the weight tile (and their scale runs)
+    const size_t mat_bytes = (size_t)ncols * nchunk * 16;
+    const uint8_t* bt = (GATEUP ? a.w13 : a.w2) + (size_t)slot * mat_bytes + (size_t)(8 * nt + 2 * wv) * nchunk * 1024;
+    const uint8_t* st_sc = MX ? (GATEUP ? a.s13 : a.s2) + (size_t)slot * ncols * nchunk + (size_t)(8 * nt + 2 * wv) * nchunk * 64
+                              : nullptr;
+    // Load unit q of this wave's share of stage s into the ring buffer at LDS byte `buf`:
+    //   q = 0, 1: 16 A rows each;
+    //   bf16:  q = 2, 3: one 64-row block of the weight tile, its 4 chunks;
+    //   MXFP4: q = 2, 3: one 64-row block's chunk; q = 4: both blocks' 64 scale bytes (lanes 0-15
+    //          and 16-31; lanes 32-63 repeat them into the unused half of the wave's 256 bytes).
     const uint32_t bvoff = (uint32_t)lane * 16;
+    const uint32_t svoff = (uint32_t)(((lane >> 4) & 1) * nchunk * 64 + (lane & 15) * 4);
     auto issue_unit = [&](uint32_t buf, int s, int q) {
       if (q < DMA_A) {
         dma16(abase + (size_t)s * (WBK * 2), aoff[q], buf + (DMA_A * wv + q) * 1024);
-      } else {
+      } else if constexpr (!MX) {
         const int rb = q - DMA_A;
         dma16x4(bt + ((size_t)rb * nchunk + 4 * s) * 1024, bvoff, buf + A_BYTES + (2 * wv + rb) * 4096);
+      } else {
+        if (q < DMA_A + 2) {
+          const int rb = q - DMA_A;
+          dma16(bt + ((size_t)rb * nchunk + s) * 1024, bvoff, buf + A_BYTES + (2 * wv + rb) * 1024);
+        } else {
+          dma4(st_sc + (size_t)s * 64, svoff, buf + A_BYTES + C::B_BYTES + wv * 256);
+        }
       }
     };
+    constexpr int UNITS = MX ? 5 : 4;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -177,53 +236,100 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     bf16x8 f0[8], f1[8];  // fragments of substeps 0 and 1: A rows 0..3, then B columns 0..3
-    // fragment n of substep u of the stage at `st`
+    uint2 braw[4];        // MXFP4: codes of the 4 B fragments (substep 0 in .x, 1 in .y)
+    uint32_t bsb[4];      // MXFP4: their E8M0 scale bytes, as read
+    float bsc[4];         // MXFP4: the scales as fp32 (converted when substep 0 is decoded)
+    // fragment n of substep u of the stage at `st` (bf16 B fragments, or A)
     auto frag = [&](const uint8_t* st, int u, int n) -> bf16x8 {
       if (n < 4) return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + n * 2048);
       return *(const bf16x8*)(st + b_rd + u * 2048 + ((n - 4) >> 1) * 4096 + ((n - 4) & 1) * 512);
     };
+    auto read_raw = [&](const uint8_t* st, int j) {  // MXFP4 B fragment j: codes and scale
+      braw[j] = *(const uint2*)(st + bx_rd + (j >> 1) * 1024 + (j & 1) * 512);
+      bsb[j] = st[sx_rd + (j >> 1) * 64 + (j & 1) * 32];
+    };
+    // MXFP4 B fragment j of substep u: codes 16 hi + 8 u .. + 7 of the chunk (dword 2 hi + u)
+    auto decode = [&](int j, int u) -> bf16x8 {
+      if (u == 0) bsc[j] = e8m0_to_f32(bsb[j]);  // the read was issued a phase earlier
+      const uint32_t w = u ? braw[j].y : braw[j].x;
+      u32x4 o;
+      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bsc[j], 0));
+      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bsc[j], 1));
+      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bsc[j], 2));
+      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bsc[j], 3));
+      return __builtin_bit_cast(bf16x8, o);
+    };
+    auto mfma = [&](int i, int j, const bf16x8& av, const bf16x8& bv) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
+    };
 
-    const int pre = min(WNS, nsteps);
+    const int pre = min(NS, nsteps);
     for (int s = 0; s < pre; ++s)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) issue_unit(ring_m0 + (uint32_t)s * STAGE_BYTES, s, q);
-    wait_newer(pre - 1);
+      for (int q = 0; q < UNITS; ++q) issue_unit(ring_m0 + (uint32_t)s * STAGE, s, q);
+    wait_newer<C::DMA>(pre - 1);
     lds_reads_done_barrier();
 #pragma unroll
-    for (int n = 0; n < 8; ++n) f0[n] = frag(ring, 0, n);
-    int cb = 0;  // ring buffer of step s
-    // One step: 16 MFMAs on substep 0 with substep 1's fragment reads between them; the wait for
-    // stage s + 1 and the barrier; 16 MFMAs on substep 1 with the next stage's substep-0 reads and
-    // (while stages remain) this wave's loads of stage s + WNS, into the buffer just released,
-    // between them.  The scheduling barriers keep that order, so reads and loads issue in the
-    // MFMAs' shadow.
-    auto step = [&](int s, auto load_ahead) {
-      const uint8_t* st = ring + cb * STAGE_BYTES;
-      const int nb = (cb + 1 == WNS) ? 0 : cb + 1;
-      const uint8_t* nst = ring + nb * STAGE_BYTES;  // past the last step: read but unused
-      const uint32_t dbuf = ring_m0 + (uint32_t)cb * STAGE_BYTES;
+    for (int n = 0; n < 4; ++n) f0[n] = frag(ring, 0, n);
+    if constexpr (MX) {
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[n >> 2], f0[4 + (n & 3)], acc[n >> 2][n & 3], 0, 0, 0);
-        if (n < 8) f1[n] = frag(st, 1, n);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j) read_raw(ring, j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f0[4 + j] = decode(j, 0);
+    } else {
+#pragma unroll
+      for (int n = 4; n < 8; ++n) f0[n] = frag(ring, 0, n);
+    }
+    int cb = 0;  // ring buffer of step s
+    // One step: 16 MFMAs on substep 0 with substep 1's fragment reads (MXFP4: A reads and B decodes)
+    // between them; the wait for stage s + 1 and the barrier; 16 MFMAs on substep 1 with the next
+    // stage's substep-0 reads (MXFP4: A reads, raw B reads, then the B decodes of its substep 0)
+    // and (while stages remain) this wave's loads of stage s + NS, into the buffer just released,
+    // between them.  The scheduling barriers keep that order, so reads, decodes and loads issue in
+    // the MFMAs' shadow.
+    auto step = [&](int s, auto load_ahead) {
+      const uint8_t* st = ring + cb * STAGE;
+      const int nb = (cb + 1 == NS) ? 0 : cb + 1;
+      const uint8_t* nst = ring + nb * STAGE;  // past the last step: read but unused
+      const uint32_t dbuf = ring_m0 + (uint32_t)cb * STAGE;
+      if constexpr (MX) {
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          mfma(n >> 2, n & 3, f0[n >> 2], f0[4 + (n & 3)]);
+          if (n < 4) f1[n] = frag(st, 1, n);
+          else if (n < 8) f1[n] = decode(n - 4, 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          mfma(n >> 2, n & 3, f0[n >> 2], f0[4 + (n & 3)]);
+          if (n < 8) f1[n] = frag(st, 1, n);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // every wave is done reading stage s and has stage s + 1 in LDS
-      if (s + 1 < nsteps) wait_newer(min(WNS - 2, nsteps - 2 - s));
+      if (s + 1 < nsteps) wait_newer<C::DMA>(min(NS - 2, nsteps - 2 - s));
       lds_reads_done_barrier();
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
-        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[n >> 2], f1[4 + (n & 3)], acc[n >> 2][n & 3], 0, 0, 0);
-        if (n < 8) f0[n] = frag(nst, 0, n);
+        mfma(n >> 2, n & 3, f1[n >> 2], f1[4 + (n & 3)]);
+        if constexpr (MX) {  // the next stage: A reads, raw B reads, then its substep-0 decode
+          if (n < 4) f0[n] = frag(nst, 0, n);
+          else if (n < 8) read_raw(nst, n - 4);
+          else if (n >= 12) f0[n - 8] = decode(n - 12, 0);
+        } else {
+          if (n < 8) f0[n] = frag(nst, 0, n);
+        }
         if constexpr (decltype(load_ahead)::value) {
-          if (n == 2 || n == 4 || n == 6 || n == 8) issue_unit(dbuf, s + WNS, (n - 2) >> 1);
+          if (n >= 2 && n < 2 + 2 * UNITS && (n & 1) == 0) issue_unit(dbuf, s + NS, (n - 2) >> 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       cb = nb;
     };
     int s = 0;
-    for (; s < nsteps - WNS; ++s) step(s, std::true_type{});
+    for (; s < nsteps - NS; ++s) step(s, std::true_type{});
     for (; s < nsteps; ++s) step(s, std::false_type{});
 
     // ---- epilogue.  Lane holds, for tile (i, j), rows 32 i + (r/4)*8 + hi*4 + r%4 and weight
@@ -238,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
     constexpr int PITCH = OCOLS * 2 + 16;         // staging row pitch in bytes
     constexpr int LPR = OCOLS * 2 / 16;           // lanes per row segment (16 bytes each)
     constexpr int RPI = 64 / LPR;                 // rows per store instruction
-    static_assert(4 * 64 * PITCH <= WNS * STAGE_BYTES, "staging fits in the ring");
+    static_assert(4 * 64 * PITCH <= NS * STAGE, "staging fits in the ring");
     uint8_t* stg = ring + wv * (64 * PITCH);
     // lane index laundered through an empty asm, so that the epilogue's per-lane offsets are
     // computed here and not hoisted out of the tile loop (where they would only take registers)
@@ -293,14 +399,14 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
   }
 }
 
-template <bool GATEUP>
+template <int FMT, bool GATEUP>
 hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
-  auto kern = gemm_wide_kernel<GATEUP>;
+  auto kern = gemm_wide_kernel<FMT, GATEUP>;
   static bool attr_set = false;
   static int cus = 0;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wide_lds_bytes(512)) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)wide_lds_bytes<FMT>(512)) != hipSuccess)
       return hipGetLastError();
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
@@ -311,18 +417,24 @@ hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   long long blocks = (long long)tiles_upper * ntiles;
   if (blocks > cus) blocks = cus;  // one block per CU (the ring takes most of its LDS)
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), wide_lds_bytes(a.E), s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), wide_lds_bytes<FMT>(a.E), s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_wide_fits(int fmt, int rows, int E) {
-  return fmt == FMT_BF16 && rows % WBN == 0 && E <= 512 && wide_lds_bytes(E) <= 160 * 1024;
+// The wide kernel needs 512-row weight tiles and at least NS K steps of 32 (so that its ring fills).
+bool gemm_wide_fits(int fmt, int rows, int K, int E) {
+  if (rows % WBN != 0 || E > 512) return false;
+  if (fmt == FMT_BF16) return K >= WideCfg<FMT_BF16>::NS * WBK && wide_lds_bytes<FMT_BF16>(E) <= 160 * 1024;
+  if (fmt == FMT_MXFP4) return K >= WideCfg<FMT_MXFP4>::NS * WBK && wide_lds_bytes<FMT_MXFP4>(E) <= 160 * 1024;
+  return false;
 }
 
 hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s) {
-  return gateup ? launch_wide<true>(a, tiles_upper, s) : launch_wide<false>(a, tiles_upper, s);
+  if (a.fmt == FMT_MXFP4)
+    return gateup ? launch_wide<FMT_MXFP4, true>(a, tiles_upper, s) : launch_wide<FMT_MXFP4, false>(a, tiles_upper, s);
+  return gateup ? launch_wide<FMT_BF16, true>(a, tiles_upper, s) : launch_wide<FMT_BF16, false>(a, tiles_upper, s);
 }
 
 }  // namespace ftk
