@@ -122,11 +122,83 @@ __device__ __forceinline__ void wait_newer(int newer) {
 // Own LDS reads complete, then the block barrier; memory operations do not move across it.
 __device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Store one finished tile.
+template <bool GATEUP>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], uint8_t* stg_base, const FfnArgs& a, int lane, int wv,
+                                           int nt, bool shared, int row0, int m0, int mrows) {
+  // Lane holds, for tile (i, j), rows 32 i + (r/4)*8 + hi*4 + r%4 and weight
+  // row 128 wv + 32 j + l32 of the tile.  Each wave stages its bf16 results for 64 rows at a time
+  // in its own slice of `stg_base` (4 x 64 x PITCH bytes), two columns per dword:
+  // lanes 2c and 2c + 1 swap one value of rows (a, a + 1), so lane 2c holds row a and lane 2c + 1
+  // row a + 1, each for columns 2c, 2c + 1.  The slice is then stored as whole row segments.
+  //   gate/up: SiLU(g) * u; device row block 8 nt + 2 wv + p holds 32 gate rows, then the 32 up
+  //            rows of intermediate columns 32 * (8 nt + 2 wv + p) + 0..31: 64 columns per wave.
+  //   down:    128 output columns per wave.
+  constexpr int OCOLS = GATEUP ? 64 : 128;      // bf16 output columns per wave
+  constexpr int PITCH = OCOLS * 2 + 16;         // staging row pitch in bytes
+  constexpr int LPR = OCOLS * 2 / 16;           // lanes per row segment (16 bytes each)
+  constexpr int RPI = 64 / LPR;                 // rows per store instruction
+  uint8_t* stg = stg_base + wv * (64 * PITCH);
+  // lane index laundered through an empty asm, so that the epilogue's per-lane offsets are
+  // computed here and not hoisted out of the tile loop (where they would only take registers)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int el32 = ln & 31, ehi = ln >> 5;
+  const bool odd = ln & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // byte selectors of the pair swap
+  uint16_t* ocol0 = GATEUP ? a.h + 32 * (8 * nt + 2 * wv) : (shared ? a.y_shared : a.y_sorted) + WBN * nt + 128 * wv;
+  const size_t opitch = GATEUP ? (size_t)a.I : (size_t)a.d;
+  const int orow0 = (GATEUP || !shared) ? row0 + m0 : m0;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * hh + ii;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int row = 32 * ii + (r >> 2) * 8 + ehi * 4 + (r & 3) + (odd ? 1 : 0);  // in the half
+#pragma unroll
+        for (int jj = 0; jj < OCOLS / 32; ++jj) {
+          float v0, v1;  // rows r, r + 1 of this lane's column
+          if (GATEUP) {
+            // SiLU(g) * u with the hardware exp and reciprocal (about 1 ulp each, far below the
+            // bf16 rounding of h)
+            const float g0 = acc[i][2 * jj][r], u0 = acc[i][2 * jj + 1][r];
+            const float g1 = acc[i][2 * jj][r + 1], u1 = acc[i][2 * jj + 1][r + 1];
+            v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
+            v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
+          } else {
+            v0 = acc[i][jj][r];
+            v1 = acc[i][jj][r + 1];
+          }
+          const bf16x2 pv = {(__bf16)v0, (__bf16)v1};
+          const uint32_t pk = __builtin_bit_cast(uint32_t, pv);
+          const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pk, 0xB1, 0xf, 0xf, false);
+          // even lane: (own row r, partner row r); odd lane: (partner row r + 1, own row r + 1)
+          const uint32_t word = __builtin_amdgcn_perm(other, pk, sel);
+          *(uint32_t*)(stg + row * PITCH + (32 * jj + (el32 & ~1)) * 2) = word;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 64 / RPI; ++q) {
+      const int row = q * RPI + ln / LPR, seg = ln % LPR;
+      const u32x4 v = *(const u32x4*)(stg + row * PITCH + seg * 16);
+      const int m = 64 * hh + row;
+      if (m < mrows) *(u32x4*)(ocol0 + (size_t)(orow0 + m) * opitch + seg * 8) = v;
+    }
+  }
+}
+
+// Staging bytes of store_tile: 4 waves x 64 rows x the down kernel's pitch (128 columns).
+constexpr int STG_BYTES = 4 * 64 * (128 * 2 + 16);
+
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
   using C = WideCfg<FMT>;
   constexpr bool MX = FMT == FMT_MXFP4;
   constexpr int NS = C::NS, STAGE = stage_bytes<FMT>();
+  static_assert(STG_BYTES <= NS * STAGE, "epilogue staging fits in the ring");
   constexpr int EPC = MX ? 32 : 8;  // K elements per 16-byte chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int E2 = a.E + 2;
@@ -332,70 +404,191 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
     for (; s < nsteps - NS; ++s) step(s, std::true_type{});
     for (; s < nsteps; ++s) step(s, std::false_type{});
 
-    // ---- epilogue.  Lane holds, for tile (i, j), rows 32 i + (r/4)*8 + hi*4 + r%4 and weight
-    // row 128 wv + 32 j + l32 of the tile.  Each wave stages its bf16 results for 64 rows at a time
-    // in its own slice of the ring (free now: every stage has been read), two columns per dword:
-    // lanes 2c and 2c + 1 swap one value of rows (a, a + 1), so lane 2c holds row a and lane 2c + 1
-    // row a + 1, each for columns 2c, 2c + 1.  The slice is then stored as whole row segments.
-    //   gate/up: SiLU(g) * u; device row block 8 nt + 2 wv + p holds 32 gate rows, then the 32 up
-    //            rows of intermediate columns 32 * (8 nt + 2 wv + p) + 0..31: 64 columns per wave.
-    //   down:    128 output columns per wave.
-    constexpr int OCOLS = GATEUP ? 64 : 128;      // bf16 output columns per wave
-    constexpr int PITCH = OCOLS * 2 + 16;         // staging row pitch in bytes
-    constexpr int LPR = OCOLS * 2 / 16;           // lanes per row segment (16 bytes each)
-    constexpr int RPI = 64 / LPR;                 // rows per store instruction
-    static_assert(4 * 64 * PITCH <= NS * STAGE, "staging fits in the ring");
-    uint8_t* stg = ring + wv * (64 * PITCH);
-    // lane index laundered through an empty asm, so that the epilogue's per-lane offsets are
-    // computed here and not hoisted out of the tile loop (where they would only take registers)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int el32 = ln & 31, ehi = ln >> 5;
-    const bool odd = ln & 1;
-    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // byte selectors of the pair swap
-    uint16_t* ocol0 = GATEUP ? a.h + 32 * (8 * nt + 2 * wv) : (shared ? a.y_shared : a.y_sorted) + WBN * nt + 128 * wv;
-    const size_t opitch = GATEUP ? (size_t)a.I : (size_t)a.d;
-    const int orow0 = (GATEUP || !shared) ? row0 + m0 : m0;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * hh + ii;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const int row = 32 * ii + (r >> 2) * 8 + ehi * 4 + (r & 3) + (odd ? 1 : 0);  // in the half
-#pragma unroll
-          for (int jj = 0; jj < OCOLS / 32; ++jj) {
-            float v0, v1;  // rows r, r + 1 of this lane's column
-            if (GATEUP) {
-              // SiLU(g) * u with the hardware exp and reciprocal (about 1 ulp each, far below the
-              // bf16 rounding of h)
-              const float g0 = acc[i][2 * jj][r], u0 = acc[i][2 * jj + 1][r];
-              const float g1 = acc[i][2 * jj][r + 1], u1 = acc[i][2 * jj + 1][r + 1];
-              v0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
-              v1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
-            } else {
-              v0 = acc[i][jj][r];
-              v1 = acc[i][jj][r + 1];
-            }
-            const bf16x2 pv = {(__bf16)v0, (__bf16)v1};
-            const uint32_t pk = __builtin_bit_cast(uint32_t, pv);
-            const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pk, 0xB1, 0xf, 0xf, false);
-            // even lane: (own row r, partner row r); odd lane: (partner row r + 1, own row r + 1)
-            const uint32_t word = __builtin_amdgcn_perm(other, pk, sel);
-            *(uint32_t*)(stg + row * PITCH + (32 * jj + (el32 & ~1)) * 2) = word;
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 64 / RPI; ++q) {
-        const int row = q * RPI + ln / LPR, seg = ln % LPR;
-        const u32x4 v = *(const u32x4*)(stg + row * PITCH + seg * 16);
-        const int m = 64 * hh + row;
-        if (m < mrows) *(u32x4*)(ocol0 + (size_t)(orow0 + m) * opitch + seg * 8) = v;
-      }
-    }
+    // ---- epilogue (staging slices in the ring: every stage has been read)
+    store_tile<GATEUP>(acc, ring, a, lane, wv, nt, shared, row0, m0, mrows);
     lds_reads_done_barrier();  // the next tile's loads overwrite the staging slices
+  }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// bf16 banks: weights straight from global memory into registers, activations through the ring.
+//
+// A wave's weight rows are used by that wave alone, so they need not pass through LDS: each lane
+// loads its own B fragments (16 bytes of one row per fragment and substep: 512-byte runs per half
+// wave) into one of 4 register sets, 3.5 steps ahead of their MFMAs.  Only the activation rows,
+// which all 4 waves read, go through the LDS ring (BD_NS stages of 128 rows x 32 K).  Per step that
+// leaves 8 KiB of LDS writes and 32 KiB of LDS reads per CU, against 40 + 64 KiB when the weights
+// also pass through LDS.
+//
+// Issue order per step s (every step issues the same loads; past the end of the tile they repeat
+// its last step, into registers or ring buffers nobody reads again):
+//   phase 0: 16 MFMAs on substep 0; between them the substep-1 A reads and the 4 B loads of
+//            substep 1 of step s + 3 (into the set whose substep-1 registers step s - 1 used);
+//   wait for A stage s + 1, barrier;
+//   phase 1: 16 MFMAs on substep 1; between them the next stage's substep-0 A reads, this wave's
+//            2 loads of A stage s + BD_NS, then the 4 B loads of substep 0 of step s + 4.
+// vmcnt counts every one of these loads in issue order, so "A stage s + 1 has landed" is "at most
+// C(s) loads outstanding", C(s) = the loads issued after it (capped at the counter's 63).
+constexpr int BD_NS = 7;       // A ring stages
+constexpr int BD_PRO_B = 28;   // B loads of the prologue: steps 0..2 whole, substep 0 of step 3
+
+__host__ __device__ inline size_t bd_lds_bytes(int E) { return wide_ring_off(E) + (size_t)BD_NS * A_BYTES + STG_BYTES; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Loads issued after A stage s + 1 by the time step s waits for it (see above), for BD_NS = 7.
+__device__ __forceinline__ void bd_wait_stage(int s) {
+  static_assert(BD_NS == 7, "counts below");
+  // s + 1 >= BD_NS: 4 + 10 (BD_NS - 2) + 4 = 58; else 2 BD_NS + BD_PRO_B + 8 s = 42 + 8 s
+  if (s >= BD_NS - 1) wait_vm<58>();
+  else if (s == 0) wait_vm<42>();
+  else if (s == 1) wait_vm<50>();
+  else if (s == 2) wait_vm<58>();
+  else wait_vm<63>();
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int E2 = a.E + 2;
+  int* s_slot = (int*)lds;
+  int* s_row0 = s_slot + E2;
+  int* s_cnt = s_row0 + E2;
+  int* s_item0 = s_cnt + E2;
+  int* s_tmp = s_item0 + E2;
+  uint8_t* ring = lds + wide_ring_off(a.E);
+  uint8_t* stg = ring + BD_NS * A_BYTES;
+  const uint32_t ring_m0 = lds_u32(ring);
+
+  const int K = GATEUP ? a.d : a.I;
+  const int ncols = GATEUP ? 2 * a.I : a.d;
+  const int ntiles = ncols / WBN;
+  const int nchunk = K / 8;
+  GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
+  GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
+  build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + WBM - 1) / WBM) * ntiles; });
+  const int nitems = s_item0[gl.n];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int TK = a.T * a.k;
+  const int nsteps = K / WBK;  // a multiple of 4 (K % 128 == 0)
+  const uint8_t* abase = GATEUP ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+  const uint32_t arow_bytes = (uint32_t)K * 2;
+  const int xo = ((l32 >> 1) ^ (l32 >> 2)) & 3;
+  const int a_rd0 = l32 * 64 + ((hi ^ xo) << 4);
+  const int a_rd1 = l32 * 64 + (((2 + hi) ^ xo) << 4);
+
+  const int NB = gridDim.x;
+  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int it = lb; it < nitems; it += NB) {
+    const int g = find_group(s_item0, gl.n, it);
+    const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int slot = __builtin_amdgcn_readfirstlane(s_slot[g]);
+    const int row0 = __builtin_amdgcn_readfirstlane(s_row0[g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[g]);
+    const bool shared = row0 >= TK;
+    const int m0 = mt * WBM;
+    const int mrows = min(WBM, cnt - m0);
+
+    uint32_t aoff[DMA_A];
+#pragma unroll
+    for (int q = 0; q < DMA_A; ++q) {
+      const int r = 16 * (DMA_A * wv + q) + (lane >> 2);
+      const int m = min(r, mrows - 1);
+      int src_row;
+      if (GATEUP)
+        src_row = shared ? (m0 + m) : a.gather[row0 + m0 + m] / a.k;
+      else
+        src_row = row0 + m0 + m;
+      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+      aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
+    }
+    // A stage s (clamped to the last) into ring buffer `b`
+    auto issue_a = [&](int b, int s, int q) {
+      const int sc = min(s, nsteps - 1);
+      dma16(abase + (size_t)sc * (WBK * 2), aoff[q], ring_m0 + (uint32_t)b * A_BYTES + (DMA_A * wv + q) * 1024);
+    };
+    // This lane's B fragment j of substep u of step s (clamped): row 32 (j % 2) + l32 of block
+    // 8 nt + 2 wv + j / 2, chunk 4 s + 2 u + hi.
+    const uint8_t* bl = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K * 2 + (size_t)(8 * nt + 2 * wv) * nchunk * 1024 +
+                        (size_t)(hi * 1024 + l32 * 16);
+    auto load_b = [&](int s, int u, int j) -> bf16x8 {
+      const int sc = min(s, nsteps - 1);
+      return *(const bf16x8*)(bl + ((size_t)(j >> 1) * nchunk + 4 * sc + 2 * u) * 1024 + (j & 1) * 512);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    bf16x8 fa0[4], fa1[4];   // A fragments of substeps 0 and 1
+    bf16x8 bq[4][2][4];      // B register sets: [step % 4][substep][fragment]
+    auto frag_a = [&](const uint8_t* st, int u, int i) -> bf16x8 {
+      return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + i * 2048);
+    };
+
+    // prologue: A stages 0..BD_NS-1, then B of steps 0..2 and substep 0 of step 3
+    for (int s = 0; s < BD_NS; ++s)
+#pragma unroll
+      for (int q = 0; q < DMA_A; ++q) issue_a(s, s, q);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (st < 3 || u == 0) bq[st][u][j] = load_b(st, u, j);
+    wait_vm<2 * (BD_NS - 1) + BD_PRO_B>();  // A stage 0
+    lds_reads_done_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa0[i] = frag_a(ring, 0, i);
+
+    int cb = 0;  // ring buffer of step s
+    auto step = [&](int s, auto kset) {
+      constexpr int k = decltype(kset)::value;
+      const uint8_t* st = ring + cb * A_BYTES;
+      const int nb = (cb + 1 == BD_NS) ? 0 : cb + 1;
+      const uint8_t* nst = ring + nb * A_BYTES;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[n >> 2], bq[k][0][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
+        if (n < 4) fa1[n] = frag_a(st, 1, n);
+        else if (n < 8) bq[(k + 3) & 3][1][n - 4] = load_b(s + 3, 1, n - 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (s + 1 < nsteps) bd_wait_stage(s);
+      lds_reads_done_barrier();
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[n >> 2], bq[k][1][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
+        if (n < 4) fa0[n] = frag_a(nst, 0, n);  // past the last step: read but unused
+        else if (n < 6) issue_a(cb, s + BD_NS, n - 4);
+        else if (n < 10) bq[k][0][n - 6] = load_b(s + 4, 0, n - 6);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cb = nb;
+    };
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s, std::integral_constant<int, 0>{});
+      step(s + 1, std::integral_constant<int, 1>{});
+      step(s + 2, std::integral_constant<int, 2>{});
+      step(s + 3, std::integral_constant<int, 3>{});
+    }
+    // The clamped loads past the end are still in flight: they land in ring buffers and registers
+    // that nothing reads, but the staging area is separate and the next tile's prologue loads
+    // complete after them (issue order), so no wait is needed here.
+    store_tile<GATEUP>(acc, stg, a, lane, wv, nt, shared, row0, m0, mrows);
+    lds_reads_done_barrier();  // staging slices and ring buffers are rewritten by the next tile
   }
 }
 
@@ -421,12 +614,34 @@ hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool GATEUP>
+hipError_t launch_bd(const FfnArgs& a, int tiles_upper, hipStream_t s) {
+  auto kern = gemm_bd_kernel<GATEUP>;
+  static bool attr_set = false;
+  static int cus = 0;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bd_lds_bytes(512)) !=
+        hipSuccess)
+      return hipGetLastError();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+    attr_set = true;
+  }
+  const int ntiles = (GATEUP ? 2 * a.I : a.d) / WBN;
+  long long blocks = (long long)tiles_upper * ntiles;
+  if (blocks > cus) blocks = cus;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), bd_lds_bytes(a.E), s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // The wide kernel needs 512-row weight tiles and at least NS K steps of 32 (so that its ring fills).
 bool gemm_wide_fits(int fmt, int rows, int K, int E) {
   if (rows % WBN != 0 || E > 512) return false;
-  if (fmt == FMT_BF16) return K >= WideCfg<FMT_BF16>::NS * WBK && wide_lds_bytes<FMT_BF16>(E) <= 160 * 1024;
+  if (fmt == FMT_BF16) return K % 128 == 0 && K >= 128 && bd_lds_bytes(E) <= 160 * 1024;
   if (fmt == FMT_MXFP4) return K >= WideCfg<FMT_MXFP4>::NS * WBK && wide_lds_bytes<FMT_MXFP4>(E) <= 160 * 1024;
   return false;
 }
@@ -434,7 +649,7 @@ bool gemm_wide_fits(int fmt, int rows, int K, int E) {
 hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s) {
   if (a.fmt == FMT_MXFP4)
     return gateup ? launch_wide<FMT_MXFP4, true>(a, tiles_upper, s) : launch_wide<FMT_MXFP4, false>(a, tiles_upper, s);
-  return gateup ? launch_wide<FMT_BF16, true>(a, tiles_upper, s) : launch_wide<FMT_BF16, false>(a, tiles_upper, s);
+  return gateup ? launch_bd<true>(a, tiles_upper, s) : launch_bd<false>(a, tiles_upper, s);
 }
 
 }  // namespace ftk
