@@ -85,6 +85,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // groups with at most this many routed rows go through the GEMV kernels when the path is automatic
 constexpr int kGemvMaxRows = ftk::GEMV_MAX_ROWS;
+constexpr int kWideAllRows = 256;  // from this many tokens the wide GEMM kernels take every group
 
 size_t h_bytes(int T, int k, int I, bool shared) {
   return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
@@ -127,6 +128,12 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     gemv_max = 0x7fffffff;
     gemm_min = 0x7fffffff;
   } else if (path == FT_PATH_GEMM) {
+    gemv_max = 0;
+    gemm_min = 1;
+  } else if (T >= kWideAllRows && ftk::gemm_wide_fits(a.fmt, 2 * a.I, a.d, E) && ftk::gemm_wide_fits(a.fmt, a.d, a.I, E)) {
+    // Many tokens on the wide GEMM kernels: small groups go there too.  A 128-row tile streams its
+    // weights at close to the HBM share of one CU while the MFMAs run, which beats the GEMV
+    // kernel's rate for groups of a few rows once the launch has enough tiles to fill the device.
     gemv_max = 0;
     gemm_min = 1;
   } else {
