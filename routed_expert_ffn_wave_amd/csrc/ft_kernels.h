@@ -45,8 +45,9 @@ constexpr int GEMV_MAX_ROWS = 16;  // largest group the automatic path sends to 
 hipError_t launch_gemm_gateup(const FfnArgs& a, int tiles_upper, hipStream_t s);
 hipError_t launch_gemm_down(const FfnArgs& a, int tiles_upper, hipStream_t s);
 constexpr int GEMM_BM = 128;  // token rows per tile
-// bf16 and MXFP4 banks whose weight rows divide into 512-row tiles: 128 x 512 tiles, 128 x 128
-// per wave, operands loaded straight into an LDS ring
+// bf16 and MXFP4 banks whose weight rows divide into 512-row tiles (128 x 512 tiles, 128 x 128 per
+// wave) and FP8-B128 banks whose rows divide into 256-row tiles (128 x 256, 128 x 64 per wave),
+// activations loaded straight into an LDS ring
 bool gemm_wide_fits(int fmt, int rows, int K, int E);
 hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s);
 

@@ -123,18 +123,20 @@ __device__ __forceinline__ void wait_newer(int newer) {
 __device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Store one finished tile.
-template <bool GATEUP>
-__device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], uint8_t* stg_base, const FfnArgs& a, int lane, int wv,
-                                           int nt, bool shared, int row0, int m0, int mrows) {
+// WJ: 32-column fragments per wave (4: 128 weight rows, 2: 64); dev_blk: the wave's first 64-row
+// device block of the matrix.
+template <bool GATEUP, int WJ>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[4][WJ], uint8_t* stg_base, const FfnArgs& a, int lane, int wv,
+                                           int dev_blk, bool shared, int row0, int m0, int mrows) {
   // Lane holds, for tile (i, j), rows 32 i + (r/4)*8 + hi*4 + r%4 and weight
   // row 128 wv + 32 j + l32 of the tile.  Each wave stages its bf16 results for 64 rows at a time
   // in its own slice of `stg_base` (4 x 64 x PITCH bytes), two columns per dword:
   // lanes 2c and 2c + 1 swap one value of rows (a, a + 1), so lane 2c holds row a and lane 2c + 1
   // row a + 1, each for columns 2c, 2c + 1.  The slice is then stored as whole row segments.
-  //   gate/up: SiLU(g) * u; device row block 8 nt + 2 wv + p holds 32 gate rows, then the 32 up
-  //            rows of intermediate columns 32 * (8 nt + 2 wv + p) + 0..31: 64 columns per wave.
-  //   down:    128 output columns per wave.
-  constexpr int OCOLS = GATEUP ? 64 : 128;      // bf16 output columns per wave
+  //   gate/up: SiLU(g) * u; device row block dev_blk + p holds 32 gate rows, then the 32 up rows
+  //            of intermediate columns 32 * (dev_blk + p) + 0..31: 16 WJ columns per wave.
+  //   down:    32 WJ output columns per wave, from column 64 dev_blk.
+  constexpr int OCOLS = GATEUP ? 16 * WJ : 32 * WJ;  // bf16 output columns per wave
   constexpr int PITCH = OCOLS * 2 + 16;         // staging row pitch in bytes
   constexpr int LPR = OCOLS * 2 / 16;           // lanes per row segment (16 bytes each)
   constexpr int RPI = 64 / LPR;                 // rows per store instruction
@@ -146,7 +148,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], uint8_t* stg_bas
   const int el32 = ln & 31, ehi = ln >> 5;
   const bool odd = ln & 1;
   const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // byte selectors of the pair swap
-  uint16_t* ocol0 = GATEUP ? a.h + 32 * (8 * nt + 2 * wv) : (shared ? a.y_shared : a.y_sorted) + WBN * nt + 128 * wv;
+  uint16_t* ocol0 = GATEUP ? a.h + 32 * dev_blk : (shared ? a.y_shared : a.y_sorted) + 64 * dev_blk;
   const size_t opitch = GATEUP ? (size_t)a.I : (size_t)a.d;
   const int orow0 = (GATEUP || !shared) ? row0 + m0 : m0;
 #pragma unroll
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(FfnArgs a) {
     for (; s < nsteps; ++s) step(s, std::false_type{});
 
     // ---- epilogue (staging slices in the ring: every stage has been read)
-    store_tile<GATEUP>(acc, ring, a, lane, wv, nt, shared, row0, m0, mrows);
+    store_tile<GATEUP, 4>(acc, ring, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
     lds_reads_done_barrier();  // the next tile's loads overwrite the staging slices
   }
 }
@@ -587,8 +589,226 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
     // The clamped loads past the end are still in flight: they land in ring buffers and registers
     // that nothing reads, but the staging area is separate and the next tile's prologue loads
     // complete after them (issue order), so no wait is needed here.
-    store_tile<GATEUP>(acc, stg, a, lane, wv, nt, shared, row0, m0, mrows);
+    store_tile<GATEUP, 4>(acc, stg, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
     lds_reads_done_barrier();  // staging slices and ring buffers are rewritten by the next tile
+  }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// FP8-B128 banks: e4m3 weights straight into registers, an fp32 scale per 128 x 128 block.
+//
+// The block scale must multiply the sum over its 128 K columns, so each wave keeps two sets of
+// accumulators in the AGPRs: `part` collects one 128-K block (4 steps, the first MFMA of a block
+// starting from zero) and is then scaled into `acc`.  That makes the wave tile 128 x 64 (4 x 2
+// MFMA tiles, 128 + 128 fp32 per lane) and the block tile 128 x 256; the wave's 64 rows are one
+// device row block, whose rows lie in one 128-row scale block for each half (gate and up rows of
+// W13, or the 64 rows of W2), so a wave needs two scales per K block.
+//
+// Each lane loads the 16 e4m3 of its row's chunk 2 s + hi for step s (one 16-byte load per
+// fragment and step, covering both substeps: the same K permutation as MXFP4, chunk 2 hi + u of A)
+// into one of 4 register sets, 4 steps ahead, and decodes them exactly to bf16 with
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.  The activations go through the same 7-stage ring.
+// Per step: phase 0 = 8 MFMAs on substep 0 (A substep-1 reads and the substep-1 decodes between
+// them), the wait and barrier, phase 1 = 8 MFMAs on substep 1 (next stage's A reads, this wave's 2
+// A loads of stage s + F8_NS, then its 2 weight loads of step s + 4).
+constexpr int F8_NS = 7;
+constexpr int F8_BN = 256;      // weight rows per tile
+constexpr int F8_SETS = 4;      // weight register sets
+constexpr int F8_STG = 4 * 64 * (64 * 2 + 16);
+
+__host__ __device__ inline size_t f8_lds_bytes(int E) { return wide_ring_off(E) + (size_t)F8_NS * A_BYTES + F8_STG; }
+
+// Loads issued after A stage s + 1 when step s waits for it: 2 + 4 (F8_NS - 2) = 22 once the ring
+// is in its steady state; in the first F8_NS - 1 steps of a tile the prologue's loads count
+// (2 (F8_NS - 2 - s) + 2 F8_SETS + 4 s = 18 + 2 s).
+__device__ __forceinline__ void f8_wait_stage(int s) {
+  static_assert(F8_NS == 7 && F8_SETS == 4, "counts below");
+  if (s >= F8_NS - 1) wait_vm<22>();
+  else if (s == 0) wait_vm<18>();
+  else if (s == 1) wait_vm<20>();
+  else if (s == 2) wait_vm<22>();
+  else if (s == 3) wait_vm<24>();
+  else if (s == 4) wait_vm<26>();
+  else wait_vm<28>();
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void gemm_f8_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int E2 = a.E + 2;
+  int* s_slot = (int*)lds;
+  int* s_row0 = s_slot + E2;
+  int* s_cnt = s_row0 + E2;
+  int* s_item0 = s_cnt + E2;
+  int* s_tmp = s_item0 + E2;
+  uint8_t* ring = lds + wide_ring_off(a.E);
+  uint8_t* stg = ring + F8_NS * A_BYTES;
+  const uint32_t ring_m0 = lds_u32(ring);
+
+  const int K = GATEUP ? a.d : a.I;
+  const int ncols = GATEUP ? 2 * a.I : a.d;
+  const int ntiles = ncols / F8_BN;
+  const int nchunk = K / 16;   // 16-byte chunks (16 e4m3) per weight row
+  const int kblocks = K / 128;
+  GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
+  GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
+  build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + WBM - 1) / WBM) * ntiles; });
+  const int nitems = s_item0[gl.n];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int TK = a.T * a.k;
+  const int nsteps = K / WBK;  // a multiple of 8 (K % 256 == 0)
+  const uint8_t* abase = GATEUP ? (const uint8_t*)a.x : (const uint8_t*)a.h;
+  const uint32_t arow_bytes = (uint32_t)K * 2;
+  const int xo = ((l32 >> 1) ^ (l32 >> 2)) & 3;
+  const int a_rd0 = l32 * 64 + (((2 * hi) ^ xo) << 4);
+  const int a_rd1 = l32 * 64 + (((2 * hi + 1) ^ xo) << 4);
+
+  const int NB = gridDim.x;
+  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int it = lb; it < nitems; it += NB) {
+    const int g = find_group(s_item0, gl.n, it);
+    const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int slot = __builtin_amdgcn_readfirstlane(s_slot[g]);
+    const int row0 = __builtin_amdgcn_readfirstlane(s_row0[g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[g]);
+    const bool shared = row0 >= TK;
+    const int m0 = mt * WBM;
+    const int mrows = min(WBM, cnt - m0);
+    const int blk = 4 * nt + wv;  // this wave's device row block
+
+    uint32_t aoff[DMA_A];
+#pragma unroll
+    for (int q = 0; q < DMA_A; ++q) {
+      const int r = 16 * (DMA_A * wv + q) + (lane >> 2);
+      const int m = min(r, mrows - 1);
+      int src_row;
+      if (GATEUP)
+        src_row = shared ? (m0 + m) : a.gather[row0 + m0 + m] / a.k;
+      else
+        src_row = row0 + m0 + m;
+      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+      aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
+    }
+    auto issue_a = [&](int b, int s, int q) {
+      const int sc = min(s, nsteps - 1);
+      dma16(abase + (size_t)sc * (WBK * 2), aoff[q], ring_m0 + (uint32_t)b * A_BYTES + (DMA_A * wv + q) * 1024);
+    };
+    // weight bytes of fragment j (rows 32 j + l32 of the block), chunk 2 s + hi
+    const uint8_t* bl = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K + (size_t)blk * nchunk * 1024 +
+                        (size_t)(hi * 1024 + l32 * 16);
+    auto load_b = [&](int s, int j) -> u32x4 {
+      const int sc = min(s, nsteps - 1);
+      return *(const u32x4*)(bl + (size_t)(2 * sc) * 1024 + j * 512);
+    };
+    // the two scales of a K block: gate and up rows of W13 (logical rows 32 blk, I + 32 blk), or
+    // the block's rows of W2 (64 blk)
+    const float* sbase = (const float*)(GATEUP ? a.s13 : a.s2) + (size_t)slot * (ncols / 128) * kblocks;
+    const int sr0 = GATEUP ? (32 * blk) / 128 : (64 * blk) / 128;
+    const int sr1 = GATEUP ? (a.I + 32 * blk) / 128 : sr0;
+
+    f32x16 acc[4][2], part[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    f32x16 zero;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
+    bf16x8 fa0[4], fa1[4], fb0[2], fb1[2];
+    u32x4 braw[F8_SETS][2];
+    auto frag_a = [&](const uint8_t* st, int u, int i) -> bf16x8 {
+      return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + i * 2048);
+    };
+    // substep u of raw fragment w: its 8 e4m3 (dwords 2 u, 2 u + 1) exactly as bf16
+    auto decode = [&](const u32x4& w, int u) -> bf16x8 {
+      u32x4 o;
+      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * u], 1.0f, false));
+      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * u], 1.0f, true));
+      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * u + 1], 1.0f, false));
+      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * u + 1], 1.0f, true));
+      return __builtin_bit_cast(bf16x8, o);
+    };
+
+    for (int s = 0; s < F8_NS; ++s)
+#pragma unroll
+      for (int q = 0; q < DMA_A; ++q) issue_a(s, s, q);
+#pragma unroll
+    for (int t = 0; t < F8_SETS; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) braw[t][j] = load_b(t, j);
+    wait_vm<2 * (F8_NS - 1) + 2 * F8_SETS>();  // A stage 0
+    lds_reads_done_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa0[i] = frag_a(ring, 0, i);
+
+    int cb = 0;
+    float sc0 = 0.0f, sc1 = 0.0f;  // the current K block's scales
+    auto step = [&](int s, auto kset) {
+      constexpr int k = decltype(kset)::value;
+      constexpr bool kb_first = (k & 3) == 0, kb_last = (k & 3) == 3;
+      const uint8_t* st = ring + cb * A_BYTES;
+      const int nb = (cb + 1 == F8_NS) ? 0 : cb + 1;
+      const uint8_t* nst = ring + nb * A_BYTES;
+      if (kb_first) {  // this K block's scales (scalar loads, used 4 steps later)
+        sc0 = sbase[(size_t)sr0 * kblocks + (s >> 2)];
+        sc1 = sbase[(size_t)sr1 * kblocks + (s >> 2)];
+      }
+      fb0[0] = decode(braw[k][0], 0);
+      fb0[1] = decode(braw[k][1], 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int i = n >> 1, j = n & 1;
+        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0[j], kb_first ? zero : part[i][j], 0, 0, 0);
+        if (n < 4) fa1[n] = frag_a(st, 1, n);
+        else if (n < 6) fb1[n - 4] = decode(braw[k][n - 4], 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (s + 1 < nsteps) {
+        if (s < F8_NS - 1)
+          f8_wait_stage(s);
+        else
+          wait_vm<22>();
+      }
+      lds_reads_done_barrier();
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int i = n >> 1, j = n & 1;
+        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], part[i][j], 0, 0, 0);
+        if (n < 4) fa0[n] = frag_a(nst, 0, n);
+        else if (n < 6) issue_a(cb, s + F8_NS, n - 4);
+        else braw[k][n - 6] = load_b(s + F8_SETS, n - 6);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kb_last) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[i][0][r] = fmaf(part[i][0][r], sc0, acc[i][0][r]);
+            acc[i][1][r] = fmaf(part[i][1][r], sc1, acc[i][1][r]);
+          }
+      }
+      cb = nb;
+    };
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s, std::integral_constant<int, 0>{});
+      step(s + 1, std::integral_constant<int, 1>{});
+      step(s + 2, std::integral_constant<int, 2>{});
+      step(s + 3, std::integral_constant<int, 3>{});
+    }
+    store_tile<GATEUP, 2>(acc, stg, a, lane, wv, blk, shared, row0, m0, mrows);
+    // every load of this tile has landed (the repeated ones past its end included) before the next
+    // tile's prologue reuses the ring and the registers
+    wait_vm<0>();
+    lds_reads_done_barrier();
   }
 }
 
@@ -636,10 +856,37 @@ hipError_t launch_bd(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool GATEUP>
+hipError_t launch_f8(const FfnArgs& a, int tiles_upper, hipStream_t s) {
+  auto kern = gemm_f8_kernel<GATEUP>;
+  static bool attr_set = false;
+  static int cus = 0;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f8_lds_bytes(512)) !=
+        hipSuccess)
+      return hipGetLastError();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+    attr_set = true;
+  }
+  const int ntiles = (GATEUP ? 2 * a.I : a.d) / F8_BN;
+  long long blocks = (long long)tiles_upper * ntiles;
+  if (blocks > cus) blocks = cus;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), f8_lds_bytes(a.E), s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// The wide kernel needs 512-row weight tiles and at least NS K steps of 32 (so that its ring fills).
+bool gemm_f8_fits(int rows, int K, int E) {
+  return rows % F8_BN == 0 && K % 256 == 0 && E <= 512 && f8_lds_bytes(E) <= 160 * 1024;
+}
+
+// The wide kernels need 512-row weight tiles and enough K steps of 32 to fill their rings.
 bool gemm_wide_fits(int fmt, int rows, int K, int E) {
+  if (fmt == FMT_FP8_B128) return gemm_f8_fits(rows, K, E);
   if (rows % WBN != 0 || E > 512) return false;
   if (fmt == FMT_BF16) return K % 128 == 0 && K >= 128 && bd_lds_bytes(E) <= 160 * 1024;
   if (fmt == FMT_MXFP4) return K >= WideCfg<FMT_MXFP4>::NS * WBK && wide_lds_bytes<FMT_MXFP4>(E) <= 160 * 1024;
@@ -647,6 +894,7 @@ bool gemm_wide_fits(int fmt, int rows, int K, int E) {
 }
 
 hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s) {
+  if (a.fmt == FMT_FP8_B128) return gateup ? launch_f8<true>(a, tiles_upper, s) : launch_f8<false>(a, tiles_upper, s);
   if (a.fmt == FMT_MXFP4)
     return gateup ? launch_wide<FMT_MXFP4, true>(a, tiles_upper, s) : launch_wide<FMT_MXFP4, false>(a, tiles_upper, s);
   return gateup ? launch_bd<true>(a, tiles_upper, s) : launch_bd<false>(a, tiles_upper, s);
