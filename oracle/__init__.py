@@ -54,6 +54,7 @@ def _bind(lib):
     i = ctypes.c_int
     lib.ora_dequant.argtypes = [i, P, P, i, i, i, i, P]
     lib.ora_route.argtypes = [P, i, i, i, P, P]
+    lib.ora_router_logits.argtypes = [P, P, i, i, i, P]
     lib.ora_permute.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_swiglu_ffn.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_combine.argtypes = [P, P, P, P, P, P, i, i, i, i, P, i, P, P]
@@ -134,6 +135,27 @@ def route(logits, k: int, lib=None):
     w = np.empty((T, k), np.float32)
     _check((lib or _load()).ora_route(_p(L), T, E, k, _p(ids), _p(w)), "route")
     return ids, w
+
+
+def router_logits(x_bf16, w_router_bf16, lib=None):
+    """fp64 [T][E] router logits x . w_router^T of bf16 activations [T][d] and router rows [E][d]
+    (torch bf16 tensors or uint16 bit arrays)."""
+    x = _bf16_bits(x_bf16)
+    wr = _bf16_bits(w_router_bf16)
+    T, d = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == d
+    out = np.empty((T, E), np.float64)
+    _check((lib or _load()).ora_router_logits(_p(x), _p(wr), T, d, E, _p(out)), "router_logits")
+    return out
+
+
+def _bf16_bits(a) -> np.ndarray:
+    """uint16 bit array of a torch bf16 tensor or of an integer array of bf16 bits."""
+    if hasattr(a, "view") and hasattr(a, "dtype") and "bfloat16" in str(getattr(a, "dtype", "")):
+        import torch  # noqa: F401  (only when given a torch tensor)
+        return np.ascontiguousarray(a.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+    return np.ascontiguousarray(np.asarray(a).astype(np.uint16))
 
 
 def permute(ids, E: int, lib=None):

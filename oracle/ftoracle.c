@@ -181,6 +181,24 @@ int ora_route(const float* logits, int T, int E, int k, int32_t* ids, float* w) 
   return 0;
 }
 
+/* ---------------------------------------------------------------- router projection
+ * The step before route: each token's router logits are its activation row against each
+ * expert's router row (the gate that picks k of the E experts, FreeToken walk-through section 五).
+ * x bf16 [T][d], wr bf16 [E][d] -> out fp64 [T][E], out[t][e] = sum_c x[t][c] * wr[e][c] with c
+ * ascending in double precision (each bf16 product is exact in fp64; only the sum rounds).
+ */
+int ora_router_logits(const uint16_t* x, const uint16_t* wr, int T, int d, int E, double* out) {
+  if (T < 0 || d <= 0 || E <= 0) return -1;
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c)
+        acc += (double)ora_bf16_value(x[(size_t)t * d + c]) * (double)ora_bf16_value(wr[(size_t)e * d + c]);
+      out[(size_t)t * E + e] = acc;
+    }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- permute
  * ids int32 [T][k] (flat index f = t*k + j) -> counts[E], offsets[E+1] (exclusive prefix sum),
  * gather[T*k] (sorted position -> f; grouped by expert id, ascending f inside a group) and

@@ -370,6 +370,59 @@ def pin_combine_cases(lib):
     assert np.abs(out - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max())
 
 
+def _bf16_bits_of(vals):
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    f = np.asarray(vals, np.float32)
+    b = f.view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def pin_router_logits_worked_example(lib):
+    """A hand-computed example: two tokens, three columns, two experts."""
+    x = _bf16_bits_of([[1.0, 2.0, -3.0], [0.5, -0.25, 4.0]])
+    wr = _bf16_bits_of([[1.0, 1.0, 1.0], [0.5, 0.0, 0.25]])
+    got = oracle.router_logits(x, wr, lib=lib)
+    # token 0: 1 + 2 - 3 = 0 and 0.5 + 0 - 0.75 = -0.25; token 1: 0.5 - 0.25 + 4 = 4.25 and
+    # 0.25 + 0 + 1 = 1.25
+    assert np.array_equal(got, np.array([[0.0, -0.25], [4.25, 1.25]]))
+
+
+def pin_router_logits_one_hot(lib):
+    """A router row with a single 1 at column c picks x[:, c] exactly; a transposed or shifted
+    operand would not."""
+    rng = np.random.default_rng(11)
+    T, d, E = 5, 64, 7
+    xf = rng.standard_normal((T, d)).astype(np.float32)
+    x = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    cols = rng.permutation(d)[:E]
+    w = np.zeros((E, d), np.float32)
+    w[np.arange(E), cols] = 1.0
+    got = oracle.router_logits(x, _bf16_bits_of(w), lib=lib)
+    xw = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, xw[:, cols])
+
+
+def pin_router_logits_exact_sum(lib):
+    """Against the exact rational sum (brute force with fractions): within the rounding bound of a
+    double-precision sum of d terms."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    T, d, E = 3, 48, 4
+    x = (rng.standard_normal((T, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wr = ((0.02 * rng.standard_normal((E, d))).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = oracle.router_logits(x, wr, lib=lib)
+    xv = (x.astype(np.uint32) << 16).view(np.float32)
+    wv = (wr.astype(np.uint32) << 16).view(np.float32)
+    for t in range(T):
+        for e in range(E):
+            terms = [Fraction(float(xv[t, c])) * Fraction(float(wv[e, c])) for c in range(d)]
+            exact = sum(terms, Fraction(0))
+            bound = d * 2.0 ** -53 * float(sum(abs(v) for v in terms))
+            assert abs(Fraction(got[t, e]) - exact) <= Fraction(bound)
+
+
 ALL_PINS = [pin_route_bruteforce, pin_route_special_cases, pin_route_weights_float64, pin_permute,
             pin_decoder_tables, pin_dequant_roundtrip, pin_dequant_layouts, pin_ffn_float64,
-            pin_layer_identical_experts, pin_layer_float64, pin_combine_cases]
+            pin_layer_identical_experts, pin_layer_float64, pin_combine_cases, pin_router_logits_worked_example,
+            pin_router_logits_one_hot, pin_router_logits_exact_sum]

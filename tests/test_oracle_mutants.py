@@ -42,6 +42,8 @@ MUTANTS = {
     "combine_no_weight": ("o[c] = o[c] + wj * yr[c];", "o[c] = o[c] + yr[c];"),
     "combine_no_shared": ("o[c] = o[c] + ys[c];", "o[c] = o[c];"),
     "mask_wrong_bit": ("bits |= 1u << j;", "bits |= 1u << (k - 1 - j);"),
+    "router_transposed": ("(double)ora_bf16_value(wr[(size_t)e * d + c]);", "(double)ora_bf16_value(wr[((size_t)c * E + e) % ((size_t)E * d)]);"),
+    "router_dropped_term": ("for (int c = 0; c < d; ++c)\n        acc +=", "for (int c = 1; c < d; ++c)\n        acc +="),
 }
 
 
