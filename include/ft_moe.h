@@ -128,6 +128,23 @@ const char* ft_moe_last_error(void);
 int ft_moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream);
 
 /*
+ * Router projection and router in one launch (the step before the path, fused into route).
+ *   x bf16 [T][d], w_router bf16 [E][d] (row-major)  ->  logits fp32 [T][E], ids int32 [T][k],
+ *   w fp32 [T][k]
+ * logits[t][e] = sum_c x[t][c] * w_router[e][c]: bf16 products accumulated in fp32 on the matrix
+ * cores (the order of the fp32 additions is the kernel's; the result is within the rounding bound
+ * of an fp32 sum of d terms).  ids and w are then exactly what ft_moe_route returns for those
+ * logits.  Requires d > 0 with d % 32 == 0, 1 <= E <= 512, 1 <= k <= min(E, 32); T = 0 is a no-op.
+ * ws: ft_moe_route_proj_workspace(T) bytes of device memory, zero-filled once by the caller; every
+ * call leaves it zero again.  Calls that may overlap need their own workspaces.
+ * The gate that picks k of E experts: [article] "为什么 MoE 模型适合做 CPU–GPU 协同？"; FreeToken
+ * walk-through "深入FreeToken架构…全链路剖析", section 五.
+ */
+size_t ft_moe_route_proj_workspace(int T);
+int ft_moe_route_proj(const uint16_t* x_bf16, const uint16_t* w_router_bf16, int T, int d, int E, int k,
+                      float* logits, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Bytes of workspace ft_moe_permute needs for (T, E, k); 0 when none is needed.
  */
 size_t ft_moe_permute_workspace(int T, int E, int k);

@@ -50,6 +50,8 @@ def _load():
         "ft_moe_abi_version": ([], i),
         "ft_moe_last_error": ([], ctypes.c_char_p),
         "ft_moe_route": ([P, i, i, i, P, P, P], i),
+        "ft_moe_route_proj_workspace": ([i], sz),
+        "ft_moe_route_proj": ([P, P, i, i, i, i, P, P, P, P, sz, P], i),
         "ft_moe_permute_workspace": ([i, i, i], sz),
         "ft_moe_permute": ([P, i, i, i, P, P, P, P, P, sz, P], i),
         "ft_moe_grouped_ffn_workspace": ([BP, i, i, i, i, i], sz),
@@ -70,7 +72,8 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_permute_workspace",
+EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_route_proj_workspace",
+            "ft_moe_route_proj", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
             "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer")
 
@@ -153,6 +156,29 @@ def ft_moe_route(logits: torch.Tensor, k: int, ids=None, w=None, stream=None):
     w = torch.empty(T, k, dtype=torch.float32, device=logits.device) if w is None else w
     _check(lib.ft_moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)))
     return ids, w
+
+
+def ft_moe_route_proj_workspace(T: int) -> int:
+    return lib.ft_moe_route_proj_workspace(T)
+
+
+def ft_moe_route_proj(x: torch.Tensor, w_router: torch.Tensor, k: int, logits=None, ids=None, w=None, ws=None,
+                      stream=None):
+    """Router logits x . w_router^T (bf16 [T][d] and [E][d]) and their top-k, in one launch.
+    `ws`: a zero-filled workspace of ft_moe_route_proj_workspace(T) bytes (allocated zeroed when
+    not given); the call leaves it zero."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty(T, k, dtype=torch.float32, device=dev) if w is None else w
+    need = lib.ft_moe_route_proj_workspace(T)
+    if ws is None:
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.ft_moe_route_proj(_ptr(x), _ptr(w_router), T, d, E, k, _ptr(logits), _ptr(ids), _ptr(w), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+    return logits, ids, w
 
 
 def ft_moe_permute_workspace(T: int, E: int, k: int) -> int:

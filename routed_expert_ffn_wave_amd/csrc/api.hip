@@ -235,6 +235,31 @@ int ft_moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* 
   }
 }
 
+size_t ft_moe_route_proj_workspace(int T) { return T < 0 ? 0 : ftk::route_proj_workspace_bytes(T); }
+
+int ft_moe_route_proj(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k, float* logits,
+                      int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    REQUIRE(E <= 512, FT_E_INVAL, "E must be at most 512 for ft_moe_route_proj (got %d)", E);
+    REQUIRE(d > 0 && d % 32 == 0, FT_E_INVAL, "d must be a positive multiple of 32 (got %d)", d);
+    if (T == 0) return ok();
+    CHECK_PTR(x, "x");
+    CHECK_PTR(w_router, "w_router");
+    CHECK_PTR(logits, "logits");
+    CHECK_PTR(ids, "ids");
+    CHECK_PTR(w, "w");
+    CHECK_PTR(ws, "ws");
+    const size_t need = ftk::route_proj_workspace_bytes(T);
+    REQUIRE(ws_bytes >= need, FT_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    return hip_status(ftk::launch_route_proj(x, w_router, T, d, E, k, logits, ids, w, ws, stream),
+                      "ft_moe_route_proj launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_route_proj: unexpected exception");
+  }
+}
+
 size_t ft_moe_permute_workspace(int T, int E, int k) {
   if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 32) return 0;
   return ftk::permute_workspace_bytes(T, E, k);

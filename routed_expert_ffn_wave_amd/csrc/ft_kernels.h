@@ -27,6 +27,11 @@ struct FfnArgs {
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 
+// router projection fused with route (x bf16 [T][d], w_router bf16 [E][d], d % 32 == 0, E <= 512)
+size_t route_proj_workspace_bytes(int T);
+hipError_t launch_route_proj(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, float* logits,
+                             int32_t* ids, float* w, void* ws, hipStream_t s);
+
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);

@@ -26,7 +26,7 @@ own bank schema).  Encodings follow the public format definitions:
 Random numbers: each tensor has its own torch generator seeded from
 numpy's SeedSequence([workload id, layer, stream, index]).  Streams:
 0 logits, 1 activations, 2 popularity ranks, 3 slot table, 4/5/6 gate/up/down
-weights (index = expert; the shared expert uses index E).  The same seed gives
+weights (index = expert; the shared expert uses index E), 7 router rows.  The same seed gives
 the same values on the same device type; CPU and GPU generators differ, which
 is harmless because each parity check hands one set of tensors to both sides.
 """
@@ -41,7 +41,7 @@ FMT_BF16, FMT_Q4_0, FMT_MXFP4, FMT_FP8_B128, FMT_NVFP4 = 0, 1, 2, 3, 4
 FMT_NAMES = {FMT_BF16: "bf16", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_FP8_B128: "fp8_b128",
              FMT_NVFP4: "nvfp4"}
 
-STREAM_LOGITS, STREAM_X, STREAM_RANK, STREAM_SLOTS, STREAM_GATE, STREAM_UP, STREAM_DOWN = range(7)
+STREAM_LOGITS, STREAM_X, STREAM_RANK, STREAM_SLOTS, STREAM_GATE, STREAM_UP, STREAM_DOWN, STREAM_ROUTER = range(8)
 
 WEIGHT_STD = 0.02
 ZIPF_S = 1.1
@@ -136,6 +136,14 @@ def activations(w: Workload, layer: int = 0, T: int | None = None, device="cpu")
     g = _gen(device, w.wid, layer, STREAM_X)
     x = torch.randn(w.T, w.d, generator=g, device=device, dtype=torch.float32)
     return x[:T].to(torch.bfloat16).contiguous()
+
+
+def router_rows(w: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """bf16 router rows [E][d] drawn N(0, 1/d) in fp32 and rounded to nearest even, so that the
+    router logits of N(0,1) activations are about N(0,1), like the workloads' logits."""
+    g = _gen(device, w.wid, layer, STREAM_ROUTER)
+    wr = torch.randn(w.E, w.d, generator=g, device=device, dtype=torch.float32) / float(np.sqrt(w.d))
+    return wr.to(torch.bfloat16).contiguous()
 
 
 def slot_table(w: Workload, layer: int = 0) -> torch.Tensor:

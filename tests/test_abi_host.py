@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -38,6 +38,20 @@ def test_abi_version():
     assert ft.ft_moe_abi_version() == 1
     m = re.search(r"#define FT_MOE_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == 1
+
+
+def test_route_proj_validation():
+    L = ft.lib
+    ws = 16 * 4
+    _err(L.ft_moe_route_proj(A, A, 4, 64, 8, 0, B, B, B, B, ws, None), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_route_proj(A, A, 4, 64, 513, 2, B, B, B, B, ws, None), ft.FT_E_INVAL, "E must be")
+    _err(L.ft_moe_route_proj(A, A, 4, 48, 8, 2, B, B, B, B, ws, None), ft.FT_E_INVAL, "d must be")
+    _err(L.ft_moe_route_proj(None, A, 4, 64, 8, 2, B, B, B, B, ws, None), ft.FT_E_INVAL, "x is null")
+    _err(L.ft_moe_route_proj(A, A, 4, 64, 8, 2, None, B, B, B, ws, None), ft.FT_E_INVAL, "logits is null")
+    _err(L.ft_moe_route_proj(A, A, 4, 64, 8, 2, B, B, B, None, ws, None), ft.FT_E_INVAL, "ws is null")
+    _err(L.ft_moe_route_proj(A, A, 40, 64, 8, 2, B, B, B, B, ws, None), ft.FT_E_WORKSPACE, "workspace")
+    assert ft.lib.ft_moe_route_proj_workspace(40) == 3 * 16 * 4
+    assert L.ft_moe_route_proj(None, None, 0, 64, 8, 2, None, None, None, None, 0, None) == ft.FT_OK
 
 
 def _err(rc, code, pattern):

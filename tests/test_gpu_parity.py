@@ -38,6 +38,45 @@ def _logits(kind, T, E, seed):
     return L
 
 
+# (T, d, E, k): one token tile to many, E below, at and past the 64-expert tiles, K tails of 32
+ROUTE_PROJ_CASES = [(16, 256, 8, 2), (8, 2048, 128, 8), (37, 512, 40, 6), (300, 7168, 256, 8), (5, 96, 512, 32),
+                    (1, 2048, 128, 8), (4096, 2048, 128, 8)]
+
+
+@pytest.mark.parametrize("T,d,E,k", ROUTE_PROJ_CASES)
+def test_route_proj(ft, T, d, E, k):
+    """Router projection + route in one launch.  Logits within the rounding bound of an fp32 sum
+    of d products against the oracle's fp64 dot products; ids bit for bit (weights within WTOL,
+    as for ft_moe_route) what the oracle's route gives for the GPU's own fp32 logits; the chosen
+    experts a top-k of the fp64 logits within that bound.  A second call with a smaller T reuses the workspace."""
+    w = synth.Workload("route_proj", 90, T=T, d=d, E=E, k=k, I=64, fmt=synth.FMT_BF16)
+    x = synth.activations(w, 0, T, device="cuda")
+    wr = synth.router_rows(w, 0, device="cuda")
+    log(f"route_proj T={T} d={d} E={E} k={k}")
+    ws = torch.zeros(max(ft.ft_moe_route_proj_workspace(T), 16), dtype=torch.uint8, device="cuda")
+    for TT in (T, max(1, T // 3)):
+        lg, ids, wt = ft.ft_moe_route_proj(x[:TT].contiguous(), wr, k, ws=ws)
+        torch.cuda.synchronize()
+        g = lg.cpu().numpy().astype(np.float64)
+        ref = oracle.router_logits(x[:TT].cpu(), wr.cpu())
+        xa = np.abs(oracle.bf16_to_f32(x[:TT].cpu())).astype(np.float64)
+        wa = np.abs(oracle.bf16_to_f32(wr.cpu())).astype(np.float64)
+        bound = d * 2.0 ** -24 * (xa @ wa.T) + 1e-30
+        err = np.abs(g - ref)
+        assert np.all(err <= bound), f"logit error {err.max()} over bound at {np.unravel_index(np.argmax(err - bound), err.shape)}"
+        oids, ow = oracle.route(lg.cpu(), k)
+        assert np.array_equal(ids.cpu().numpy(), oids)
+        assert np.abs(wt.cpu().numpy() - ow).max() <= WTOL
+        ids_np = ids.cpu().numpy()
+        for t in range(TT):
+            chosen = np.zeros(E, bool)
+            chosen[ids_np[t]] = True
+            if chosen.all():
+                continue
+            assert ref[t][chosen].min() >= ref[t][~chosen].max() - 2 * bound[t].max()
+        assert not ws.any(), "the workspace must be left zero"
+
+
 ROUTE_CASES = [(1, 8, 2, "normal"), (37, 8, 2, "ties"), (64, 10, 4, "ties"), (300, 128, 8, "normal"),
                (513, 256, 8, "zipf"), (64, 1024, 32, "ties"), (5, 32, 32, "normal"), (33, 7, 1, "ties"),
                (20, 1, 1, "normal"), (100, 65, 8, "wide"), (16384, 256, 8, "zipf")]
