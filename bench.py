@@ -184,6 +184,47 @@ def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_byte
     print(json.dumps(rec, indent=1))
 
 
+def bench_route_proj(w: synth.Workload, T: int, steps: int, warmup: int):
+    """Router projection + route (ft_moe_route_proj) on the workload's shape: one call is one step;
+    printed as its own JSON line (the step before the layer, not part of the layer's metric)."""
+    x = synth.activations(w, 0, T, device="cuda")
+    wr = synth.router_rows(w, 0, device="cuda")
+    ws = torch.zeros(max(ft.ft_moe_route_proj_workspace(T), 16), dtype=torch.uint8, device="cuda")
+    logits = torch.empty(T, w.E, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, w.k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, w.k, dtype=torch.float32, device="cuda")
+    call = lambda: ft.ft_moe_route_proj(x, wr, w.k, logits=logits, ids=ids, w=wt, ws=ws)  # noqa: E731
+    for _ in range(max(warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    reps = max(steps, 1) * 10
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        call()
+    b.record(s)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = T * w.d * 2 + w.E * w.d * 2 + T * w.E * 4 + T * w.k * 8
+    flops = 2.0 * T * w.E * w.d
+    hbm = nbytes / (us * 1e-6) / 1e9
+    tf = flops / (us * 1e-6) / 1e12
+    decode = T <= 64
+    roof = ({"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm / HBM_PEAK_GBS, 4)}
+            if decode else
+            {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+             "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)})
+    roof.update({"traffic": None, "kernel": "route_proj_kernel (router projection on MFMA + top-k, one launch)",
+                 "per_call_us": round(us, 3), "algorithmic_bytes_per_call": nbytes, "algorithmic_flops_per_call": int(flops)})
+    print(json.dumps({"metric": "router projection + top-k latency", "value": round(us, 3), "unit": "us/call",
+                      "n_gpus": 1, "steps": reps, "warmup": warmup, "ms_per_step": round(us / 1e3, 5),
+                      "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic (seeded)",
+                      "config": {"workload": f"route_proj/{w.name}", "T": T, "d": w.d, "E": w.E, "k": w.k},
+                      "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +238,8 @@ def main():
     ap.add_argument("--ffn-reps", type=int, default=3)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run the counter-calibration copy kernel over BYTES")
+    ap.add_argument("--route-proj", action="store_true",
+                    help="time ft_moe_route_proj (router projection + top-k) on the workload's shape instead")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -215,6 +258,9 @@ def main():
     T = args.T or w.T
     n_layers = args.layers or w.layers
     decode = T <= 64
+    if args.route_proj:
+        bench_route_proj(w, T, args.steps, args.warmup)
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
     log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}")
