@@ -167,6 +167,9 @@ def _small_workloads():
         "q4_0_prefill": W["decode_q4_0"].replace(T=150, d=512, I=256, E=16, k=4, layers=1),
         "nvfp4_decode": W["nvfp4_decode"].replace(layers=1),
         "nvfp4_prefill": W["nvfp4_decode"].replace(T=150, d=512, I=256, E=16, k=4, layers=1),
+        # the shared expert's group on the bf16 and FP8 GEMM kernels (T >= 256: every group on them)
+        "bf16_shared": W["mxfp4_shared"].replace(fmt=synth.FMT_BF16, T=300, d=512, I=256, E=32, k=4),
+        "fp8_shared": W["mxfp4_shared"].replace(fmt=synth.FMT_FP8_B128, T=300, d=512, I=256, E=32, k=4),
     }
 
 
