@@ -8,6 +8,8 @@ The arithmetic lives in ftoracle.c (plain scalar C, fp32, sums in the order writ
 arrays, and composes the five steps of the layer in the order the walk-through of the FreeToken
 engine gives the request path ("深入FreeToken架构…全链路剖析", section 一: expert dispatch, then the
 kernels; section 五: per-format expert banks, hot experts on the GPU, cold experts elsewhere).
+`cache_update` is one step of the global LRU expert cache that decides which experts are on the
+GPU (ora_cache_update; integer bookkeeping, no arithmetic on values).
 """
 from __future__ import annotations
 
@@ -58,6 +60,7 @@ def _bind(lib):
     lib.ora_permute.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_swiglu_ffn.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_combine.argtypes = [P, P, P, P, P, P, i, i, i, i, P, i, P, P]
+    lib.ora_cache_update.argtypes = [P, i, i, i, P, P, P, P, P, P]
     for f in ("ora_bf16_value", "ora_fp16_value"):
         getattr(lib, f).argtypes = [ctypes.c_uint16]
         getattr(lib, f).restype = ctypes.c_float
@@ -169,6 +172,39 @@ def permute(ids, E: int, lib=None):
     _check((lib or _load()).ora_permute(_p(a), T, E, k, _p(counts), _p(offsets), _p(gather), _p(inv)),
            "permute")
     return counts, offsets, gather, inv
+
+
+class CacheState:
+    """Host copy of the expert cache's tables: slot_of_expert [E], expert_of_slot [S] (int32, -1 =
+    none), last_use [S] and tick (uint32).  A fresh state has every slot empty."""
+
+    def __init__(self, E: int, S: int):
+        self.slot_of_expert = np.full(E, -1, np.int32)
+        self.expert_of_slot = np.full(S, -1, np.int32)
+        self.last_use = np.zeros(S, np.uint32)
+        self.tick = np.zeros(1, np.uint32)
+
+    def copy(self):
+        c = CacheState.__new__(CacheState)
+        for f in ("slot_of_expert", "expert_of_slot", "last_use", "tick"):
+            setattr(c, f, getattr(self, f).copy())
+        return c
+
+
+def cache_update(counts, state: CacheState, max_loads: int, lib=None):
+    """One step of the global LRU expert cache on `state` (updated in place).
+
+    Returns (compute_slot int32 [E], loads int32 [n][2] of (expert, slot))."""
+    c = _np(counts, np.int32)
+    E, S = c.shape[0], state.expert_of_slot.shape[0]
+    compute_slot = np.empty(E, np.int32)
+    loads = np.empty(2 * max(max_loads, 1), np.int32)
+    n = (lib or _load()).ora_cache_update(_p(c), E, S, max_loads, _p(state.slot_of_expert),
+                                          _p(state.expert_of_slot), _p(state.last_use), _p(state.tick),
+                                          _p(compute_slot), _p(loads))
+    if n < 0:
+        raise ValueError("oracle cache_update rejected its arguments")
+    return compute_slot, loads[:2 * n].reshape(n, 2).copy()
 
 
 def swiglu_ffn(x_f32, w13_f32, w2_f32, lib=None):

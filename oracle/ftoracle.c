@@ -295,3 +295,69 @@ int ora_combine(const float* y_sorted, const float* y_shared, const int32_t* ids
   }
   return 0;
 }
+
+/* ---------------------------------------------------------------- expert cache step
+ * The GPU keeps the most used experts in a fixed set of S bank slots under one global
+ * least-recently-used policy (zuoshipin.com FreeToken article, mechanism four; walk-through
+ * section 五: hot experts resident on the GPU, cold ones in pinned host memory, a global LRU
+ * expert cache, copies overlapped with compute; the paper summary's key insights: the LRU is
+ * CUDA-Graph compatible).  The pages fix no order of choice, so one step reads:
+ *
+ *   - the step's clock is tick + 1; an expert is demanded when counts[e] > 0;
+ *   - a demanded expert that is resident marks its slot used at this step;
+ *   - repeatedly, while fewer than max_loads loads are chosen: take the demanded absent expert
+ *     with the most tokens (ties to the lowest index) and the slot to reuse: empty slots before
+ *     occupied ones, then the least recently used, ties to the lowest slot index; a slot whose
+ *     expert is demanded at this step is never taken.  Stop when either is missing.  The slot's
+ *     old expert becomes absent; the new one is resident there and its slot used at this step;
+ *   - compute_slot[e] is e's slot if e was resident before the step and still is, else -1: the
+ *     step computes with the experts that were already on the device, while the chosen loads are
+ *     copied in beside that work and serve from the next step on.
+ *
+ * State: slot_of_expert[E] and expert_of_slot[S] (-1 = none, a bijection on the resident set),
+ * last_use[S] and *tick; all updated in place.  loads[2n], loads[2n+1] = (expert, slot) of the
+ * n-th load.  Returns the number of loads, or -1 on bad arguments.
+ */
+int ora_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t* slot_of_expert,
+                     int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
+                     int32_t* loads) {
+  if (E <= 0 || S <= 0 || max_loads < 0) return -1;
+  const uint32_t now = *tick + 1u;
+  int32_t* before = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!before) return -1;
+  for (int e = 0; e < E; ++e) before[e] = slot_of_expert[e];
+  for (int e = 0; e < E; ++e)
+    if (counts[e] > 0 && slot_of_expert[e] >= 0) last_use[slot_of_expert[e]] = now;
+  int n = 0;
+  while (n < max_loads) {
+    int want = -1;
+    for (int e = 0; e < E; ++e)
+      if (counts[e] > 0 && slot_of_expert[e] < 0 && (want < 0 || counts[e] > counts[want])) want = e;
+    if (want < 0) break;
+    int slot = -1;
+    for (int s = 0; s < S; ++s) {
+      const int v = expert_of_slot[s];
+      if (v >= 0 && counts[v] > 0) continue;
+      if (slot < 0) {
+        slot = s;
+        continue;
+      }
+      const int occ = v >= 0, occ_best = expert_of_slot[slot] >= 0;
+      if (occ < occ_best || (occ == occ_best && last_use[s] < last_use[slot])) slot = s;
+    }
+    if (slot < 0) break;
+    const int old = expert_of_slot[slot];
+    if (old >= 0) slot_of_expert[old] = -1;
+    slot_of_expert[want] = slot;
+    expert_of_slot[slot] = want;
+    last_use[slot] = now;
+    loads[2 * n] = want;
+    loads[2 * n + 1] = slot;
+    ++n;
+  }
+  for (int e = 0; e < E; ++e)
+    compute_slot[e] = (before[e] >= 0 && slot_of_expert[e] == before[e]) ? before[e] : -1;
+  *tick = now;
+  free(before);
+  return n;
+}

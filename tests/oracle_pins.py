@@ -422,7 +422,112 @@ def pin_router_logits_exact_sum(lib):
             assert abs(Fraction(got[t, e]) - exact) <= Fraction(bound)
 
 
+# ------------------------------------------------------------------------------ expert cache
+
+def pin_cache_textbook_lru(lib):
+    """One demanded expert and at most one load per step: the cache is then a textbook LRU cache
+    of S entries (on a miss with every entry taken, the least recently requested one goes), so
+    the resident set, the hits and the misses must agree with an OrderedDict LRU step by step."""
+    from collections import OrderedDict
+    rng = np.random.default_rng(31)
+    for E, S, steps in ((12, 4, 300), (7, 1, 60), (5, 5, 50), (40, 9, 500)):
+        st = oracle.CacheState(E, S)
+        ref = OrderedDict()
+        ranks = np.minimum(rng.geometric(0.25, size=steps) - 1, E - 1)   # skewed: hits and misses
+        reqs = rng.permutation(E)[ranks]
+        for step, e in enumerate(reqs):
+            e = int(e)
+            counts = np.zeros(E, np.int32)
+            counts[e] = 1 + step % 3
+            hit = e in ref
+            if hit:
+                ref.move_to_end(e)
+            else:
+                if len(ref) == S:
+                    ref.popitem(last=False)
+                ref[e] = True
+            cs, loads = oracle.cache_update(counts, st, 1, lib=lib)
+            assert set(np.flatnonzero(st.slot_of_expert >= 0).tolist()) == set(ref), (E, S, step)
+            if hit:
+                assert len(loads) == 0 and cs[e] == st.slot_of_expert[e] >= 0
+            else:
+                assert len(loads) == 1 and loads[0, 0] == e and st.slot_of_expert[e] == loads[0, 1]
+                assert cs[e] == -1
+            assert int(st.tick[0]) == step + 1
+
+
+def pin_cache_worked_example(lib):
+    """Six experts, three slots, worked by hand from the policy's definition (misses by token count,
+    ties to the lower expert; empty slots first, then least recently used, ties to the lower slot;
+    slots of demanded experts are kept; this step computes only with experts already resident)."""
+    st = oracle.CacheState(6, 3)
+    steps = [
+        # counts, max_loads, loads, compute_slot, slot_of_expert, expert_of_slot, last_use
+        ([0, 3, 0, 3, 1, 0], 2, [(1, 0), (3, 1)], [-1] * 6, [-1, 0, -1, 1, -1, -1], [1, 3, -1], [1, 1, 0]),
+        ([2, 0, 0, 1, 5, 0], 2, [(4, 2), (0, 0)], [-1, -1, -1, 1, -1, -1], [0, -1, -1, 1, 2, -1], [0, 3, 4],
+         [2, 2, 2]),
+        ([0, 1, 1, 0, 0, 1], 2, [(1, 0), (2, 1)], [-1, -1, -1, -1, 2, -1], [-1, 0, 1, -1, 2, -1], [1, 2, 4],
+         [3, 3, 2]),
+        ([0, 4, 0, 0, 0, 2], 2, [(5, 2)], [-1, 0, 1, -1, -1, -1], [-1, 0, 1, -1, -1, 2], [1, 2, 5], [4, 3, 4]),
+        ([1, 1, 1, 1, 0, 1], 2, [], [-1, 0, 1, -1, -1, 2], [-1, 0, 1, -1, -1, 2], [1, 2, 5], [5, 5, 5]),
+        ([0, 0, 0, 0, 0, 0], 2, [], [-1, 0, 1, -1, -1, 2], [-1, 0, 1, -1, -1, 2], [1, 2, 5], [5, 5, 5]),
+        ([7, 0, 0, 0, 0, 0], 0, [], [-1, 0, 1, -1, -1, 2], [-1, 0, 1, -1, -1, 2], [1, 2, 5], [5, 5, 5]),
+    ]
+    for i, (counts, ml, loads, cs, soe, eos, lu) in enumerate(steps):
+        got_cs, got_loads = oracle.cache_update(np.array(counts, np.int32), st, ml, lib=lib)
+        assert [tuple(int(v) for v in r) for r in got_loads] == loads, (i, got_loads)
+        assert got_cs.tolist() == cs, (i, got_cs)
+        assert st.slot_of_expert.tolist() == soe and st.expert_of_slot.tolist() == eos, i
+        assert st.last_use.tolist() == lu and int(st.tick[0]) == i + 1, i
+
+
+def _zipf_ids(rng, T, E, k, pop):
+    p = 1.0 / np.arange(1, E + 1)
+    p /= p.sum()
+    return np.stack([pop[rng.choice(E, size=k, replace=False, p=p)] for _ in range(T)]).astype(np.int32)
+
+
+def pin_cache_invariants(lib):
+    """Random Zipf-skewed steps: the tables stay a bijection, demanded resident experts keep their
+    slots, the loads are the misses with the most tokens put into the empty, then least recently
+    used, slots whose experts are idle, and as many as the step allows."""
+    rng = np.random.default_rng(32)
+    for E, S, T, k, max_loads, steps in ((64, 16, 4, 4, 3, 80), (32, 32, 8, 2, 32, 40), (20, 6, 3, 3, 6, 60),
+                                         (128, 96, 16, 8, 8, 40)):
+        st = oracle.CacheState(E, S)
+        pop = rng.permutation(E)
+        for step in range(steps):
+            counts = np.bincount(_zipf_ids(rng, T, E, k, pop).reshape(-1), minlength=E).astype(np.int32)
+            prev = st.copy()
+            cs, loads = oracle.cache_update(counts, st, max_loads, lib=lib)
+            dem = counts > 0
+            for sl in range(S):
+                if st.expert_of_slot[sl] >= 0:
+                    assert st.slot_of_expert[st.expert_of_slot[sl]] == sl
+            assert (st.slot_of_expert >= 0).sum() == (st.expert_of_slot >= 0).sum()
+            keep = dem & (prev.slot_of_expert >= 0)
+            assert (st.slot_of_expert[keep] == prev.slot_of_expert[keep]).all()
+            misses = [e for e in range(E) if dem[e] and prev.slot_of_expert[e] < 0]
+            idle = [sl for sl in range(S) if prev.expert_of_slot[sl] < 0 or not dem[prev.expert_of_slot[sl]]]
+            n = min(len(misses), max_loads, len(idle))
+            assert len(loads) == n
+            assert loads[:, 0].tolist() == sorted(misses, key=lambda e: (-counts[e], e))[:n]
+            order = sorted(idle, key=lambda sl: (bool(prev.expert_of_slot[sl] >= 0), int(prev.last_use[sl]), sl))
+            assert loads[:, 1].tolist() == order[:n]
+            for e in range(E):
+                same = prev.slot_of_expert[e] >= 0 and st.slot_of_expert[e] == prev.slot_of_expert[e]
+                assert cs[e] == (prev.slot_of_expert[e] if same else -1)
+            for e, sl in loads:
+                assert st.slot_of_expert[e] == sl and st.last_use[sl] == step + 1
+            for sl in range(S):
+                v = st.expert_of_slot[sl]
+                if v >= 0 and dem[v]:
+                    assert st.last_use[sl] == step + 1
+            assert int(st.tick[0]) == step + 1
+
+
 ALL_PINS = [pin_route_bruteforce, pin_route_special_cases, pin_route_weights_float64, pin_permute,
             pin_decoder_tables, pin_dequant_roundtrip, pin_dequant_layouts, pin_ffn_float64,
             pin_layer_identical_experts, pin_layer_float64, pin_combine_cases, pin_router_logits_worked_example,
-            pin_router_logits_one_hot, pin_router_logits_exact_sum]
+            pin_router_logits_one_hot, pin_router_logits_exact_sum, pin_cache_textbook_lru,
+            pin_cache_worked_example, pin_cache_invariants]

@@ -44,6 +44,13 @@ MUTANTS = {
     "mask_wrong_bit": ("bits |= 1u << j;", "bits |= 1u << (k - 1 - j);"),
     "router_transposed": ("(double)ora_bf16_value(wr[(size_t)e * d + c]);", "(double)ora_bf16_value(wr[((size_t)c * E + e) % ((size_t)E * d)]);"),
     "router_dropped_term": ("for (int c = 0; c < d; ++c)\n        acc +=", "for (int c = 1; c < d; ++c)\n        acc +="),
+    "lru_evicts_mru": ("(occ == occ_best && last_use[s] < last_use[slot])", "(occ == occ_best && last_use[s] > last_use[slot])"),
+    "lru_ties_to_highest_slot": ("last_use[s] < last_use[slot])) slot = s;", "last_use[s] <= last_use[slot])) slot = s;"),
+    "lru_occupied_first": ("if (occ < occ_best ||", "if (occ > occ_best ||"),
+    "lru_misses_by_index": ("(want < 0 || counts[e] > counts[want])", "(want < 0)"),
+    "lru_evicts_demanded": ("if (v >= 0 && counts[v] > 0) continue;", "if (v >= 0 && counts[v] < 0) continue;"),
+    "lru_no_refresh": ("last_use[slot_of_expert[e]] = now;", "last_use[slot_of_expert[e]] = last_use[slot_of_expert[e]];"),
+    "lru_compute_with_loads": ("compute_slot[e] = (before[e] >= 0 && slot_of_expert[e] == before[e]) ? before[e] : -1;", "compute_slot[e] = slot_of_expert[e];"),
 }
 
 
