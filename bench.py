@@ -225,6 +225,96 @@ def bench_route_proj(w: synth.Workload, T: int, steps: int, warmup: int):
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
+PCIE_PEAK_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+
+
+def bench_cache(w: synth.Workload, T: int, steps: int, warmup: int, n_slots: int, max_loads: int):
+    """Layer steps with the global LRU expert cache: route, permute and the cache update on the main
+    stream; the fill of the chosen experts from pinned host memory on a second stream beside the
+    grouped FFN and combine (which use the step's compute_slot); the streams join at the end of the
+    step.  Logits change every step over one Zipf popularity order.  Printed as its own JSON line:
+    value = bytes the fill kernel moved per second of its own duration (the dominant kernel here,
+    bound by the host link)."""
+    full_w = w.replace(n_resident=None, shared=False)
+    log(f"cache: {w.name} T={T} E={w.E} slots={n_slots} max_loads={max_loads}; packing {w.E} experts")
+    c = synth.make_bank(full_w, 0, device="cuda")
+    full = ft.ft_moe_pack_bank(c.fmt, w.E, c.d, c.I, c.w13, c.w2, c.s13, c.s2)
+    del c
+    src = full.to_pinned_host()
+    del full
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    dst = ft.DeviceBank.empty(w.fmt, n_slots, w.d, w.I)
+    cache = ft.ExpertCache(w.E, n_slots, max_loads)
+    n_seq = warmup + steps
+    logits = [synth.step_logits(w, i, T, device="cuda") for i in range(n_seq)]
+    x = synth.activations(w, 0, T, device="cuda")
+    k, E = w.k, w.E
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    gather = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pws = torch.empty(max(ft.ft_moe_permute_workspace(T, E, k), 16), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T * k, w.d, dtype=torch.bfloat16, device="cuda")
+    fws = torch.empty(max(ft.ft_moe_grouped_ffn_workspace(dst, T, E, k), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, w.d, dtype=torch.float32, device="cuda")
+    mask = torch.empty(T, dtype=torch.int32, device="cuda")
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    nl_hist = torch.zeros(n_seq, dtype=torch.int32, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    marks = [(ev(), ev(), ev(), ev(), ev()) for _ in range(n_seq)]
+
+    def step(i):
+        t0, f0, f1, g0, g1 = marks[i]
+        t0.record(main)
+        ft.ft_moe_route(logits[i], k, ids=ids, w=wt)
+        ft.ft_moe_permute(ids, E, counts=counts, offsets=offsets, gather=gather, inv=inv, ws=pws)
+        cs, _, nl = cache.update(counts)
+        side.wait_stream(main)
+        f0.record(side)
+        cache.fill(src, dst, stream=side)
+        f1.record(side)
+        g0.record(main)
+        ft.ft_moe_grouped_ffn(dst, cs, x, k, offsets, gather, y_sorted=y, ws=fws)
+        ft.ft_moe_combine(y, None, ids, wt, inv, cs, w.d, out=out, residual_mask=mask)
+        g1.record(main)
+        main.wait_stream(side)
+        nl_hist[i:i + 1].copy_(nl)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(main)
+    for i in range(warmup, n_seq):
+        step(i)
+    b.record(main)
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) * 1e3 / steps
+    fill_us = sum(marks[i][1].elapsed_time(marks[i][2]) for i in range(warmup, n_seq)) * 1e3 / steps
+    ffn_us = sum(marks[i][3].elapsed_time(marks[i][4]) for i in range(warmup, n_seq)) * 1e3 / steps
+    nls = nl_hist[warmup:].cpu().numpy()
+    per_expert = sum(ft.ft_moe_bank_bytes(w.fmt, 1, w.d, w.I, which) for which in range(4))
+    moved = float(nls.sum()) * per_expert
+    gbs = moved / (fill_us * steps * 1e-6) / 1e9 if fill_us > 0 else 0.0
+    log(f"cache: {nls.sum()} loads over {steps} steps ({moved / 1e6:.1f} MB); fill {fill_us:.1f} us/step, "
+        f"FFN+combine {ffn_us:.1f} us/step, whole step {step_us:.1f} us")
+    roof = {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+            "kernel": "cache_fill_kernel (pinned host bank -> device slots, 32 blocks)",
+            "bytes_per_expert": per_expert, "loads": int(nls.sum()), "fill_us_per_step": round(fill_us, 2),
+            "ffn_combine_us_per_step": round(ffn_us, 2), "step_us": round(step_us, 2)}
+    print(json.dumps({"metric": "expert streaming bandwidth (fill kernel)", "value": round(gbs, 2), "unit": "GB/s",
+                      "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(step_us / 1e3, 5),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                      "dtype": synth.FMT_NAMES[w.fmt], "data": "synthetic (seeded)",
+                      "config": {"workload": f"cache/{w.name}", "T": T, "E": E, "k": k, "d": w.d, "I": w.I,
+                                 "slots": n_slots, "max_loads": max_loads},
+                      "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +330,9 @@ def main():
                     help="first run the counter-calibration copy kernel over BYTES")
     ap.add_argument("--route-proj", action="store_true",
                     help="time ft_moe_route_proj (router projection + top-k) on the workload's shape instead")
+    ap.add_argument("--cache", type=int, default=0, metavar="SLOTS",
+                    help="time layer steps with the LRU expert cache over SLOTS device slots instead")
+    ap.add_argument("--max-loads", type=int, default=4, help="experts the cache may load per step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -260,6 +353,9 @@ def main():
     decode = T <= 64
     if args.route_proj:
         bench_route_proj(w, T, args.steps, args.warmup)
+        return
+    if args.cache:
+        bench_cache(w, T, args.steps, args.warmup, args.cache, args.max_loads)
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)

@@ -229,6 +229,58 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
                  uint16_t* y_shared, void* out, uint32_t* residual_mask, void* ws, size_t ws_bytes,
                  int flags, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- expert cache */
+
+/*
+ * One step of the global LRU expert cache (FreeToken article on zuoshipin.com, mechanism four:
+ * frequently used experts stay on the GPU under one global LRU policy; FreeToken walk-through,
+ * section 五: hot experts resident on the GPU, cold experts in pinned host memory; FreeToken paper
+ * summary, key insights: an LRU that CUDA Graphs can hold).  Everything it reads and writes is in
+ * device memory, so a step needs no host round trip.
+ *
+ * counts [E] int32: tokens per expert in this step (the `counts` of ft_moe_permute); an expert
+ * with counts > 0 is demanded.  Cache state, updated in place (caller-owned device memory, kept
+ * between steps; start: every entry -1, last_use and tick 0, or any consistent preload):
+ *   slot_of_expert [E] int32    slot of each expert in the device bank, -1 = not resident;
+ *   expert_of_slot [n_slots]    expert held by each slot, -1 = empty (the inverse of the former);
+ *   last_use [n_slots] uint32   step at which the slot was last used;  tick [1] uint32: step clock.
+ * One step, at clock now = tick + 1:
+ *   - each demanded resident expert marks its slot used now;
+ *   - the demanded absent experts, by counts descending then expert index, are paired with the
+ *     slots whose expert is not demanded, empty slots first, then by last_use ascending, then slot
+ *     index; min(#absent, #such slots, max_loads) pairs are made.  Each pair evicts the slot's
+ *     expert (its slot_of_expert becomes -1), puts the new expert there and marks the slot used now;
+ *   - compute_slot [E] int32 (out): an expert's slot when it was resident before the step and still
+ *     is, else -1.  Pass it as the slot table of this step's ft_moe_grouped_ffn and ft_moe_combine:
+ *     the experts being loaded are then left to the residual mask in this step and serve from the
+ *     next one;
+ *   - loads [max_loads][2] int32 (out): (expert, slot) per load in pairing order; n_loads [1] int32
+ *     (out): their number.  Copy them with ft_moe_cache_fill before the next step's update.
+ * Limits: 1 <= E <= 1024, 1 <= n_slots <= 1024, 0 <= max_loads <= n_slots.  Pointers 16-byte
+ * aligned.  Entries of the tables outside their ranges are read as -1.  last_use wraps after 2^32
+ * steps.  One kernel launch (one block); none allocates or syncs.
+ */
+int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, int32_t* slot_of_expert,
+                        int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
+                        int32_t* loads, int32_t* n_loads, hipStream_t stream);
+
+/*
+ * Copy the experts listed by ft_moe_cache_update from the bank that holds every expert (`src`,
+ * expert e in slot e, normally in pinned host memory: the walk-through's cold tier) into their slots
+ * of the device bank `dst` (same fmt, d and I): every array of the format, byte for byte.  The load
+ * list is read on the device (loads [max_loads][2], n_loads [1]: the update's outputs), so the copy
+ * is enqueued without knowing it on the host; run it on a second stream beside the step's grouped
+ * FFN (the walk-through's copies overlapped with compute): the slots it writes hold no expert that
+ * this step's compute_slot names.  The caller orders the streams: the fill after the update, and
+ * the next step's update and FFN after the fill.
+ * `src` and `dst` are host pointers to bank descriptions; src's arrays are pinned host memory
+ * (hipHostMalloc; the kernel reads it over the bus) or device memory; pageable host memory is
+ * refused (FT_E_INVAL).  Entries naming an expert >= src->n_slots or a slot >= dst->n_slots are
+ * skipped.  max_loads = 0 is a no-op.
+ */
+int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int32_t* loads, const int32_t* n_loads,
+                      int max_loads, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------ set-up calls */
 
 /*

@@ -62,6 +62,8 @@ def _load():
         "ft_moe_dequant": ([BP, i, i, P, P], i),
         "ft_moe_layer_workspace": ([BP, i, i, i, i, i], sz),
         "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
+        "ft_moe_cache_update": ([P, i, i, i, P, P, P, P, P, P, P, P], i),
+        "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -75,7 +77,8 @@ lib = _load()
 EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_route_proj_workspace",
             "ft_moe_route_proj", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
-            "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer")
+            "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer",
+            "ft_moe_cache_update", "ft_moe_cache_fill")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -128,6 +131,18 @@ class DeviceBank:
             arrs.append(torch.empty(n, dtype=torch.uint8, device=device) if n else None)
         return DeviceBank(fmt, n_slots, d, I, *arrs)
 
+    def to_pinned_host(self) -> "DeviceBank":
+        """The same bank copied into pinned host memory (the cold tier ft_moe_cache_fill reads)."""
+        arrs = []
+        for t in (self.w13, self.w2, self.s13, self.s2):
+            if t is None:
+                arrs.append(None)
+                continue
+            h = torch.empty(t.numel(), dtype=torch.uint8, pin_memory=True)
+            h.copy_(t.view(torch.uint8).reshape(-1))
+            arrs.append(h)
+        return DeviceBank(self.fmt, self.n_slots, self.d, self.I, *arrs)
+
 
 def ft_moe_bank_bytes(fmt: int, n_slots: int, d: int, I: int, which: int) -> int:
     return lib.ft_moe_bank_bytes(fmt, n_slots, d, I, which)
@@ -146,6 +161,50 @@ def ft_moe_dequant(bank: DeviceBank, slot: int, which: int, out=None, stream=Non
     out = torch.empty(rows, K, dtype=torch.float32, device=bank.w13.device) if out is None else out
     _check(lib.ft_moe_dequant(bank.ref, slot, which, _ptr(out), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------------------------- expert cache
+
+def ft_moe_cache_update(counts, slot_of_expert, expert_of_slot, last_use, tick, max_loads: int, compute_slot=None,
+                        loads=None, n_loads=None, stream=None):
+    """One step of the global LRU expert cache on device-resident state (int32 tensors; last_use and
+    tick hold uint32 bits).  Returns (compute_slot [E], loads [max_loads][2], n_loads [1])."""
+    E, S = counts.shape[0], expert_of_slot.shape[0]
+    dev = counts.device
+    compute_slot = torch.empty(E, dtype=torch.int32, device=dev) if compute_slot is None else compute_slot
+    loads = torch.empty(max(max_loads, 1), 2, dtype=torch.int32, device=dev) if loads is None else loads
+    n_loads = torch.empty(1, dtype=torch.int32, device=dev) if n_loads is None else n_loads
+    _check(lib.ft_moe_cache_update(_ptr(counts), E, S, max_loads, _ptr(slot_of_expert), _ptr(expert_of_slot),
+                                   _ptr(last_use), _ptr(tick), _ptr(compute_slot), _ptr(loads), _ptr(n_loads),
+                                   _stream(stream)))
+    return compute_slot, loads, n_loads
+
+
+def ft_moe_cache_fill(src: DeviceBank, dst: DeviceBank, loads, n_loads, max_loads: int, stream=None):
+    """Copy the listed experts from `src` (every expert, pinned host or device memory) into `dst`."""
+    _check(lib.ft_moe_cache_fill(src.ref, dst.ref, _ptr(loads), _ptr(n_loads), max_loads, _stream(stream)))
+
+
+class ExpertCache:
+    """Device state of the global LRU expert cache over slots 0..n_slots-1 of a device bank, and the
+    buffers one step writes.  Starts with every slot empty."""
+
+    def __init__(self, E: int, n_slots: int, max_loads: int, device="cuda"):
+        self.E, self.n_slots, self.max_loads = E, n_slots, max_loads
+        self.slot_of_expert = torch.full((E,), -1, dtype=torch.int32, device=device)
+        self.expert_of_slot = torch.full((n_slots,), -1, dtype=torch.int32, device=device)
+        self.last_use = torch.zeros(n_slots, dtype=torch.int32, device=device)
+        self.tick = torch.zeros(1, dtype=torch.int32, device=device)
+        self.compute_slot = torch.empty(E, dtype=torch.int32, device=device)
+        self.loads = torch.empty(max(max_loads, 1), 2, dtype=torch.int32, device=device)
+        self.n_loads = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def update(self, counts, stream=None):
+        return ft_moe_cache_update(counts, self.slot_of_expert, self.expert_of_slot, self.last_use, self.tick,
+                                   self.max_loads, self.compute_slot, self.loads, self.n_loads, stream)
+
+    def fill(self, src: DeviceBank, dst: DeviceBank, stream=None):
+        ft_moe_cache_fill(src, dst, self.loads, self.n_loads, self.max_loads, stream)
 
 
 # ------------------------------------------------------------------------------------- the four calls

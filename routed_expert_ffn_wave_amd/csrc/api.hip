@@ -445,6 +445,100 @@ int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hip
   }
 }
 
+int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, int32_t* slot_of_expert,
+                        int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
+                        int32_t* loads, int32_t* n_loads, hipStream_t stream) {
+  try {
+    REQUIRE(E >= 1 && E <= 1024, FT_E_INVAL, "E must be in [1, 1024] (got %d)", E);
+    REQUIRE(n_slots >= 1 && n_slots <= 1024, FT_E_INVAL, "n_slots must be in [1, 1024] (got %d)", n_slots);
+    REQUIRE(max_loads >= 0 && max_loads <= n_slots, FT_E_INVAL, "max_loads must be in [0, n_slots] (got %d)",
+            max_loads);
+    CHECK_PTR(counts, "counts");
+    CHECK_PTR(slot_of_expert, "slot_of_expert");
+    CHECK_PTR(expert_of_slot, "expert_of_slot");
+    CHECK_PTR(last_use, "last_use");
+    CHECK_PTR(tick, "tick");
+    CHECK_PTR(compute_slot, "compute_slot");
+    CHECK_PTR(loads, "loads");
+    CHECK_PTR(n_loads, "n_loads");
+    return hip_status(ftk::launch_cache_update(counts, E, n_slots, max_loads, slot_of_expert, expert_of_slot,
+                                               last_use, tick, compute_slot, loads, n_loads, stream),
+                      "ft_moe_cache_update launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_cache_update: unexpected exception");
+  }
+}
+
+// Device-visible address of a source-bank array: pinned host memory (its mapped address) or device
+// memory (as is).  Pageable host memory is refused.
+static int source_view(const void* p, const char* name, const uint8_t** out) {
+  hipPointerAttribute_t attr{};
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FT_E_INVAL, "%s is neither pinned host memory nor device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = (const uint8_t*)p;
+    return FT_OK;
+  }
+  REQUIRE(attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr, FT_E_INVAL,
+          "%s is neither pinned host memory nor device memory", name);
+  const uint8_t* dev = (const uint8_t*)attr.devicePointer;
+  *out = attr.hostPointer ? dev + ((const uint8_t*)p - (const uint8_t*)attr.hostPointer) : dev;
+  return FT_OK;
+}
+
+constexpr int kFillBlocks = 32;  // enough copies in flight for a PCIe link; leaves the CUs to the FFN
+
+int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int32_t* loads, const int32_t* n_loads,
+                      int max_loads, hipStream_t stream) {
+  try {
+    int rc = check_bank(src);
+    if (rc) return rc;
+    rc = check_bank(dst);
+    if (rc) return rc;
+    REQUIRE(src->fmt == dst->fmt && src->d == dst->d && src->I == dst->I, FT_E_INVAL,
+            "source and destination banks differ in format or shape");
+    REQUIRE(max_loads >= 0 && max_loads <= dst->n_slots, FT_E_INVAL, "max_loads must be in [0, dst->n_slots] (got %d)",
+            max_loads);
+    if (max_loads == 0) return ok();
+    CHECK_PTR(loads, "loads");
+    CHECK_PTR(n_loads, "n_loads");
+    const int fmt = dst->fmt, d = dst->d, I = dst->I;
+    ftk::CacheFillArgs a{};
+    const uint8_t* sv[4] = {nullptr, nullptr, nullptr, nullptr};
+    rc = source_view(src->w13, "src->w13", &sv[0]);
+    if (rc == FT_OK) rc = source_view(src->w2, "src->w2", &sv[1]);
+    if (rc == FT_OK && fmt != FT_W_BF16) rc = source_view(src->s13, "src->s13", &sv[2]);
+    if (rc == FT_OK && fmt != FT_W_BF16) rc = source_view(src->s2, "src->s2", &sv[3]);
+    if (rc) return rc;
+    a.seg[0] = {sv[0], (uint8_t*)dst->w13, (long long)ft_moe_bank_bytes(fmt, 1, d, I, 0)};
+    a.seg[1] = {sv[1], (uint8_t*)dst->w2, (long long)ft_moe_bank_bytes(fmt, 1, d, I, 1)};
+    a.nseg = 2;
+    if (fmt == FT_W_NVFP4) {  // per-slot block scales, then one matrix scale per slot after every slot's blocks
+      const long long b13 = 2LL * I * (d / 32) * 2, b2 = (long long)d * (I / 32) * 2;
+      a.seg[2] = {sv[2], (uint8_t*)dst->s13, b13};
+      a.seg[3] = {sv[3], (uint8_t*)dst->s2, b2};
+      a.seg[4] = {sv[2] + b13 * src->n_slots, (uint8_t*)dst->s13 + b13 * dst->n_slots, 4};
+      a.seg[5] = {sv[3] + b2 * src->n_slots, (uint8_t*)dst->s2 + b2 * dst->n_slots, 4};
+      a.nseg = 6;
+    } else if (fmt != FT_W_BF16) {
+      a.seg[2] = {sv[2], (uint8_t*)dst->s13, (long long)ft_moe_bank_bytes(fmt, 1, d, I, 2)};
+      a.seg[3] = {sv[3], (uint8_t*)dst->s2, (long long)ft_moe_bank_bytes(fmt, 1, d, I, 3)};
+      a.nseg = 4;
+    }
+    a.n_src = src->n_slots;
+    a.n_dst = dst->n_slots;
+    a.max_loads = max_loads;
+    a.loads = loads;
+    a.n_loads = n_loads;
+    return hip_status(ftk::launch_cache_fill(a, kFillBlocks, stream), "ft_moe_cache_fill launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_cache_fill: unexpected exception");
+  }
+}
+
 size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
   if (bank == nullptr || check_tek(T, E, k) != FT_OK || check_bank_shape(bank->fmt, bank->n_slots, bank->d, bank->I)) {
     g_err[0] = 0;

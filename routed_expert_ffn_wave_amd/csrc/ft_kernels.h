@@ -32,6 +32,23 @@ size_t route_proj_workspace_bytes(int T);
 hipError_t launch_route_proj(const uint16_t* x, const uint16_t* wr, int T, int d, int E, int k, float* logits,
                              int32_t* ids, float* w, void* ws, hipStream_t s);
 
+// global LRU expert cache: one bookkeeping step (E, S <= 1024) and the copy of the chosen experts
+hipError_t launch_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t* slot_of_expert,
+                               int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
+                               int32_t* loads, int32_t* n_loads, hipStream_t s);
+struct CacheFillSeg {
+  const uint8_t* src;  // expert e's bytes at src + e * bytes (device-visible address of pinned host memory)
+  uint8_t* dst;        // slot s's bytes at dst + s * bytes
+  long long bytes;     // a multiple of 4
+};
+struct CacheFillArgs {
+  CacheFillSeg seg[6];
+  int nseg, n_src, n_dst, max_loads;
+  const int32_t* loads;    // [max_loads][2] (expert, slot)
+  const int32_t* n_loads;  // [1]
+};
+hipError_t launch_cache_fill(const CacheFillArgs& a, int blocks, hipStream_t s);
+
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);

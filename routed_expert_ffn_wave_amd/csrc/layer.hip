@@ -370,7 +370,6 @@ static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   constexpr int NT = LAYER_NT;
   auto kern = layer_decode_kernel<FMT, WPB, NT, VPL, OUT_BF16>;
   const FfnArgs& a = L.f;
-  const int K = a.d > a.I ? a.d : a.I;
   const size_t lds = ((layer_meta_ints(a.T, a.E, a.k, NT) * 4 + 15) & ~(size_t)15) +
                      layer_union_bytes(FMT, a.d, a.I, NT, WPB);
   static int resident_per_cu = -1;

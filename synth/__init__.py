@@ -130,6 +130,26 @@ def logits(w: Workload, layer: int = 0, T: int | None = None, device="cpu") -> t
     return L[:T].contiguous()
 
 
+def step_logits(w: Workload, step: int, T: int | None = None, device="cpu") -> torch.Tensor:
+    """Router logits [T][E] of one step of a stream of steps: fresh N(0,1) per step plus one Zipf
+    popularity bias for the whole stream (the first layer's), so popular experts recur."""
+    T = w.T if T is None else T
+    g = _gen(device, w.wid, 0, STREAM_LOGITS, 1 + step)
+    L = torch.randn(T, w.E, generator=g, device=device, dtype=torch.float32)
+    return (L + zipf_bias(w, 0).to(device)).contiguous()
+
+
+def zipf_counts(E: int, T: int, k: int, seed: int, step: int) -> np.ndarray:
+    """int32 [E] tokens per expert of one step: each of T tokens picks k distinct experts with
+    probability proportional to 1/rank over a seeded popularity order (the same for every step)."""
+    order = np.random.default_rng([seed, 0]).permutation(E)
+    p = 1.0 / np.arange(1, E + 1)
+    p /= p.sum()
+    rng = np.random.default_rng([seed, 1 + step])
+    ids = np.concatenate([order[rng.choice(E, size=k, replace=False, p=p)] for _ in range(T)])
+    return np.bincount(ids, minlength=E).astype(np.int32)
+
+
 def activations(w: Workload, layer: int = 0, T: int | None = None, device="cpu") -> torch.Tensor:
     """bf16 activations [T][d] drawn N(0,1) in fp32 and rounded to nearest even."""
     T = w.T if T is None else T

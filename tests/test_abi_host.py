@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -52,6 +52,35 @@ def test_route_proj_validation():
     _err(L.ft_moe_route_proj(A, A, 40, 64, 8, 2, B, B, B, B, ws, None), ft.FT_E_WORKSPACE, "workspace")
     assert ft.lib.ft_moe_route_proj_workspace(40) == 3 * 16 * 4
     assert L.ft_moe_route_proj(None, None, 0, 64, 8, 2, None, None, None, None, 0, None) == ft.FT_OK
+
+
+def test_cache_update_validation():
+    L = ft.lib
+    args = lambda E, S, ml: (A, E, S, ml, A, A, A, A, A, A, A)
+    _err(L.ft_moe_cache_update(*args(0, 4, 1), None), ft.FT_E_INVAL, "E must be")
+    _err(L.ft_moe_cache_update(*args(1025, 4, 1), None), ft.FT_E_INVAL, "E must be")
+    _err(L.ft_moe_cache_update(*args(8, 0, 0), None), ft.FT_E_INVAL, "n_slots must be")
+    _err(L.ft_moe_cache_update(*args(8, 1025, 1), None), ft.FT_E_INVAL, "n_slots must be")
+    _err(L.ft_moe_cache_update(*args(8, 4, 5), None), ft.FT_E_INVAL, "max_loads must be")
+    _err(L.ft_moe_cache_update(*args(8, 4, -1), None), ft.FT_E_INVAL, "max_loads must be")
+    _err(L.ft_moe_cache_update(None, 8, 4, 1, A, A, A, A, A, A, A, None), ft.FT_E_INVAL, "counts is null")
+    _err(L.ft_moe_cache_update(A, 8, 4, 1, A, A, MIS, A, A, A, A, None), ft.FT_E_INVAL, "last_use is not 16-byte")
+    _err(L.ft_moe_cache_update(A, 8, 4, 1, A, A, A, A, A, None, A, None), ft.FT_E_INVAL, "loads is null")
+
+
+def test_cache_fill_validation():
+    L = ft.lib
+    bank = lambda fmt, n, d, I: ft.ft_moe_bank(fmt, n, d, I, 0x10000, 0x20000, 0x30000, 0x40000)
+    src, dst = bank(ft.FT_W_Q4_0, 16, 256, 128), bank(ft.FT_W_Q4_0, 4, 256, 128)
+    ref = ctypes.byref
+    _err(L.ft_moe_cache_fill(ref(src), ref(bank(ft.FT_W_MXFP4, 4, 256, 128)), A, A, 2, None), ft.FT_E_INVAL,
+         "differ in format or shape")
+    _err(L.ft_moe_cache_fill(ref(src), ref(bank(ft.FT_W_Q4_0, 4, 256, 192)), A, A, 2, None), ft.FT_E_INVAL,
+         "differ in format or shape")
+    _err(L.ft_moe_cache_fill(ref(src), ref(dst), A, A, 5, None), ft.FT_E_INVAL, "max_loads must be")
+    _err(L.ft_moe_cache_fill(ref(src), ref(dst), None, A, 2, None), ft.FT_E_INVAL, "loads is null")
+    _err(L.ft_moe_cache_fill(None, ref(dst), A, A, 2, None), ft.FT_E_INVAL, "bank is null")
+    assert L.ft_moe_cache_fill(ref(src), ref(dst), None, None, 0, None) == ft.FT_OK
 
 
 def _err(rc, code, pattern):
