@@ -303,7 +303,7 @@ def bench_cache(w: synth.Workload, T: int, steps: int, warmup: int, n_slots: int
         f"FFN+combine {ffn_us:.1f} us/step, whole step {step_us:.1f} us")
     roof = {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
-            "kernel": "cache_fill_kernel (pinned host bank -> device slots, 32 blocks)",
+            "kernel": "cache_fill_kernel (pinned host bank -> device slots, 8 blocks)",
             "bytes_per_expert": per_expert, "loads": int(nls.sum()), "fill_us_per_step": round(fill_us, 2),
             "ffn_combine_us_per_step": round(ffn_us, 2), "step_us": round(step_us, 2)}
     print(json.dumps({"metric": "expert streaming bandwidth (fill kernel)", "value": round(gbs, 2), "unit": "GB/s",

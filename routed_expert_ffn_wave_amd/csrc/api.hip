@@ -489,7 +489,7 @@ static int source_view(const void* p, const char* name, const uint8_t** out) {
   return FT_OK;
 }
 
-constexpr int kFillBlocks = 32;  // enough copies in flight for a PCIe link; leaves the CUs to the FFN
+constexpr int kFillBlocks = 8;  // 128 KiB in flight saturate the host link; every other CU is left to the FFN
 
 int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int32_t* loads, const int32_t* n_loads,
                       int max_loads, hipStream_t stream) {

@@ -54,7 +54,9 @@ __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32
                                                                        int32_t* __restrict__ n_loads) {
   __shared__ int cnt[CACHE_THREADS], soe[CACHE_THREADS], eos[CACHE_THREADS];
   __shared__ uint32_t lu[CACHE_THREADS];
-  __shared__ int list[CACHE_THREADS];  // the misses, later the idle slots, in index order
+  // ordering keys of the misses, later of the idle slots, compacted in index order; a smaller key
+  // ranks first and no two keys are equal, so a key's rank is the number of smaller keys
+  __shared__ unsigned long long keys[CACHE_THREADS];
   __shared__ int miss_by_rank[CACHE_THREADS], slot_by_rank[CACHE_THREADS];
   __shared__ int wave_tot[CACHE_THREADS / 64];
   const int t = threadIdx.x;
@@ -77,15 +79,14 @@ __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32
   int nmiss = 0;
   const bool is_miss = t < E && cnt[t] > 0 && before < 0;
   const int pm = block_compact(is_miss, wave_tot, nmiss);
-  if (is_miss) list[pm] = t;
+  // more tokens first, then the lower expert index
+  const unsigned long long mkey = ((unsigned long long)(uint32_t)(0x7fffffff - (is_miss ? cnt[t] : 0)) << 32) | t;
+  if (is_miss) keys[pm] = mkey;
   __syncthreads();
-  if (is_miss) {  // rank: more tokens first, then the lower expert index
-    const int c = cnt[t];
+  if (is_miss) {
     int r = 0;
-    for (int j = 0; j < nmiss; ++j) {
-      const int o = list[j], co = cnt[o];
-      r += (co > c) || (co == c && o < t);
-    }
+#pragma unroll 8
+    for (int j = 0; j < nmiss; ++j) r += keys[j] < mkey;
     miss_by_rank[r] = t;
   }
   __syncthreads();
@@ -94,17 +95,15 @@ __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32
   const int v = t < S ? eos[t] : -1;
   const bool is_idle = t < S && (v < 0 || cnt[v] == 0);
   const int pi = block_compact(is_idle, wave_tot, nidle);
-  if (is_idle) list[pi] = t;
+  // empty first, then the earlier last use, then the lower slot (slot < 1024: 10 bits)
+  const unsigned long long ikey =
+      ((unsigned long long)(v >= 0) << 42) | ((unsigned long long)(t < S ? lu[t] : 0u) << 10) | t;
+  if (is_idle) keys[pi] = ikey;
   __syncthreads();
-  if (is_idle) {  // rank: empty first, then the earlier last use, then the lower slot
-    const int occ = v >= 0;
-    const uint32_t l = lu[t];
+  if (is_idle) {
     int r = 0;
-    for (int j = 0; j < nidle; ++j) {
-      const int o = list[j], oo = eos[o] >= 0;
-      const uint32_t lo = lu[o];
-      r += (oo < occ) || (oo == occ && (lo < l || (lo == l && o < t)));
-    }
+#pragma unroll 8
+    for (int j = 0; j < nidle; ++j) r += keys[j] < ikey;
     slot_by_rank[r] = t;
   }
   __syncthreads();
