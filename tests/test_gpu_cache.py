@@ -208,3 +208,89 @@ def test_cache_streamed_layer_steps(ft, fmt):
         compare_layer(li, g, label=f"streamed step {step} ({int(nl.item())} loads, "
                                    f"{int((cs_ref >= 0).sum())} resident for compute)")
     _check_state(cache, st, "final")
+
+
+def test_cache_step_graph_replay(ft):
+    """A whole cache step (route, permute, cache update; the fill on a second stream beside the
+    grouped FFN and combine) captured once into a HIP graph and replayed step after step with new
+    logits copied in between: after every replay the outputs and the cache state equal those of the
+    same steps run eagerly on a second cache from the same start, bit for bit."""
+    E, S, T, k, ml, steps = 16, 6, 16, 4, 3, 6
+    w = synth.Workload("cache_graph", 85, T=T, d=256, E=E, k=k, I=128, fmt=synth.FMT_Q4_0, zipf=True)
+    log("cache step graph replay")
+    full = device_bank(synth.make_bank(w, 0))
+    src = full.to_pinned_host()
+    x = synth.activations(w, 0, T).cuda()
+    seq = [synth.step_logits(w, i, T).cuda() for i in range(steps)]
+    dev = "cuda"
+
+    def make():
+        dst = ft.DeviceBank.empty(w.fmt, S, w.d, w.I)
+        cache = ft.ExpertCache(E, S, ml)
+        b = dict(logits=torch.empty(T, E, dtype=torch.float32, device=dev),
+                 ids=torch.empty(T, k, dtype=torch.int32, device=dev),
+                 w=torch.empty(T, k, dtype=torch.float32, device=dev),
+                 counts=torch.empty(E, dtype=torch.int32, device=dev),
+                 offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 gather=torch.empty(T * k, dtype=torch.int32, device=dev),
+                 inv=torch.empty(T * k, dtype=torch.int32, device=dev),
+                 pws=torch.empty(max(ft.ft_moe_permute_workspace(T, E, k), 16), dtype=torch.uint8, device=dev),
+                 y=torch.empty(T * k, w.d, dtype=torch.bfloat16, device=dev),
+                 fws=torch.empty(max(ft.ft_moe_grouped_ffn_workspace(dst, T, E, k), 256), dtype=torch.uint8,
+                                 device=dev),
+                 out=torch.empty(T, w.d, dtype=torch.float32, device=dev),
+                 mask=torch.empty(T, dtype=torch.int32, device=dev))
+        return dst, cache, b, torch.cuda.Stream()
+
+    def step(dst, cache, b, side):
+        main = torch.cuda.current_stream()
+        ft.ft_moe_route(b["logits"], k, ids=b["ids"], w=b["w"])
+        ft.ft_moe_permute(b["ids"], E, counts=b["counts"], offsets=b["offsets"], gather=b["gather"], inv=b["inv"],
+                          ws=b["pws"])
+        cs, _, _ = cache.update(b["counts"])
+        side.wait_stream(main)
+        cache.fill(src, dst, stream=side)
+        ft.ft_moe_grouped_ffn(dst, cs, x, k, b["offsets"], b["gather"], y_sorted=b["y"], ws=b["fws"])
+        ft.ft_moe_combine(b["y"], None, b["ids"], b["w"], b["inv"], cs, w.d, out=b["out"], residual_mask=b["mask"])
+        main.wait_stream(side)
+
+    def snapshot(cache, b):
+        return [t.clone() for t in (b["out"], b["mask"], cache.compute_slot, cache.slot_of_expert,
+                                    cache.expert_of_slot, cache.last_use, cache.tick, cache.n_loads)]
+
+    A = make()
+    eager = []
+    for i in range(steps):
+        A[2]["logits"].copy_(seq[i])
+        step(*A)
+        torch.cuda.synchronize()
+        eager.append(snapshot(A[1], A[2]))
+
+    B = make()
+    dst, cache, b, side = B
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm-up outside the capture, then back to the empty start
+        b["logits"].copy_(seq[0])
+        step(*B)
+        torch.cuda.synchronize()
+        cache.slot_of_expert.fill_(-1)
+        cache.expert_of_slot.fill_(-1)
+        cache.last_use.zero_()
+        cache.tick.zero_()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step(*B)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        b["logits"].copy_(seq[i])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot(cache, b)
+        names = ("out", "mask", "compute_slot", "slot_of_expert", "expert_of_slot", "last_use", "tick", "n_loads")
+        for n, g_, e_ in zip(names, got, eager[i]):
+            assert torch.equal(g_, e_), f"replay {i}: {n} differs from the eager step"
+    assert int(cache.tick.item()) == steps
+    log(f"  ok: {steps} replays")
