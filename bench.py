@@ -21,6 +21,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -315,6 +316,75 @@ def bench_cache(w: synth.Workload, T: int, steps: int, warmup: int, n_slots: int
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
+def bench_residual(w: synth.Workload, T: int, steps: int, warmup: int, threads: int):
+    """The layer with its cold experts: the device layer on the workload's resident bank, then the
+    masked pairs on the host cores from the bank of every expert in host memory, merged into the
+    device output.  Own JSON line: value = host residual time per layer call; roofline = bytes of
+    the cold experts' weights the host decoded per second against the host's read bandwidth measured
+    in the same process (a multi-threaded sum over 2 GiB)."""
+    import time as _time
+    li = synth.layer_inputs(w, 0, T, device="cuda")
+    bank = ft.ft_moe_pack_bank(li.bank.fmt, li.bank.n_slots, w.d, w.I, li.bank.w13, li.bank.w2, li.bank.s13,
+                               li.bank.s2)
+    log(f"residual: {w.name} T={T}; packing the {w.E} experts for the host bank")
+    c = synth.make_bank(w.replace(n_resident=None, shared=False), 0, device="cuda")
+    host = ft.ft_moe_pack_bank(c.fmt, w.E, w.d, w.I, c.w13, c.w2, c.s13, c.s2).to_pinned_host()
+    del c
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layer = ft.MoELayer(bank, li.slot_of_expert, w.k, T, shared_slot=w.shared_slot)
+    x_host = li.x.cpu()
+    res_dev = torch.empty(T, w.d, dtype=torch.float32, device="cuda")
+    torch.set_num_threads(threads)
+    probe = torch.ones(1 << 29, dtype=torch.float32)
+    probe.sum()
+    t0 = _time.perf_counter()
+    for _ in range(3):
+        probe.sum()
+    host_gbs = 3 * probe.numel() * 4 / (_time.perf_counter() - t0) / 1e9
+    del probe
+    per_expert = sum(ft.ft_moe_bank_bytes(w.fmt, 1, w.d, w.I, which) for which in range(4))
+
+    def step():
+        t_a = _time.perf_counter()
+        out, mask = layer.forward(li.logits, li.x)
+        ids, wt, m = layer.ids[:T].cpu(), layer.w[:T].cpu(), mask.cpu()
+        t_b = _time.perf_counter()
+        res = ft.ft_moe_residual_host(host, x_host, ids, wt, m, n_threads=threads)
+        t_c = _time.perf_counter()
+        res_dev.copy_(res, non_blocking=False)
+        ft.ft_moe_residual_add(out, res_dev)
+        torch.cuda.synchronize()
+        t_d = _time.perf_counter()
+        mk = m.numpy().view(np.uint32)
+        cold = {int(ids[t, j]) for t in range(T) for j in range(w.k) if (mk[t] >> j) & 1}
+        pairs = sum(bin(int(v)).count("1") for v in mk)
+        return t_b - t_a, t_c - t_b, t_d - t_c, len(cold), pairs
+
+    for _ in range(max(warmup, 1)):
+        step()
+    r = [step() for _ in range(max(steps, 1))]
+    dev_ms = 1e3 * sum(v[0] for v in r) / len(r)
+    host_ms = 1e3 * sum(v[1] for v in r) / len(r)
+    merge_ms = 1e3 * sum(v[2] for v in r) / len(r)
+    cold, pairs = r[-1][3], r[-1][4]
+    gbs = cold * per_expert / (host_ms * 1e-3) / 1e9
+    log(f"residual: {pairs} cold pairs on {cold} experts; device layer + copies {dev_ms:.2f} ms, host residual "
+        f"{host_ms:.2f} ms ({gbs:.1f} GB/s of weights; host read bandwidth {host_gbs:.1f} GB/s), merge {merge_ms:.2f} ms")
+    roof = {"bound": "host", "achieved": round(gbs, 2), "peak": round(host_gbs, 1), "unit": "GB/s",
+            "frac": round(gbs / host_gbs, 4), "traffic": None,
+            "kernel": f"ft_moe_residual_host ({threads} host threads)", "cold_pairs": pairs, "cold_experts": cold,
+            "bytes_per_expert": per_expert, "device_layer_and_copies_ms": round(dev_ms, 3),
+            "merge_ms": round(merge_ms, 3)}
+    print(json.dumps({"metric": "cold-expert residual on the host", "value": round(host_ms, 3), "unit": "ms/layer",
+                      "n_gpus": 1, "steps": len(r), "warmup": warmup, "ms_per_step": round(dev_ms + host_ms + merge_ms, 3),
+                      "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+                      "dtype": synth.FMT_NAMES[w.fmt], "data": "synthetic (seeded)",
+                      "config": {"workload": f"residual/{w.name}", "T": T, "E": w.E, "k": w.k, "d": w.d, "I": w.I,
+                                 "resident": w.n_resident, "threads": threads},
+                      "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +403,9 @@ def main():
     ap.add_argument("--cache", type=int, default=0, metavar="SLOTS",
                     help="time layer steps with the LRU expert cache over SLOTS device slots instead")
     ap.add_argument("--max-loads", type=int, default=4, help="experts the cache may load per step")
+    ap.add_argument("--residual", action="store_true",
+                    help="time the layer with its cold experts on the host (ft_moe_residual_host) instead")
+    ap.add_argument("--threads", type=int, default=16, help="host threads of the residual path")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -353,6 +426,9 @@ def main():
     decode = T <= 64
     if args.route_proj:
         bench_route_proj(w, T, args.steps, args.warmup)
+        return
+    if args.residual:
+        bench_residual(w, T, args.steps, args.warmup, args.threads)
         return
     if args.cache:
         bench_cache(w, T, args.steps, args.warmup, args.cache, args.max_loads)

@@ -281,6 +281,31 @@ int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads
 int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int32_t* loads, const int32_t* n_loads,
                       int max_loads, hipStream_t stream);
 
+/* ---------------------------------------------------------------------- cold-expert residual */
+
+/*
+ * The pairs the device layer leaves to another path, computed on the host cores (FreeToken
+ * walk-through, section 五: cold experts stay in host memory and run on the CPU beside the GPU;
+ * zuoshipin.com FreeToken article, mechanism two: CPU-GPU co-execution).  For every token t and
+ * slot j with bit j of residual_mask[t] set (the mask ft_moe_combine or ft_moe_layer wrote) and
+ * e = ids[t][j] < host_bank->n_slots: y = SiLU(x[t] Wg_e^T) * (x[t] Wu_e^T) Wd_e^T with fp32 sums,
+ * h and y rounded to bf16 as on the device; then out[t] = sum over those j, in order j, of
+ * w[t][j] * y.  out [T][d] fp32 is overwritten (zero for a token with no such pair).
+ * Everything is host memory: host_bank (a host pointer to a bank description whose arrays are in
+ * host memory, pinned or not, in the device layout of ft_moe_pack_bank, expert e in slot e: the bank
+ * ft_moe_cache_fill reads), x bf16 [T][d], ids [T][k], w [T][k], residual_mask [T], out.  Runs on
+ * n_threads host threads (0: the hardware's thread count, at most 256) and returns when done; it
+ * does not touch the GPU.  Add the result to the device output with ft_moe_residual_add.
+ */
+int ft_moe_residual_host(const ft_moe_bank* host_bank, const uint16_t* x, const int32_t* ids, const float* w,
+                         const uint32_t* residual_mask, int T, int E, int k, float* out, int n_threads);
+
+/*
+ * out[t][c] += residual[t][c] on the device, out fp32 or (FT_OUT_BF16) bf16 rounded to nearest even,
+ * both [T][d] device memory: the merge of the host residual into the layer output.
+ */
+int ft_moe_residual_add(void* out, const float* residual, int T, int d, int flags, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------ set-up calls */
 
 /*

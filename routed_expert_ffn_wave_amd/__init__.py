@@ -64,6 +64,8 @@ def _load():
         "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
         "ft_moe_cache_update": ([P, i, i, i, P, P, P, P, P, P, P, P], i),
         "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
+        "ft_moe_residual_host": ([BP, P, P, P, P, i, i, i, P, i], i),
+        "ft_moe_residual_add": ([P, P, i, i, i, P], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -78,7 +80,7 @@ EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_r
             "ft_moe_route_proj", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
             "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer",
-            "ft_moe_cache_update", "ft_moe_cache_fill")
+            "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -205,6 +207,28 @@ class ExpertCache:
 
     def fill(self, src: DeviceBank, dst: DeviceBank, stream=None):
         ft_moe_cache_fill(src, dst, self.loads, self.n_loads, self.max_loads, stream)
+
+
+# ------------------------------------------------------------------------------------- cold-expert residual
+
+def ft_moe_residual_host(host_bank: DeviceBank, x, ids, w, residual_mask, out=None, n_threads: int = 0,
+                         E: int | None = None):
+    """Host compute of the masked pairs: all arguments host (CPU) tensors; host_bank holds every expert
+    (expert e in slot e) in host memory; E defaults to its slot count.  Returns out fp32 [T][d]."""
+    T, k = ids.shape
+    d = x.shape[1]
+    out = torch.empty(T, d, dtype=torch.float32) if out is None else out
+    E = int(host_bank.n_slots) if E is None else E
+    _check(lib.ft_moe_residual_host(host_bank.ref, _ptr(x), _ptr(ids), _ptr(w), _ptr(residual_mask), T, E, k,
+                                    _ptr(out), n_threads))
+    return out
+
+
+def ft_moe_residual_add(out, residual, flags: int = 0, stream=None):
+    """out += residual on the device (out fp32, or bf16 with FT_OUT_BF16)."""
+    T, d = residual.shape
+    _check(lib.ft_moe_residual_add(_ptr(out), _ptr(residual), T, d, flags, _stream(stream)))
+    return out
 
 
 # ------------------------------------------------------------------------------------- the four calls

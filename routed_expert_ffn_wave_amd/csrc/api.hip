@@ -1,6 +1,7 @@
 // C ABI of the MoE layer (declared in include/ft_moe.h): host-side validation, workspace sizing,
-// path selection and kernel launches on the caller's stream.  No call allocates, synchronises or
-// throws across the ABI.
+// path selection and kernel launches on the caller's stream.  No device call allocates device
+// memory or synchronises, and nothing throws across the ABI; the host residual call computes on the
+// host threads it starts and returns when done.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -8,6 +9,8 @@
 #include <climits>
 #include <cstring>
 #include <exception>
+#include <new>
+#include <thread>
 
 #include "../../include/ft_moe.h"
 #include "ft_kernels.h"
@@ -536,6 +539,47 @@ int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int3
     return hip_status(ftk::launch_cache_fill(a, kFillBlocks, stream), "ft_moe_cache_fill launch");
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_cache_fill: unexpected exception");
+  }
+}
+
+int ft_moe_residual_host(const ft_moe_bank* host_bank, const uint16_t* x, const int32_t* ids, const float* w,
+                         const uint32_t* residual_mask, int T, int E, int k, float* out, int n_threads) {
+  try {
+    int rc = check_tek(T, E, k);
+    if (rc) return rc;
+    rc = check_bank(host_bank);
+    if (rc) return rc;
+    REQUIRE(n_threads >= 0, FT_E_INVAL, "n_threads must be >= 0 (got %d)", n_threads);
+    if (T == 0) return ok();
+    REQUIRE(x != nullptr && ids != nullptr && w != nullptr && residual_mask != nullptr && out != nullptr, FT_E_INVAL,
+            "x, ids, w, residual_mask and out must not be null");
+    int threads = n_threads;
+    if (threads == 0) threads = (int)std::thread::hardware_concurrency();
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    const ft_moe_bank* b = host_bank;
+    ftk::residual_host(b->fmt, b->n_slots, b->d, b->I, (const uint8_t*)b->w13, (const uint8_t*)b->w2,
+                       (const uint8_t*)b->s13, (const uint8_t*)b->s2, x, ids, w, residual_mask, T, E, k, out, threads);
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(FT_E_INTERNAL, "ft_moe_residual_host: out of host memory");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_residual_host: unexpected exception");
+  }
+}
+
+int ft_moe_residual_add(void* out, const float* residual, int T, int d, int flags, hipStream_t stream) {
+  try {
+    REQUIRE(T >= 0, FT_E_INVAL, "T must be >= 0 (got %d)", T);
+    REQUIRE(d > 0 && d % 8 == 0, FT_E_INVAL, "d must be a positive multiple of 8 (got %d)", d);
+    REQUIRE((flags & ~FT_OUT_BF16) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return ok();
+    CHECK_PTR(out, "out");
+    CHECK_PTR(residual, "residual");
+    return hip_status(ftk::launch_residual_add(out, residual, (long long)T * d, (flags & FT_OUT_BF16) != 0, stream),
+                      "ft_moe_residual_add launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_residual_add: unexpected exception");
   }
 }
 

@@ -49,6 +49,13 @@ struct CacheFillArgs {
 };
 hipError_t launch_cache_fill(const CacheFillArgs& a, int blocks, hipStream_t s);
 
+// residual path of the cold experts: host compute of the masked pairs (returns the pair count) and
+// the device add of its result into the layer output
+int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, const uint8_t* w2, const uint8_t* s13,
+                  const uint8_t* s2, const uint16_t* x, const int32_t* ids, const float* w, const uint32_t* mask,
+                  int T, int E, int k, float* out, int threads);
+hipError_t launch_residual_add(void* out, const float* res, long long n, bool out_bf16, hipStream_t s);
+
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);

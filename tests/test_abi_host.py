@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -81,6 +81,72 @@ def test_cache_fill_validation():
     _err(L.ft_moe_cache_fill(ref(src), ref(dst), None, A, 2, None), ft.FT_E_INVAL, "loads is null")
     _err(L.ft_moe_cache_fill(None, ref(dst), A, A, 2, None), ft.FT_E_INVAL, "bank is null")
     assert L.ft_moe_cache_fill(ref(src), ref(dst), None, None, 0, None) == ft.FT_OK
+
+
+def test_residual_validation():
+    L = ft.lib
+    bank = ft.ft_moe_bank(ft.FT_W_Q4_0, 16, 256, 128, 0x10000, 0x20000, 0x30000, 0x40000)
+    ref = ctypes.byref(bank)
+    _err(L.ft_moe_residual_host(ref, A, A, A, A, 4, 16, 0, A, 0), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_residual_host(None, A, A, A, A, 4, 16, 2, A, 0), ft.FT_E_INVAL, "bank is null")
+    _err(L.ft_moe_residual_host(ref, A, A, A, A, 4, 16, 2, A, -1), ft.FT_E_INVAL, "n_threads")
+    _err(L.ft_moe_residual_host(ref, None, A, A, A, 4, 16, 2, A, 0), ft.FT_E_INVAL, "must not be null")
+    assert L.ft_moe_residual_host(ref, None, None, None, None, 0, 16, 2, None, 0) == ft.FT_OK
+    _err(L.ft_moe_residual_add(A, A, 4, 12, 0, None), ft.FT_E_INVAL, "d must be")
+    _err(L.ft_moe_residual_add(A, A, 4, 64, 0x8, None), ft.FT_E_INVAL, "unknown flags")
+    _err(L.ft_moe_residual_add(None, A, 4, 64, 0, None), ft.FT_E_INVAL, "out is null")
+    assert L.ft_moe_residual_add(None, None, 0, 64, 0, None) == ft.FT_OK
+
+
+def test_residual_host_bf16_on_cpu():
+    """The host residual needs no GPU: a bf16 bank laid out by hand in the documented device layout
+    (16-byte chunks interleaved in 64-row blocks; W13 device block b = gate rows 32b.. then up rows)
+    against the fp32 oracle's FFN of the same weights, rounded as the device rounds h and y."""
+    import numpy as np
+    import torch
+    import oracle
+    rng = np.random.default_rng(5)
+    T, d, E, k, I = 5, 128, 3, 2, 64
+    w13 = (rng.standard_normal((E, 2 * I, d)) * 0.05).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, I)) * 0.05).astype(np.float32)
+    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    w13b, w2b = to_bf16(w13), to_bf16(w2)
+
+    def device_layout(mat_bf16, perm_I):  # [E][R][K] bf16 -> interleaved bytes
+        Em, R, K = mat_bf16.shape
+        rows = mat_bf16.reshape(Em * R, K).view(torch.int16).numpy().view(np.uint16)
+        out = np.zeros(Em * R * K, np.uint16)
+        nch = K // 8
+        for g in range(Em * R):
+            slot, L = divmod(g, R)
+            if perm_I:
+                dr = 64 * (L >> 5) + (L & 31) if L < perm_I else 64 * ((L - perm_I) >> 5) + 32 + ((L - perm_I) & 31)
+            else:
+                dr = L
+            G = slot * R + dr
+            for c in range(nch):
+                off = (((G >> 6) * nch + c) * 64 + (G & 63)) * 8
+                out[off:off + 8] = rows[g, 8 * c:8 * c + 8]
+        return torch.from_numpy(out.view(np.uint8).copy())
+
+    a13, a2 = device_layout(w13b, I), device_layout(w2b, 0)
+    hb = ft.DeviceBank(ft.FT_W_BF16, E, d, I, a13, a2)
+    x = to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+    ids = torch.tensor([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0]], dtype=torch.int32)
+    wts = torch.from_numpy(rng.random((T, k)).astype(np.float32))
+    mask = torch.tensor([0b01, 0b11, 0b00, 0b10, 0b01], dtype=torch.int32)
+    got = ft.ft_moe_residual_host(hb, x, ids, wts, mask, n_threads=3).numpy()
+    xf = x.float().numpy()
+    ref = np.zeros((T, d), np.float64)
+    for t in range(T):
+        for j in range(k):
+            if (int(mask[t]) >> j) & 1:
+                e = int(ids[t, j])
+                _, y = oracle.swiglu_ffn(xf[t:t + 1], w13b[e].float().numpy(), w2b[e].float().numpy())
+                ref[t] += float(wts[t, j]) * y[0].astype(np.float64)
+    assert np.array_equal(got[2], np.zeros(d, np.float32))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < 5e-3, rel
 
 
 def _err(rc, code, pattern):
