@@ -332,6 +332,8 @@ class MoELayer:
                  flags: int = FT_PATH_AUTO, out_bf16: bool = False, mode: str = "layer"):
         if mode not in ("layer", "calls"):
             raise ValueError(f"mode must be 'layer' or 'calls', not {mode!r}")
+        if flags & FT_OUT_BF16:  # the output dtype is the layer's own buffer: take the bit from either place
+            out_bf16, flags = True, flags & ~FT_OUT_BF16
         dev = bank.w13.device
         E = slot_of_expert.shape[0]
         self.bank, self.slot_of, self.k, self.T, self.E, self.mode = bank, slot_of_expert, k, T, E, mode

@@ -149,6 +149,18 @@ def test_residual_host_bf16_on_cpu():
     assert rel < 5e-3, rel
 
 
+def test_moelayer_takes_bf16_output_from_flags():
+    """FT_OUT_BF16 given in `flags` makes the layer's own output buffer bf16 (as out_bf16=True does):
+    the layer call would otherwise write bf16 values into an fp32 buffer."""
+    import torch
+    bank = ft.DeviceBank.empty(ft.FT_W_Q4_0, 4, 256, 128, device="cpu")
+    slots = torch.arange(4, dtype=torch.int32)
+    a = ft.MoELayer(bank, slots, 2, 8, flags=ft.FT_OUT_BF16)
+    b = ft.MoELayer(bank, slots, 2, 8, out_bf16=True)
+    assert a.out.dtype == b.out.dtype == torch.bfloat16
+    assert a.flags == b.flags and a.out_flags == b.out_flags == ft.FT_OUT_BF16
+
+
 def _err(rc, code, pattern):
     assert rc == code, (rc, ft.ft_moe_last_error())
     assert re.search(pattern, ft.ft_moe_last_error()), ft.ft_moe_last_error()

@@ -35,7 +35,7 @@ def _case(fmt, T, shared):
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: synth.FMT_NAMES[f])
 def test_residual_completes_the_layer(ft, fmt, out_bf16):
     T = 24
-    w = _case(fmt, T, shared=(fmt == synth.FMT_MXFP4))
+    w = _case(fmt, T, shared=False)
     log(f"residual {synth.FMT_NAMES[fmt]} T={T} out_bf16={out_bf16}")
     li = synth.layer_inputs(w, layer=0, T=T)
     flags = ft.FT_OUT_BF16 if out_bf16 else 0
@@ -55,12 +55,7 @@ def test_residual_completes_the_layer(ft, fmt, out_bf16):
     torch.cuda.synchronize()
     merged = out.float().cpu().numpy()
     full_slots = torch.arange(w.E, dtype=torch.int32)
-    bank_full = canon_all
-    shared_slot = -1
-    if w.shared:   # the shared expert stays on the device; the oracle's full bank gets it as slot E
-        bank_full = synth.make_bank(w.replace(n_resident=None), 0)
-        shared_slot = w.E
-    ora_full = oracle.layer(li.logits, li.x, bank_full, full_slots, w.k, shared_slot=shared_slot, workers=WORKERS)
+    ora_full = oracle.layer(li.logits, li.x, canon_all, full_slots, w.k, workers=WORKERS)
     ora_part = oracle.layer(li.logits, li.x, li.bank, li.slot_of_expert, w.k, shared_slot=w.shared_slot,
                             workers=WORKERS)
     assert np.array_equal(g["mask"], ora_part["mask"])
