@@ -2,8 +2,9 @@
 
     python -m routed_expert_ffn_wave_amd.build
 
-Every HIP source under csrc/ is compiled for gfx950 (object files go to _build/, which is not part
-of the source tree) and linked into routed_expert_ffn_wave_amd/libftmoe.so.  Packed fp32 vector
+Every HIP source under csrc/ is compiled for gfx950, every host-only C++ source (*.cpp, the host
+residual path) with the host compiler (object files go to _build/, which is not part of the source
+tree), and all are linked into routed_expert_ffn_wave_amd/libftmoe.so.  Packed fp32 vector
 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -28,14 +29,21 @@ HIPFLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall"]   # host-only sources (*.cpp)
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *HIPFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *HIPFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{err}")
+        raise RuntimeError(f"{cmd[0]} failed on {os.path.basename(src)}:\n{err}")
     if err.strip():
         print(err, file=sys.stderr)
     return obj
@@ -43,12 +51,12 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     workers = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 8)
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
