@@ -9,8 +9,8 @@
 // j, from the same device-layout bank bytes the expert cache copies to the GPU.
 //
 // Plain C++ (no device code): the inner loops are compiled for AVX-512, AVX2 + FMA and the baseline,
-// and the loader picks the widest the host supports.  Element decoders are branch-free bit formulas
-// so that the compiler vectorises them.
+// and the loader picks the widest the host supports.  Element codes are decoded through tables built
+// once from the formats' definitions.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -50,24 +50,36 @@ inline float round_bf16(float f) {  // to the nearest bf16, ties to even (NaN ke
 }
 
 // OCP e4m3fn: exponent bias 7, subnormals m * 2^-9, S.1111.111 is NaN, no infinities.
-inline float e4m3(uint32_t v) {
+inline float decode_e4m3(uint32_t v) {
   const uint32_t s = (v & 0x80u) << 24, e = (v >> 3) & 15u, m = v & 7u;
-  const float normal = from_bits(s | ((e + 120u) << 23) | (m << 20));
-  const float sub = from_bits(s | to_bits((float)m * 0.001953125f));
-  const float r = e ? normal : sub;
-  return (e == 15u && m == 7u) ? NAN : r;
+  if (e == 15u && m == 7u) return NAN;
+  return from_bits(s | (e ? (((e + 120u) << 23) | (m << 20)) : to_bits((float)m * 0.001953125f)));
 }
 // OCP e2m1: exponent bias 1, values {0, 0.5, 1, 1.5, 2, 3, 4, 6} and their negatives.
 inline float e2m1(uint32_t q) {
   const uint32_t s = (q & 8u) << 28, e = (q >> 1) & 3u, m = q & 1u;
-  const uint32_t normal = ((e + 126u) << 23) | (m << 22);
-  const uint32_t sub = m ? 0x3f000000u : 0u;  // 0.5 or 0
-  return from_bits(s | (e ? normal : sub));
+  return from_bits(s | (e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u)));
 }
 // OCP E8M0: 2^(s - 127), s = 255 is NaN.
 inline float e8m0(uint32_t s) {
   if (s == 255u) return NAN;
   return s ? from_bits(s << 23) : from_bits(0x00400000u);
+}
+// Decode tables: every e4m3 byte, and every byte of two e2m1 codes (low nibble first).
+struct Tables {
+  float e4m3[256];
+  float fp4_pair[256][2];
+  Tables() {
+    for (uint32_t v = 0; v < 256; ++v) {
+      e4m3[v] = decode_e4m3(v);
+      fp4_pair[v][0] = e2m1(v & 15u);
+      fp4_pair[v][1] = e2m1(v >> 4);
+    }
+  }
+};
+const Tables& tables() {
+  static const Tables t;
+  return t;
 }
 // IEEE binary16.
 inline float half_value(uint16_t h) {
@@ -94,6 +106,7 @@ struct MatView {
 
 // Logical row L of the slot to fp32 values out[0..K).
 FT_HOST_CLONES void decode_row(const MatView& m, int L, float* __restrict__ out) {
+  const Tables& tb = tables();
   const long long g = m.row0 + (m.perm_I ? w13_row(L, m.perm_I) : L);
   const size_t blk = (size_t)(g >> 6) * m.nchunk, lane = (size_t)(g & 63);
   switch (m.fmt) {
@@ -108,7 +121,7 @@ FT_HOST_CLONES void decode_row(const MatView& m, int L, float* __restrict__ out)
       for (int c = 0; c < m.nchunk; ++c) {
         const uint8_t* ch = m.codes + ((blk + c) * 64 + lane) * 16;
         const float s = sc[(16 * c) / 128];
-        for (int i = 0; i < 16; ++i) out[16 * c + i] = s * e4m3(ch[i]);
+        for (int i = 0; i < 16; ++i) out[16 * c + i] = s * tb.e4m3[ch[i]];
       }
       break;
     }
@@ -118,8 +131,8 @@ FT_HOST_CLONES void decode_row(const MatView& m, int L, float* __restrict__ out)
         const uint8_t* ch = m.codes + idx * 16;
         const float s = e8m0(m.scales[idx]);
         for (int i = 0; i < 16; ++i) {
-          out[32 * c + 2 * i] = s * e2m1(ch[i] & 15u);
-          out[32 * c + 2 * i + 1] = s * e2m1(ch[i] >> 4);
+          out[32 * c + 2 * i] = s * tb.fp4_pair[ch[i]][0];
+          out[32 * c + 2 * i + 1] = s * tb.fp4_pair[ch[i]][1];
         }
       }
       break;
@@ -129,11 +142,11 @@ FT_HOST_CLONES void decode_row(const MatView& m, int L, float* __restrict__ out)
         const size_t idx = (blk + c) * 64 + lane;
         const uint8_t* ch = m.codes + idx * 16;
         const uint16_t pair = ((const uint16_t*)m.scales)[idx];
-        const float s0 = e4m3(pair & 255u), s1 = e4m3(pair >> 8);
+        const float s0 = tb.e4m3[pair & 255u], s1 = tb.e4m3[pair >> 8];
         for (int i = 0; i < 16; ++i) {
           const float s = i < 8 ? s0 : s1;
-          out[32 * c + 2 * i] = t * (e2m1(ch[i] & 15u) * s);
-          out[32 * c + 2 * i + 1] = t * (e2m1(ch[i] >> 4) * s);
+          out[32 * c + 2 * i] = t * (tb.fp4_pair[ch[i]][0] * s);
+          out[32 * c + 2 * i + 1] = t * (tb.fp4_pair[ch[i]][1] * s);
         }
       }
       break;
@@ -155,16 +168,60 @@ FT_HOST_CLONES void decode_row(const MatView& m, int L, float* __restrict__ out)
   }
 }
 
-// 16 partial sums, then a fixed tree.
+// 64 partial sums (four independent vector chains at AVX-512 width), then a fixed tree.
 FT_HOST_CLONES float dot(const float* __restrict__ a, const float* __restrict__ b, int n) {
-  float acc[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  float acc[64];
+  for (int l = 0; l < 64; ++l) acc[l] = 0.0f;
   int i = 0;
-  for (; i + 16 <= n; i += 16)
-    for (int l = 0; l < 16; ++l) acc[l] += a[i + l] * b[i + l];
-  for (; i < n; ++i) acc[i & 15] += a[i] * b[i];
-  for (int h = 8; h > 0; h >>= 1)
+  for (; i + 64 <= n; i += 64)
+    for (int l = 0; l < 64; ++l) acc[l] += a[i + l] * b[i + l];
+  for (; i < n; ++i) acc[i & 63] += a[i] * b[i];
+  for (int h = 32; h > 0; h >>= 1)
     for (int l = 0; l < h; ++l) acc[l] += acc[l + h];
   return acc[0];
+}
+
+// Four dot products against one row: the row is loaded once per four multiply-adds; 16 partial sums
+// per product (one vector chain each), then the same fixed tree as dot.
+FT_HOST_CLONES void dot4(const float* __restrict__ wr, const float* __restrict__ x0, const float* __restrict__ x1,
+                         const float* __restrict__ x2, const float* __restrict__ x3, int n, float* __restrict__ r) {
+  float a0[16], a1[16], a2[16], a3[16];
+  for (int l = 0; l < 16; ++l) a0[l] = a1[l] = a2[l] = a3[l] = 0.0f;
+  int i = 0;
+  for (; i + 16 <= n; i += 16)
+    for (int l = 0; l < 16; ++l) {
+      const float v = wr[i + l];
+      a0[l] += v * x0[i + l];
+      a1[l] += v * x1[i + l];
+      a2[l] += v * x2[i + l];
+      a3[l] += v * x3[i + l];
+    }
+  for (; i < n; ++i) {
+    a0[i & 15] += wr[i] * x0[i];
+    a1[i & 15] += wr[i] * x1[i];
+    a2[i & 15] += wr[i] * x2[i];
+    a3[i & 15] += wr[i] * x3[i];
+  }
+  for (int h = 8; h > 0; h >>= 1)
+    for (int l = 0; l < h; ++l) {
+      a0[l] += a0[l + h];
+      a1[l] += a1[l + h];
+      a2[l] += a2[l + h];
+      a3[l] += a3[l + h];
+    }
+  r[0] = a0[0];
+  r[1] = a1[0];
+  r[2] = a2[0];
+  r[3] = a3[0];
+}
+
+// Dot products of one row with the rows p0..p1-1 of xs (stride n) into out[p - p0].
+inline void dots(const float* wr, const float* xs, int p0, int p1, int n, float* out) {
+  int p = p0;
+  for (; p + 4 <= p1; p += 4)
+    dot4(wr, xs + (size_t)p * n, xs + (size_t)(p + 1) * n, xs + (size_t)(p + 2) * n, xs + (size_t)(p + 3) * n, n,
+         out + (p - p0));
+  for (; p < p1; ++p) out[p - p0] = dot(wr, xs + (size_t)p * n, n);
 }
 
 template <class F>
@@ -237,14 +294,18 @@ int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, cons
   run_parallel(ng * hb, threads, [&](int it, std::vector<float>& buf) {
     const int e = groups[it / hb], i0 = (it % hb) * 32;
     const MatView m = view(e, true);
-    buf.resize(2 * (size_t)d);
+    const int np = cnt[e + 1] - cnt[e];
+    buf.resize(2 * (size_t)d + 2 * (size_t)np);
+    float* gs = buf.data() + 2 * (size_t)d;
+    float* us = gs + np;
     for (int i = i0; i < i0 + 32 && i < I; ++i) {
       decode_row(m, i, buf.data());
       decode_row(m, I + i, buf.data() + d);
-      for (int p = cnt[e]; p < cnt[e + 1]; ++p) {
-        const float* xr = xf.data() + (size_t)p * d;
-        const float gv = dot(xr, buf.data(), d), uv = dot(xr, buf.data() + d, d);
-        h[(size_t)p * I + i] = round_bf16(gv / (1.0f + expf(-gv)) * uv);
+      dots(buf.data(), xf.data(), cnt[e], cnt[e + 1], d, gs);
+      dots(buf.data() + d, xf.data(), cnt[e], cnt[e + 1], d, us);
+      for (int q = 0; q < np; ++q) {
+        const float gv = gs[q], uv = us[q];
+        h[(size_t)(cnt[e] + q) * I + i] = round_bf16(gv / (1.0f + expf(-gv)) * uv);
       }
     }
   });
@@ -253,11 +314,13 @@ int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, cons
   run_parallel(ng * yb, threads, [&](int it, std::vector<float>& buf) {
     const int e = groups[it / yb], r0 = (it % yb) * 64;
     const MatView m = view(e, false);
-    buf.resize((size_t)I);
+    const int np = cnt[e + 1] - cnt[e];
+    buf.resize((size_t)I + (size_t)np);
+    float* ys = buf.data() + I;
     for (int r = r0; r < r0 + 64 && r < d; ++r) {
       decode_row(m, r, buf.data());
-      for (int p = cnt[e]; p < cnt[e + 1]; ++p)
-        y[(size_t)p * d + r] = round_bf16(dot(h.data() + (size_t)p * I, buf.data(), I));
+      dots(buf.data(), h.data(), cnt[e], cnt[e + 1], I, ys);
+      for (int q = 0; q < np; ++q) y[(size_t)(cnt[e] + q) * d + r] = round_bf16(ys[q]);
     }
   });
   // per token, the masked slots in order j
