@@ -8,6 +8,19 @@
 namespace ftk {
 
 constexpr int SEG = 1024;  // flat entries per wave segment
+constexpr int SEG_STEPS = SEG / 64;
+
+// The segment's expert ids, lane l holding entries seg_begin + 64 i + l: every load is issued before
+// the first is used, so the segment costs one memory latency, not one per step.
+__device__ __forceinline__ void load_segment(const int32_t* __restrict__ ids, int seg_begin, int seg_end,
+                                             int (&ev)[SEG_STEPS]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < SEG_STEPS; ++i) {
+    const int f = seg_begin + 64 * i + lane;
+    ev[i] = f < seg_end ? ids[f] : -1;
+  }
+}
 
 __device__ __forceinline__ uint64_t peers_of(int e, bool active, int id_bits) {
   uint64_t m = __ballot(active);
@@ -26,9 +39,14 @@ __device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids,
   const int lane = threadIdx.x & 63;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int seg_end = min(seg_begin + SEG, n);
-  for (int f0 = seg_begin; f0 < seg_end; f0 += 64) {
+  int ev[SEG_STEPS];
+  load_segment(ids, seg_begin, seg_end, ev);
+#pragma unroll
+  for (int i = 0; i < SEG_STEPS; ++i) {
+    const int f0 = seg_begin + 64 * i;
+    if (f0 >= seg_end) break;
     const int f = f0 + lane;
-    const int e_raw = f < seg_end ? ids[f] : 0;
+    const int e_raw = ev[i];
     const bool active = f < seg_end && (unsigned)e_raw < (unsigned)E;  // invalid ids get no position
     const int e = active ? e_raw : 0;
     const uint64_t peers = peers_of(e, active, id_bits);
@@ -48,11 +66,13 @@ __device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids,
 
 __device__ __forceinline__ void count_segment(const int32_t* __restrict__ ids, int n, int E, int seg_begin,
                                               int* hist) {
-  const int lane = threadIdx.x & 63;
   const int seg_end = min(seg_begin + SEG, n);
-  for (int f = seg_begin + lane; f < seg_end; f += 64) {
-    const int e = ids[f];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);  // ids outside [0, E) are skipped
+  int ev[SEG_STEPS];
+  load_segment(ids, seg_begin, seg_end, ev);
+#pragma unroll
+  for (int i = 0; i < SEG_STEPS; ++i) {
+    const int e = ev[i];  // -1 past the end; ids outside [0, E) are skipped
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
   }
 }
 
