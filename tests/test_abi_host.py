@@ -161,6 +161,57 @@ def test_moelayer_takes_bf16_output_from_flags():
     assert a.flags == b.flags and a.out_flags == b.out_flags == ft.FT_OUT_BF16
 
 
+def test_residual_host_fp8_on_cpu():
+    """The FP8-B128 decode of the host residual (the vector path where the host has AVX-512): a bank
+    whose codes cover every finite e4m3 byte, laid out by hand in the documented device layout (16
+    codes per chunk, 64-row interleave, fp32 scales per 128 x 128 block of logical rows), against the
+    oracle's FFN of the weights its own e4m3 decoder gives."""
+    import numpy as np
+    import torch
+    import oracle
+    rng = np.random.default_rng(6)
+    T, d, E, k, I = 3, 256, 2, 2, 128
+    finite = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
+    table = np.array([oracle.e4m3_value(int(c)) for c in range(256)], np.float32)
+
+    def make(R, K, perm_I):
+        codes = finite[rng.integers(0, len(finite), size=(E, R, K))]
+        scales = (2.0 ** rng.integers(-12, -6, size=(E, R // 128, K // 128))).astype(np.float32)
+        vals = table[codes] * np.repeat(np.repeat(scales, 128, axis=1), 128, axis=2)
+        out = np.zeros(E * R * K, np.uint8)
+        nch = K // 16
+        for g in range(E * R):
+            slot, L = divmod(g, R)
+            if perm_I:
+                dr = 64 * (L >> 5) + (L & 31) if L < perm_I else 64 * ((L - perm_I) >> 5) + 32 + ((L - perm_I) & 31)
+            else:
+                dr = L
+            G = slot * R + dr
+            for c in range(nch):
+                off = (((G >> 6) * nch + c) * 64 + (G & 63)) * 16
+                out[off:off + 16] = codes[slot, L, 16 * c:16 * c + 16]
+        return torch.from_numpy(out), torch.from_numpy(scales.reshape(-1).copy()), vals.astype(np.float32)
+
+    c13, s13, v13 = make(2 * I, d, I)
+    c2, s2, v2 = make(d, I, 0)
+    hb = ft.DeviceBank(ft.FT_W_FP8_B128, E, d, I, c13, c2, s13.view(torch.uint8), s2.view(torch.uint8))
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    ids = torch.tensor([[0, 1], [1, 0], [0, 1]], dtype=torch.int32)
+    wts = torch.tensor([[0.6, 0.4], [0.7, 0.3], [0.5, 0.5]], dtype=torch.float32)
+    mask = torch.tensor([0b11, 0b01, 0b10], dtype=torch.int32)
+    got = ft.ft_moe_residual_host(hb, x, ids, wts, mask, n_threads=2).numpy()
+    xf = x.float().numpy()
+    ref = np.zeros((T, d), np.float64)
+    for t in range(T):
+        for j in range(k):
+            if (int(mask[t]) >> j) & 1:
+                e = int(ids[t, j])
+                _, y = oracle.swiglu_ffn(xf[t:t + 1], v13[e], v2[e])
+                ref[t] += float(wts[t, j]) * y[0].astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert np.isfinite(got).all() and rel < 5e-3, rel
+
+
 def _err(rc, code, pattern):
     assert rc == code, (rc, ft.ft_moe_last_error())
     assert re.search(pattern, ft.ft_moe_last_error()), ft.ft_moe_last_error()
