@@ -498,6 +498,9 @@ def main():
     roof["algorithmic_bytes_per_call"] = round(bytes_call)
     roof["algorithmic_flops_per_call"] = round(flops_call)
     roof["other_bound"] = other
+    # intermediate rows that cross kernel (or, in the one-launch layer, block) boundaries through
+    # memory: h written by gate/up and read by down, y written by down and read by combine
+    roof["boundary_bytes_per_call"] = round(2 * pairs * (w.d + w.I) * 2)
     log(f"layer call {ffn_us:.2f} us; {touched:.1f} experts touched, {pairs:.1f} pairs; {roof}")
 
     # ---- CPU baseline: the oracle on host cores, bounded sample
