@@ -456,19 +456,24 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # ---- timed region
+    # ---- timed region (events between steps give the spread; the value is the whole region's time)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             run_step(layers)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     us_per_layer = ms_per_step * 1e3 / n_layers
-    log(f"{ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer")
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    spread = {q: round(float(np.percentile(per_step, p)), 4) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+    log(f"{ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer; per-step ms {spread}")
 
     # ---- dominant unit: the layer call, event-timed on its stream
     ffn_us = time_layer_calls(layers, args.ffn_reps)
@@ -530,6 +535,7 @@ def main():
                    "graph": graph is not None},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_ms": spread,
     }
     print(json.dumps(line), flush=True)
 
