@@ -60,7 +60,7 @@ def _bind(lib):
     lib.ora_permute.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_swiglu_ffn.argtypes = [P, i, i, i, P, P, P, P]
     lib.ora_combine.argtypes = [P, P, P, P, P, P, i, i, i, i, P, i, P, P]
-    lib.ora_cache_update.argtypes = [P, i, i, i, P, P, P, P, P, P]
+    lib.ora_cache_update.argtypes = [P, i, i, i, ctypes.c_float, P, P, P, P, P, P, P]
     for f in ("ora_bf16_value", "ora_fp16_value"):
         getattr(lib, f).argtypes = [ctypes.c_uint16]
         getattr(lib, f).restype = ctypes.c_float
@@ -191,20 +191,24 @@ class CacheState:
         return c
 
 
-def cache_update(counts, state: CacheState, max_loads: int, lib=None):
+def cache_update(counts, state: CacheState, max_loads: int, load_fraction: float = 0.0, lib=None,
+                 with_load_slot: bool = False):
     """One step of the global LRU expert cache on `state` (updated in place).
 
-    Returns (compute_slot int32 [E], loads int32 [n][2] of (expert, slot))."""
+    Returns (compute_slot int32 [E], loads int32 [n][2] of (expert, slot)), and load_slot int32 [E]
+    after them when with_load_slot."""
     c = _np(counts, np.int32)
     E, S = c.shape[0], state.expert_of_slot.shape[0]
     compute_slot = np.empty(E, np.int32)
+    load_slot = np.empty(E, np.int32)
     loads = np.empty(2 * max(max_loads, 1), np.int32)
-    n = (lib or _load()).ora_cache_update(_p(c), E, S, max_loads, _p(state.slot_of_expert),
+    n = (lib or _load()).ora_cache_update(_p(c), E, S, max_loads, float(load_fraction), _p(state.slot_of_expert),
                                           _p(state.expert_of_slot), _p(state.last_use), _p(state.tick),
-                                          _p(compute_slot), _p(loads))
+                                          _p(compute_slot), _p(load_slot), _p(loads))
     if n < 0:
         raise ValueError("oracle cache_update rejected its arguments")
-    return compute_slot, loads[:2 * n].reshape(n, 2).copy()
+    out = (compute_slot, loads[:2 * n].reshape(n, 2).copy())
+    return out + (load_slot,) if with_load_slot else out
 
 
 def swiglu_ffn(x_f32, w13_f32, w2_f32, lib=None):

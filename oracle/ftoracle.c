@@ -305,22 +305,26 @@ int ora_combine(const float* y_sorted, const float* y_shared, const int32_t* ids
  *
  *   - the step's clock is tick + 1; an expert is demanded when counts[e] > 0;
  *   - a demanded expert that is resident marks its slot used at this step;
- *   - repeatedly, while fewer than max_loads loads are chosen: take the demanded absent expert
+ *   - at most max_loads loads, and when load_fraction > 0 at most ceil(load_fraction * m) of them
+ *     (fp32 product), m being the number of demanded absent experts: the share of the cold experts
+ *     that is copied to the GPU, the rest being computed on the host (the bandwidth-adaptive split
+ *     of the walk-through's section 五 and the article's mechanism two);
+ *   - repeatedly, while fewer loads than that are chosen: take the demanded absent expert
  *     with the most tokens (ties to the lowest index) and the slot to reuse: empty slots before
  *     occupied ones, then the least recently used, ties to the lowest slot index; a slot whose
  *     expert is demanded at this step is never taken.  Stop when either is missing.  The slot's
  *     old expert becomes absent; the new one is resident there and its slot used at this step;
  *   - compute_slot[e] is e's slot if e was resident before the step and still is, else -1: the
- *     step computes with the experts that were already on the device, while the chosen loads are
- *     copied in beside that work and serve from the next step on.
+ *     experts that were already on the device; load_slot[e] is e's slot if it was loaded in this
+ *     step, else -1 (a caller may compute those once their copy is done, or from the next step on).
  *
  * State: slot_of_expert[E] and expert_of_slot[S] (-1 = none, a bijection on the resident set),
  * last_use[S] and *tick; all updated in place.  loads[2n], loads[2n+1] = (expert, slot) of the
  * n-th load.  Returns the number of loads, or -1 on bad arguments.
  */
-int ora_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t* slot_of_expert,
-                     int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
-                     int32_t* loads) {
+int ora_cache_update(const int32_t* counts, int E, int S, int max_loads, float load_fraction,
+                     int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick,
+                     int32_t* compute_slot, int32_t* load_slot, int32_t* loads) {
   if (E <= 0 || S <= 0 || max_loads < 0) return -1;
   const uint32_t now = *tick + 1u;
   int32_t* before = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
@@ -328,8 +332,15 @@ int ora_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t
   for (int e = 0; e < E; ++e) before[e] = slot_of_expert[e];
   for (int e = 0; e < E; ++e)
     if (counts[e] > 0 && slot_of_expert[e] >= 0) last_use[slot_of_expert[e]] = now;
+  int limit = max_loads;
+  if (load_fraction > 0.0f) {
+    int m = 0;
+    for (int e = 0; e < E; ++e) m += counts[e] > 0 && slot_of_expert[e] < 0;
+    const int share = (int)ceilf(load_fraction * (float)m);
+    if (share < limit) limit = share;
+  }
   int n = 0;
-  while (n < max_loads) {
+  while (n < limit) {
     int want = -1;
     for (int e = 0; e < E; ++e)
       if (counts[e] > 0 && slot_of_expert[e] < 0 && (want < 0 || counts[e] > counts[want])) want = e;
@@ -355,8 +366,10 @@ int ora_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t
     loads[2 * n + 1] = slot;
     ++n;
   }
-  for (int e = 0; e < E; ++e)
+  for (int e = 0; e < E; ++e) {
     compute_slot[e] = (before[e] >= 0 && slot_of_expert[e] == before[e]) ? before[e] : -1;
+    load_slot[e] = (before[e] < 0 && slot_of_expert[e] >= 0) ? slot_of_expert[e] : -1;
+  }
   *tick = now;
   free(before);
   return n;

@@ -481,6 +481,40 @@ def pin_cache_worked_example(lib):
         assert st.last_use.tolist() == lu and int(st.tick[0]) == i + 1, i
 
 
+def pin_cache_load_fraction(lib):
+    """The load fraction caps the loads at ceil(q * m) of the m demanded absent experts (fp32 product),
+    and load_slot names exactly this step's loads; worked by hand from the policy's definition."""
+    st = oracle.CacheState(6, 4)
+    steps = [
+        # counts, max_loads, q, loads, compute_slot, load_slot
+        ([1, 1, 1, 0, 0, 0], 4, 0.5, [(0, 0), (1, 1)], [-1] * 6, [0, 1, -1, -1, -1, -1]),
+        ([0, 0, 3, 2, 0, 1], 4, 0.2, [(2, 2)], [0, 1, -1, -1, -1, -1], [-1, -1, 2, -1, -1, -1]),
+        ([2, 0, 0, 1, 1, 0], 4, 1.0, [(3, 3), (4, 1)], [0, -1, 2, -1, -1, -1], [-1, -1, -1, 3, 1, -1]),
+        ([0, 0, 0, 0, 0, 5], 4, 0.0, [(5, 2)], [0, -1, -1, 3, 1, -1], [-1, -1, -1, -1, -1, 2]),
+    ]
+    for i, (counts, ml, q, loads, cs, ls) in enumerate(steps):
+        got_cs, got_loads, got_ls = oracle.cache_update(np.array(counts, np.int32), st, ml, q, lib=lib,
+                                                        with_load_slot=True)
+        assert [tuple(int(v) for v in r) for r in got_loads] == loads, (i, got_loads)
+        assert got_cs.tolist() == cs and got_ls.tolist() == ls, (i, got_cs, got_ls)
+    rng = np.random.default_rng(33)
+    for q in (0.1, 0.37, 0.5, 0.9):
+        st = oracle.CacheState(64, 24)
+        pop = rng.permutation(64)
+        for step in range(30):
+            counts = np.bincount(_zipf_ids(rng, 6, 64, 4, pop).reshape(-1), minlength=64).astype(np.int32)
+            prev = st.copy()
+            cs, loads, ls = oracle.cache_update(counts, st, 24, q, lib=lib, with_load_slot=True)
+            m = int(((counts > 0) & (prev.slot_of_expert < 0)).sum())
+            idle = sum(1 for sl in range(24) if prev.expert_of_slot[sl] < 0 or counts[prev.expert_of_slot[sl]] == 0)
+            share = int(np.ceil(np.float32(q) * np.float32(m)))
+            assert len(loads) == min(m, idle, share), (q, step)
+            want = np.full(64, -1, np.int32)
+            for e, sl in loads:
+                want[e] = sl
+            assert np.array_equal(ls, want)
+
+
 def _zipf_ids(rng, T, E, k, pop):
     p = 1.0 / np.arange(1, E + 1)
     p /= p.sum()
@@ -530,4 +564,4 @@ ALL_PINS = [pin_route_bruteforce, pin_route_special_cases, pin_route_weights_flo
             pin_decoder_tables, pin_dequant_roundtrip, pin_dequant_layouts, pin_ffn_float64,
             pin_layer_identical_experts, pin_layer_float64, pin_combine_cases, pin_router_logits_worked_example,
             pin_router_logits_one_hot, pin_router_logits_exact_sum, pin_cache_textbook_lru,
-            pin_cache_worked_example, pin_cache_invariants]
+            pin_cache_worked_example, pin_cache_invariants, pin_cache_load_fraction]

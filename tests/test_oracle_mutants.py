@@ -50,6 +50,8 @@ MUTANTS = {
     "lru_misses_by_index": ("(want < 0 || counts[e] > counts[want])", "(want < 0)"),
     "lru_evicts_demanded": ("if (v >= 0 && counts[v] > 0) continue;", "if (v >= 0 && counts[v] < 0) continue;"),
     "lru_no_refresh": ("last_use[slot_of_expert[e]] = now;", "last_use[slot_of_expert[e]] = last_use[slot_of_expert[e]];"),
+    "lru_fraction_floor": ("const int share = (int)ceilf(load_fraction * (float)m);", "const int share = (int)floorf(load_fraction * (float)m);"),
+    "lru_load_slot_all": ("load_slot[e] = (before[e] < 0 && slot_of_expert[e] >= 0) ? slot_of_expert[e] : -1;", "load_slot[e] = slot_of_expert[e];"),
     "lru_compute_with_loads": ("compute_slot[e] = (before[e] >= 0 && slot_of_expert[e] == before[e]) ? before[e] : -1;", "compute_slot[e] = slot_of_expert[e];"),
 }
 
