@@ -248,21 +248,29 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
  *   - each demanded resident expert marks its slot used now;
  *   - the demanded absent experts, by counts descending then expert index, are paired with the
  *     slots whose expert is not demanded, empty slots first, then by last_use ascending, then slot
- *     index; min(#absent, #such slots, max_loads) pairs are made.  Each pair evicts the slot's
- *     expert (its slot_of_expert becomes -1), puts the new expert there and marks the slot used now;
+ *     index; min(#absent, #such slots, max_loads) pairs are made, and with load_fraction q > 0 at
+ *     most ceil(q * #absent) (fp32 product; q in [0, 1], 0 = no such limit): the share of the cold
+ *     experts copied to the GPU, the rest being left to the host (the bandwidth-adaptive CPU-GPU
+ *     split of the walk-through, section 五, and the zuoshipin.com article, mechanism two).  Each
+ *     pair evicts the slot's expert (its slot_of_expert becomes -1), puts the new expert there and
+ *     marks the slot used now;
  *   - compute_slot [E] int32 (out): an expert's slot when it was resident before the step and still
- *     is, else -1.  Pass it as the slot table of this step's ft_moe_grouped_ffn and ft_moe_combine:
- *     the experts being loaded are then left to the residual mask in this step and serve from the
- *     next one;
+ *     is, else -1.  Pass it as the slot table of this step's ft_moe_grouped_ffn: the experts being
+ *     loaded are not computed from it;
+ *   - load_slot [E] int32 (out, may be NULL): an expert's slot when it was loaded in this step, else
+ *     -1.  A caller that computes the loaded experts in the same step runs a second
+ *     ft_moe_grouped_ffn with this table after the fill, and combines with slot_of_expert (the
+ *     table after the step); one that leaves them to the next step combines with compute_slot;
  *   - loads [max_loads][2] int32 (out): (expert, slot) per load in pairing order; n_loads [1] int32
  *     (out): their number.  Copy them with ft_moe_cache_fill before the next step's update.
  * Limits: 1 <= E <= 1024, 1 <= n_slots <= 1024, 0 <= max_loads <= n_slots.  Pointers 16-byte
  * aligned.  Entries of the tables outside their ranges are read as -1.  last_use wraps after 2^32
  * steps.  One kernel launch (one block); none allocates or syncs.
  */
-int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, int32_t* slot_of_expert,
-                        int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
-                        int32_t* loads, int32_t* n_loads, hipStream_t stream);
+int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, float load_fraction,
+                        int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick,
+                        int32_t* compute_slot, int32_t* load_slot, int32_t* loads, int32_t* n_loads,
+                        hipStream_t stream);
 
 /*
  * Copy the experts listed by ft_moe_cache_update from the bank that holds every expert (`src`,
@@ -287,10 +295,13 @@ int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int3
  * The pairs the device layer leaves to another path, computed on the host cores (FreeToken
  * walk-through, section 五: cold experts stay in host memory and run on the CPU beside the GPU;
  * zuoshipin.com FreeToken article, mechanism two: CPU-GPU co-execution).  For every token t and
- * slot j with bit j of residual_mask[t] set (the mask ft_moe_combine or ft_moe_layer wrote) and
- * e = ids[t][j] < host_bank->n_slots: y = SiLU(x[t] Wg_e^T) * (x[t] Wu_e^T) Wd_e^T with fp32 sums,
+ * slot j whose pair is cold and e = ids[t][j] < min(E, host_bank->n_slots): y = SiLU(x[t] Wg_e^T) * (x[t] Wu_e^T) Wd_e^T with fp32 sums,
  * h and y rounded to bf16 as on the device; then out[t] = sum over those j, in order j, of
- * w[t][j] * y.  out [T][d] fp32 is overwritten (zero for a token with no such pair).
+ * w[t][j] * y.  out [T][d] fp32 is overwritten (zero for a token with no such pair).  A pair is
+ * cold when bit j of residual_mask[t] is set (the mask ft_moe_combine or ft_moe_layer wrote), or,
+ * with residual_mask NULL, when slot_of_expert[e] < 0 (a host copy of the slot table the device
+ * layer uses, so the host can start as soon as the routing is known, beside the device layer).
+ * Exactly one of the two is given.
  * Everything is host memory: host_bank (a host pointer to a bank description whose arrays are in
  * host memory, pinned or not, in the device layout of ft_moe_pack_bank, expert e in slot e: the bank
  * ft_moe_cache_fill reads), x bf16 [T][d], ids [T][k], w [T][k], residual_mask [T], out.  Runs on
@@ -298,7 +309,8 @@ int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int3
  * does not touch the GPU.  Add the result to the device output with ft_moe_residual_add.
  */
 int ft_moe_residual_host(const ft_moe_bank* host_bank, const uint16_t* x, const int32_t* ids, const float* w,
-                         const uint32_t* residual_mask, int T, int E, int k, float* out, int n_threads);
+                         const uint32_t* residual_mask, const int32_t* slot_of_expert, int T, int E, int k,
+                         float* out, int n_threads);
 
 /*
  * out[t][c] += residual[t][c] on the device, out fp32 or (FT_OUT_BF16) bf16 rounded to nearest even,

@@ -62,9 +62,9 @@ def _load():
         "ft_moe_dequant": ([BP, i, i, P, P], i),
         "ft_moe_layer_workspace": ([BP, i, i, i, i, i], sz),
         "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
-        "ft_moe_cache_update": ([P, i, i, i, P, P, P, P, P, P, P, P], i),
+        "ft_moe_cache_update": ([P, i, i, i, ctypes.c_float, P, P, P, P, P, P, P, P, P], i),
         "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
-        "ft_moe_residual_host": ([BP, P, P, P, P, i, i, i, P, i], i),
+        "ft_moe_residual_host": ([BP, P, P, P, P, P, i, i, i, P, i], i),
         "ft_moe_residual_add": ([P, P, i, i, i, P], i),
     }
     for name, (args, res) in sig.items():
@@ -167,18 +167,20 @@ def ft_moe_dequant(bank: DeviceBank, slot: int, which: int, out=None, stream=Non
 
 # ------------------------------------------------------------------------------------- expert cache
 
-def ft_moe_cache_update(counts, slot_of_expert, expert_of_slot, last_use, tick, max_loads: int, compute_slot=None,
-                        loads=None, n_loads=None, stream=None):
+def ft_moe_cache_update(counts, slot_of_expert, expert_of_slot, last_use, tick, max_loads: int,
+                        load_fraction: float = 0.0, compute_slot=None, load_slot=None, loads=None, n_loads=None,
+                        stream=None):
     """One step of the global LRU expert cache on device-resident state (int32 tensors; last_use and
-    tick hold uint32 bits).  Returns (compute_slot [E], loads [max_loads][2], n_loads [1])."""
+    tick hold uint32 bits).  Returns (compute_slot [E], loads [max_loads][2], n_loads [1]); load_slot
+    [E] is written when given."""
     E, S = counts.shape[0], expert_of_slot.shape[0]
     dev = counts.device
     compute_slot = torch.empty(E, dtype=torch.int32, device=dev) if compute_slot is None else compute_slot
     loads = torch.empty(max(max_loads, 1), 2, dtype=torch.int32, device=dev) if loads is None else loads
     n_loads = torch.empty(1, dtype=torch.int32, device=dev) if n_loads is None else n_loads
-    _check(lib.ft_moe_cache_update(_ptr(counts), E, S, max_loads, _ptr(slot_of_expert), _ptr(expert_of_slot),
-                                   _ptr(last_use), _ptr(tick), _ptr(compute_slot), _ptr(loads), _ptr(n_loads),
-                                   _stream(stream)))
+    _check(lib.ft_moe_cache_update(_ptr(counts), E, S, max_loads, float(load_fraction), _ptr(slot_of_expert),
+                                   _ptr(expert_of_slot), _ptr(last_use), _ptr(tick), _ptr(compute_slot),
+                                   _ptr(load_slot), _ptr(loads), _ptr(n_loads), _stream(stream)))
     return compute_slot, loads, n_loads
 
 
@@ -191,19 +193,21 @@ class ExpertCache:
     """Device state of the global LRU expert cache over slots 0..n_slots-1 of a device bank, and the
     buffers one step writes.  Starts with every slot empty."""
 
-    def __init__(self, E: int, n_slots: int, max_loads: int, device="cuda"):
-        self.E, self.n_slots, self.max_loads = E, n_slots, max_loads
+    def __init__(self, E: int, n_slots: int, max_loads: int, device="cuda", load_fraction: float = 0.0):
+        self.E, self.n_slots, self.max_loads, self.load_fraction = E, n_slots, max_loads, load_fraction
         self.slot_of_expert = torch.full((E,), -1, dtype=torch.int32, device=device)
         self.expert_of_slot = torch.full((n_slots,), -1, dtype=torch.int32, device=device)
         self.last_use = torch.zeros(n_slots, dtype=torch.int32, device=device)
         self.tick = torch.zeros(1, dtype=torch.int32, device=device)
         self.compute_slot = torch.empty(E, dtype=torch.int32, device=device)
+        self.load_slot = torch.empty(E, dtype=torch.int32, device=device)
         self.loads = torch.empty(max(max_loads, 1), 2, dtype=torch.int32, device=device)
         self.n_loads = torch.zeros(1, dtype=torch.int32, device=device)
 
     def update(self, counts, stream=None):
         return ft_moe_cache_update(counts, self.slot_of_expert, self.expert_of_slot, self.last_use, self.tick,
-                                   self.max_loads, self.compute_slot, self.loads, self.n_loads, stream)
+                                   self.max_loads, self.load_fraction, self.compute_slot, self.load_slot, self.loads,
+                                   self.n_loads, stream)
 
     def fill(self, src: DeviceBank, dst: DeviceBank, stream=None):
         ft_moe_cache_fill(src, dst, self.loads, self.n_loads, self.max_loads, stream)
@@ -211,16 +215,17 @@ class ExpertCache:
 
 # ------------------------------------------------------------------------------------- cold-expert residual
 
-def ft_moe_residual_host(host_bank: DeviceBank, x, ids, w, residual_mask, out=None, n_threads: int = 0,
-                         E: int | None = None):
-    """Host compute of the masked pairs: all arguments host (CPU) tensors; host_bank holds every expert
-    (expert e in slot e) in host memory; E defaults to its slot count.  Returns out fp32 [T][d]."""
+def ft_moe_residual_host(host_bank: DeviceBank, x, ids, w, residual_mask=None, out=None, n_threads: int = 0,
+                         E: int | None = None, slot_of_expert=None):
+    """Host compute of the cold pairs (residual_mask bits, or slot_of_expert < 0 when the mask is not
+    given): all arguments host (CPU) tensors; host_bank holds every expert (expert e in slot e) in host
+    memory; E defaults to its slot count.  Returns out fp32 [T][d]."""
     T, k = ids.shape
     d = x.shape[1]
     out = torch.empty(T, d, dtype=torch.float32) if out is None else out
     E = int(host_bank.n_slots) if E is None else E
-    _check(lib.ft_moe_residual_host(host_bank.ref, _ptr(x), _ptr(ids), _ptr(w), _ptr(residual_mask), T, E, k,
-                                    _ptr(out), n_threads))
+    _check(lib.ft_moe_residual_host(host_bank.ref, _ptr(x), _ptr(ids), _ptr(w), _ptr(residual_mask),
+                                    _ptr(slot_of_expert), T, E, k, _ptr(out), n_threads))
     return out
 
 

@@ -448,14 +448,18 @@ int ft_moe_dequant(const ft_moe_bank* bank, int slot, int which, float* out, hip
   }
 }
 
-int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, int32_t* slot_of_expert,
-                        int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
-                        int32_t* loads, int32_t* n_loads, hipStream_t stream) {
+int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads, float load_fraction,
+                        int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick,
+                        int32_t* compute_slot, int32_t* load_slot, int32_t* loads, int32_t* n_loads,
+                        hipStream_t stream) {
   try {
     REQUIRE(E >= 1 && E <= 1024, FT_E_INVAL, "E must be in [1, 1024] (got %d)", E);
     REQUIRE(n_slots >= 1 && n_slots <= 1024, FT_E_INVAL, "n_slots must be in [1, 1024] (got %d)", n_slots);
     REQUIRE(max_loads >= 0 && max_loads <= n_slots, FT_E_INVAL, "max_loads must be in [0, n_slots] (got %d)",
             max_loads);
+    REQUIRE(load_fraction >= 0.0f && load_fraction <= 1.0f, FT_E_INVAL, "load_fraction must be in [0, 1] (got %g)",
+            (double)load_fraction);
+    if (load_slot) CHECK_PTR(load_slot, "load_slot");
     CHECK_PTR(counts, "counts");
     CHECK_PTR(slot_of_expert, "slot_of_expert");
     CHECK_PTR(expert_of_slot, "expert_of_slot");
@@ -464,8 +468,9 @@ int ft_moe_cache_update(const int32_t* counts, int E, int n_slots, int max_loads
     CHECK_PTR(compute_slot, "compute_slot");
     CHECK_PTR(loads, "loads");
     CHECK_PTR(n_loads, "n_loads");
-    return hip_status(ftk::launch_cache_update(counts, E, n_slots, max_loads, slot_of_expert, expert_of_slot,
-                                               last_use, tick, compute_slot, loads, n_loads, stream),
+    return hip_status(ftk::launch_cache_update(counts, E, n_slots, max_loads, load_fraction, slot_of_expert,
+                                               expert_of_slot, last_use, tick, compute_slot, load_slot, loads,
+                                               n_loads, stream),
                       "ft_moe_cache_update launch");
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_cache_update: unexpected exception");
@@ -543,7 +548,8 @@ int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int3
 }
 
 int ft_moe_residual_host(const ft_moe_bank* host_bank, const uint16_t* x, const int32_t* ids, const float* w,
-                         const uint32_t* residual_mask, int T, int E, int k, float* out, int n_threads) {
+                         const uint32_t* residual_mask, const int32_t* slot_of_expert, int T, int E, int k,
+                         float* out, int n_threads) {
   try {
     int rc = check_tek(T, E, k);
     if (rc) return rc;
@@ -551,15 +557,18 @@ int ft_moe_residual_host(const ft_moe_bank* host_bank, const uint16_t* x, const 
     if (rc) return rc;
     REQUIRE(n_threads >= 0, FT_E_INVAL, "n_threads must be >= 0 (got %d)", n_threads);
     if (T == 0) return ok();
-    REQUIRE(x != nullptr && ids != nullptr && w != nullptr && residual_mask != nullptr && out != nullptr, FT_E_INVAL,
-            "x, ids, w, residual_mask and out must not be null");
+    REQUIRE(x != nullptr && ids != nullptr && w != nullptr && out != nullptr, FT_E_INVAL,
+            "x, ids, w and out must not be null");
+    REQUIRE((residual_mask != nullptr) != (slot_of_expert != nullptr), FT_E_INVAL,
+            "exactly one of residual_mask and slot_of_expert must be given");
     int threads = n_threads;
     if (threads == 0) threads = (int)std::thread::hardware_concurrency();
     if (threads < 1) threads = 1;
     if (threads > 256) threads = 256;
     const ft_moe_bank* b = host_bank;
     ftk::residual_host(b->fmt, b->n_slots, b->d, b->I, (const uint8_t*)b->w13, (const uint8_t*)b->w2,
-                       (const uint8_t*)b->s13, (const uint8_t*)b->s2, x, ids, w, residual_mask, T, E, k, out, threads);
+                       (const uint8_t*)b->s13, (const uint8_t*)b->s2, x, ids, w, residual_mask, slot_of_expert, T, E, k,
+                       out, threads);
     return ok();
   } catch (const std::bad_alloc&) {
     return fail(FT_E_INTERNAL, "ft_moe_residual_host: out of host memory");

@@ -14,9 +14,11 @@
 //   - a demanded resident expert marks its slot used now;
 //   - loads pair the demanded absent experts, by token count descending then expert index, with
 //     the slots whose experts are idle in this step, empty slots first, then by last use
-//     ascending, then slot index; as many as the shorter list and max_loads allow;
-//   - compute_slot keeps an expert's slot only if it was resident before the step and still is:
-//     the step computes with what was on the device, the loads serve from the next step on.
+//     ascending, then slot index; as many as the shorter list and max_loads allow, and with a load
+//     fraction q > 0 at most ceil(q m) of the m demanded absent experts (the share of the cold
+//     experts copied to the GPU, the rest being left to the host: the bandwidth-adaptive split);
+//   - compute_slot keeps an expert's slot only if it was resident before the step and still is;
+//     load_slot names the slots loaded in this step (usable once their copy is done).
 #include "ft_device.h"
 #include "ft_kernels.h"
 
@@ -44,12 +46,13 @@ __device__ __forceinline__ int block_compact(bool pred, int* wave_tot, int& tota
 }
 
 __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32_t* __restrict__ counts, int E,
-                                                                       int S, int max_loads,
+                                                                       int S, int max_loads, float load_fraction,
                                                                        int32_t* __restrict__ soe_g,
                                                                        int32_t* __restrict__ eos_g,
                                                                        uint32_t* __restrict__ lu_g,
                                                                        uint32_t* __restrict__ tick,
                                                                        int32_t* __restrict__ compute_slot,
+                                                                       int32_t* __restrict__ load_slot,
                                                                        int32_t* __restrict__ loads,
                                                                        int32_t* __restrict__ n_loads) {
   __shared__ int cnt[CACHE_THREADS], soe[CACHE_THREADS], eos[CACHE_THREADS];
@@ -108,7 +111,8 @@ __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32
   }
   __syncthreads();
 
-  const int nl = min(min(nmiss, nidle), max_loads);
+  int nl = min(min(nmiss, nidle), max_loads);
+  if (load_fraction > 0.0f) nl = min(nl, (int)ceilf(load_fraction * (float)nmiss));
   if (t < nl) {  // distinct experts and slots per thread: no two threads touch the same entry
     const int e = miss_by_rank[t], s = slot_by_rank[t], old = eos[s];
     if (old >= 0) soe[old] = -1;
@@ -122,6 +126,7 @@ __global__ __launch_bounds__(CACHE_THREADS) void cache_update_kernel(const int32
   if (t < E) {
     soe_g[t] = soe[t];
     compute_slot[t] = (before >= 0 && soe[t] == before) ? before : -1;
+    if (load_slot) load_slot[t] = (before < 0 && soe[t] >= 0) ? soe[t] : -1;
   }
   if (t < S) {
     eos_g[t] = eos[t];
@@ -179,11 +184,12 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(CacheFillArgs a) {
 
 }  // namespace
 
-hipError_t launch_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t* slot_of_expert,
-                               int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
-                               int32_t* loads, int32_t* n_loads, hipStream_t s) {
-  hipLaunchKernelGGL(cache_update_kernel, dim3(1), dim3(CACHE_THREADS), 0, s, counts, E, S, max_loads,
-                     slot_of_expert, expert_of_slot, last_use, tick, compute_slot, loads, n_loads);
+hipError_t launch_cache_update(const int32_t* counts, int E, int S, int max_loads, float load_fraction,
+                               int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick,
+                               int32_t* compute_slot, int32_t* load_slot, int32_t* loads, int32_t* n_loads,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(cache_update_kernel, dim3(1), dim3(CACHE_THREADS), 0, s, counts, E, S, max_loads, load_fraction,
+                     slot_of_expert, expert_of_slot, last_use, tick, compute_slot, load_slot, loads, n_loads);
   return hipGetLastError();
 }
 

@@ -33,9 +33,10 @@ hipError_t launch_route_proj(const uint16_t* x, const uint16_t* wr, int T, int d
                              int32_t* ids, float* w, void* ws, hipStream_t s);
 
 // global LRU expert cache: one bookkeeping step (E, S <= 1024) and the copy of the chosen experts
-hipError_t launch_cache_update(const int32_t* counts, int E, int S, int max_loads, int32_t* slot_of_expert,
-                               int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick, int32_t* compute_slot,
-                               int32_t* loads, int32_t* n_loads, hipStream_t s);
+hipError_t launch_cache_update(const int32_t* counts, int E, int S, int max_loads, float load_fraction,
+                               int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use, uint32_t* tick,
+                               int32_t* compute_slot, int32_t* load_slot, int32_t* loads, int32_t* n_loads,
+                               hipStream_t s);
 struct CacheFillSeg {
   const uint8_t* src;  // expert e's bytes at src + e * bytes (device-visible address of pinned host memory)
   uint8_t* dst;        // slot s's bytes at dst + s * bytes
@@ -53,7 +54,7 @@ hipError_t launch_cache_fill(const CacheFillArgs& a, int blocks, hipStream_t s);
 // the device add of its result into the layer output
 int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, const uint8_t* w2, const uint8_t* s13,
                   const uint8_t* s2, const uint16_t* x, const int32_t* ids, const float* w, const uint32_t* mask,
-                  int T, int E, int k, float* out, int threads);
+                  const int32_t* slot_of_expert, int T, int E, int k, float* out, int threads);
 hipError_t launch_residual_add(void* out, const float* res, long long n, bool out_bf16, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int k);

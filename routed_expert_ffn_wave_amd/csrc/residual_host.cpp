@@ -29,7 +29,7 @@ enum { RF_BF16 = 0, RF_Q4_0 = 1, RF_MXFP4 = 2, RF_FP8_B128 = 3, RF_NVFP4 = 4 };
 
 int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, const uint8_t* w2, const uint8_t* s13,
                   const uint8_t* s2, const uint16_t* x, const int32_t* ids, const float* w, const uint32_t* mask,
-                  int T, int E, int k, float* out, int threads);
+                  const int32_t* slot_of_expert, int T, int E, int k, float* out, int threads);
 
 namespace {
 
@@ -269,11 +269,13 @@ void run_parallel(int items, int threads, F&& f) {
 
 int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, const uint8_t* w2, const uint8_t* s13,
                   const uint8_t* s2, const uint16_t* x, const int32_t* ids, const float* w, const uint32_t* mask,
-                  int T, int E, int k, float* out, int threads) {
-  // the masked pairs, grouped by expert (flat pair index ascending inside a group)
+                  const int32_t* slot_of_expert, int T, int E, int k, float* out, int threads) {
+  // the cold pairs (mask bit set, or the expert's slot negative), grouped by expert (flat pair
+  // index ascending inside a group)
   auto take = [&](int t, int j) {
     const int e = ids[(size_t)t * k + j];
-    return ((mask[t] >> j) & 1u) && e >= 0 && e < E && e < n_experts;
+    if (e < 0 || e >= E || e >= n_experts) return false;
+    return mask ? ((mask[t] >> j) & 1u) != 0 : slot_of_expert[e] < 0;
   };
   std::vector<int> cnt(E + 1, 0);
   for (int t = 0; t < T; ++t)

@@ -56,16 +56,22 @@ def test_route_proj_validation():
 
 def test_cache_update_validation():
     L = ft.lib
-    args = lambda E, S, ml: (A, E, S, ml, A, A, A, A, A, A, A)
+    args = lambda E, S, ml, q=0.0: (A, E, S, ml, q, A, A, A, A, A, None, A, A)  # noqa: E731
     _err(L.ft_moe_cache_update(*args(0, 4, 1), None), ft.FT_E_INVAL, "E must be")
     _err(L.ft_moe_cache_update(*args(1025, 4, 1), None), ft.FT_E_INVAL, "E must be")
     _err(L.ft_moe_cache_update(*args(8, 0, 0), None), ft.FT_E_INVAL, "n_slots must be")
     _err(L.ft_moe_cache_update(*args(8, 1025, 1), None), ft.FT_E_INVAL, "n_slots must be")
     _err(L.ft_moe_cache_update(*args(8, 4, 5), None), ft.FT_E_INVAL, "max_loads must be")
     _err(L.ft_moe_cache_update(*args(8, 4, -1), None), ft.FT_E_INVAL, "max_loads must be")
-    _err(L.ft_moe_cache_update(None, 8, 4, 1, A, A, A, A, A, A, A, None), ft.FT_E_INVAL, "counts is null")
-    _err(L.ft_moe_cache_update(A, 8, 4, 1, A, A, MIS, A, A, A, A, None), ft.FT_E_INVAL, "last_use is not 16-byte")
-    _err(L.ft_moe_cache_update(A, 8, 4, 1, A, A, A, A, A, None, A, None), ft.FT_E_INVAL, "loads is null")
+    _err(L.ft_moe_cache_update(*args(8, 4, 1, 1.5), None), ft.FT_E_INVAL, "load_fraction must be")
+    _err(L.ft_moe_cache_update(*args(8, 4, 1, -0.1), None), ft.FT_E_INVAL, "load_fraction must be")
+    _err(L.ft_moe_cache_update(*args(8, 4, 1, float("nan")), None), ft.FT_E_INVAL, "load_fraction must be")
+    _err(L.ft_moe_cache_update(None, 8, 4, 1, 0.0, A, A, A, A, A, None, A, A, None), ft.FT_E_INVAL, "counts is null")
+    _err(L.ft_moe_cache_update(A, 8, 4, 1, 0.0, A, A, MIS, A, A, None, A, A, None), ft.FT_E_INVAL,
+         "last_use is not 16-byte")
+    _err(L.ft_moe_cache_update(A, 8, 4, 1, 0.0, A, A, A, A, A, MIS, A, A, None), ft.FT_E_INVAL,
+         "load_slot is not 16-byte")
+    _err(L.ft_moe_cache_update(A, 8, 4, 1, 0.0, A, A, A, A, A, None, None, A, None), ft.FT_E_INVAL, "loads is null")
 
 
 def test_cache_fill_validation():
@@ -87,11 +93,13 @@ def test_residual_validation():
     L = ft.lib
     bank = ft.ft_moe_bank(ft.FT_W_Q4_0, 16, 256, 128, 0x10000, 0x20000, 0x30000, 0x40000)
     ref = ctypes.byref(bank)
-    _err(L.ft_moe_residual_host(ref, A, A, A, A, 4, 16, 0, A, 0), ft.FT_E_INVAL, "k must be")
-    _err(L.ft_moe_residual_host(None, A, A, A, A, 4, 16, 2, A, 0), ft.FT_E_INVAL, "bank is null")
-    _err(L.ft_moe_residual_host(ref, A, A, A, A, 4, 16, 2, A, -1), ft.FT_E_INVAL, "n_threads")
-    _err(L.ft_moe_residual_host(ref, None, A, A, A, 4, 16, 2, A, 0), ft.FT_E_INVAL, "must not be null")
-    assert L.ft_moe_residual_host(ref, None, None, None, None, 0, 16, 2, None, 0) == ft.FT_OK
+    _err(L.ft_moe_residual_host(ref, A, A, A, A, None, 4, 16, 0, A, 0), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_residual_host(None, A, A, A, A, None, 4, 16, 2, A, 0), ft.FT_E_INVAL, "bank is null")
+    _err(L.ft_moe_residual_host(ref, A, A, A, A, None, 4, 16, 2, A, -1), ft.FT_E_INVAL, "n_threads")
+    _err(L.ft_moe_residual_host(ref, None, A, A, A, None, 4, 16, 2, A, 0), ft.FT_E_INVAL, "must not be null")
+    _err(L.ft_moe_residual_host(ref, A, A, A, A, A, 4, 16, 2, A, 0), ft.FT_E_INVAL, "exactly one of")
+    _err(L.ft_moe_residual_host(ref, A, A, A, None, None, 4, 16, 2, A, 0), ft.FT_E_INVAL, "exactly one of")
+    assert L.ft_moe_residual_host(ref, None, None, None, None, None, 0, 16, 2, None, 0) == ft.FT_OK
     _err(L.ft_moe_residual_add(A, A, 4, 12, 0, None), ft.FT_E_INVAL, "d must be")
     _err(L.ft_moe_residual_add(A, A, 4, 64, 0x8, None), ft.FT_E_INVAL, "unknown flags")
     _err(L.ft_moe_residual_add(None, A, 4, 64, 0, None), ft.FT_E_INVAL, "out is null")
@@ -145,6 +153,12 @@ def test_residual_host_bf16_on_cpu():
                 _, y = oracle.swiglu_ffn(xf[t:t + 1], w13b[e].float().numpy(), w2b[e].float().numpy())
                 ref[t] += float(wts[t, j]) * y[0].astype(np.float64)
     assert np.array_equal(got[2], np.zeros(d, np.float32))
+    # the slot-table form: experts 0 and 2 cold for the tokens whose mask marks them
+    slots = torch.tensor([-1, 5, -1], dtype=torch.int32)
+    by_slots = ft.ft_moe_residual_host(hb, x, ids, wts, None, n_threads=2, slot_of_expert=slots).numpy()
+    mask2 = torch.tensor([sum(1 << j for j in range(k) if int(slots[int(ids[t, j])]) < 0) for t in range(T)],
+                         dtype=torch.int32)
+    assert np.array_equal(by_slots, ft.ft_moe_residual_host(hb, x, ids, wts, mask2, n_threads=2).numpy())
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel < 5e-3, rel
 

@@ -45,6 +45,9 @@ UPDATE_CASES = [
     (32, 32, 8, 2, 32, 30, False),
     (16, 8, 4, 2, 0, 10, True),
 ]
+# (E, n_slots, T, k, max_loads, steps, load fraction)
+FRACTION_CASES = [(64, 16, 4, 4, 16, 40, 0.5), (256, 96, 16, 8, 32, 30, 0.37), (128, 32, 8, 8, 8, 30, 1.0),
+                  (32, 8, 8, 2, 8, 30, 0.1)]
 
 
 @pytest.mark.parametrize("case", UPDATE_CASES, ids=lambda c: "E{}_S{}_T{}_k{}_ml{}_n{}_{}".format(*c))
@@ -81,6 +84,25 @@ def test_cache_update_matches_oracle(ft, case):
         _check_state(cache, st, label)
         total_loads += n
     log(f"  ok: {total_loads} loads over {steps} steps")
+
+
+@pytest.mark.parametrize("case", FRACTION_CASES, ids=lambda c: "E{}_S{}_T{}_k{}_ml{}_n{}_q{}".format(*c))
+def test_cache_update_load_fraction(ft, case):
+    """The load fraction and the table of this step's loads, bit for bit against the oracle."""
+    E, S, T, k, ml, steps, q = case
+    log(f"cache update with load fraction {q}: E={E} S={S}")
+    st = oracle.CacheState(E, S)
+    cache = ft.ExpertCache(E, S, ml, load_fraction=q)
+    for step in range(steps):
+        counts = synth.zipf_counts(E, T, k, 9000 + E + S, step)
+        cs_ref, loads_ref, ls_ref = oracle.cache_update(counts, st, ml, q, with_load_slot=True)
+        cs, loads, nl = cache.update(torch.from_numpy(counts).cuda())
+        torch.cuda.synchronize()
+        n = int(nl.item())
+        assert n == len(loads_ref) and np.array_equal(loads[:n].cpu().numpy(), loads_ref), f"step {step}: loads"
+        assert np.array_equal(cs.cpu().numpy(), cs_ref), f"step {step}: compute_slot"
+        assert np.array_equal(cache.load_slot.cpu().numpy(), ls_ref), f"step {step}: load_slot"
+        _check_state(cache, st, f"step {step}")
 
 
 def _slot_arrays(bank, s: int):
@@ -294,3 +316,56 @@ def test_cache_step_graph_replay(ft):
             assert torch.equal(g_, e_), f"replay {i}: {n} differs from the eager step"
     assert int(cache.tick.item()) == steps
     log(f"  ok: {steps} replays")
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_0, synth.FMT_FP8_B128], ids=lambda f: synth.FMT_NAMES[f])
+def test_coexecuted_steps(ft, fmt):
+    """The bandwidth-adaptive split in one step: a fraction of the cold experts is copied to the GPU
+    and computed there after the copy, the rest on the host at the same time.  Per step: route,
+    permute, cache update (load fraction 0.5); the host reads ids, w and the updated slot table and
+    computes the pairs whose expert has no slot, while the device runs the fill (second stream), the
+    FFN of the experts resident before the step, then, after the fill, the FFN of the experts just
+    loaded, and the combine over the updated table.  The merged output equals the oracle layer with
+    every expert resident; the mask marks exactly the pairs the host computed."""
+    import threading
+    E, S, T, k, ml, steps, q = 16, 6, 16, 4, 4, 6, 0.5
+    w = synth.Workload("coexec", 86 + fmt, T=T, d=256, E=E, k=k, I=128, fmt=fmt, zipf=True)
+    log(f"co-executed steps {synth.FMT_NAMES[fmt]}")
+    canon_full = synth.make_bank(w, 0)
+    host = device_bank(canon_full).to_pinned_host()
+    dst = ft.DeviceBank.empty(fmt, S, w.d, w.I)
+    cache = ft.ExpertCache(E, S, ml, load_fraction=q)
+    st = oracle.CacheState(E, S)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    x_host = synth.activations(w, 0, T)
+    x = x_host.cuda()
+    for step in range(steps):
+        logits_host = synth.step_logits(w, step, T)
+        ids, wts = ft.ft_moe_route(logits_host.cuda(), k)
+        counts, offsets, gather, inv = ft.ft_moe_permute(ids, E)
+        cs, loads, nl = cache.update(counts)
+        ids_h, w_h, slots_h = ids.cpu(), wts.cpu(), cache.slot_of_expert.cpu()   # waits for the update
+        res = {}
+        th = threading.Thread(target=lambda: res.update(
+            r=ft.ft_moe_residual_host(host, x_host, ids_h, w_h, None, n_threads=4, slot_of_expert=slots_h)))
+        th.start()
+        side.wait_stream(main)
+        cache.fill(host, dst, stream=side)
+        y, _ = ft.ft_moe_grouped_ffn(dst, cs, x, k, offsets, gather)
+        main.wait_stream(side)
+        ft.ft_moe_grouped_ffn(dst, cache.load_slot, x, k, offsets, gather, y_sorted=y)
+        out, mask = ft.ft_moe_combine(y, None, ids, wts, inv, cache.slot_of_expert, w.d)
+        th.join()
+        ft.ft_moe_residual_add(out, res["r"].cuda())
+        torch.cuda.synchronize()
+        cs_ref, loads_ref, ls_ref = oracle.cache_update(counts.cpu().numpy(), st, ml, q, with_load_slot=True)
+        assert np.array_equal(cs.cpu().numpy(), cs_ref) and np.array_equal(cache.load_slot.cpu().numpy(), ls_ref)
+        m = mask.cpu().numpy().view(np.uint32)
+        want = ((slots_h.numpy()[ids_h.numpy()] < 0).astype(np.uint32) << np.arange(k, dtype=np.uint32)).sum(axis=1)
+        assert np.array_equal(m, want.astype(np.uint32)), f"step {step}: mask"
+        ora = oracle.layer(logits_host, x_host, canon_full, torch.arange(E, dtype=torch.int32), k)
+        assert np.array_equal(ids_h.numpy(), ora["ids"])
+        from gpu_util import assert_ffn_close
+        assert_ffn_close(out.cpu().numpy(), ora["out"], f"step {step}: co-executed layer")
+        log(f"  step {step}: {int(nl.item())} loads computed on the GPU this step, "
+            f"{int(sum(bin(int(v)).count('1') for v in m))} pairs on the host")
