@@ -385,6 +385,107 @@ def bench_residual(w: synth.Workload, T: int, steps: int, warmup: int, threads: 
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
+def bench_coexec(w: synth.Workload, T: int, steps: int, warmup: int, threads: int, fraction: float, max_loads: int):
+    """Co-executed steps: the cold experts of each step are split between the host link (a fraction
+    q of them copied to the GPU and computed there after the copy) and the host cores (the rest),
+    both at once, beside the device FFN of the resident experts.  The device bank starts with the
+    workload's resident set.  The same steps run with q = 0 (every cold pair on the host) for
+    comparison.  Own JSON line: value = ms per co-executed step (host thread joined, result merged)."""
+    import threading
+    import time as _time
+    S = w.n_resident or w.E
+    log(f"coexec: {w.name} T={T} slots={S} q={fraction} max_loads={max_loads}; packing {w.E} experts")
+    c = synth.make_bank(w.replace(n_resident=None, shared=False), 0, device="cuda")
+    host = ft.ft_moe_pack_bank(c.fmt, w.E, w.d, w.I, c.w13, c.w2, c.s13, c.s2).to_pinned_host()
+    del c
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    table = synth.slot_table(w, 0)
+    eos = torch.full((S,), -1, dtype=torch.int32)
+    for e in torch.nonzero(table >= 0).flatten().tolist():
+        eos[int(table[e])] = e
+    dst = ft.DeviceBank.empty(w.fmt, S, w.d, w.I)
+    pre = ft.ExpertCache(w.E, S, S)
+    pre.loads.copy_(torch.stack([eos, torch.arange(S, dtype=torch.int32)], dim=1))
+    pre.n_loads.fill_(S)
+    pre.fill(host, dst)
+    x_host = synth.activations(w, 0, T)
+    x = x_host.cuda()
+    k, E = w.k, w.E
+    n_seq = warmup + steps
+    logits = [synth.step_logits(w, i, T, device="cuda") for i in range(n_seq)]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    per_expert = sum(ft.ft_moe_bank_bytes(w.fmt, 1, w.d, w.I, which) for which in range(4))
+
+    def run(q, ml):
+        cache = ft.ExpertCache(E, S, ml, load_fraction=q)
+        cache.slot_of_expert.copy_(table)
+        cache.expert_of_slot.copy_(eos)
+        torch.cuda.synchronize()
+        rows = []
+        for i in range(n_seq):
+            t0 = _time.perf_counter()
+            ids, wt = ft.ft_moe_route(logits[i], k)
+            counts, offsets, gather, inv = ft.ft_moe_permute(ids, E)
+            cs, _, nl = cache.update(counts)
+            ids_h, w_h, slots_h = ids.cpu(), wt.cpu(), cache.slot_of_expert.cpu()
+            res, ht = {}, {}
+
+            def host_part():
+                a = _time.perf_counter()
+                res["r"] = ft.ft_moe_residual_host(host, x_host, ids_h, w_h, None, n_threads=threads,
+                                                   slot_of_expert=slots_h)
+                ht["s"] = _time.perf_counter() - a
+
+            th = threading.Thread(target=host_part)
+            th.start()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            side.wait_stream(main)
+            f0.record(side)
+            cache.fill(host, dst, stream=side)
+            f1.record(side)
+            y, _ = ft.ft_moe_grouped_ffn(dst, cs, x, k, offsets, gather)
+            main.wait_stream(side)
+            ft.ft_moe_grouped_ffn(dst, cache.load_slot, x, k, offsets, gather, y_sorted=y)
+            out, mask = ft.ft_moe_combine(y, None, ids, wt, inv, cache.slot_of_expert, w.d)
+            torch.cuda.synchronize()
+            t_gpu = _time.perf_counter() - t0
+            th.join()
+            ft.ft_moe_residual_add(out, res["r"].cuda())
+            torch.cuda.synchronize()
+            t_all = _time.perf_counter() - t0
+            cold = int((slots_h.numpy()[ids_h.numpy()] < 0).sum())
+            rows.append((t_all, t_gpu, ht["s"], f0.elapsed_time(f1) * 1e-3, int(nl.item()), cold))
+        return rows[warmup:]
+
+    base = run(0.0, 0)
+    co = run(fraction, max_loads)
+    mean = lambda rows, i: sum(r[i] for r in rows) / len(rows)  # noqa: E731
+    base_ms, co_ms = 1e3 * mean(base, 0), 1e3 * mean(co, 0)
+    host_ms, fill_ms, gpu_ms = 1e3 * mean(co, 2), 1e3 * mean(co, 3), 1e3 * mean(co, 1)
+    loads, cold = mean(co, 4), mean(co, 5)
+    log(f"coexec: host only {base_ms:.2f} ms/step (host {1e3 * mean(base, 2):.2f} ms, {mean(base, 5):.1f} cold pairs); "
+        f"q={fraction}: {co_ms:.2f} ms/step (host {host_ms:.2f} ms for {cold:.1f} pairs, fill {fill_ms:.2f} ms for "
+        f"{loads:.1f} experts, device part {gpu_ms:.2f} ms)")
+    fill_gbs = loads * per_expert / (fill_ms * 1e-3) / 1e9 if fill_ms > 0 else 0.0
+    if fill_ms >= host_ms:
+        roof = {"bound": "pcie", "achieved": round(fill_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                "frac": round(fill_gbs / PCIE_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "host", "achieved": round(host_ms, 3), "peak": None, "unit": "ms", "frac": None}
+    roof.update({"traffic": None, "kernel": "cache_fill_kernel (host link) beside ft_moe_residual_host (host cores)",
+                 "host_only_ms_per_step": round(base_ms, 3), "host_ms": round(host_ms, 3), "fill_ms": round(fill_ms, 3),
+                 "device_part_ms": round(gpu_ms, 3), "loads_per_step": round(loads, 2),
+                 "host_pairs_per_step": round(cold, 2), "fill_gbs": round(fill_gbs, 2)})
+    print(json.dumps({"metric": "co-executed layer step (cold experts split between host link and host cores)",
+                      "value": round(co_ms, 3), "unit": "ms/step", "n_gpus": 1, "steps": steps, "warmup": warmup,
+                      "ms_per_step": round(co_ms, 3), "higher_is_better": False, "scaling": "weak",
+                      "vs_baseline": None, "dtype": synth.FMT_NAMES[w.fmt], "data": "synthetic (seeded)",
+                      "config": {"workload": f"coexec/{w.name}", "T": T, "E": E, "k": k, "d": w.d, "I": w.I,
+                                 "slots": S, "load_fraction": fraction, "max_loads": max_loads, "threads": threads},
+                      "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +507,8 @@ def main():
     ap.add_argument("--residual", action="store_true",
                     help="time the layer with its cold experts on the host (ft_moe_residual_host) instead")
     ap.add_argument("--threads", type=int, default=16, help="host threads of the residual path")
+    ap.add_argument("--coexec", type=float, default=None, metavar="Q",
+                    help="time co-executed steps: a fraction Q of each step's cold experts copied to the GPU, the rest on the host")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -426,6 +529,9 @@ def main():
     decode = T <= 64
     if args.route_proj:
         bench_route_proj(w, T, args.steps, args.warmup)
+        return
+    if args.coexec is not None:
+        bench_coexec(w, T, args.steps, args.warmup, args.threads, args.coexec, args.max_loads)
         return
     if args.residual:
         bench_residual(w, T, args.steps, args.warmup, args.threads)
