@@ -7,10 +7,15 @@ for the default decode workload (T=8, d=2048, E=128, k=8, I=768, Q4_0 banks) a s
 layers run back to back on one stream, captured once into a HIP graph and replayed.  Inputs are seeded
 synthetic tensors already resident in HBM.  Prints one JSON line.
 
-The dominant unit is the grouped-FFN call; its average duration is timed with HIP events on the
-stream it runs on, over timed eager replays of the same steps, and compared with the HBM (decode) or
-MFMA (prefill) roofline of its algorithmic bytes or flops.  The CPU baseline times the scalar oracle
-on a bounded sample of the same workload on the host.
+The dominant unit is the layer call; its average duration is timed with HIP events on the stream
+it runs on, over timed eager replays of the same steps, and compared with the HBM and MFMA
+rooflines of its algorithmic bytes and flops (the bound is the one with the longer roofline time).
+The CPU baseline times the scalar oracle on a bounded sample of the same workload on the host.
+
+Other modes print their own line instead: --route-proj (router projection + top-k), --cache SLOTS
+(layer steps with the expert cache streaming cold experts from pinned host memory), --residual
+(the cold pairs computed on the host cores), --coexec Q (the cold experts of each step split
+between the host link and the host cores by load fraction Q).
 """
 from __future__ import annotations
 

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import compare_layer, device_bank, log
+from gpu_util import assert_ffn_close, compare_layer, device_bank, log
 
 pytestmark = pytest.mark.gpu
 
@@ -365,7 +365,6 @@ def test_coexecuted_steps(ft, fmt):
         assert np.array_equal(m, want.astype(np.uint32)), f"step {step}: mask"
         ora = oracle.layer(logits_host, x_host, canon_full, torch.arange(E, dtype=torch.int32), k)
         assert np.array_equal(ids_h.numpy(), ora["ids"])
-        from gpu_util import assert_ffn_close
         assert_ffn_close(out.cpu().numpy(), ora["out"], f"step {step}: co-executed layer")
         log(f"  step {step}: {int(nl.item())} loads computed on the GPU this step, "
             f"{int(sum(bin(int(v)).count('1') for v in m))} pairs on the host")
