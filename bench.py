@@ -390,12 +390,15 @@ def bench_residual(w: synth.Workload, T: int, steps: int, warmup: int, threads: 
                       "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
-def bench_coexec(w: synth.Workload, T: int, steps: int, warmup: int, threads: int, fraction: float, max_loads: int):
+def bench_coexec(w: synth.Workload, T: int, steps: int, warmup: int, threads: int, fraction, max_loads: int):
     """Co-executed steps: the cold experts of each step are split between the host link (a fraction
     q of them copied to the GPU and computed there after the copy) and the host cores (the rest),
     both at once, beside the device FFN of the resident experts.  The device bank starts with the
     workload's resident set.  The same steps run with q = 0 (every cold pair on the host) for
-    comparison.  Own JSON line: value = ms per co-executed step (host thread joined, result merged)."""
+    comparison.  With fraction "auto" the split is chosen the way the pages' engine does at start-up:
+    the host link rate P (one fill of 8 experts) and the host residual rate H (every pair of the first
+    step on the host) are measured, and q = P / (P + H) makes both paths finish together.  Own JSON
+    line: value = ms per co-executed step (host thread joined, result merged)."""
     import threading
     import time as _time
     S = w.n_resident or w.E
@@ -410,17 +413,43 @@ def bench_coexec(w: synth.Workload, T: int, steps: int, warmup: int, threads: in
     for e in torch.nonzero(table >= 0).flatten().tolist():
         eos[int(table[e])] = e
     dst = ft.DeviceBank.empty(w.fmt, S, w.d, w.I)
+    x_host = synth.activations(w, 0, T)
+    per_expert = sum(ft.ft_moe_bank_bytes(w.fmt, 1, w.d, w.I, which) for which in range(4))
+    auto = None
+    if fraction == "auto":
+        nprobe = min(8, S)
+        probe = ft.ExpertCache(w.E, S, nprobe)
+        probe.loads.copy_(torch.stack([torch.arange(nprobe, dtype=torch.int32)] * 2, dim=1))
+        probe.n_loads.fill_(nprobe)
+        probe.fill(host, dst)                         # first touch of the pages
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        probe.fill(host, dst)
+        b.record()
+        torch.cuda.synchronize()
+        P = nprobe * per_expert / (a.elapsed_time(b) * 1e-3) / 1e9
+        ids0, w0 = ft.ft_moe_route(synth.step_logits(w, 0, T, device="cuda"), w.k)
+        ids0, w0 = ids0.cpu(), w0.cpu()
+        nocache = torch.full((w.E,), -1, dtype=torch.int32)
+        ft.ft_moe_residual_host(host, x_host, ids0, w0, None, n_threads=threads, slot_of_expert=nocache)
+        t0 = _time.perf_counter()
+        ft.ft_moe_residual_host(host, x_host, ids0, w0, None, n_threads=threads, slot_of_expert=nocache)
+        H = len(set(ids0.flatten().tolist())) * per_expert / (_time.perf_counter() - t0) / 1e9
+        fraction = round(P / (P + H), 3)
+        auto = {"link_gbs": round(P, 2), "host_gbs": round(H, 2), "q": fraction}
+        log(f"coexec: measured host link {P:.1f} GB/s, host residual {H:.1f} GB/s of weights -> q = {fraction}")
+    else:
+        fraction = float(fraction)
     pre = ft.ExpertCache(w.E, S, S)
     pre.loads.copy_(torch.stack([eos, torch.arange(S, dtype=torch.int32)], dim=1))
     pre.n_loads.fill_(S)
     pre.fill(host, dst)
-    x_host = synth.activations(w, 0, T)
     x = x_host.cuda()
     k, E = w.k, w.E
     n_seq = warmup + steps
     logits = [synth.step_logits(w, i, T, device="cuda") for i in range(n_seq)]
     main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-    per_expert = sum(ft.ft_moe_bank_bytes(w.fmt, 1, w.d, w.I, which) for which in range(4))
 
     def run(q, ml):
         cache = ft.ExpertCache(E, S, ml, load_fraction=q)
@@ -481,7 +510,7 @@ def bench_coexec(w: synth.Workload, T: int, steps: int, warmup: int, threads: in
     roof.update({"traffic": None, "kernel": "cache_fill_kernel (host link) beside ft_moe_residual_host (host cores)",
                  "host_only_ms_per_step": round(base_ms, 3), "host_ms": round(host_ms, 3), "fill_ms": round(fill_ms, 3),
                  "device_part_ms": round(gpu_ms, 3), "loads_per_step": round(loads, 2),
-                 "host_pairs_per_step": round(cold, 2), "fill_gbs": round(fill_gbs, 2)})
+                 "host_pairs_per_step": round(cold, 2), "fill_gbs": round(fill_gbs, 2), "measured_split": auto})
     print(json.dumps({"metric": "co-executed layer step (cold experts split between host link and host cores)",
                       "value": round(co_ms, 3), "unit": "ms/step", "n_gpus": 1, "steps": steps, "warmup": warmup,
                       "ms_per_step": round(co_ms, 3), "higher_is_better": False, "scaling": "weak",
@@ -512,8 +541,9 @@ def main():
     ap.add_argument("--residual", action="store_true",
                     help="time the layer with its cold experts on the host (ft_moe_residual_host) instead")
     ap.add_argument("--threads", type=int, default=16, help="host threads of the residual path")
-    ap.add_argument("--coexec", type=float, default=None, metavar="Q",
-                    help="time co-executed steps: a fraction Q of each step's cold experts copied to the GPU, the rest on the host")
+    ap.add_argument("--coexec", default=None, metavar="Q",
+                    help="time co-executed steps: a fraction Q of each step's cold experts copied to the GPU, the rest "
+                         "on the host ('auto': Q from the host link and host residual rates measured first)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
