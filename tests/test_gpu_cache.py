@@ -368,3 +368,15 @@ def test_coexecuted_steps(ft, fmt):
         assert_ffn_close(out.cpu().numpy(), ora["out"], f"step {step}: co-executed layer")
         log(f"  step {step}: {int(nl.item())} loads computed on the GPU this step, "
             f"{int(sum(bin(int(v)).count('1') for v in m))} pairs on the host")
+
+
+def test_cache_fill_refuses_pageable_source(ft):
+    """A source bank in ordinary (pageable) host memory is refused before any launch."""
+    E, S, d, I = 4, 2, 256, 128
+    fmt = synth.FMT_Q4_0
+    arrs = [torch.zeros(ft.ft_moe_bank_bytes(fmt, E, d, I, which), dtype=torch.uint8) for which in range(4)]
+    src = ft.DeviceBank(fmt, E, d, I, *arrs)
+    dst = ft.DeviceBank.empty(fmt, S, d, I)
+    cache = ft.ExpertCache(E, S, 1)
+    with pytest.raises(ft.FtError, match="neither pinned host memory nor device memory"):
+        cache.fill(src, dst)
