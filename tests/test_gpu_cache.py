@@ -44,6 +44,8 @@ UPDATE_CASES = [
     (1024, 16, 64, 8, 16, 12, True),
     (32, 32, 8, 2, 32, 30, False),
     (16, 8, 4, 2, 0, 10, True),
+    (1, 1, 4, 1, 1, 6, False),            # one expert, one slot
+    (1024, 1024, 128, 8, 1024, 4, False),  # the largest tables, every slot loadable in one step
 ]
 # (E, n_slots, T, k, max_loads, steps, load fraction)
 FRACTION_CASES = [(64, 16, 4, 4, 16, 40, 0.5), (256, 96, 16, 8, 32, 30, 0.37), (128, 32, 8, 8, 8, 30, 1.0),
