@@ -300,8 +300,9 @@ int ft_moe_cache_fill(const ft_moe_bank* src, const ft_moe_bank* dst, const int3
  * w[t][j] * y.  out [T][d] fp32 is overwritten (zero for a token with no such pair).  A pair is
  * cold when bit j of residual_mask[t] is set (the mask ft_moe_combine or ft_moe_layer wrote), or,
  * with residual_mask NULL, when slot_of_expert[e] < 0 (a host copy of the slot table the device
- * layer uses, so the host can start as soon as the routing is known, beside the device layer).
- * Exactly one of the two is given.
+ * layer uses, so the host can start as soon as the routing is known, beside the device layer; the
+ * host does not know the device bank's slot count, so such a table marks every expert without a
+ * valid slot with -1, as the tables of ft_moe_cache_update do).  Exactly one of the two is given.
  * Everything is host memory: host_bank (a host pointer to a bank description whose arrays are in
  * host memory, pinned or not, in the device layout of ft_moe_pack_bank, expert e in slot e: the bank
  * ft_moe_cache_fill reads), x bf16 [T][d], ids [T][k], w [T][k], residual_mask [T], out.  Runs on
