@@ -261,14 +261,18 @@ def dequant_slot(bank, slot: int, lib=None):
 
 # ------------------------------------------------------------------------- the layer
 
+CHUNK_ROWS = 256   # rows per job of the threaded layer
+
+
 def layer(logits, x_bf16, bank, slot_of, k: int, shared_slot: int = -1, tokens=None, lib=None, workers: int = 1):
     """One MoE layer, optionally only for a sample of tokens.
 
     Returns a dict with ids, w, counts, offsets, gather, inv (whole layer), and for the computed
     tokens: mask [T], out [T][d] (zero rows for tokens not computed), y_pos (sorted positions
     computed), y_rows fp32 [len(y_pos)][d], y_shared fp32 [T][d] or None.
-    `workers` > 1 runs independent expert groups on that many threads (the C calls release the
-    GIL); each group's arithmetic is unchanged.
+    `workers` > 1 runs the expert groups on that many threads (the C calls release the GIL), large
+    groups cut into runs of at most CHUNK_ROWS rows so that a skewed routing still spreads over the
+    threads; every row's arithmetic is the same as with one worker (rows are independent).
     """
     lib = lib or _load()
     L = _np(logits, np.float32)
@@ -286,8 +290,9 @@ def layer(logits, x_bf16, bank, slot_of, k: int, shared_slot: int = -1, tokens=N
             continue
         pos = np.arange(offsets[e], offsets[e + 1])
         pos = pos[want[gather[pos] // k]]
-        if len(pos):
-            jobs.append((s, pos))
+        step = CHUNK_ROWS if workers > 1 else max(len(pos), 1)
+        for r0 in range(0, len(pos), step):
+            jobs.append((s, pos[r0:r0 + step]))
 
     def run(job):
         s, pos = job

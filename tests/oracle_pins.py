@@ -337,6 +337,45 @@ def pin_layer_float64(lib):
     assert np.linalg.norm(r["out"] - out) <= 1e-5 * np.linalg.norm(out)
 
 
+def pin_layer_sampled_threaded(lib, ora=oracle):
+    """The layer restricted to a token sample and run on several threads (the form the full-size GPU
+    tests check against) equals the whole single-threaded layer on the sampled tokens, bit for bit:
+    same rows of out, mask and y_shared, zero rows elsewhere, and y rows for exactly the resident
+    pairs of the sampled tokens (their sorted positions from the definition of the permutation).
+    `ora` is the oracle module (a planted copy in the mutant tests)."""
+    rng = np.random.default_rng(20)
+    old_rows = ora.CHUNK_ROWS
+    ora.CHUNK_ROWS = 5            # groups of these tiny layers span several threaded runs
+    try:
+        for fmt, (T, d, E, k, I) in ((0, (40, 64, 7, 3, 32)), (1, (33, 64, 9, 2, 64)), (2, (24, 32, 5, 4, 32))):
+            w, bank, L, x = _tiny_layer_inputs(rng, T, d, E + 1, k, I, fmt=fmt)    # slot E: shared expert
+            L = L[:, :E].copy()
+            slot_of = rng.permutation(E).astype(np.int32)
+            slot_of[rng.choice(E, size=2, replace=False)] = -1                     # two experts not resident
+            full = ora.layer(L, x, bank, slot_of, k, shared_slot=E, lib=lib)
+            ids_flat = full["ids"].reshape(-1)
+            for S in (rng.choice(T, size=T // 3, replace=False), np.array([0]), np.array([T - 1]), np.arange(T)):
+                S = np.sort(S)
+                part = ora.layer(L, x, bank, slot_of, k, shared_slot=E, tokens=S, lib=lib, workers=4)
+                for key in ("ids", "w", "counts", "offsets", "gather", "inv"):
+                    assert np.array_equal(part[key], full[key]), key
+                assert np.array_equal(part["tokens"], S)
+                inS = np.zeros(T, bool)
+                inS[S] = True
+                assert np.array_equal(part["out"][inS], full["out"][inS])
+                assert (part["out"][~inS] == 0).all()
+                assert np.array_equal(part["mask"][inS], full["mask"][inS]) and (part["mask"][~inS] == 0).all()
+                assert np.array_equal(part["y_shared"][inS], full["y_shared"][inS])
+                assert (part["y_shared"][~inS] == 0).all()
+                want = [p for p in range(T * k) if inS[full["gather"][p] // k] and slot_of[ids_flat[full["gather"][p]]] >= 0]
+                assert part["y_pos"].tolist() == want
+                where = {int(p): i for i, p in enumerate(full["y_pos"])}
+                rows = [where[int(p)] for p in part["y_pos"]]
+                assert np.array_equal(part["y_rows"], full["y_rows"][rows])
+    finally:
+        ora.CHUNK_ROWS = old_rows
+
+
 def pin_combine_cases(lib):
     rng = np.random.default_rng(19)
     T, d, E, k = 9, 32, 5, 3
@@ -562,6 +601,6 @@ def pin_cache_invariants(lib):
 
 ALL_PINS = [pin_route_bruteforce, pin_route_special_cases, pin_route_weights_float64, pin_permute,
             pin_decoder_tables, pin_dequant_roundtrip, pin_dequant_layouts, pin_ffn_float64,
-            pin_layer_identical_experts, pin_layer_float64, pin_combine_cases, pin_router_logits_worked_example,
+            pin_layer_identical_experts, pin_layer_float64, pin_layer_sampled_threaded, pin_combine_cases, pin_router_logits_worked_example,
             pin_router_logits_one_hot, pin_router_logits_exact_sum, pin_cache_textbook_lru,
             pin_cache_worked_example, pin_cache_invariants, pin_cache_load_fraction]

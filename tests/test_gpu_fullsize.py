@@ -2,12 +2,16 @@
 calls captured into a HIP graph and replayed.  Inputs follow the seeded recipe, generated on the GPU
 (large banks) and copied to the host for the oracle.  Routing, permutation and mask are compared
 bit for bit over the whole layer; FFN rows and outputs over every token where the oracle finishes
-in seconds, else over a seeded token sample that holds the first and last token."""
+in seconds (the bf16 prefill layer of 4096 tokens included), else over a seeded token sample that
+holds the first and last token and, for the Zipf-routed resident bank, every token of the smallest
+expert groups."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from gpu_util import compare_layer, device_bank, host_inputs, log, run_gpu_layer_graph, sample_tokens
 
@@ -45,11 +49,24 @@ def _make_bank(w: synth.Workload, layer: int):
     return bank
 
 
-def _check(ft, li, bank_dev, n_sample: int, label: str):
+def _small_group_tokens(host, n_groups: int):
+    """Every token of the n_groups smallest non-empty resident expert groups (their rows sit in the
+    partly filled tail tiles of the GEMM kernels), from the oracle's routing of the same logits."""
+    w = host.workload
+    ids, _ = oracle.route(host.logits, w.k)
+    slot = host.slot_of_expert.numpy()
+    counts = np.bincount(ids.reshape(-1), minlength=w.E)
+    groups = [e for e in np.argsort(counts, kind="stable") if counts[e] > 0 and slot[e] >= 0][:n_groups]
+    return np.unique(np.nonzero(np.isin(ids, groups).any(axis=1))[0])
+
+
+def _check(ft, li, bank_dev, n_sample: int, label: str, small_groups: int = 0):
     log(f"{label}: T={li.T} d={li.workload.d} E={li.workload.E} k={li.workload.k} I={li.workload.I}")
     g = run_gpu_layer_graph(li, bank_dev)
     host = host_inputs(li)
     tokens = None if li.T <= n_sample else sample_tokens(li.T, n_sample, seed=li.T + 17 * li.layer)
+    if tokens is not None and small_groups:
+        tokens = np.union1d(tokens, _small_group_tokens(host, small_groups))
     compare_layer(host, g, tokens=tokens, label=label)
 
 
@@ -63,7 +80,7 @@ def test_decode_q4_0_full(ft, layer):
 def test_prefill_bf16_zipf_full(ft):
     w = W["prefill_bf16_zipf"]
     li = _inputs(w, 0, w.T)
-    _check(ft, li, device_bank(li.bank), n_sample=12, label="prefill_bf16_zipf")
+    _check(ft, li, device_bank(li.bank), n_sample=w.T, label="prefill_bf16_zipf")  # every token
 
 
 @pytest.fixture(scope="module")
@@ -98,9 +115,9 @@ def fp8_bank(ft):
     return host, dev
 
 
-@pytest.mark.parametrize("T,n_sample", [(1, 1), (16, 16), (256, 8), (4096, 8), (16384, 8)])
+@pytest.mark.parametrize("T,n_sample", [(1, 1), (16, 16), (256, 256), (4096, 8), (16384, 8)])
 def test_fp8_resident_full(ft, fp8_bank, T, n_sample):
     w = W["fp8_resident"]
     host, dev = fp8_bank
     li = _inputs(w, 0, T, bank=host)
-    _check(ft, li, dev, n_sample=n_sample, label=f"fp8_resident T={T}")
+    _check(ft, li, dev, n_sample=n_sample, label=f"fp8_resident T={T}", small_groups=4)

@@ -73,3 +73,44 @@ def test_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name} passed every pin"
+
+
+# Planted mistakes in the Python composition of the layer (oracle/__init__.py): the token filter,
+# the threaded runs and the compaction of the computed rows.  Each must trip the pin of the
+# sampled, threaded layer (or the other layer pins).
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+PY_MUTANTS = {
+    "filter_by_slot_index": ("pos = pos[want[gather[pos] // k]]", "pos = pos[want[gather[pos] % k]]"),
+    "filter_dropped": ("pos = pos[want[gather[pos] // k]]", "pos = pos"),
+    "threaded_runs_reordered": ("ys = list(ex.map(run, jobs))", "ys = list(ex.map(run, jobs))[::-1]"),
+    "run_truncated": ("jobs.append((s, pos[r0:r0 + step]))", "jobs.append((s, pos[r0:r0 + step - 1]))"),
+    "compaction_uses_sorted_row": ("local_inv[flat_ok] = local[inv[flat_ok]]", "local_inv[flat_ok] = inv[flat_ok]"),
+    "shared_rows_unfiltered": ("_, ysh = swiglu_ffn(xf[tok], w13, w2, lib=lib)", "_, ysh = swiglu_ffn(xf[:len(tok)], w13, w2, lib=lib)"),
+    "combine_all_tokens": ("tok_list = np.nonzero(want)[0].astype(np.int32)", "tok_list = np.arange(T, dtype=np.int32)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_layer_mutant_is_caught(name, tmp_path):
+    import importlib.util
+
+    from oracle_pins import pin_layer_float64, pin_layer_identical_experts, pin_layer_sampled_threaded
+    old, new = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site of {name} not found exactly once"
+    path = tmp_path / "oracle_mutant.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"oracle_mutant_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    lib = oracle._load()
+    caught = []
+    for pin in (pin_layer_sampled_threaded,):
+        try:
+            pin(lib, ora=mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed the layer pins"
+    # the unplanted module passes the same pins (the planted copy differs only at the mutation site)
+    for pin in (pin_layer_float64, pin_layer_identical_experts):
+        pin(lib)
