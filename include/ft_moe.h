@@ -28,7 +28,9 @@
  *     readable with ft_moe_last_error() on the same host thread.  No C++ exception crosses the ABI.
  *   - Every device pointer must be 16-byte aligned; all arrays are dense and row-major.
  *   - Limits: T >= 0 (T == 0 enqueues nothing), 1 <= E <= 1024, 1 <= k <= min(E, 32).
- *   - Calls are reentrant; independent calls may run on different streams concurrently.
+ *   - Calls are reentrant: host threads may call concurrently, and independent calls may run on
+ *     different streams concurrently (ft_moe_layer's one-kernel path expects the device to itself:
+ *     see there).
  */
 #ifndef FT_MOE_H
 #define FT_MOE_H
@@ -221,6 +223,11 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
  * zero).  Its first int32 is a status word that the fused kernel sets non-zero if an internal
  * dependency wait gave up (results are then invalid); the library never clears it, and it stays 0
  * in every correct run.  Calls that may overlap need separate workspaces.
+ * The one-kernel path sizes its grid to the blocks the device holds at once and its waits end
+ * promptly only when all of them run together: it expects the device's compute units to itself.
+ * Beside a long kernel on another stream its waits can last until that kernel ends, or give up
+ * after 2^20 polls (about a second) with the status word set; use FT_LAYER_UNFUSED for such
+ * overlap.
  * flags: FT_PATH_*, FT_OUT_BF16, FT_LAYER_UNFUSED.  T == 0 only writes counts = offsets = 0.
  */
 int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,

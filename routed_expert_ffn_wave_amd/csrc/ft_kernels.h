@@ -4,7 +4,52 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace ftk {
+
+// What a kernel's launch code reuses from call to call: the device's CU count and the blocks of the
+// kernel one CU holds at the largest dynamic-LDS size it has been given on that device (so the count
+// never exceeds what a smaller request allows).  One instance per kernel; every read and update is
+// under its mutex, so host threads may launch concurrently on any devices.
+struct LaunchFacts {
+  int per_cu;  // blocks per CU
+  int cus;     // compute units of the current device
+};
+class LaunchCache {
+ public:
+  // Sets the kernel's dynamic-LDS limit to at least `lds` on the current device (once per larger
+  // size) and returns the facts above for `threads` threads per block.
+  hipError_t get(const void* kern, int threads, size_t lds, LaunchFacts* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu_);
+    if (cus_[dev] == 0 &&
+        hipDeviceGetAttribute(&cus_[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      cus_[dev] = 0;
+      return hipGetLastError();
+    }
+    if (per_cu_[dev] == 0 || lds > lds_[dev]) {
+      int per_cu = 0;
+      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return hipGetLastError();
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess)
+        return hipGetLastError();
+      per_cu_[dev] = per_cu > 0 ? per_cu : 1;
+      lds_[dev] = lds;
+    }
+    *out = LaunchFacts{per_cu_[dev], cus_[dev]};
+    return hipSuccess;
+  }
+
+ private:
+  static constexpr int MAXDEV = 64;
+  std::mutex mu_;
+  size_t lds_[MAXDEV] = {};
+  int per_cu_[MAXDEV] = {};
+  int cus_[MAXDEV] = {};
+};
 
 // Everything the grouped FFN kernels read or write, in device memory.
 struct FfnArgs {

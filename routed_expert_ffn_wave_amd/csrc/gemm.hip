@@ -336,22 +336,12 @@ template <int FMT, bool GATEUP, int WN>
 static hipError_t launch_gemm_cfg(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   auto kern = gemm_kernel<FMT, GATEUP, WN>;
   const size_t lds = gemm_lds_bytes(a.E, 64 * WN);
-  static int resident_per_cu = -1;
-  static size_t resident_lds = 0;
-  if (resident_per_cu < 0 || lds > resident_lds) {
-    int per_cu = 0;
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipGetLastError();
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) return hipGetLastError();
-    resident_per_cu = per_cu > 0 ? per_cu : 1;
-    resident_lds = lds;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+  static LaunchCache cache;
+  LaunchFacts f;
+  if (cache.get((const void*)kern, 256, lds, &f) != hipSuccess) return hipGetLastError();
   const int ntiles = (GATEUP ? 2 * a.I : a.d) / (64 * WN);
   long long blocks = (long long)tiles_upper * ntiles;
-  const long long cap = (long long)resident_per_cu * cus;
+  const long long cap = (long long)f.per_cu * f.cus;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, s, a);

@@ -815,17 +815,10 @@ __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(FfnArgs a) {
 template <int FMT, bool GATEUP>
 hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   auto kern = gemm_wide_kernel<FMT, GATEUP>;
-  static bool attr_set = false;
-  static int cus = 0;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)wide_lds_bytes<FMT>(512)) != hipSuccess)
-      return hipGetLastError();
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
-    attr_set = true;
-  }
+  static LaunchCache cache;  // the LDS limit is set once for the largest E (512)
+  LaunchFacts f;
+  if (cache.get((const void*)kern, 256, wide_lds_bytes<FMT>(512), &f) != hipSuccess) return hipGetLastError();
+  const int cus = f.cus;
   const int ntiles = (GATEUP ? 2 * a.I : a.d) / WBN;
   long long blocks = (long long)tiles_upper * ntiles;
   if (blocks > cus) blocks = cus;  // one block per CU (the ring takes most of its LDS)
@@ -837,17 +830,10 @@ hipError_t launch_wide(const FfnArgs& a, int tiles_upper, hipStream_t s) {
 template <bool GATEUP>
 hipError_t launch_bd(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   auto kern = gemm_bd_kernel<GATEUP>;
-  static bool attr_set = false;
-  static int cus = 0;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bd_lds_bytes(512)) !=
-        hipSuccess)
-      return hipGetLastError();
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
-    attr_set = true;
-  }
+  static LaunchCache cache;  // the LDS limit is set once for the largest E (512)
+  LaunchFacts f;
+  if (cache.get((const void*)kern, 256, bd_lds_bytes(512), &f) != hipSuccess) return hipGetLastError();
+  const int cus = f.cus;
   const int ntiles = (GATEUP ? 2 * a.I : a.d) / WBN;
   long long blocks = (long long)tiles_upper * ntiles;
   if (blocks > cus) blocks = cus;
@@ -859,17 +845,10 @@ hipError_t launch_bd(const FfnArgs& a, int tiles_upper, hipStream_t s) {
 template <bool GATEUP>
 hipError_t launch_f8(const FfnArgs& a, int tiles_upper, hipStream_t s) {
   auto kern = gemm_f8_kernel<GATEUP>;
-  static bool attr_set = false;
-  static int cus = 0;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f8_lds_bytes(512)) !=
-        hipSuccess)
-      return hipGetLastError();
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
-    attr_set = true;
-  }
+  static LaunchCache cache;  // the LDS limit is set once for the largest E (512)
+  LaunchFacts f;
+  if (cache.get((const void*)kern, 256, f8_lds_bytes(512), &f) != hipSuccess) return hipGetLastError();
+  const int cus = f.cus;
   const int ntiles = (GATEUP ? 2 * a.I : a.d) / F8_BN;
   long long blocks = (long long)tiles_upper * ntiles;
   if (blocks > cus) blocks = cus;

@@ -62,24 +62,13 @@ static hipError_t launch_cfg(const FfnArgs& a, int groups_upper, long long rows_
   auto kern = gemv_kernel<FMT, GATEUP, WPB, NT>;
   const int K = GATEUP ? a.d : a.I;
   const size_t lds = gv_group_bytes(a.E) + gv_union_bytes(FMT, K, NT, WPB);
-  static int resident_per_cu = -1;  // blocks of this kernel per CU, for the largest LDS request seen
-  static size_t resident_lds = 0;
-  if (resident_per_cu < 0 || lds > resident_lds) {
-    int per_cu = 0;
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipGetLastError();
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WPB * 64, lds) != hipSuccess)
-      return hipGetLastError();
-    resident_per_cu = per_cu > 0 ? per_cu : 1;
-    resident_lds = lds;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+  static LaunchCache cache;
+  LaunchFacts f;
+  if (cache.get((const void*)kern, WPB * 64, lds, &f) != hipSuccess) return hipGetLastError();
   const int ncb = (GATEUP ? 2 * a.I : a.d) / 64;
   const long long chunks = (rows_upper + NT - 1) / NT + groups_upper;
   long long blocks = chunks * ncb;
-  const long long cap = (long long)resident_per_cu * cus;
+  const long long cap = (long long)f.per_cu * f.cus;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WPB * 64), lds, s, a);

@@ -136,6 +136,8 @@ __device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int
         L.gather[p] = f;
         L.inv[f] = p;
       }
+    } else if (f < n) {
+      s_crow[f] = -1;  // an id outside [0, E) (a row of NaN logits): no y row, as in the combine kernel
     }
   }
   int ex_lt[VPL], ex_eq[VPL];
@@ -372,23 +374,12 @@ static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   const FfnArgs& a = L.f;
   const size_t lds = ((layer_meta_ints(a.T, a.E, a.k, NT) * 4 + 15) & ~(size_t)15) +
                      layer_union_bytes(FMT, a.d, a.I, NT, WPB);
-  static int resident_per_cu = -1;
-  static size_t resident_lds = 0;
-  if (resident_per_cu < 0 || lds > resident_lds) {
-    int per_cu = 0;
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipGetLastError();
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WPB * 64, lds) != hipSuccess)
-      return hipGetLastError();
-    resident_per_cu = per_cu > 0 ? per_cu : 1;
-    resident_lds = lds;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipGetLastError();
+  static LaunchCache cache;
+  LaunchFacts f;
+  if (cache.get((const void*)kern, WPB * 64, lds, &f) != hipSuccess) return hipGetLastError();
   // at most the blocks the device holds at once (every block runs, so every queue advances)
   const long long items = (long long)L.n_rc * (2 * a.I / 64 + a.d / (64 * LAYER_RPL2));
-  long long blocks = (long long)resident_per_cu * cus;
+  long long blocks = (long long)f.per_cu * f.cus;
   if (blocks > items) blocks = items;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WPB * 64), lds, s, L);

@@ -370,3 +370,89 @@ def test_graph_capture_replays(ft):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out, eager)
+
+
+@pytest.mark.parametrize("unfused", [False, True])
+def test_layer_nan_row_wide_router(ft, unfused):
+    """A token whose logits are all NaN (unspecified input) with E = 512, where routing runs one
+    token per wave and gives that token no valid expert: the layer still completes with status 0,
+    the token carries every mask bit and a zero output row, and every other token matches the
+    oracle (run with that row replaced by zeros; tokens are routed independently)."""
+    from gpu_util import assert_ffn_close
+    w = synth.Workload("nan_row", 71, T=6, d=256, E=512, k=8, I=128, fmt=synth.FMT_BF16)
+    li = synth.layer_inputs(w, layer=0)
+    bad = 2
+    li.logits = li.logits.clone()
+    li.logits[bad] = float("nan")
+    bank = device_bank(li.bank)
+    layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, w.T,
+                        flags=ft.FT_LAYER_UNFUSED if unfused else 0)
+    out, mask = layer.forward(li.logits.cuda(), li.x.cuda())
+    torch.cuda.synchronize()
+    assert layer.status_word() == 0
+    out, mask = out.cpu().numpy(), mask.cpu().numpy().astype(np.uint32)
+    assert mask[bad] == (1 << w.k) - 1
+    assert (out[bad] == 0).all()
+    L0 = li.logits.clone()
+    L0[bad] = 0.0
+    ora = oracle.layer(L0, li.x, li.bank, li.slot_of_expert, w.k)
+    keep = np.arange(w.T) != bad
+    assert np.array_equal(layer.ids[:w.T].cpu().numpy()[keep], ora["ids"][keep])
+    assert np.array_equal(mask[keep], ora["mask"][keep])
+    assert_ffn_close(out[keep], ora["out"][keep], f"nan row unfused={unfused}: other tokens")
+
+
+def test_two_host_threads(ft):
+    """Launch code called from two host threads at once: layers of two shapes (different LDS sizes of
+    the one-kernel decode path, and the GEMV and GEMM kernels of the four calls), repeated.  First
+    both threads run the one-kernel path on one stream (the device runs them in turn; the host-side
+    launch facts are shared between the threads); then on two streams, one thread the one-kernel path
+    and the other the four calls.  Every result matches the oracle and every status word is 0."""
+    import threading
+    from gpu_util import assert_ffn_close
+    shapes = {
+        "q4_0_T8": SMALL["decode_q4_0"].replace(T=8),
+        "mxfp4_T16": EDGE.replace(T=16),
+        "bf16_T300": SMALL["prefill_bf16_zipf"],
+    }
+    inputs = {n: synth.layer_inputs(w, layer=5) for n, w in shapes.items()}
+    banks = {n: device_bank(li.bank) for n, li in inputs.items()}
+    refs = {n: oracle.layer(li.logits, li.x, li.bank, li.slot_of_expert, li.workload.k,
+                            shared_slot=li.workload.shared_slot) for n, li in inputs.items()}
+
+    def run(name, mode, stream, results, reps=4):
+        try:
+            li = inputs[name]
+            w = li.workload
+            layer = ft.MoELayer(banks[name], li.slot_of_expert.cuda(), w.k, li.T, shared_slot=w.shared_slot, mode=mode)
+            logits, x = li.logits.cuda(), li.x.cuda()
+            torch.cuda.synchronize()
+            outs = []
+            for _ in range(reps):
+                out, mask = layer.forward(logits, x, stream=stream)
+                outs.append((out.clone(), mask.clone()))
+            stream.synchronize()
+            results[name] = (outs, layer.status_word())
+        except Exception as e:  # reported by the main thread
+            results[name] = e
+
+    for plan in ((("q4_0_T8", "layer", 0), ("mxfp4_T16", "layer", 0)),
+                 (("q4_0_T8", "layer", 0), ("bf16_T300", "calls", 1))):
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        results = {}
+        threads = [threading.Thread(target=run, args=(n, m, streams[si], results)) for n, m, si in plan]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+        for name, mode, _ in plan:
+            r = results[name]
+            assert not isinstance(r, Exception), f"{name}: {r!r}"
+            outs, status = r
+            assert status == 0, f"{name}: status word {status}"
+            ref = refs[name]
+            for out, mask in outs:
+                assert np.array_equal(mask.cpu().numpy().astype(np.uint32), ref["mask"]), name
+                assert_ffn_close(out.float().cpu().numpy(), ref["out"], f"two threads {name} ({mode})")
+            log(f"two threads: {name} ({mode}) ok over {len(outs)} calls")
