@@ -20,7 +20,11 @@
 #include <thread>
 #include <vector>
 
+// A build may define FT_HOST_CLONES empty (one baseline version of each loop): the thread-sanitizer
+// build of the tests does, since its runtime cannot start beside the clones' load-time resolvers.
+#ifndef FT_HOST_CLONES
 #define FT_HOST_CLONES __attribute__((target_clones("avx512f", "arch=haswell", "default")))
+#endif
 
 namespace ftk {
 

@@ -113,33 +113,11 @@ def test_residual_host_bf16_on_cpu():
     import numpy as np
     import torch
     import oracle
+    from host_banks import bf16_bank
     rng = np.random.default_rng(5)
     T, d, E, k, I = 5, 128, 3, 2, 64
-    w13 = (rng.standard_normal((E, 2 * I, d)) * 0.05).astype(np.float32)
-    w2 = (rng.standard_normal((E, d, I)) * 0.05).astype(np.float32)
-    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
-    w13b, w2b = to_bf16(w13), to_bf16(w2)
-
-    def device_layout(mat_bf16, perm_I):  # [E][R][K] bf16 -> interleaved bytes
-        Em, R, K = mat_bf16.shape
-        rows = mat_bf16.reshape(Em * R, K).view(torch.int16).numpy().view(np.uint16)
-        out = np.zeros(Em * R * K, np.uint16)
-        nch = K // 8
-        for g in range(Em * R):
-            slot, L = divmod(g, R)
-            if perm_I:
-                dr = 64 * (L >> 5) + (L & 31) if L < perm_I else 64 * ((L - perm_I) >> 5) + 32 + ((L - perm_I) & 31)
-            else:
-                dr = L
-            G = slot * R + dr
-            for c in range(nch):
-                off = (((G >> 6) * nch + c) * 64 + (G & 63)) * 8
-                out[off:off + 8] = rows[g, 8 * c:8 * c + 8]
-        return torch.from_numpy(out.view(np.uint8).copy())
-
-    a13, a2 = device_layout(w13b, I), device_layout(w2b, 0)
-    hb = ft.DeviceBank(ft.FT_W_BF16, E, d, I, a13, a2)
-    x = to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+    hb, w13, w2 = bf16_bank(rng, E, d, I)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
     ids = torch.tensor([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0]], dtype=torch.int32)
     wts = torch.from_numpy(rng.random((T, k)).astype(np.float32))
     mask = torch.tensor([0b01, 0b11, 0b00, 0b10, 0b01], dtype=torch.int32)
@@ -150,7 +128,7 @@ def test_residual_host_bf16_on_cpu():
         for j in range(k):
             if (int(mask[t]) >> j) & 1:
                 e = int(ids[t, j])
-                _, y = oracle.swiglu_ffn(xf[t:t + 1], w13b[e].float().numpy(), w2b[e].float().numpy())
+                _, y = oracle.swiglu_ffn(xf[t:t + 1], w13[e], w2[e])
                 ref[t] += float(wts[t, j]) * y[0].astype(np.float64)
     assert np.array_equal(got[2], np.zeros(d, np.float32))
     # the slot-table form: experts 0 and 2 cold for the tokens whose mask marks them
@@ -183,32 +161,11 @@ def test_residual_host_fp8_on_cpu():
     import numpy as np
     import torch
     import oracle
+    from host_banks import fp8_bank
     rng = np.random.default_rng(6)
     T, d, E, k, I = 3, 256, 2, 2, 128
-    finite = np.array([c for c in range(256) if (c & 0x7f) != 0x7f], np.uint8)
     table = np.array([oracle.e4m3_value(int(c)) for c in range(256)], np.float32)
-
-    def make(R, K, perm_I):
-        codes = finite[rng.integers(0, len(finite), size=(E, R, K))]
-        scales = (2.0 ** rng.integers(-12, -6, size=(E, R // 128, K // 128))).astype(np.float32)
-        vals = table[codes] * np.repeat(np.repeat(scales, 128, axis=1), 128, axis=2)
-        out = np.zeros(E * R * K, np.uint8)
-        nch = K // 16
-        for g in range(E * R):
-            slot, L = divmod(g, R)
-            if perm_I:
-                dr = 64 * (L >> 5) + (L & 31) if L < perm_I else 64 * ((L - perm_I) >> 5) + 32 + ((L - perm_I) & 31)
-            else:
-                dr = L
-            G = slot * R + dr
-            for c in range(nch):
-                off = (((G >> 6) * nch + c) * 64 + (G & 63)) * 16
-                out[off:off + 16] = codes[slot, L, 16 * c:16 * c + 16]
-        return torch.from_numpy(out), torch.from_numpy(scales.reshape(-1).copy()), vals.astype(np.float32)
-
-    c13, s13, v13 = make(2 * I, d, I)
-    c2, s2, v2 = make(d, I, 0)
-    hb = ft.DeviceBank(ft.FT_W_FP8_B128, E, d, I, c13, c2, s13.view(torch.uint8), s2.view(torch.uint8))
+    hb, v13, v2 = fp8_bank(rng, E, d, I, table)
     x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
     ids = torch.tensor([[0, 1], [1, 0], [0, 1]], dtype=torch.int32)
     wts = torch.tensor([[0.6, 0.4], [0.7, 0.3], [0.5, 0.5]], dtype=torch.float32)
