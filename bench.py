@@ -10,7 +10,13 @@ synthetic tensors already resident in HBM.  Prints one JSON line.
 The dominant unit is the layer call; its average duration is timed with HIP events on the stream
 it runs on, over timed eager replays of the same steps, and compared with the HBM and MFMA
 rooflines of its algorithmic bytes and flops (the bound is the one with the longer roofline time).
-The CPU baseline times the scalar oracle on a bounded sample of the same workload on the host.
+A single-layer decode workload rotates over copies of its bank (at least 4, and at least 1 GB
+touched per pass) so that the 256 MB MALL cannot serve it.  The run exits with status 3, printing
+nothing, if the one-kernel decode layer reports a dependency wait that gave up.
+Beside a decode workload the same run also measures the prefill workload (default: 4096 tokens,
+bf16 banks, Zipf routing) and adds it to the line as "prefill" (tokens/s, its own roofline).
+The CPU baseline times the scalar oracle on a bounded sample of the same workload on the host
+cores (all usable cores up to 16, and one core), with the CPU model.
 
 Other modes print their own line instead: --route-proj (router projection + top-k), --cache SLOTS
 (layer steps with the expert cache streaming cold experts from pinned host memory), --residual
@@ -52,7 +58,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build_layers(w: synth.Workload, T: int, n_layers: int):
+def build_layers(w: synth.Workload, T: int, n_layers: int, copies: int = 1):
+    """The step's layers.  copies > 1 (single-layer workloads): the layer is repeated over that many
+    copies of its bank and buffers at distinct addresses, run back to back, so that one pass touches
+    more bytes than the caches hold (the MALL is 256 MB)."""
     layers = []
     for l in range(n_layers):
         canon = synth.make_bank(w, layer=l, device="cuda")
@@ -60,12 +69,16 @@ def build_layers(w: synth.Workload, T: int, n_layers: int):
                                    canon.s2)
         del canon
         slot = synth.slot_table(w, l).cuda()
-        layer = ft.MoELayer(bank, slot, w.k, T, shared_slot=w.shared_slot)
         logits = synth.logits(w, l, T, device="cuda")
         x = synth.activations(w, l, T, device="cuda")
-        layers.append((layer, logits, x))
+        for c in range(copies):
+            b = bank if c == 0 else ft.DeviceBank(bank.fmt, bank.n_slots, bank.d, bank.I,
+                                                  *[None if t is None else t.clone()
+                                                    for t in (bank.w13, bank.w2, bank.s13, bank.s2)])
+            layer = ft.MoELayer(b, slot.clone(), w.k, T, shared_slot=w.shared_slot)
+            layers.append((layer, logits.clone(), x.clone()))
         if (l + 1) % 8 == 0 or l + 1 == n_layers:
-            log(f"generated {l + 1}/{n_layers} layers")
+            log(f"generated {l + 1}/{n_layers} layers" + (f" ({copies} copies each)" if copies > 1 else ""))
     torch.cuda.synchronize()
     return layers
 
@@ -73,6 +86,15 @@ def build_layers(w: synth.Workload, T: int, n_layers: int):
 def run_step(layers):
     for layer, logits, x in layers:
         layer.forward(logits, x)
+
+
+def check_status(layers, what: str):
+    """Exit non-zero if the one-kernel decode path of any layer reports a dependency wait that gave up
+    (its results would be invalid, so no figure of the run may be printed)."""
+    bad = [i for i, (layer, _, _) in enumerate(layers) if layer.status_word() != 0]
+    if bad:
+        log(f"{what}: status word set in layer(s) {bad[:8]}: a dependency wait of the fused kernel gave up")
+        sys.exit(3)
 
 
 def algorithmic_work(w: synth.Workload, layers, T: int):
@@ -113,21 +135,57 @@ def time_layer_calls(layers, reps: int):
     return sum(ms) / len(ms) * 1e3  # us
 
 
-def cpu_baseline(w: synth.Workload, T: int, budget_s: float):
+def host_cpu():
+    """Model name of the host CPU, the cores the OS reports and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return model, os.cpu_count() or 1, usable
+
+
+def cpu_baseline(w: synth.Workload, T: int, budget_s: float, workers: int = 1, max_layers: int | None = None):
     """Time the scalar oracle on host cores over whole layers of the same workload until the budget
-    is used (at least one layer)."""
+    is used (at least one layer); workers > 1 runs its expert groups on that many threads."""
     import oracle
     t_total, n = 0.0, 0
-    while t_total < budget_s and n < w.layers:
+    limit = w.layers if max_layers is None else min(w.layers, max_layers)
+    while t_total < budget_s and n < limit:
         li = synth.layer_inputs(w, layer=n, T=T, device="cuda")
         bank_cpu = li.bank.to("cpu")
         L, x, so = li.logits.cpu(), li.x.cpu(), li.slot_of_expert.cpu()
         del li
         t0 = time.perf_counter()
-        oracle.layer(L, x, bank_cpu, so, w.k, shared_slot=w.shared_slot)
+        oracle.layer(L, x, bank_cpu, so, w.k, shared_slot=w.shared_slot, workers=workers)
         t_total += time.perf_counter() - t0
         n += 1
     return t_total, n
+
+
+def cpu_baseline_record(w: synth.Workload, T: int, budget_s: float, decode: bool):
+    """The oracle on the host cores (all the cores this process may use, at most the 16 of a one-GPU
+    share), and on one core, each over whole layers within its share of the budget."""
+    model, nproc, usable = host_cpu()
+    workers = max(1, min(16, usable))
+
+    def rate(t, n):
+        return round(t / n * 1e6, 1) if decode else round(T * n / t, 3)
+    t_all, n_all = cpu_baseline(w, T, budget_s / 2, workers=workers)
+    t_one, n_one = cpu_baseline(w, T, budget_s / 2, workers=1)
+    rec = {"value": rate(t_all, n_all), "unit": "us/layer" if decode else "tokens/s", "cores": workers,
+           "kind": "oracle",
+           "sample": f"{n_all} whole layer(s) of {w.name} (T={T}), scalar C oracle, expert groups on {workers} threads",
+           "single_core": {"value": rate(t_one, n_one), "cores": 1,
+                           "sample": f"{n_one} whole layer(s), one thread"},
+           "cpu_model": model, "nproc": nproc, "usable_cores": usable}
+    log(f"cpu baseline {rec}")
+    return rec
 
 
 def copy_probe(nbytes: int, reps: int = 5):
@@ -529,8 +587,14 @@ def main():
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's)")
     ap.add_argument("--layers", type=int, default=None, help="layers per step (default: the workload's)")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle time for the CPU baseline (half all-core, half one core)")
     ap.add_argument("--ffn-reps", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=None,
+                    help="bank copies a single-layer workload rotates over (default: >= 4 and >= 1 GB per pass at decode)")
+    ap.add_argument("--prefill", default="prefill_bf16_zipf", metavar="WORKLOAD",
+                    help="prefill workload measured beside a decode workload in the same run ('' for none)")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run the counter-calibration copy kernel over BYTES")
     ap.add_argument("--route-proj", action="store_true",
@@ -576,14 +640,68 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
-    log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}")
-    layers = build_layers(w, T, n_layers)
+    copies = args.copies
+    if copies is None:  # single-layer decode workloads: at least 4 copies and 1 GB touched per pass
+        copies = 1
+        if n_layers == 1 and decode:
+            per_layer = expected_touched_bytes(w, T)
+            copies = int(min(16, max(4, -(-1e9 // per_layer))))
+    m = measure(w, T, n_layers, args.steps, args.warmup, not args.no_graph, args.ffn_reps, copies)
 
-    for _ in range(max(args.warmup, 1)):
+    # ---- the prefill half of the metric, measured in the same run beside the default decode workload
+    prefill = None
+    if args.prefill and decode:
+        wp = synth.WORKLOADS[args.prefill]
+        mp = measure(wp, wp.T, 1, args.prefill_steps, args.warmup, not args.no_graph, args.ffn_reps, 1)
+        prefill = {"metric": "MoE-layer prefill throughput", "value": round(mp["tokens_per_s"], 1),
+                   "unit": "tokens/s", "ms_per_layer": round(mp["ms_per_step"], 4), "steps": args.prefill_steps,
+                   "config": mp["config"], "roofline": mp["roofline"], "step_ms": mp["spread"]}
+
+    # ---- CPU baseline: the oracle on host cores, bounded sample
+    cpu = cpu_baseline_record(w, T, args.cpu_budget, decode) if args.cpu_budget > 0 else None
+
+    if decode:
+        metric, value, unit, hib = "MoE-layer decode latency", m["us_per_layer"], "us/layer", False
+    else:
+        metric, value, unit, hib = "MoE-layer prefill throughput", m["tokens_per_s"], "tokens/s", True
+    line = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": hib, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": m["config"],
+        "roofline": m["roofline"],
+        "cpu_baseline": cpu,
+        "step_ms": m["spread"],
+    }
+    if prefill is not None:
+        line["prefill"] = prefill
+    print(json.dumps(line), flush=True)
+
+
+def expected_touched_bytes(w: synth.Workload, T: int) -> float:
+    """Bytes a layer call is expected to touch before its routing is known: the resident experts a
+    batch of T tokens reaches at most (T * k, E or the resident count), plus the shared expert."""
+    resident = w.n_resident or w.E
+    experts = min(T * w.k, resident) + (1 if w.shared else 0)
+    return max(experts * synth.expert_bytes(w.fmt, w.d, w.I), 1.0)
+
+
+def measure(w: synth.Workload, T: int, n_layers: int, steps: int, warmup: int, use_graph: bool, ffn_reps: int,
+            copies: int = 1):
+    """One workload: warm-up, a HIP graph of one step (every layer call of it) replayed `steps`
+    times in the timed region, then the layer call timed on its stream against the rooflines."""
+    log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}"
+        + (f" x {copies} bank copies" if copies > 1 else ""))
+    layers = build_layers(w, T, n_layers, copies)
+    calls = n_layers * copies  # layer calls per step
+
+    for _ in range(max(warmup, 1)):
         run_step(layers)
     torch.cuda.synchronize()
+    check_status(layers, "warm-up")
     graph = None
-    if not args.no_graph:
+    if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -593,16 +711,17 @@ def main():
             with torch.cuda.graph(graph, stream=s):
                 run_step(layers)
         torch.cuda.synchronize()
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             graph.replay()
         torch.cuda.synchronize()
+        check_status(layers, "graph warm-up")
 
     # ---- timed region (events between steps give the spread; the value is the whole region's time)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     marks[0].record()
-    for i in range(args.steps):
+    for i in range(steps):
         if graph is not None:
             graph.replay()
         else:
@@ -610,14 +729,16 @@ def main():
         marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    us_per_layer = ms_per_step * 1e3 / n_layers
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    check_status(layers, "timed steps")
+    ms_per_step = elapsed / steps * 1e3
+    us_per_layer = ms_per_step * 1e3 / calls
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
     spread = {q: round(float(np.percentile(per_step, p)), 4) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     log(f"{ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer; per-step ms {spread}")
 
     # ---- dominant unit: the layer call, event-timed on its stream
-    ffn_us = time_layer_calls(layers, args.ffn_reps)
+    ffn_us = time_layer_calls(layers, ffn_reps)
+    check_status(layers, "event-timed layer calls")
     bytes_call, flops_call, pairs, touched = algorithmic_work(w, layers, T)
     # the bound is the resource whose roofline time (algorithmic bytes at the HBM peak, or algorithmic
     # flops at the bf16 MFMA peak) is the longer, i.e. the one with the larger fraction; the other is
@@ -648,37 +769,17 @@ def main():
     # memory: h written by gate/up and read by down, y written by down and read by combine
     roof["boundary_bytes_per_call"] = round(2 * pairs * (w.d + w.I) * 2)
     log(f"layer call {ffn_us:.2f} us; {touched:.1f} experts touched, {pairs:.1f} pairs; {roof}")
-
-    # ---- CPU baseline: the oracle on host cores, bounded sample
-    cpu = None
-    if args.cpu_budget > 0:
-        t_cpu, n_cpu = cpu_baseline(w, T, args.cpu_budget)
-        if decode:
-            cpu = {"value": round(t_cpu / n_cpu * 1e6, 1), "unit": "us/layer"}
-        else:
-            cpu = {"value": round(T * n_cpu / t_cpu, 3), "unit": "tokens/s"}
-        cpu.update({"cores": 1, "kind": "oracle",
-                    "sample": f"{n_cpu} whole layer(s) of {w.name} (T={T}), single-threaded scalar C oracle"})
-        log(f"cpu baseline {cpu}")
-
-    if decode:
-        metric, value, unit, hib = "MoE-layer decode latency", us_per_layer, "us/layer", False
-    else:
-        metric, value, unit, hib = "MoE-layer prefill throughput", T / (ms_per_step * 1e-3 / n_layers), "tokens/s", True
-    line = {
-        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": hib, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded)",
-        "config": {"workload": w.name, "T": T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
-                   "bank_format": synth.FMT_NAMES[w.fmt], "layers_per_step": n_layers,
-                   "shared_expert": w.shared, "resident_experts": w.n_resident or w.E,
-                   "graph": graph is not None},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "step_ms": spread,
-    }
-    print(json.dumps(line), flush=True)
+    config = {"workload": w.name, "T": T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
+              "bank_format": synth.FMT_NAMES[w.fmt], "layers_per_step": n_layers,
+              "shared_expert": w.shared, "resident_experts": w.n_resident or w.E, "graph": graph is not None}
+    if copies > 1:
+        config["bank_copies"] = copies
+    out = dict(ms_per_step=ms_per_step, us_per_layer=us_per_layer, tokens_per_s=T / (ms_per_step * 1e-3 / calls),
+               spread=spread, roofline=roof, config=config)
+    del graph, layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
