@@ -428,9 +428,10 @@ def test_two_host_threads(ft):
             logits, x = li.logits.cuda(), li.x.cuda()
             torch.cuda.synchronize()
             outs = []
-            for _ in range(reps):
-                out, mask = layer.forward(logits, x, stream=stream)
-                outs.append((out.clone(), mask.clone()))
+            with torch.cuda.stream(stream):  # the copies of each result are ordered after its layer call
+                for _ in range(reps):
+                    out, mask = layer.forward(logits, x)
+                    outs.append((out.clone(), mask.clone()))
             stream.synchronize()
             results[name] = (outs, layer.status_word())
         except Exception as e:  # reported by the main thread
