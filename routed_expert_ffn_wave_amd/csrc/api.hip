@@ -600,97 +600,121 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
   return layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags)).total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// ft_moe_layer after its checks of T, E, k, the bank, the flags and shared_slot: the rest of the
+// validation and the launches, with the workspace `wsb` (ws_bytes long; null when missing).
+int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
+                  const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                  int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
+                  uint32_t* residual_mask, uint8_t* wsb, size_t ws_bytes, int flags, hipStream_t stream) {
+  int rc;
+  CHECK_PTR(counts, "counts");
+  CHECK_PTR(offsets, "offsets");
+  const bool shared = shared_slot >= 0;
+  const bool fused = layer_fused(bank, T, E, k, flags);
+  const LayerWs W = layer_ws(bank->d, bank->I, T, E, k, shared, fused);
+  REQUIRE(wsb != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
+          W.total, ws_bytes, wsb ? "" : ", null pointer");
+  REQUIRE(aligned16(wsb), FT_E_INVAL, "ws is not 16-byte aligned");
+  if (T == 0)  // counts and offsets are still defined (all zero)
+    return hip_status(ftk::launch_permute(ids, 0, E, k, counts, offsets, gather, inv, wsb + W.perm, stream),
+                      "ft_moe_layer permute launch");
+  CHECK_PTR(slot_of_expert, "slot_of_expert");
+  CHECK_PTR(logits, "logits");
+  CHECK_PTR(x, "x");
+  CHECK_PTR(ids, "ids");
+  CHECK_PTR(w, "w");
+  CHECK_PTR(gather, "gather");
+  CHECK_PTR(inv, "inv");
+  CHECK_PTR(y_sorted, "y_sorted");
+  if (y_shared) CHECK_PTR(y_shared, "y_shared");
+  CHECK_PTR(out, "out");
+  if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
+  const bool out_bf16 = (flags & FT_OUT_BF16) != 0;
+  if (!fused) {
+    hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
+    if (e != hipSuccess) return hip_status(e, "ft_moe_layer route launch");
+    e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
+    if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
+    rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
+                            (uint16_t*)(wsb + W.h), flags & FT_PATH_MASK, stream);
+    if (rc) return rc;
+    return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
+                                          bank->d, out, residual_mask, out_bf16, stream),
+                      "ft_moe_layer combine launch");
+  }
+  ftk::LayerArgs L{};
+  ftk::FfnArgs& a = L.f;
+  a.fmt = bank->fmt;
+  a.d = bank->d;
+  a.I = bank->I;
+  a.n_slots = bank->n_slots;
+  a.w13 = (const uint8_t*)bank->w13;
+  a.w2 = (const uint8_t*)bank->w2;
+  a.s13 = (const uint8_t*)bank->s13;
+  a.s2 = (const uint8_t*)bank->s2;
+  a.slot_of = slot_of_expert;
+  a.shared_slot = shared_slot;
+  a.x = x;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.offsets = offsets;
+  a.gather = gather;
+  a.h = (uint16_t*)(wsb + W.h);
+  a.y_sorted = y_sorted;
+  a.y_shared = y_shared;
+  a.min_cnt = 1;
+  a.max_cnt = 0x7fffffff;
+  L.logits = logits;
+  L.ids = ids;
+  L.w = w;
+  L.counts = counts;
+  L.offsets = offsets;
+  L.gather = gather;
+  L.inv = inv;
+  L.mask = residual_mask;
+  L.out = out;
+  L.out_bf16 = out_bf16 ? 1 : 0;
+  L.id_bits = id_bits_of(E);
+  L.ctl = (int32_t*)(wsb + W.ctl);
+  L.done13 = (int32_t*)(wsb + W.done13);
+  L.n_rc = W.n_rc;
+  L.cdone = (int32_t*)(wsb + W.cdone);
+  return hip_status(ftk::launch_layer_decode(L, stream), "ft_moe_layer fused launch");
+}
+
+// ft_moe_layer's own checks of the arguments that are not buffers
+int layer_args(const ft_moe_bank* bank, int shared_slot, int T, int E, int k, const uint16_t* y_shared, int flags) {
+  int rc = check_tek(T, E, k);
+  if (rc) return rc;
+  rc = check_bank(bank);
+  if (rc) return rc;
+  REQUIRE((flags & ~(FT_PATH_MASK | FT_OUT_BF16 | FT_LAYER_UNFUSED)) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+  REQUIRE((flags & FT_PATH_MASK) != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
+  REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
+          shared_slot, bank->n_slots);
+  REQUIRE((shared_slot >= 0) == (y_shared != nullptr), FT_E_INVAL,
+          "y_shared must be given exactly when shared_slot >= 0");
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
                  const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                  int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
                  uint32_t* residual_mask, void* ws, size_t ws_bytes, int flags, hipStream_t stream) {
   try {
-    int rc = check_tek(T, E, k);
+    const int rc = layer_args(bank, shared_slot, T, E, k, y_shared, flags);
     if (rc) return rc;
-    rc = check_bank(bank);
-    if (rc) return rc;
-    REQUIRE((flags & ~(FT_PATH_MASK | FT_OUT_BF16 | FT_LAYER_UNFUSED)) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
-    REQUIRE((flags & FT_PATH_MASK) != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
-    REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
-            shared_slot, bank->n_slots);
-    REQUIRE((shared_slot >= 0) == (y_shared != nullptr), FT_E_INVAL,
-            "y_shared must be given exactly when shared_slot >= 0");
-    CHECK_PTR(counts, "counts");
-    CHECK_PTR(offsets, "offsets");
-    const bool shared = shared_slot >= 0;
-    const bool fused = layer_fused(bank, T, E, k, flags);
-    const LayerWs W = layer_ws(bank->d, bank->I, T, E, k, shared, fused);
-    REQUIRE(ws != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
-            W.total, ws_bytes, ws ? "" : ", null pointer");
-    REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
-    uint8_t* wsb = (uint8_t*)ws;
-    if (T == 0)  // counts and offsets are still defined (all zero)
-      return hip_status(ftk::launch_permute(ids, 0, E, k, counts, offsets, gather, inv, wsb + W.perm, stream),
-                        "ft_moe_layer permute launch");
-    CHECK_PTR(slot_of_expert, "slot_of_expert");
-    CHECK_PTR(logits, "logits");
-    CHECK_PTR(x, "x");
-    CHECK_PTR(ids, "ids");
-    CHECK_PTR(w, "w");
-    CHECK_PTR(gather, "gather");
-    CHECK_PTR(inv, "inv");
-    CHECK_PTR(y_sorted, "y_sorted");
-    if (y_shared) CHECK_PTR(y_shared, "y_shared");
-    CHECK_PTR(out, "out");
-    if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
-    const bool out_bf16 = (flags & FT_OUT_BF16) != 0;
-    if (!fused) {
-      hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
-      if (e != hipSuccess) return hip_status(e, "ft_moe_layer route launch");
-      e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
-      if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
-      rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
-                              (uint16_t*)(wsb + W.h), flags & FT_PATH_MASK, stream);
-      if (rc) return rc;
-      return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
-                                            bank->d, out,
-                                            residual_mask, out_bf16, stream),
-                        "ft_moe_layer combine launch");
-    }
-    ftk::LayerArgs L{};
-    ftk::FfnArgs& a = L.f;
-    a.fmt = bank->fmt;
-    a.d = bank->d;
-    a.I = bank->I;
-    a.n_slots = bank->n_slots;
-    a.w13 = (const uint8_t*)bank->w13;
-    a.w2 = (const uint8_t*)bank->w2;
-    a.s13 = (const uint8_t*)bank->s13;
-    a.s2 = (const uint8_t*)bank->s2;
-    a.slot_of = slot_of_expert;
-    a.shared_slot = shared_slot;
-    a.x = x;
-    a.T = T;
-    a.E = E;
-    a.k = k;
-    a.offsets = offsets;
-    a.gather = gather;
-    a.h = (uint16_t*)(wsb + W.h);
-    a.y_sorted = y_sorted;
-    a.y_shared = y_shared;
-    a.min_cnt = 1;
-    a.max_cnt = 0x7fffffff;
-    L.logits = logits;
-    L.ids = ids;
-    L.w = w;
-    L.counts = counts;
-    L.offsets = offsets;
-    L.gather = gather;
-    L.inv = inv;
-    L.mask = residual_mask;
-    L.out = out;
-    L.out_bf16 = out_bf16 ? 1 : 0;
-    L.id_bits = id_bits_of(E);
-    L.ctl = (int32_t*)(wsb + W.ctl);
-    L.done13 = (int32_t*)(wsb + W.done13);
-    L.n_rc = W.n_rc;
-    L.cdone = (int32_t*)(wsb + W.cdone);
-    return hip_status(ftk::launch_layer_decode(L, stream), "ft_moe_layer fused launch");
+    return layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
+                         y_sorted, y_shared, out, residual_mask, (uint8_t*)ws, ws_bytes, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_layer: unexpected exception");
   }
