@@ -236,6 +236,35 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
                  uint16_t* y_shared, void* out, uint32_t* residual_mask, void* ws, size_t ws_bytes,
                  int flags, hipStream_t stream);
 
+/*
+ * Scratch bytes of ft_moe_layer_noalloc: one static array per device that the library runs on,
+ * held until the process ends.
+ */
+#define FT_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * ft_moe_layer for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid allocation): the same call, arguments, results and
+ * kernels, with the workspace taken from a static device array of the library
+ * (FT_NOALLOC_SCRATCH_BYTES per device) instead of a ws argument.  Nothing is allocated.
+ *   - A layer whose workspace (ft_moe_layer_workspace with the same arguments) exceeds
+ *     FT_NOALLOC_SCRATCH_BYTES is refused with FT_E_WORKSPACE and enqueues nothing.
+ *   - The first call on a device enqueues a clear of the whole scratch before the layer; every call
+ *     leaves it ready for the next one.
+ *   - status: optional device int32, 4-byte aligned: receives this call's status word (0 in every
+ *     correct run; non-zero when a dependency wait of the one-kernel path gave up and the results
+ *     are invalid).  A one-thread kernel after the layer moves the word there and clears it, also
+ *     when status is NULL.
+ *   - Every call on a device shares that device's scratch: calls that may overlap on one device
+ *     (different streams, or host threads without ordering) race and give wrong results.  Order
+ *     them on one stream.
+ */
+int ft_moe_layer_noalloc(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
+                         const float* logits, const uint16_t* x, int T, int E, int k, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* inv,
+                         uint16_t* y_sorted, uint16_t* y_shared, void* out, uint32_t* residual_mask,
+                         int32_t* status, int flags, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- expert cache */
 
 /*

@@ -22,6 +22,7 @@ FT_OUT_BF16 = 4
 FT_LAYER_UNFUSED = 8
 FT_PATH_MASK = 3
 LAYER_MAX_T = 16   # largest T of the fused decode kernels
+FT_NOALLOC_SCRATCH_BYTES = 8 << 20   # static scratch of ft_moe_layer_noalloc, per device
 
 STATUS_NAMES = {0: "FT_OK", 1: "FT_E_INVAL", 2: "FT_E_UNSUPPORTED", 3: "FT_E_WORKSPACE", 4: "FT_E_HIP",
                 5: "FT_E_INTERNAL"}
@@ -62,6 +63,7 @@ def _load():
         "ft_moe_dequant": ([BP, i, i, P, P], i),
         "ft_moe_layer_workspace": ([BP, i, i, i, i, i], sz),
         "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
+        "ft_moe_layer_noalloc": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i, P], i),
         "ft_moe_cache_update": ([P, i, i, i, ctypes.c_float, P, P, P, P, P, P, P, P, P], i),
         "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
         "ft_moe_residual_host": ([BP, P, P, P, P, P, i, i, i, P, i], i),
@@ -80,7 +82,7 @@ EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_r
             "ft_moe_route_proj", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
             "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer",
-            "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add")
+            "ft_moe_layer_noalloc", "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -365,6 +367,17 @@ class MoELayer:
             self.perm_ws = torch.empty(max(pws, 256), dtype=torch.uint8, device=dev)
             fws = lib.ft_moe_grouped_ffn_workspace(bank.ref, T, E, k, shared_slot, flags)
             self.ffn_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
+
+    def forward_noalloc(self, logits: torch.Tensor, x: torch.Tensor, status: torch.Tensor | None = None, stream=None):
+        """The same layer through ft_moe_layer_noalloc: the library's static scratch instead of this
+        layer's workspace (status: optional int32 device tensor of one element)."""
+        s = _stream(stream)
+        _check(lib.ft_moe_layer_noalloc(self.bank.ref, _ptr(self.slot_of), self.shared_slot, _ptr(logits), _ptr(x),
+                                        self.T, self.E, self.k, _ptr(self.ids), _ptr(self.w), _ptr(self.counts),
+                                        _ptr(self.offsets), _ptr(self.gather), _ptr(self.inv), _ptr(self.y_sorted),
+                                        _ptr(self.y_shared), _ptr(self.out), _ptr(self.mask), _ptr(status),
+                                        self.flags | self.out_flags, s))
+        return self.out[: self.T], self.mask[: self.T]
 
     def status_word(self) -> int:
         """The layer workspace's status word (non-zero: a wait of the fused kernel gave up; the

@@ -9,6 +9,7 @@
 #include <climits>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <new>
 #include <thread>
 
@@ -609,7 +610,8 @@ namespace {
 int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
                   const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                   int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
-                  uint32_t* residual_mask, uint8_t* wsb, size_t ws_bytes, int flags, hipStream_t stream) {
+                  uint32_t* residual_mask, uint8_t* wsb, size_t ws_bytes, int flags, hipStream_t stream,
+                  bool check_only = false) {
   int rc;
   CHECK_PTR(counts, "counts");
   CHECK_PTR(offsets, "offsets");
@@ -619,9 +621,11 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   REQUIRE(wsb != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
           W.total, ws_bytes, wsb ? "" : ", null pointer");
   REQUIRE(aligned16(wsb), FT_E_INVAL, "ws is not 16-byte aligned");
-  if (T == 0)  // counts and offsets are still defined (all zero)
+  if (T == 0) {  // counts and offsets are still defined (all zero)
+    if (check_only) return FT_OK;
     return hip_status(ftk::launch_permute(ids, 0, E, k, counts, offsets, gather, inv, wsb + W.perm, stream),
                       "ft_moe_layer permute launch");
+  }
   CHECK_PTR(slot_of_expert, "slot_of_expert");
   CHECK_PTR(logits, "logits");
   CHECK_PTR(x, "x");
@@ -633,6 +637,7 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   if (y_shared) CHECK_PTR(y_shared, "y_shared");
   CHECK_PTR(out, "out");
   if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
+  if (check_only) return FT_OK;
   const bool out_bf16 = (flags & FT_OUT_BF16) != 0;
   if (!fused) {
     hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
@@ -717,6 +722,107 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
                          y_sorted, y_shared, out, residual_mask, (uint8_t*)ws, ws_bytes, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_layer: unexpected exception");
+  }
+}
+
+}  // extern "C"
+
+// ---- ft_moe_layer_noalloc: the layer workspace in a static device array of the library
+
+// The scratch of ft_moe_layer_noalloc: one copy per device, loaded with the code object and held
+// until the process ends.  Host code never uses this name as an address (in host code it stands for
+// a host-side shadow); it uses the device address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[FT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each device
+bool g_scratch_clear[kMaxDevices] = {};    // its first clear has been enqueued
+
+__global__ void scratch_clear_kernel(uint4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Moves the status word of the call that ran before it on the stream into *status (when given) and
+// clears it, so that every call starts with a clear word.
+__global__ void scratch_status_kernel(int32_t* word, int32_t* status) {
+  const int v = __hip_atomic_exchange(word, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (status) *status = v;
+}
+
+// Device address of the scratch on the current device (looked up once per device, with that device
+// current); `fresh` is set on the first call for the device, whose scratch the caller clears.
+int scratch_of_device(uint8_t** ptr, bool* fresh) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "ft_moe_layer_noalloc: hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, FT_E_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "ft_moe_layer_noalloc: hipGetSymbolAddress of the scratch");
+    REQUIRE(p != nullptr && ((uintptr_t)p & 255u) == 0, FT_E_INTERNAL, "scratch address %p is not 256-byte aligned",
+            p);
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *fresh = !g_scratch_clear[dev];
+  g_scratch_clear[dev] = true;
+  *ptr = g_scratch_ptr[dev];
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ft_moe_layer_noalloc(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
+                         const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts,
+                         int32_t* offsets, int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared,
+                         void* out, uint32_t* residual_mask, int32_t* status, int flags, hipStream_t stream) {
+  try {
+    int rc = layer_args(bank, shared_slot, T, E, k, y_shared, flags);
+    if (rc) return rc;
+    const size_t need =
+        layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags)).total;
+    REQUIRE(need <= FT_NOALLOC_SCRATCH_BYTES, FT_E_WORKSPACE,
+            "ft_moe_layer_noalloc: this layer needs %zu bytes of scratch, more than the %zu of the static scratch "
+            "(call ft_moe_layer with a workspace)",
+            need, (size_t)FT_NOALLOC_SCRATCH_BYTES);
+    REQUIRE(status == nullptr || ((uintptr_t)status & 3u) == 0, FT_E_INVAL, "status is not 4-byte aligned");
+    // every check of the call runs before anything is enqueued (the scratch's address stands in)
+    uint8_t* sp = nullptr;
+    bool fresh = false;
+    rc = scratch_of_device(&sp, &fresh);
+    if (rc) return rc;
+    rc = layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
+                       y_sorted, y_shared, out, residual_mask, sp, FT_NOALLOC_SCRATCH_BYTES, flags, stream, true);
+    if (rc) {
+      if (fresh) {  // nothing was enqueued: the first clear is still to come
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) g_scratch_clear[dev] = false;
+      }
+      return rc;
+    }
+    if (fresh) {  // counters, queues and the status word start at zero: clear the whole scratch once
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, (uint4*)sp,
+                         (size_t)FT_NOALLOC_SCRATCH_BYTES / 16);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_status(e, "ft_moe_layer_noalloc scratch clear launch");
+    }
+    rc = layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
+                       y_sorted, y_shared, out, residual_mask, sp, FT_NOALLOC_SCRATCH_BYTES, flags, stream);
+    if (rc) return rc;
+    // the status word is the first int32 of the layer workspace's control block
+    hipLaunchKernelGGL(scratch_status_kernel, dim3(1), dim3(1), 0, stream, (int32_t*)sp, status);
+    return hip_status(hipGetLastError(), "ft_moe_layer_noalloc status launch");
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_layer_noalloc: unexpected exception");
   }
 }
 

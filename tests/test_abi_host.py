@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -52,6 +52,20 @@ def test_route_proj_validation():
     _err(L.ft_moe_route_proj(A, A, 40, 64, 8, 2, B, B, B, B, ws, None), ft.FT_E_WORKSPACE, "workspace")
     assert ft.lib.ft_moe_route_proj_workspace(40) == 3 * 16 * 4
     assert L.ft_moe_route_proj(None, None, 0, 64, 8, 2, None, None, None, None, 0, None) == ft.FT_OK
+
+
+def test_layer_noalloc_refuses_oversize_layers():
+    """ft_moe_layer_noalloc refuses a layer whose workspace exceeds its static scratch before any HIP
+    call (no GPU needed), and applies ft_moe_layer's own argument checks first."""
+    L = ft.lib
+    bank = ft.ft_moe_bank(ft.FT_W_FP8_B128, 96, 7168, 2048, 0x10000, 0x20000, 0x30000, 0x40000)
+    args = lambda T, k, flags=0: (ctypes.byref(bank), A, -1, A, A, T, 256, k, A, A, A, A, A, A, A, None, A, A, None,  # noqa: E731
+                                  flags, None)
+    need = L.ft_moe_layer_workspace(ctypes.byref(bank), 4096, 256, 8, -1, 0)
+    assert need > ft.FT_NOALLOC_SCRATCH_BYTES
+    _err(L.ft_moe_layer_noalloc(*args(4096, 8)), ft.FT_E_WORKSPACE, "static scratch")
+    _err(L.ft_moe_layer_noalloc(*args(4, 0)), ft.FT_E_INVAL, "k must be")
+    _err(L.ft_moe_layer_noalloc(*args(4, 8, 0x40)), ft.FT_E_INVAL, "unknown flags")
 
 
 def test_cache_update_validation():
