@@ -58,7 +58,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build_layers(w: synth.Workload, T: int, n_layers: int, copies: int = 1):
+def build_layers(w: synth.Workload, T: int, n_layers: int, copies: int = 1, flags: int = 0):
     """The step's layers.  copies > 1 (single-layer workloads): the layer is repeated over that many
     copies of its bank and buffers at distinct addresses, run back to back, so that one pass touches
     more bytes than the caches hold (the MALL is 256 MB)."""
@@ -75,7 +75,7 @@ def build_layers(w: synth.Workload, T: int, n_layers: int, copies: int = 1):
             b = bank if c == 0 else ft.DeviceBank(bank.fmt, bank.n_slots, bank.d, bank.I,
                                                   *[None if t is None else t.clone()
                                                     for t in (bank.w13, bank.w2, bank.s13, bank.s2)])
-            layer = ft.MoELayer(b, slot.clone(), w.k, T, shared_slot=w.shared_slot)
+            layer = ft.MoELayer(b, slot.clone(), w.k, T, shared_slot=w.shared_slot, flags=flags)
             layers.append((layer, logits.clone(), x.clone()))
         if (l + 1) % 8 == 0 or l + 1 == n_layers:
             log(f"generated {l + 1}/{n_layers} layers" + (f" ({copies} copies each)" if copies > 1 else ""))
@@ -595,6 +595,8 @@ def main():
     ap.add_argument("--prefill", default="prefill_bf16_zipf", metavar="WORKLOAD",
                     help="prefill workload measured beside a decode workload in the same run ('' for none)")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--widen", action="store_true",
+                    help="MXFP4 / FP8 GEMM groups on the bf16 MFMA with widened weights (FT_GEMM_WIDEN)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run the counter-calibration copy kernel over BYTES")
     ap.add_argument("--route-proj", action="store_true",
@@ -646,7 +648,8 @@ def main():
         if n_layers == 1 and decode:
             per_layer = expected_touched_bytes(w, T)
             copies = int(min(16, max(4, -(-1e9 // per_layer))))
-    m = measure(w, T, n_layers, args.steps, args.warmup, not args.no_graph, args.ffn_reps, copies)
+    m = measure(w, T, n_layers, args.steps, args.warmup, not args.no_graph, args.ffn_reps, copies,
+                ft.FT_GEMM_WIDEN if args.widen else 0)
 
     # ---- the prefill half of the metric, measured in the same run beside the default decode workload
     prefill = None
@@ -688,12 +691,12 @@ def expected_touched_bytes(w: synth.Workload, T: int) -> float:
 
 
 def measure(w: synth.Workload, T: int, n_layers: int, steps: int, warmup: int, use_graph: bool, ffn_reps: int,
-            copies: int = 1):
+            copies: int = 1, flags: int = 0):
     """One workload: warm-up, a HIP graph of one step (every layer call of it) replayed `steps`
     times in the timed region, then the layer call timed on its stream against the rooflines."""
     log(f"workload {w.name}: T={T} d={w.d} E={w.E} k={w.k} I={w.I} fmt={synth.FMT_NAMES[w.fmt]} layers={n_layers}"
         + (f" x {copies} bank copies" if copies > 1 else ""))
-    layers = build_layers(w, T, n_layers, copies)
+    layers = build_layers(w, T, n_layers, copies, flags)
     calls = n_layers * copies  # layer calls per step
 
     for _ in range(max(warmup, 1)):
@@ -774,6 +777,8 @@ def measure(w: synth.Workload, T: int, n_layers: int, steps: int, warmup: int, u
               "shared_expert": w.shared, "resident_experts": w.n_resident or w.E, "graph": graph is not None}
     if copies > 1:
         config["bank_copies"] = copies
+    if flags & ft.FT_GEMM_WIDEN:
+        config["gemm"] = "bf16 MFMA, weights widened"
     out = dict(ms_per_step=ms_per_step, us_per_layer=us_per_layer, tokens_per_s=T / (ms_per_step * 1e-3 / calls),
                spread=spread, roofline=roof, config=config)
     del graph, layers

@@ -69,6 +69,9 @@ enum ft_weight_format {
 #define FT_PATH_GEMV 0x1  /* every group through the streaming GEMV kernels */
 #define FT_PATH_GEMM 0x2  /* every group through the MFMA GEMM kernels */
 #define FT_PATH_MASK 0x3
+#define FT_GEMM_WIDEN 0x10  /* MXFP4 and FP8-B128 GEMM groups decode their weights to bf16 in registers and
+                               run the bf16 MFMA, instead of the scaled MFMA on the stored fp4 / fp8
+                               codes with two-term activations (the default where the shape fits) */
 
 /* ft_moe_combine / ft_moe_layer flags */
 #define FT_OUT_BF16 0x4   /* write `out` as bf16 instead of fp32 */
@@ -180,7 +183,7 @@ size_t ft_moe_grouped_ffn_workspace(const ft_moe_bank* bank, int T, int E, int k
  *   y_shared        bf16 [T][d]: FFN_shared(x[t]); required iff shared_slot >= 0, else NULL
  * FFN_s(x) = (SiLU(x Wg^T) * (x Wu^T)) W2^T with Wg = W13[0:I], Wu = W13[I:2I], SiLU(g) = g/(1+e^-g);
  * products accumulate in fp32; the intermediate h is rounded to bf16 once, y to bf16 once.
- * flags: FT_PATH_* (which kernels run; results agree within rounding).
+ * flags: FT_PATH_*, FT_GEMM_WIDEN (which kernels run; results agree within rounding).
  * ws: device workspace of at least ft_moe_grouped_ffn_workspace(...) bytes.
  */
 int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
@@ -228,7 +231,7 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
  * Beside a long kernel on another stream its waits can last until that kernel ends, or give up
  * after 2^20 polls (about a second) with the status word set; use FT_LAYER_UNFUSED for such
  * overlap.
- * flags: FT_PATH_*, FT_OUT_BF16, FT_LAYER_UNFUSED.  T == 0 only writes counts = offsets = 0.
+ * flags: FT_PATH_*, FT_GEMM_WIDEN, FT_OUT_BF16, FT_LAYER_UNFUSED.  T == 0 only writes counts = offsets = 0.
  */
 int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
                  const float* logits, const uint16_t* x, int T, int E, int k, int32_t* ids, float* w,

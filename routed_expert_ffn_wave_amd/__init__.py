@@ -20,6 +20,7 @@ FT_W_BF16, FT_W_Q4_0, FT_W_MXFP4, FT_W_FP8_B128, FT_W_NVFP4 = range(5)
 FT_PATH_AUTO, FT_PATH_GEMV, FT_PATH_GEMM = 0, 1, 2
 FT_OUT_BF16 = 4
 FT_LAYER_UNFUSED = 8
+FT_GEMM_WIDEN = 16   # MXFP4 / FP8-B128 GEMM groups on the bf16 MFMA (weights widened) instead of fp4 / fp8
 FT_PATH_MASK = 3
 LAYER_MAX_T = 16   # largest T of the fused decode kernels
 FT_NOALLOC_SCRATCH_BYTES = 8 << 20   # static scratch of ft_moe_layer_noalloc, per device

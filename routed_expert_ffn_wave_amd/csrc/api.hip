@@ -95,10 +95,29 @@ size_t h_bytes(int T, int k, int I, bool shared) {
   return round256((size_t)((long long)T * k + (shared ? T : 0)) * I * 2);
 }
 
-// FfnArgs for one grouped-FFN call and its launches (arguments already validated).
+// MXFP4 and FP8-B128 banks whose shapes the scaled low-precision MFMA kernels take run their GEMM
+// groups there (weights in their stored format, activations as two terms of the operand format).
+// (The kernels address each array of activation terms with 32-bit offsets: both stay below 4 GiB.)
+bool mx_path(const ft_moe_bank* b, int T, int E, int k, bool shared, int flags) {
+  if ((flags & FT_GEMM_WIDEN) != 0) return false;
+  if (!((b->fmt == FT_W_MXFP4 || b->fmt == FT_W_FP8_B128) && ftk::gemm_mx_fits(b->fmt, 2 * b->I, b->d, E) &&
+        ftk::gemm_mx_fits(b->fmt, b->d, b->I, E)))
+    return false;
+  const long long rows = (long long)T * k + (shared ? T : 0);
+  return ftk::mx_term_bytes(b->fmt, T, b->d) < (1ull << 32) && ftk::mx_term_bytes(b->fmt, rows, b->I) < (1ull << 32);
+}
+// Workspace after the h rows: the activation terms of x (T rows of d) and of h (every h row, of I)
+size_t mx_ws_bytes(const ft_moe_bank* b, int T, int E, int k, bool shared, int flags) {
+  if (T <= 0 || !mx_path(b, T, E, k, shared, flags)) return 0;
+  const long long rows = (long long)T * k + (shared ? T : 0);
+  return ftk::mx_term_bytes(b->fmt, T, b->d) + ftk::mx_term_bytes(b->fmt, rows, b->I);
+}
+
+// FfnArgs for one grouped-FFN call and its launches (arguments already validated).  terms: the
+// mx_ws_bytes region (unused by the other formats).
 int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
                        int T, int E, int k, const int32_t* offsets, const int32_t* gather, uint16_t* y_sorted,
-                       uint16_t* y_shared, uint16_t* h, int flags, hipStream_t stream) {
+                       uint16_t* y_shared, uint16_t* h, uint8_t* terms, int flags, hipStream_t stream) {
   const int path = flags & FT_PATH_MASK;
   const bool shared = shared_slot >= 0;
   ftk::FfnArgs a{};
@@ -153,6 +172,9 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     const long long g_up = big_upper < groups_upper ? big_upper : groups_upper;
     gemm_tiles = (rows_total + BM - 1) / BM + g_up;
   }
+  const bool mx = run_gemm && mx_path(bank, T, E, k, shared, flags);
+  uint8_t* xterms = terms;
+  uint8_t* hterms = mx ? terms + ftk::mx_term_bytes(bank->fmt, T, bank->d) : nullptr;
   hipError_t e = hipSuccess;
   if (run_gemv) {
     a.min_cnt = 1;
@@ -163,7 +185,13 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   if (run_gemm) {
     a.min_cnt = gemm_min;
     a.max_cnt = 0x7fffffff;
-    e = ftk::launch_gemm_gateup(a, (int)gemm_tiles, stream);
+    if (mx) {
+      e = ftk::launch_quant_act(bank->fmt, x, T, bank->d, xterms, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn activation terms launch");
+      e = ftk::launch_gemm_mx(a, true, xterms, T, (int)gemm_tiles, stream);
+    } else {
+      e = ftk::launch_gemm_gateup(a, (int)gemm_tiles, stream);
+    }
     if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm gate/up launch");
   }
   if (run_gemv) {
@@ -175,7 +203,13 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   if (run_gemm) {
     a.min_cnt = gemm_min;
     a.max_cnt = 0x7fffffff;
-    e = ftk::launch_gemm_down(a, (int)gemm_tiles, stream);
+    if (mx) {
+      e = ftk::launch_quant_act(bank->fmt, h, rows_total, bank->I, hterms, stream);
+      if (e != hipSuccess) return hip_status(e, "grouped_ffn h terms launch");
+      e = ftk::launch_gemm_mx(a, false, hterms, rows_total, (int)gemm_tiles, stream);
+    } else {
+      e = ftk::launch_gemm_down(a, (int)gemm_tiles, stream);
+    }
     if (e != hipSuccess) return hip_status(e, "grouped_ffn gemm down launch");
   }
   return ok();
@@ -184,7 +218,7 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
 // Workspace of ft_moe_layer: control words and the fused path's counters, then the h rows and the
 // permutation workspace of the unfused path.
 struct LayerWs {
-  size_t ctl, done13, cdone, h, perm, total;
+  size_t ctl, done13, cdone, h, terms, perm, total;
   int n_rc;
 };
 
@@ -193,7 +227,8 @@ bool layer_fused(const ft_moe_bank* b, int T, int E, int k, int flags) {
          (flags & FT_PATH_MASK) != FT_PATH_GEMM && ftk::layer_decode_fits(b->fmt, T, E, k, b->d, b->I);
 }
 
-LayerWs layer_ws(int d, int I, int T, int E, int k, bool shared, bool fused) {
+LayerWs layer_ws(const ft_moe_bank* b, int T, int E, int k, bool shared, bool fused, int flags) {
+  const int d = b->d, I = b->I;
   LayerWs L{};
   size_t o = 0;
   L.ctl = o;
@@ -205,6 +240,8 @@ LayerWs layer_ws(int d, int I, int T, int E, int k, bool shared, bool fused) {
   o += fused ? round256((size_t)T * (d / 64) * ftk::CNT_STRIDE * 4) : 0;
   L.h = o;
   o += h_bytes(T, k, I, shared);
+  L.terms = o;
+  o += fused ? 0 : round256(mx_ws_bytes(b, T, E, k, shared, flags));
   L.perm = o;
   o += round256(ftk::permute_workspace_bytes(T, E, k));
   L.total = o;
@@ -296,10 +333,8 @@ int ft_moe_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int
 }
 
 size_t ft_moe_grouped_ffn_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
-  (void)E;
-  (void)flags;
-  if (!bank || T < 0 || k < 1) return 0;
-  return h_bytes(T, k, bank->I, shared_slot >= 0);
+  if (!bank || T < 0 || k < 1 || E < 1) return 0;
+  return h_bytes(T, k, bank->I, shared_slot >= 0) + mx_ws_bytes(bank, T, E, k, shared_slot >= 0, flags);
 }
 
 int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
@@ -310,7 +345,7 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     if (rc) return rc;
     rc = check_bank(bank);
     if (rc) return rc;
-    REQUIRE((flags & ~FT_PATH_MASK) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+    REQUIRE((flags & ~(FT_PATH_MASK | FT_GEMM_WIDEN)) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
     const int path = flags & FT_PATH_MASK;
     REQUIRE(path != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
     REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
@@ -325,13 +360,14 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     CHECK_PTR(y_sorted, "y_sorted");
     if (y_shared) CHECK_PTR(y_shared, "y_shared");
     const bool shared = shared_slot >= 0;
-    const size_t need = h_bytes(T, k, bank->I, shared);
+    const size_t hb = h_bytes(T, k, bank->I, shared);
+    const size_t need = hb + mx_ws_bytes(bank, T, E, k, shared, flags);
     REQUIRE(ws != nullptr && ws_bytes >= need, FT_E_WORKSPACE, "grouped_ffn needs %zu bytes of workspace (got %zu%s)",
             need, ws_bytes, ws ? "" : ", null pointer");
     REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
 
     return launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
-                              (uint16_t*)ws, flags, stream);
+                              (uint16_t*)ws, (uint8_t*)ws + hb, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_grouped_ffn: unexpected exception");
   }
@@ -598,7 +634,7 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
     g_err[0] = 0;
     return 0;
   }
-  return layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags)).total;
+  return layer_ws(bank, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags), flags).total;
 }
 
 }  // extern "C"
@@ -617,7 +653,7 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   CHECK_PTR(offsets, "offsets");
   const bool shared = shared_slot >= 0;
   const bool fused = layer_fused(bank, T, E, k, flags);
-  const LayerWs W = layer_ws(bank->d, bank->I, T, E, k, shared, fused);
+  const LayerWs W = layer_ws(bank, T, E, k, shared, fused, flags);
   REQUIRE(wsb != nullptr && ws_bytes >= W.total, FT_E_WORKSPACE, "layer needs %zu bytes of workspace (got %zu%s)",
           W.total, ws_bytes, wsb ? "" : ", null pointer");
   REQUIRE(aligned16(wsb), FT_E_INVAL, "ws is not 16-byte aligned");
@@ -645,7 +681,7 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
     e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
     rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
-                            (uint16_t*)(wsb + W.h), flags & FT_PATH_MASK, stream);
+                            (uint16_t*)(wsb + W.h), wsb + W.terms, flags & (FT_PATH_MASK | FT_GEMM_WIDEN), stream);
     if (rc) return rc;
     return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
                                           bank->d, out, residual_mask, out_bf16, stream),
@@ -698,7 +734,8 @@ int layer_args(const ft_moe_bank* bank, int shared_slot, int T, int E, int k, co
   if (rc) return rc;
   rc = check_bank(bank);
   if (rc) return rc;
-  REQUIRE((flags & ~(FT_PATH_MASK | FT_OUT_BF16 | FT_LAYER_UNFUSED)) == 0, FT_E_INVAL, "unknown flags 0x%x", flags);
+  REQUIRE((flags & ~(FT_PATH_MASK | FT_GEMM_WIDEN | FT_OUT_BF16 | FT_LAYER_UNFUSED)) == 0, FT_E_INVAL,
+          "unknown flags 0x%x", flags);
   REQUIRE((flags & FT_PATH_MASK) != 3, FT_E_INVAL, "FT_PATH_GEMV and FT_PATH_GEMM are exclusive");
   REQUIRE(shared_slot >= -1 && shared_slot < bank->n_slots, FT_E_INVAL, "shared_slot %d out of range [-1, %d)",
           shared_slot, bank->n_slots);
@@ -788,7 +825,7 @@ int ft_moe_layer_noalloc(const ft_moe_bank* bank, const int32_t* slot_of_expert,
     int rc = layer_args(bank, shared_slot, T, E, k, y_shared, flags);
     if (rc) return rc;
     const size_t need =
-        layer_ws(bank->d, bank->I, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags)).total;
+        layer_ws(bank, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags), flags).total;
     REQUIRE(need <= FT_NOALLOC_SCRATCH_BYTES, FT_E_WORKSPACE,
             "ft_moe_layer_noalloc: this layer needs %zu bytes of scratch, more than the %zu of the static scratch "
             "(call ft_moe_layer with a workspace)",

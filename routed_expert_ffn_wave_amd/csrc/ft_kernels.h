@@ -126,6 +126,16 @@ constexpr int GEMM_BM = 128;  // token rows per tile
 bool gemm_wide_fits(int fmt, int rows, int K, int E);
 hipError_t launch_gemm_wide(const FfnArgs& a, bool gateup, int tiles_upper, hipStream_t s);
 
+// Grouped GEMM on the scaled low-precision MFMA with the weights in their stored format (MXFP4:
+// e2m3 x e2m1, FP8-B128: e4m3 x e4m3), activations carried as two terms of the operand format.
+// launch_quant_act writes the terms of `rows` bf16 rows of K values into `terms` (mx_term_bytes);
+// launch_gemm_mx reads the A rows' terms from there (term_rows: rows the terms array holds).
+bool gemm_mx_fits(int fmt, int rows, int K, int E);
+size_t mx_term_bytes(int fmt, long long rows, int K);
+hipError_t launch_quant_act(int fmt, const uint16_t* src, long long rows, int K, uint8_t* terms, hipStream_t s);
+hipError_t launch_gemm_mx(const FfnArgs& a, bool gateup, const uint8_t* terms, long long term_rows, int tiles_upper,
+                          hipStream_t s);
+
 // ---- fused decode layer: one kernel whose blocks each route and permute the (few) tokens in LDS,
 // then share one list of gate/up and down items through per-XCD work queues, and combine.  Its
 // counters start at zero and the last block to finish returns them to zero.

@@ -292,6 +292,24 @@ def test_grouped_ffn_validation():
     assert call(T=0) == ft.FT_OK
 
 
+def test_grouped_ffn_workspace_holds_activation_terms():
+    """MXFP4 and FP8-B128 banks whose shapes the scaled-MFMA kernels take add the two-term activations
+    of x (T rows of d) and of every h row (of I) to the grouped FFN's workspace, unless
+    FT_GEMM_WIDEN sends their groups to the bf16 kernels; other formats need the h rows only."""
+    L = ft.lib
+    T, E, k, d, I = 300, 16, 4, 512, 256
+    h = T * k * I * 2
+    r256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    for fmt, cb in ((ft.FT_W_MXFP4, 48), (ft.FT_W_FP8_B128, 64)):
+        b = _bank(fmt=fmt, n=E, d=d, I=I)
+        terms = lambda rows, K: r256(rows * (K // 32) * cb) + r256(rows * (K // 32) * 2)  # noqa: E731
+        full = L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, 0)
+        assert full == r256(h) + terms(T, d) + terms(T * k, I), (fmt, full)
+        assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, ft.FT_GEMM_WIDEN) == r256(h)
+    b = _bank(fmt=ft.FT_W_BF16, n=E, d=d, I=I)
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, 0) == r256(h)
+
+
 def test_layer_validation_and_workspace():
     L = ft.lib
     b = _bank(fmt=ft.FT_W_Q4_0, n=8, d=256, I=512)
@@ -305,7 +323,7 @@ def test_layer_validation_and_workspace():
                               kw.get("out", B), kw.get("mask", None), kw.get("ws", A), kw.get("ws_bytes", ws),
                               kw.get("flags", 0), None)
     _err(call(bank=None), ft.FT_E_INVAL, "bank is null")
-    _err(call(flags=16), ft.FT_E_INVAL, "unknown flags")
+    _err(call(flags=0x40), ft.FT_E_INVAL, "unknown flags")
     _err(call(flags=3), ft.FT_E_INVAL, "exclusive")
     _err(call(k=9), ft.FT_E_INVAL, "k must be")
     _err(call(shared=3), ft.FT_E_INVAL, "y_shared")

@@ -176,12 +176,15 @@ def _small_workloads():
 SMALL = _small_workloads()
 
 
-@pytest.mark.parametrize("path", ["auto", "gemv", "gemm", "calls"])
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm", "calls", "widen"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_small(ft, name, path):
-    """ft_moe_layer with each FFN path (fused decode kernels where T <= 16), and the four calls."""
+    """ft_moe_layer with each FFN path (fused decode kernels where T <= 16), and the four calls;
+    "widen": every group on the GEMM kernels with MXFP4 / FP8 weights widened to bf16 (the other
+    formats run their usual GEMM kernels)."""
     w = SMALL[name]
-    flags = {"auto": 0, "gemv": ft.FT_PATH_GEMV, "gemm": ft.FT_PATH_GEMM, "calls": 0}[path]
+    flags = {"auto": 0, "gemv": ft.FT_PATH_GEMV, "gemm": ft.FT_PATH_GEMM, "calls": 0,
+             "widen": ft.FT_PATH_GEMM | ft.FT_GEMM_WIDEN}[path]
     T = w.T if name in ("tiny_bf16", "decode_q4_0") else min(w.T, 40 if path == "gemv" else w.T)
     log(f"layer {name} T={T} path={path}")
     li = synth.layer_inputs(w, layer=0, T=T)
