@@ -23,6 +23,8 @@
 //            (lanes 32-63) -> h = SiLU(g) * u for 32 columns, rounded to bf16 into the h workspace;
 //   down:    W2 rows 64cb..64cb+63 -> 64 output columns of y, rounded to bf16.
 #pragma once
+#include <type_traits>
+
 #include "ft_device.h"
 #include "ft_kernels.h"
 
@@ -70,15 +72,24 @@ __device__ __forceinline__ u32x4 load_u32x4_agent(const uint16_t* p) {
 // Wait until this wave's stores have completed (a compiler barrier too).
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// No block-wide step between the weight prefetch and the activation rows (see gemv_item).
+struct NoPre {
+  __device__ void operator()() const {}
+};
+
 // One work item: the RPL 64-row device blocks RPL*cb .. RPL*cb+RPL-1 of bank slot `slot` against the
 // nt (<= NT) token rows t0.. of a group whose sorted rows start at row0 (`shared`: the shared
 // expert's group).  Writes 32 columns of h per row block (gate/up) or 64 columns of y (down).  All threads of the block call it;
 // it ends with a block barrier, after which the LDS union may be reused.  COH: h rows are read and
 // h / y rows written with agent-scope atomic accesses (other blocks of the launch use them).
 // s_tok: token of each sorted row in LDS, or null to read a.gather through the scalar cache.
-template <int FMT, bool GATEUP, int WPB, int NT, bool COH = false, int RPL = 1>
+// `pre`: a block-wide step that the activation rows depend on (a dependency wait): when given, the
+// item's first PF - 1 weight chunks are issued before it (the weights do not depend on it) and the
+// rows and scales after it; otherwise the rows and scales are issued first.
+template <int FMT, bool GATEUP, int WPB, int NT, bool COH = false, int RPL = 1, class Pre = NoPre>
 __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, int slot, int row0, int t0, int nt,
-                                          int cb, bool shared, const int* s_tok = nullptr) {
+                                          int cb, bool shared, const int* s_tok = nullptr, Pre pre = Pre{}) {
+  constexpr bool WEIGHTS_FIRST = !std::is_same<Pre, NoPre>::value;
   using C = Chunk<FMT>;
   constexpr int PF = GV_PF / RPL, NTHR = WPB * 64;  // the same bytes in flight for any RPL
   const int K = GATEUP ? a.d : a.I;
@@ -145,6 +156,26 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   };
   const int nx = nt * nx8;
   auto load_piece = [&](int v) { return load_x(row_of(v / nx8) + 8 * (v % nx8)); };
+  // ---- prefetch ring of PF chunks of codes.  Loads are issued unconditionally, with indices past
+  // the wave's last chunk clamped to it, so every path keeps the same loads in flight.
+  u32x4 buf[PF][RPL];
+  auto issue = [&](u32x4* b, int j) {
+    const int c = chunk_of(j);
+#pragma unroll
+    for (int q = 0; q < RPL; ++q)  // streamed once: non-temporal, so they do not evict what is reused
+      b[q] = __builtin_nontemporal_load((const u32x4*)(rowp[q] + (size_t)c * CSTRIDE));
+  };
+  auto issue_ring = [&]() {
+    if (niter > 0) {
+#pragma unroll
+      for (int p = 0; p < PF - 1; ++p) issue(buf[p], min(p, jlast));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (WEIGHTS_FIRST) {
+    issue_ring();
+    pre();
+  }
   u32x4 xv[FLAT ? 1 : XMAX][NXR];
   u32x4 xf[FLAT ? XB : 1];
   if constexpr (FLAT) {
@@ -170,20 +201,7 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- prefetch ring of PF chunks of codes.  Loads are issued unconditionally, with indices past
-  // the wave's last chunk clamped to it, so every path keeps the same loads in flight.
-  u32x4 buf[PF][RPL];
-  auto issue = [&](u32x4* b, int j) {
-    const int c = chunk_of(j);
-#pragma unroll
-    for (int q = 0; q < RPL; ++q)  // streamed once: non-temporal, so they do not evict what is reused
-      b[q] = __builtin_nontemporal_load((const u32x4*)(rowp[q] + (size_t)c * CSTRIDE));
-  };
-  if (niter > 0) {
-#pragma unroll
-    for (int p = 0; p < PF - 1; ++p) issue(buf[p], min(p, jlast));
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!WEIGHTS_FIRST) issue_ring();
 
   // Q4_0 weights are decoded as 128 + q, so each block needs the sum of its 32 activations; four
   // consecutive threads hold one block (K/8 is a multiple of 4, so they stay together)

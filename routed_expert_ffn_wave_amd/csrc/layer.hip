@@ -302,20 +302,24 @@ __global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
       __syncthreads();
       if (tid == 0) atomic_add_agent(L.done13 + rc * CNT_STRIDE, 1);
     } else {
-      if (tid == 0) {
-        int spins = 0;
-        while (atomic_load_agent(L.done13 + rc * CNT_STRIDE) < ncb13) {
-          __builtin_amdgcn_s_sleep(8);
-          if (++spins >= SPIN_LIMIT) {
-            atomic_add_agent(L.ctl + CTL_ERR, 1);
-            break;
+      // the wait for the row chunk's h runs after the item's first weight chunks are issued (W2 does
+      // not depend on h); after it, h is read with agent-scope loads
+      auto dep_wait = [&]() {
+        if (tid == 0) {
+          int spins = 0;
+          while (atomic_load_agent(L.done13 + rc * CNT_STRIDE) < ncb13) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++spins >= SPIN_LIMIT) {
+              atomic_add_agent(L.ctl + CTL_ERR, 1);
+              break;
+            }
+            // after one wait has given up, later waits give up at once
+            if ((spins & 63) == 0 && atomic_load_agent(L.ctl + CTL_ERR) != 0) break;
           }
-          // after one wait has given up, later waits give up at once
-          if ((spins & 63) == 0 && atomic_load_agent(L.ctl + CTL_ERR) != 0) break;
         }
-      }
-      __syncthreads();  // the row chunk's h is complete: read it below with agent-scope loads
-      gemv_item<FMT, false, WPB, NT, true, RPL2>(a, s_union, slot, row0, t0, nt, cb, shared, s_gather);
+        __syncthreads();
+      };
+      gemv_item<FMT, false, WPB, NT, true, RPL2>(a, s_union, slot, row0, t0, nt, cb, shared, s_gather, dep_wait);
       wait_stores();  // this wave's y stores have completed before the counts move
       __syncthreads();
       if (tid < nt * RPL2) {  // one contribution per (token, 64-column block) of the item
