@@ -113,11 +113,15 @@ size_t mx_ws_bytes(const ft_moe_bank* b, int T, int E, int k, bool shared, int f
   return ftk::mx_term_bytes(b->fmt, T, b->d) + ftk::mx_term_bytes(b->fmt, rows, b->I);
 }
 
+// Bytes of the work-queue counters at the start of a grouped-FFN workspace (cleared by each call).
+constexpr size_t kQctrBytes = (ftk::FFN_QCTR_INTS * 4 + 255) & ~(size_t)255;
+
 // FfnArgs for one grouped-FFN call and its launches (arguments already validated).  terms: the
-// mx_ws_bytes region (unused by the other formats).
+// mx_ws_bytes region (unused by the other formats); qctr: kQctrBytes of queue counters.
 int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
                        int T, int E, int k, const int32_t* offsets, const int32_t* gather, uint16_t* y_sorted,
-                       uint16_t* y_shared, uint16_t* h, uint8_t* terms, int flags, hipStream_t stream) {
+                       uint16_t* y_shared, uint16_t* h, uint8_t* terms, int32_t* qctr, int flags,
+                       hipStream_t stream) {
   const int path = flags & FT_PATH_MASK;
   const bool shared = shared_slot >= 0;
   ftk::FfnArgs a{};
@@ -175,16 +179,21 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   const bool mx = run_gemm && mx_path(bank, T, E, k, shared, flags);
   uint8_t* xterms = terms;
   uint8_t* hterms = mx ? terms + ftk::mx_term_bytes(bank->fmt, T, bank->d) : nullptr;
-  hipError_t e = hipSuccess;
+  // every launch below takes its items from its own queue counters, cleared here
+  hipError_t e = ftk::launch_zero_ints(qctr, ftk::FFN_QCTR_INTS, stream);
+  if (e != hipSuccess) return hip_status(e, "grouped_ffn queue clear launch");
+  constexpr int QL = ftk::FFN_QCTR_INTS / 4;  // counters of one launch
   if (run_gemv) {
     a.min_cnt = 1;
     a.max_cnt = gemv_max;
+    a.qctr = qctr;
     e = ftk::launch_gemv_gateup(a, (int)groups_upper, rows_total, stream);
     if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv gate/up launch");
   }
   if (run_gemm) {
     a.min_cnt = gemm_min;
     a.max_cnt = 0x7fffffff;
+    a.qctr = qctr + QL;
     if (mx) {
       e = ftk::launch_quant_act(bank->fmt, x, T, bank->d, xterms, stream);
       if (e != hipSuccess) return hip_status(e, "grouped_ffn activation terms launch");
@@ -197,12 +206,14 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   if (run_gemv) {
     a.min_cnt = 1;
     a.max_cnt = gemv_max;
+    a.qctr = qctr + 2 * QL;
     e = ftk::launch_gemv_down(a, (int)groups_upper, rows_total, stream);
     if (e != hipSuccess) return hip_status(e, "grouped_ffn gemv down launch");
   }
   if (run_gemm) {
     a.min_cnt = gemm_min;
     a.max_cnt = 0x7fffffff;
+    a.qctr = qctr + 3 * QL;
     if (mx) {
       e = ftk::launch_quant_act(bank->fmt, h, rows_total, bank->I, hterms, stream);
       if (e != hipSuccess) return hip_status(e, "grouped_ffn h terms launch");
@@ -218,7 +229,7 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
 // Workspace of ft_moe_layer: control words and the fused path's counters, then the h rows and the
 // permutation workspace of the unfused path.
 struct LayerWs {
-  size_t ctl, done13, cdone, h, terms, perm, total;
+  size_t ctl, done13, cdone, qctr, h, terms, perm, total;
   int n_rc;
 };
 
@@ -238,6 +249,8 @@ LayerWs layer_ws(const ft_moe_bank* b, int T, int E, int k, bool shared, bool fu
   o += round256((size_t)L.n_rc * ftk::CNT_STRIDE * 4);
   L.cdone = o;
   o += fused ? round256((size_t)T * (d / 64) * ftk::CNT_STRIDE * 4) : 0;
+  L.qctr = o;
+  o += fused ? 0 : kQctrBytes;
   L.h = o;
   o += h_bytes(T, k, I, shared);
   L.terms = o;
@@ -334,7 +347,7 @@ int ft_moe_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int
 
 size_t ft_moe_grouped_ffn_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
   if (!bank || T < 0 || k < 1 || E < 1) return 0;
-  return h_bytes(T, k, bank->I, shared_slot >= 0) + mx_ws_bytes(bank, T, E, k, shared_slot >= 0, flags);
+  return kQctrBytes + h_bytes(T, k, bank->I, shared_slot >= 0) + mx_ws_bytes(bank, T, E, k, shared_slot >= 0, flags);
 }
 
 int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
@@ -361,13 +374,14 @@ int ft_moe_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
     if (y_shared) CHECK_PTR(y_shared, "y_shared");
     const bool shared = shared_slot >= 0;
     const size_t hb = h_bytes(T, k, bank->I, shared);
-    const size_t need = hb + mx_ws_bytes(bank, T, E, k, shared, flags);
+    const size_t need = kQctrBytes + hb + mx_ws_bytes(bank, T, E, k, shared, flags);
     REQUIRE(ws != nullptr && ws_bytes >= need, FT_E_WORKSPACE, "grouped_ffn needs %zu bytes of workspace (got %zu%s)",
             need, ws_bytes, ws ? "" : ", null pointer");
     REQUIRE(aligned16(ws), FT_E_INVAL, "ws is not 16-byte aligned");
 
+    uint8_t* wsb = (uint8_t*)ws;
     return launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
-                              (uint16_t*)ws, (uint8_t*)ws + hb, flags, stream);
+                              (uint16_t*)(wsb + kQctrBytes), wsb + kQctrBytes + hb, (int32_t*)wsb, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_grouped_ffn: unexpected exception");
   }
@@ -681,7 +695,8 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
     e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
     rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
-                            (uint16_t*)(wsb + W.h), wsb + W.terms, flags & (FT_PATH_MASK | FT_GEMM_WIDEN), stream);
+                            (uint16_t*)(wsb + W.h), wsb + W.terms, (int32_t*)(wsb + W.qctr),
+                            flags & (FT_PATH_MASK | FT_GEMM_WIDEN), stream);
     if (rc) return rc;
     return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
                                           bank->d, out, residual_mask, out_bf16, stream),

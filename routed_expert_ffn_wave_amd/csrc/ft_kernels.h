@@ -68,7 +68,12 @@ struct FfnArgs {
   uint16_t* y_sorted;  // bf16 [T*k][d]
   uint16_t* y_shared;  // bf16 [T][d] or null
   int min_cnt, max_cnt;  // groups this launch handles, by routed-row count
+  int32_t* qctr;         // work-queue counters of this launch ([QN][Q_STRIDE], zero at launch), or null:
+                         // the kernels that take items from queues (GEMV, scaled-MFMA GEMM) need them
 };
+// Grouped FFN launches: every launch's queue counters ([4][QN * Q_STRIDE] ints) cleared in one kernel
+constexpr int FFN_QCTR_INTS = 4 * 8 * 16;
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 

@@ -34,6 +34,7 @@
 #include "ft_device.h"
 #include "ft_groups.h"
 #include "ft_kernels.h"
+#include "ft_queue.h"
 #include "ft_tile.h"
 
 namespace ftk {
@@ -223,10 +224,18 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   int unit_scale = 127;
   asm volatile("" : "+v"(unit_scale));
 
-  // blocks go to the 8 XCDs round-robin: each XCD takes a contiguous run of the tile list
-  const int NB = gridDim.x;
-  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int it = lb; it < nitems; it += NB) {
+  // tiles from the launch's work queues: block b serves the run of XCD b % 8 first (blocks go to
+  // the XCDs round-robin, so tiles that share activation rows or weights share an L2), then the
+  // others; a block that starts late takes fewer tiles (claimed one tile ahead)
+  int* s_claim = s_tmp + 1;
+  int qoff = 0;
+  if (tid == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
+  __syncthreads();
+  int it = s_claim[0];
+  __syncthreads();
+  for (; it >= 0 && it < nitems;) {
+    int nxt = -1;
+    if (tid == 0) nxt = queue_claim(a.qctr, nitems, qoff);
     const int g = find_group(s_item0, gl.n, it);
     const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
     const int mt = local / ntiles, nt = local % ntiles;
@@ -443,6 +452,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
     const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
     store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
     __syncthreads();  // the next tile's activations overwrite the staging slices
+    if (tid == 0) s_claim[0] = nxt;
+    __syncthreads();
+    it = s_claim[0];
+    __syncthreads();
   }
 }
 

@@ -21,13 +21,25 @@
 //   gate/up: a W13 device block holds gate rows 32cb.. (lanes 0-31) and the matching up rows
 //            (lanes 32-63) -> h = SiLU(g) * u for 32 columns, rounded to bf16 into the h workspace;
 //   down:    W2 rows 64cb..64cb+63 -> 64 output columns of y, rounded to bf16.
-// The grid is sized to the blocks the device holds at once; blocks walk the item list with a stride.
+// The grid is sized to the blocks the device holds at once; blocks take items from per-XCD work
+// queues (ft_queue.h), so a block that starts late takes fewer items.
 #include "ft_device.h"
 #include "ft_gemv.h"
 #include "ft_groups.h"
 #include "ft_kernels.h"
+#include "ft_queue.h"
 
 namespace ftk {
+
+__global__ void zero_ints_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 template <int FMT, bool GATEUP, int WPB, int NT>
 __global__ __launch_bounds__(WPB * 64, 4) void gemv_kernel(FfnArgs a) {
@@ -45,13 +57,34 @@ __global__ __launch_bounds__(WPB * 64, 4) void gemv_kernel(FfnArgs a) {
   build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + NT - 1) / NT) * ncb; });
   const int nitems = s_item0[gl.n];
   const int TK = a.T * a.k;
-  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+  // items from the launch's work queues (claimed one item ahead), or a fixed stride without them
+  int* s_claim = s_tmp + 1;
+  const bool queued = a.qctr != nullptr;
+  int qoff = 0;
+  int it = blockIdx.x;
+  if (queued) {
+    if (threadIdx.x == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
+    __syncthreads();
+    it = s_claim[0];
+    __syncthreads();
+  }
+  while (it >= 0 && it < nitems) {
+    int nxt = -1;
+    if (queued && threadIdx.x == 0) nxt = queue_claim(a.qctr, nitems, qoff);
     const int g = find_group(s_item0, gl.n, it);
     const int local = it - s_item0[g];
     const int tchunk = local / ncb, cb = local % ncb;
     const int row0 = s_row0[g], cnt = s_cnt[g];
     const int t0 = tchunk * NT;
     gemv_item<FMT, GATEUP, WPB, NT>(a, s_union, s_slot[g], row0, t0, min(NT, cnt - t0), cb, row0 >= TK);
+    if (queued) {
+      if (threadIdx.x == 0) s_claim[0] = nxt;
+      __syncthreads();
+      it = s_claim[0];
+      __syncthreads();
+    } else {
+      it += gridDim.x;
+    }
   }
 }
 

@@ -286,9 +286,9 @@ def test_grouped_ffn_validation():
     _err(call(bank=ctypes.byref(odd_i)), ft.FT_E_INVAL, "multiple of 64")
     fp8 = _bank(fmt=ft.FT_W_FP8_B128, d=256, I=64)
     _err(call(bank=ctypes.byref(fp8)), ft.FT_E_INVAL, "FP8_B128 needs I")
-    # workspace query: bf16 h rows for every routed pair, plus the shared expert's rows
-    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, -1, 0) == 16 * 2 * 512 * 2
-    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, 3, 0) == (16 * 2 + 16) * 512 * 2
+    # workspace query: the work-queue counters, then bf16 h rows for every routed pair (and the shared expert)
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, -1, 0) == 4 * 8 * 16 * 4 + 16 * 2 * 512 * 2
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), 16, 8, 2, 3, 0) == 4 * 8 * 16 * 4 + (16 * 2 + 16) * 512 * 2
     assert call(T=0) == ft.FT_OK
 
 
@@ -300,14 +300,15 @@ def test_grouped_ffn_workspace_holds_activation_terms():
     T, E, k, d, I = 300, 16, 4, 512, 256
     h = T * k * I * 2
     r256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    q = 4 * 8 * 16 * 4   # the work-queue counters of the call's four kernel launches
     for fmt, cb in ((ft.FT_W_MXFP4, 48), (ft.FT_W_FP8_B128, 64)):
         b = _bank(fmt=fmt, n=E, d=d, I=I)
         terms = lambda rows, K: r256(rows * (K // 32) * cb) + r256(rows * (K // 32) * 2)  # noqa: E731
         full = L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, 0)
-        assert full == r256(h) + terms(T, d) + terms(T * k, I), (fmt, full)
-        assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, ft.FT_GEMM_WIDEN) == r256(h)
+        assert full == q + r256(h) + terms(T, d) + terms(T * k, I), (fmt, full)
+        assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, ft.FT_GEMM_WIDEN) == q + r256(h)
     b = _bank(fmt=ft.FT_W_BF16, n=E, d=d, I=I)
-    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, 0) == r256(h)
+    assert L.ft_moe_grouped_ffn_workspace(ctypes.byref(b), T, E, k, -1, 0) == q + r256(h)
 
 
 def test_layer_validation_and_workspace():
@@ -339,10 +340,11 @@ def test_layer_validation_and_workspace():
     unfused = L.ft_moe_layer_workspace(ctypes.byref(b), 8, 8, 2, -1, ft.FT_LAYER_UNFUSED)
     h = 8 * 2 * 512 * 2
     ctl = 10 * 64 * 4   # status word, a work-queue counter per XCD and the exit counter, each on its own line
-    assert unfused == ctl + h
+    qctr = 4 * 8 * 16 * 4  # the four calls' work-queue counters (grouped FFN kernels)
+    assert unfused == ctl + qctr + h
     assert fused > unfused
     big = L.ft_moe_layer_workspace(ctypes.byref(b), 4096, 8, 2, -1, 0)
-    assert big == ctl + 4096 * 2 * 512 * 2
+    assert big == ctl + qctr + 4096 * 2 * 512 * 2
     assert L.ft_moe_layer_workspace(ctypes.byref(b), 16, 8, 9, -1, 0) == 0
     assert L.ft_moe_layer_workspace(None, 16, 8, 2, -1, 0) == 0
 
