@@ -190,15 +190,22 @@ def test_cache_fill_full_shape(ft):
     log("  ok")
 
 
+# (T, d, I, steps): few tokens run the GEMV kernels beside the fill; from 256 tokens every group
+# runs on the GEMM kernels (the scaled-MFMA ones for MXFP4 and FP8-B128)
+STREAM_SHAPES = {"gemv_T16": (16, 256, 128, 8), "gemm_T300": (300, 512, 256, 4)}
+
+
+@pytest.mark.parametrize("shape", list(STREAM_SHAPES))
 @pytest.mark.parametrize("fmt", [synth.FMT_Q4_0, synth.FMT_MXFP4, synth.FMT_FP8_B128],
                          ids=lambda f: synth.FMT_NAMES[f])
-def test_cache_streamed_layer_steps(ft, fmt):
+def test_cache_streamed_layer_steps(ft, fmt, shape):
     """Layer steps with the cache: route, permute, cache update; the fill on a second stream beside
     the grouped FFN and combine, which use this step's compute_slot.  Each step's ids, permutation,
     mask and outputs equal the oracle layer's on the full bank with the oracle cache's compute_slot."""
-    E, S, T, k, ml, steps = 16, 6, 16, 4, 3, 8
-    w = synth.Workload("cache_layer", 84, T=T, d=256, E=E, k=k, I=128, fmt=fmt, zipf=True)
-    log(f"streamed layer steps {synth.FMT_NAMES[fmt]}")
+    T, d, I, steps = STREAM_SHAPES[shape]
+    E, S, k, ml = 16, 6, 4, 3
+    w = synth.Workload("cache_layer", 84, T=T, d=d, E=E, k=k, I=I, fmt=fmt, zipf=True)
+    log(f"streamed layer steps {synth.FMT_NAMES[fmt]} T={T} d={d} I={I}")
     canon_full = synth.make_bank(w, 0)
     full = device_bank(canon_full)
     src = full.to_pinned_host()
