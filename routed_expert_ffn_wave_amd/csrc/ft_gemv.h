@@ -41,10 +41,14 @@ __device__ __forceinline__ size_t mat_bytes(int rows, int K) {
 
 // dynamic LDS: [groups: 4 x (E+2) ints][tmp: 4 ints][x rows NT x K bf16, item scales | partial sums]
 __host__ __device__ inline size_t gv_group_bytes(int E) { return ((size_t)4 * (E + 2) * 4 + 16 + 15) & ~(size_t)15; }
-// per-(row, chunk) scale bytes of one 64-row block (Q4_0: fp16, MXFP4: E8M0, NVFP4: two e4m3;
-// none otherwise)
+// per-(row, chunk) scale bytes of one 64-row block (Q4_0: fp16, MXFP4: E8M0, NVFP4: two e4m3), or
+// for FP8-B128 the fp32 block scales of the 128-row blocks the 64 rows lie in: two (a gate/up
+// device block holds gate and up rows) of K/128 each
 __host__ __device__ inline size_t gv_scale_bytes(int fmt, int K) {
-  return (fmt == FMT_Q4_0 || fmt == FMT_NVFP4) ? (size_t)64 * (K / 32) * 2 : fmt == FMT_MXFP4 ? (size_t)64 * (K / 32) : 0;
+  return (fmt == FMT_Q4_0 || fmt == FMT_NVFP4) ? (size_t)64 * (K / 32) * 2
+         : fmt == FMT_MXFP4                   ? (size_t)64 * (K / 32)
+         : fmt == FMT_FP8_B128                ? (size_t)2 * (K / 128) * 4
+                                              : 0;
 }
 // Q4_0: per-(token, 32-element block) activation sums, fp32
 __host__ __device__ inline size_t gv_xsum_bytes(int fmt, int K, int NT) {
@@ -90,6 +94,7 @@ template <int FMT, bool GATEUP, int WPB, int NT, bool COH = false, int RPL = 1, 
 __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, int slot, int row0, int t0, int nt,
                                           int cb, bool shared, const int* s_tok = nullptr, Pre pre = Pre{}) {
   constexpr bool WEIGHTS_FIRST = !std::is_same<Pre, NoPre>::value;
+  static_assert(!GATEUP || RPL == 1, "gate/up items cover one 64-row block");
   using C = Chunk<FMT>;
   constexpr int PF = GV_PF / RPL, NTHR = WPB * 64;  // the same bytes in flight for any RPL
   const int K = GATEUP ? a.d : a.I;
@@ -134,6 +139,18 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   constexpr int SB = (FMT == FMT_Q4_0 || FMT == FMT_NVFP4) ? 2 : 1;
   constexpr bool STAGE_SCALES = FMT == FMT_Q4_0 || FMT == FMT_MXFP4 || FMT == FMT_NVFP4;
   const int nx8 = K / 8;
+  // FP8-B128: the fp32 scales of the item's NSEL 128-row blocks (gate/up: the gate rows' and the up
+  // rows'; down: one per 64-row block), staged as s_scf[sel][K/128] with the activation rows, so
+  // that the K loop issues nothing but weight loads (a scale load there would have to wait for
+  // every weight load in flight before it: the vector-load counter is in order)
+  constexpr int NSEL = GATEUP ? 2 : RPL;
+  const int nsb = FMT == FMT_FP8_B128 ? K / 128 : 0;
+  float* s_scf = (float*)s_sc;
+  auto fp8_scale_src = [&](int v) -> const float* {  // v = sel * nsb + column block
+    const int sel = v / nsb, b = v % nsb;
+    const int rb = GATEUP ? (32 * cb + (sel ? a.I : 0)) / 128 : (64 * (RPL * cb + sel)) / 128;
+    return (const float*)scales + ((size_t)slot * (nrows / 128) + rb) * nsb + b;
+  };
   const int nsv = STAGE_SCALES ? RPL * nchunk * 64 * SB / 16 : 0;  // the RPL row blocks' scales are one run
   const uint8_t* ssrc = scales + ((size_t)slot * nrows * nchunk + (size_t)RPL * cb * nchunk * 64) * SB;
   auto row_of = [&](int tt) -> const uint16_t* {  // activation row of the item's token tt
@@ -199,6 +216,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
     const int v = threadIdx.x + i * NTHR;
     if (v < nsv) sv[i] = *(const u32x4*)(ssrc + 16 * (size_t)v);
   }
+  float f8s = 0.0f;  // one scale per thread here, the rest (rows longer than NTHR * 64) further down
+  if constexpr (FMT == FMT_FP8_B128) {
+    if ((int)threadIdx.x < NSEL * nsb) f8s = *fp8_scale_src(threadIdx.x);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (!WEIGHTS_FIRST) issue_ring();
@@ -255,6 +276,10 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
   }
   for (int v = threadIdx.x + SMAX * NTHR; v < nsv; v += NTHR)
     *(u32x4*)(s_sc + 16 * (size_t)v) = *(const u32x4*)(ssrc + 16 * (size_t)v);
+  if constexpr (FMT == FMT_FP8_B128) {
+    if ((int)threadIdx.x < NSEL * nsb) s_scf[threadIdx.x] = f8s;
+    for (int v = threadIdx.x + NTHR; v < NSEL * nsb; v += NTHR) s_scf[v] = *fp8_scale_src(v);
+  }
 
   __syncthreads();
 
@@ -277,10 +302,9 @@ __device__ __forceinline__ void gemv_item(const FfnArgs& a, uint8_t* s_union, in
           fsc_hi[q] = 1.0f;
           if constexpr (FMT == FMT_FP8_B128) {
             // one fp32 scale per 128x128 block of logical rows (a gate/up device block holds 32 gate
-            // rows in lanes 0-31 and the matching 32 up rows in lanes 32-63)
-            const float* s32 = (const float*)scales + (size_t)slot * (size_t)(nrows / 128) * (K / 128);
-            const int rb = (GATEUP ? 32 * (RPL * cb + q) + (lane >= 32 ? a.I : 0) : 64 * (RPL * cb + q)) / 128;
-            fsc[q] = s32[(size_t)rb * (K / 128) + (c * 16) / 128];
+            // rows in lanes 0-31 and the matching 32 up rows in lanes 32-63), staged above
+            const int sel = GATEUP ? (lane >= 32 ? 1 : 0) : q;
+            fsc[q] = s_scf[sel * nsb + (c * C::ELEMS) / 128];
           } else if constexpr (FMT == FMT_Q4_0) {
             fsc[q] = fp16_bits_to_f32(((const uint16_t*)s_sc)[(q * nchunk + c) * 64 + lane]);
           } else if constexpr (FMT == FMT_MXFP4) {

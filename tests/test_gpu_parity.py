@@ -282,6 +282,35 @@ def test_layer_small_sweep_fp8(ft, T):
 
 # ------------------------------------------------------------------------------------- degenerate cases
 
+# rows longer than 2048 on the fused path: 8 waves per block, FP8 block scales of two 128-row
+# blocks per item, every format at a reduced shape (the full-size tests cover FP8 and MXFP4 only)
+LONG = synth.Workload("long_rows", 72, T=16, d=4096, E=16, k=4, I=256, fmt=synth.FMT_FP8_B128, zipf=True)
+LONG_FMTS = [synth.FMT_BF16, synth.FMT_Q4_0, synth.FMT_MXFP4, synth.FMT_FP8_B128, synth.FMT_NVFP4]
+
+
+@pytest.mark.parametrize("case", ["plain", "shared", "one_expert_takes_all"])
+@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("fmt", LONG_FMTS, ids=lambda f: synth.FMT_NAMES[f])
+def test_fused_long_rows(ft, fmt, T, case):
+    """The fused layer at d = 4096: against the oracle on every token, against the four calls
+    within the FFN tolerance, and bit for bit on a second run."""
+    from gpu_util import assert_ffn_close
+    w = LONG.replace(fmt=fmt, shared=case == "shared")
+    li = synth.layer_inputs(w, layer=1, T=T)
+    if case == "one_expert_takes_all":   # one group of all T tokens
+        li.logits[:, 5] += 100.0
+    bank = device_bank(li.bank)
+    label = f"long rows {synth.FMT_NAMES[fmt]} {case} T={T}"
+    a = run_gpu_layer(li, bank, mode="layer")
+    compare_layer(li, a, label=label)
+    b = run_gpu_layer(li, bank, mode="calls")
+    for key in ("ids", "counts", "offsets", "gather", "inv", "mask"):
+        assert np.array_equal(a[key], b[key]), f"{label}: {key}"
+    assert_ffn_close(a["out"], b["out"], f"{label}: fused vs calls")
+    again = run_gpu_layer(li, bank, mode="layer")
+    assert np.array_equal(a["out"].view(np.uint32), again["out"].view(np.uint32)), f"{label}: not repeatable"
+
+
 EDGE = synth.Workload("edge", 70, T=33, d=256, E=8, k=2, I=128, fmt=synth.FMT_MXFP4, shared=True)
 
 
