@@ -222,8 +222,10 @@ size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int 
  * grouping); here a slot_of_expert entry outside [0, n_slots) counts as not resident everywhere.
  * Dispatch and combine follow [walk-through] sections 一 and 五.
  * ws: device workspace of ft_moe_layer_workspace(...) bytes, zero-filled by the caller before its
- * first use; every call leaves it ready for the next one (the fused kernel returns its counters to
- * zero).  Its first int32 is a status word that the fused kernel sets non-zero if an internal
+ * first use; every call leaves it ready for the next call of the same shape (bank shape, T, E, k,
+ * shared_slot, flags): the fused kernel returns its counters to zero.  A call of another shape may
+ * find other data where its counters lie: zero the workspace again before it, or give each shape a
+ * workspace of its own.  Its first int32 is a status word that the fused kernel sets non-zero if an internal
  * dependency wait gave up (results are then invalid); the library never clears it, and it stays 0
  * in every correct run.  Calls that may overlap need separate workspaces.
  * The one-kernel path sizes its grid to the blocks the device holds at once and its waits end
@@ -252,8 +254,9 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
  * (FT_NOALLOC_SCRATCH_BYTES per device) instead of a ws argument.  Nothing is allocated.
  *   - A layer whose workspace (ft_moe_layer_workspace with the same arguments) exceeds
  *     FT_NOALLOC_SCRATCH_BYTES is refused with FT_E_WORKSPACE and enqueues nothing.
- *   - The first call on a device enqueues a clear of the whole scratch before the layer; every call
- *     leaves it ready for the next one.
+ *   - The counters a call needs at zero sit at the start of the scratch.  Before the layer, a clear
+ *     kernel zeroes the part of them that earlier calls (of other shapes) may have used for other
+ *     data; every call leaves its own counters at zero.
  *   - status: optional device int32, 4-byte aligned: receives this call's status word (0 in every
  *     correct run; non-zero when a dependency wait of the one-kernel path gave up and the results
  *     are invalid).  A one-thread kernel after the layer moves the word there and clears it, also

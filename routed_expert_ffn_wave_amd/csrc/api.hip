@@ -226,10 +226,12 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   return ok();
 }
 
-// Workspace of ft_moe_layer: control words and the fused path's counters, then the h rows and the
+// Workspace of ft_moe_layer: control words and the fused path's counters (every one of them zero
+// when a fused call starts and again when it ends; they end at `zeroed`), then the grouped FFN's
+// queue counters (cleared by each unfused call), the h rows, the activation terms and the
 // permutation workspace of the unfused path.
 struct LayerWs {
-  size_t ctl, done13, cdone, qctr, h, terms, perm, total;
+  size_t ctl, done13, cdone, zeroed, qctr, h, terms, perm, total;
   int n_rc;
 };
 
@@ -249,6 +251,7 @@ LayerWs layer_ws(const ft_moe_bank* b, int T, int E, int k, bool shared, bool fu
   o += round256((size_t)L.n_rc * ftk::CNT_STRIDE * 4);
   L.cdone = o;
   o += fused ? round256((size_t)T * (d / 64) * ftk::CNT_STRIDE * 4) : 0;
+  L.zeroed = o;
   L.qctr = o;
   o += fused ? 0 : kQctrBytes;
   L.h = o;
@@ -791,7 +794,11 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 uint8_t* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each device
-bool g_scratch_clear[kMaxDevices] = {};    // its first clear has been enqueued
+// Bytes at the start of each device's scratch that hold zeros once the work enqueued so far has run
+// (the counters a fused call needs zero at its start lie in such a prefix; calls of other shapes
+// leave other data past their own counters).  Starts at 0: the array's initial contents are not
+// relied on.
+size_t g_scratch_zero[kMaxDevices] = {};
 
 __global__ void scratch_clear_kernel(uint4* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -806,8 +813,8 @@ __global__ void scratch_status_kernel(int32_t* word, int32_t* status) {
 }
 
 // Device address of the scratch on the current device (looked up once per device, with that device
-// current); `fresh` is set on the first call for the device, whose scratch the caller clears.
-int scratch_of_device(uint8_t** ptr, bool* fresh) {
+// current) and the device's index.
+int scratch_of_device(uint8_t** ptr, int* device) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "ft_moe_layer_noalloc: hipGetDevice");
@@ -822,9 +829,8 @@ int scratch_of_device(uint8_t** ptr, bool* fresh) {
             p);
     g_scratch_ptr[dev] = (uint8_t*)p;
   }
-  *fresh = !g_scratch_clear[dev];
-  g_scratch_clear[dev] = true;
   *ptr = g_scratch_ptr[dev];
+  *device = dev;
   return FT_OK;
 }
 
@@ -839,37 +845,39 @@ int ft_moe_layer_noalloc(const ft_moe_bank* bank, const int32_t* slot_of_expert,
   try {
     int rc = layer_args(bank, shared_slot, T, E, k, y_shared, flags);
     if (rc) return rc;
-    const size_t need =
-        layer_ws(bank, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags), flags).total;
-    REQUIRE(need <= FT_NOALLOC_SCRATCH_BYTES, FT_E_WORKSPACE,
+    const LayerWs W = layer_ws(bank, T, E, k, shared_slot >= 0, layer_fused(bank, T, E, k, flags), flags);
+    REQUIRE(W.total <= FT_NOALLOC_SCRATCH_BYTES, FT_E_WORKSPACE,
             "ft_moe_layer_noalloc: this layer needs %zu bytes of scratch, more than the %zu of the static scratch "
             "(call ft_moe_layer with a workspace)",
-            need, (size_t)FT_NOALLOC_SCRATCH_BYTES);
+            W.total, (size_t)FT_NOALLOC_SCRATCH_BYTES);
     REQUIRE(status == nullptr || ((uintptr_t)status & 3u) == 0, FT_E_INVAL, "status is not 4-byte aligned");
     // every check of the call runs before anything is enqueued (the scratch's address stands in)
     uint8_t* sp = nullptr;
-    bool fresh = false;
-    rc = scratch_of_device(&sp, &fresh);
+    int dev = 0;
+    rc = scratch_of_device(&sp, &dev);
     if (rc) return rc;
     rc = layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
                        y_sorted, y_shared, out, residual_mask, sp, FT_NOALLOC_SCRATCH_BYTES, flags, stream, true);
-    if (rc) {
-      if (fresh) {  // nothing was enqueued: the first clear is still to come
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) g_scratch_clear[dev] = false;
-      }
-      return rc;
-    }
-    if (fresh) {  // counters, queues and the status word start at zero: clear the whole scratch once
-      hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, (uint4*)sp,
-                         (size_t)FT_NOALLOC_SCRATCH_BYTES / 16);
+    if (rc) return rc;
+    // the control words and counters this call needs zero: clear what earlier calls may have left
+    // there (the status word, the first of them, is zero after every call)
+    std::unique_lock<std::mutex> lock(g_scratch_mu);
+    const size_t zero = g_scratch_zero[dev];
+    g_scratch_zero[dev] = 0;  // unknown until this call's work is enqueued
+    lock.unlock();
+    if (W.zeroed > zero) {
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(64), dim3(256), 0, stream, (uint4*)(sp + zero),
+                         (W.zeroed - zero) / 16);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_status(e, "ft_moe_layer_noalloc scratch clear launch");
     }
     rc = layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
                        y_sorted, y_shared, out, residual_mask, sp, FT_NOALLOC_SCRATCH_BYTES, flags, stream);
     if (rc) return rc;
+    // the call leaves its counters at zero and other data after them
+    lock.lock();
+    g_scratch_zero[dev] = W.zeroed;
+    lock.unlock();
     // the status word is the first int32 of the layer workspace's control block
     hipLaunchKernelGGL(scratch_status_kernel, dim3(1), dim3(1), 0, stream, (int32_t*)sp, status);
     return hip_status(hipGetLastError(), "ft_moe_layer_noalloc status launch");

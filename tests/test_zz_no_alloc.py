@@ -1,8 +1,8 @@
 """ft_moe_layer_noalloc (the layer with the library's static device scratch instead of a workspace)
 against ft_moe_layer (the same call with the caller's workspace) through the C ABI: two calls in a
-row on one stream, the second with fewer tokens, on the one-kernel decode path and on the four-call
-path.  Both calls run the same kernels on the same inputs, so every result matches bit for bit;
-the outputs also meet the FFN tolerance against the oracle, and the status word is 0."""
+row on one stream, the second with fewer tokens (or, once, more), on the one-kernel decode path and
+on the four-call path.  Both calls run the same kernels on the same inputs, so every result matches
+bit for bit; the outputs also meet the FFN tolerance against the oracle, and the status word is 0."""
 from __future__ import annotations
 
 import numpy as np
@@ -22,6 +22,12 @@ CASES = {
                      (16, 3)),
     # four calls (T > 16): route, permute, grouped FFN on GEMV and GEMM kernels, combine
     "bf16_calls": (synth.WORKLOADS["prefill_bf16_zipf"].replace(T=40, d=512, I=256, E=16, k=4), (40, 17)),
+    # more tokens after fewer: the second call's counters lie where the first left h rows
+    "mxfp4_grow": (synth.Workload("noalloc_mx", 72, T=16, d=256, E=8, k=2, I=128, fmt=synth.FMT_MXFP4, shared=True),
+                   (3, 16)),
+    # rows of 4096 (8 waves per block, FP8 block scales staged per item)
+    "fp8_long_rows": (synth.Workload("noalloc_long", 73, T=16, d=4096, E=8, k=8, I=2048, fmt=synth.FMT_FP8_B128),
+                      (16, 9)),
 }
 
 
@@ -46,10 +52,10 @@ def test_noalloc_matches_layer(ft, name):
     li = synth.layer_inputs(w, layer=1, T=max(Ts))
     bank = device_bank(li.bank)
     slot = li.slot_of_expert.clone()
-    if name == "mxfp4_shared":
+    if name.startswith("mxfp4"):
         slot[[1, 6]] = -1  # two experts not resident: their pairs go to the mask
     status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
-    for T in Ts:  # two calls in a row, the second with fewer tokens
+    for T in Ts:  # two calls in a row
         log(f"noalloc {name}: T={T}")
         logits, x = li.logits[:T].cuda().contiguous(), li.x[:T].cuda().contiguous()
         ref_layer = ft.MoELayer(bank, slot.cuda(), w.k, T, shared_slot=w.shared_slot)
