@@ -213,6 +213,10 @@ def _pmc_per_kernel(path: str, counter: str):
     return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
 
 
+def traffic_key(workload: str, T: int) -> str:
+    return f"{workload}@T{T}"
+
+
 def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str):
     """HBM bytes per layer call from two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
     dispatch), each scaled by what the counter reads for the copy probe of known size: the bytes of
@@ -241,7 +245,7 @@ def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_byte
            "write_bytes_per_call": per_call("write_bytes")}
     rec["bytes_per_call"] = rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"]
     db = json.load(open(out_json)) if os.path.exists(out_json) else {}
-    db[workload] = rec
+    db[traffic_key(workload, T)] = rec
     with open(out_json, "w") as fh:
         json.dump(db, fh, indent=1, sort_keys=True)
         fh.write("\n")
@@ -758,17 +762,25 @@ def measure(w: synth.Workload, T: int, n_layers: int, steps: int, warmup: int, u
     # reported beside it
     gbs = bytes_call / (ffn_us * 1e-6) / 1e9
     tfs = flops_call / (ffn_us * 1e-6) / 1e12
-    peak = MFMA_PEAK_TFLOPS["bf16"]
+    # the MFMA type the GEMM groups run on: MXFP4 (e2m3 activation terms x e2m1 weights) and FP8-B128
+    # (e4m3 x e4m3) on the scaled low-precision MFMA above the one-launch decode sizes, unless widened
+    # to bf16; two activation terms per element issue twice the algorithmic MFMA flops
+    mx = T > 16 and not (flags & ft.FT_GEMM_WIDEN) and w.fmt in (synth.FMT_MXFP4, synth.FMT_FP8_B128)
+    mfma_dtype = ("fp4" if w.fmt == synth.FMT_MXFP4 else "fp8") if mx else "bf16"
+    peak = MFMA_PEAK_TFLOPS[mfma_dtype]
     hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    mfma = {"bound": "mfma", "achieved": round(tfs, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4)}
+    mfma = {"bound": "mfma", "achieved": round(tfs, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+            "mfma_dtype": mfma_dtype}
+    if mx:
+        mfma["two_term_issued_flops_per_call"] = round(2 * flops_call)
     roof, other = (hbm, mfma) if gbs / HBM_PEAK_GBS >= tfs / peak else (mfma, hbm)
     roof = dict(roof)
     roof["traffic"] = None
     prof = os.path.join(ROOT, "profiles", "traffic.json")
     src_hash = kernel_source_hash()
     if os.path.exists(prof):
-        rec = json.load(open(prof)).get(w.name)
+        rec = json.load(open(prof)).get(traffic_key(w.name, T))
         if rec and rec.get("source_hash") == src_hash and rec.get("T") == T:
             roof["traffic"] = rec["bytes_per_call"]
     roof["kernel"] = ("ft_moe_layer: layer_decode_kernel (one launch: routing, permutation, streaming GEMV, "
