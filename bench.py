@@ -252,6 +252,21 @@ def pmc_summary(workload: str, T: int, fetch_csv: str, write_csv: str, copy_byte
     print(json.dumps(rec, indent=1))
 
 
+def calibrate():
+    """The device's achievable rates against the published peaks: a 4 GiB streaming read over every
+    CU (HBM), a 1 GiB read of pinned host memory by the cache fill's 8 blocks (host link), and
+    register-only MFMA loops (bf16, e4m3 x e4m3, e2m3 x e2m1).  Own JSON line."""
+    r = ft.ft_moe_measure_rates(dev_bytes=4 << 30, host_bytes=1 << 30, reps=5)
+    peaks = {"hbm_read_gbs": HBM_PEAK_GBS, "host_read_gbs": PCIE_PEAK_GBS, "mfma_bf16_tflops": MFMA_PEAK_TFLOPS["bf16"],
+             "mfma_fp8_tflops": MFMA_PEAK_TFLOPS["fp8"], "mfma_fp6_fp4_tflops": MFMA_PEAK_TFLOPS["fp4"]}
+    rates = {k: {"achieved": round(r[k], 1), "peak": p, "frac": round(r[k] / p, 4)} for k, p in peaks.items()}
+    log(f"rates: {rates}; MFMA clock implied by the bf16 rate {r['mfma_clock_ghz']:.3f} GHz")
+    print(json.dumps({"metric": "achievable device rates (ft_moe_measure_rates)", "value": round(r["hbm_read_gbs"], 1),
+                      "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "vs_baseline": None,
+                      "data": "synthetic", "rates": rates, "mfma_clock_ghz": round(r["mfma_clock_ghz"], 3),
+                      "compute_units": r["compute_units"], "stream_blocks": r["stream_blocks"]}), flush=True)
+
+
 def bench_route_proj(w: synth.Workload, T: int, steps: int, warmup: int):
     """Router projection + route (ft_moe_route_proj) on the workload's shape: one call is one step;
     printed as its own JSON line (the step before the layer, not part of the layer's metric)."""
@@ -624,6 +639,8 @@ def main():
     ap.add_argument("--coexec", default=None, metavar="Q",
                     help="time co-executed steps: a fraction Q of each step's cold experts copied to the GPU, the rest "
                          "on the host ('auto': Q from the host link and host residual rates measured first)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure the device's achievable rates (ft_moe_measure_rates) and print them as one JSON line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -642,6 +659,9 @@ def main():
     T = args.T or w.T
     n_layers = args.layers or w.layers
     decode = T <= 64
+    if args.calibrate:
+        calibrate()
+        return
     if args.route_proj:
         bench_route_proj(w, T, args.steps, args.warmup)
         return

@@ -271,6 +271,37 @@ int ft_moe_layer_noalloc(const ft_moe_bank* bank, const int32_t* slot_of_expert,
                          uint16_t* y_sorted, uint16_t* y_shared, void* out, uint32_t* residual_mask,
                          int32_t* status, int flags, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- start-up rates */
+
+/*
+ * Rates of the device at hand, measured by ft_moe_measure_rates (the start-up measurement of the
+ * [walk-through] section 五: the engine measures the host link and memory bandwidths and sizes its
+ * CPU-GPU split from them).  Rates are the best of `reps` timed launches.
+ */
+typedef struct ft_moe_rates {
+  double hbm_read_gbs;        /* device memory read by a streaming kernel on every CU (GB/s) */
+  double host_read_gbs;       /* pinned host memory read by the same kernel with the cache fill's 8
+                                 blocks: the host link rate P of the load fraction (0: no host_buf) */
+  double mfma_bf16_tflops;    /* dense v_mfma_f32_32x32x16_bf16, register operands, every SIMD */
+  double mfma_fp8_tflops;     /* v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3 operands */
+  double mfma_fp6_fp4_tflops; /* the same instruction with e2m3 x e2m1 operands (the MXFP4 prefill path) */
+  double mfma_clock_ghz;      /* the clock at which the bf16 rate is one MFMA per 32 cycles per SIMD */
+  int compute_units;
+  int stream_blocks;          /* blocks of the device-memory streaming launch (resident per CU x CUs) */
+} ft_moe_rates;
+
+/*
+ * Measures the rates above.  dev_buf: device memory of dev_bytes >= 64 MiB, 256-byte aligned, whose
+ * contents are overwritten (its first MiB takes the kernels' results; the rest is read).  host_buf:
+ * pinned host memory of host_bytes >= 1 MiB, 16-byte aligned, only read; NULL skips the host link.
+ * reps in [1, 100].  Unlike every other call this one blocks: it records HIP events on `stream` and
+ * waits for them (about 10 ms with reps = 3 on a 1 GiB buffer), so it is a start-up call and cannot be
+ * captured into a graph.  It allocates no device memory (two HIP events for the length of the call).
+ * On success *out holds the rates; on error it is left unchanged.
+ */
+int ft_moe_measure_rates(void* dev_buf, size_t dev_bytes, const void* host_buf, size_t host_bytes, int reps,
+                         ft_moe_rates* out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- expert cache */
 
 /*

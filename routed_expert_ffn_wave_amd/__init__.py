@@ -41,6 +41,13 @@ class ft_moe_bank(ctypes.Structure):
                 ("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
+class ft_moe_rates(ctypes.Structure):
+    _fields_ = [("hbm_read_gbs", ctypes.c_double), ("host_read_gbs", ctypes.c_double),
+                ("mfma_bf16_tflops", ctypes.c_double), ("mfma_fp8_tflops", ctypes.c_double),
+                ("mfma_fp6_fp4_tflops", ctypes.c_double), ("mfma_clock_ghz", ctypes.c_double),
+                ("compute_units", ctypes.c_int32), ("stream_blocks", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m routed_expert_ffn_wave_amd.build`")
@@ -69,6 +76,7 @@ def _load():
         "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
         "ft_moe_residual_host": ([BP, P, P, P, P, P, i, i, i, P, i], i),
         "ft_moe_residual_add": ([P, P, i, i, i, P], i),
+        "ft_moe_measure_rates": ([P, sz, P, sz, i, ctypes.POINTER(ft_moe_rates), P], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -83,7 +91,8 @@ EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_r
             "ft_moe_route_proj", "ft_moe_permute_workspace",
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
             "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer",
-            "ft_moe_layer_noalloc", "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add")
+            "ft_moe_layer_noalloc", "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add",
+            "ft_moe_measure_rates")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -237,6 +246,17 @@ def ft_moe_residual_add(out, residual, flags: int = 0, stream=None):
     T, d = residual.shape
     _check(lib.ft_moe_residual_add(_ptr(out), _ptr(residual), T, d, flags, _stream(stream)))
     return out
+
+
+def ft_moe_measure_rates(dev_bytes: int = 1 << 30, host_bytes: int = 256 << 20, reps: int = 3, stream=None) -> dict:
+    """The device's rates (ft_moe_measure_rates): a device buffer of dev_bytes and a pinned host buffer
+    of host_bytes (0: no host link figure) are allocated here for the call.  Blocks until measured."""
+    dev = torch.empty(dev_bytes, dtype=torch.uint8, device="cuda")
+    host = torch.ones(host_bytes, dtype=torch.uint8, pin_memory=True) if host_bytes else None
+    r = ft_moe_rates()
+    _check(lib.ft_moe_measure_rates(_ptr(dev), dev_bytes, _ptr(host), host_bytes if host is not None else 0, reps,
+                                    ctypes.byref(r), _stream(stream)))
+    return {name: getattr(r, name) for name, _ in ft_moe_rates._fields_}
 
 
 # ------------------------------------------------------------------------------------- the four calls

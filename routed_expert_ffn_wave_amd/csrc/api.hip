@@ -646,6 +646,86 @@ int ft_moe_residual_add(void* out, const float* residual, int T, int d, int flag
   }
 }
 
+// ---- start-up rates
+
+constexpr size_t kRatesSink = 1u << 20;          // sink words at the start of dev_buf
+constexpr size_t kRatesMinDev = 64u << 20;       // device bytes: the sink, then at least 63 MiB to stream
+constexpr int kRatesMfmaIters = 4096;            // x 4 MFMAs per wave and launch
+
+int ft_moe_measure_rates(void* dev_buf, size_t dev_bytes, const void* host_buf, size_t host_bytes, int reps,
+                         ft_moe_rates* out, hipStream_t stream) {
+  try {
+    CHECK_PTR(out, "out");
+    CHECK_PTR(dev_buf, "dev_buf");
+    REQUIRE(((uintptr_t)dev_buf & 255u) == 0, FT_E_INVAL, "dev_buf is not 256-byte aligned");
+    REQUIRE(dev_bytes >= kRatesMinDev, FT_E_INVAL, "dev_bytes must be at least %zu (got %zu)", kRatesMinDev,
+            dev_bytes);
+    REQUIRE(reps >= 1 && reps <= 100, FT_E_INVAL, "reps must be in [1, 100] (got %d)", reps);
+    const uint8_t* hv = nullptr;
+    if (host_buf != nullptr) {
+      REQUIRE(((uintptr_t)host_buf & 15u) == 0, FT_E_INVAL, "host_buf is not 16-byte aligned");
+      REQUIRE(host_bytes >= (1u << 20), FT_E_INVAL, "host_bytes must be at least 1 MiB (got %zu)", host_bytes);
+      int rc = source_view(host_buf, "host_buf", &hv);
+      if (rc) return rc;
+    }
+    int blocks = 0, cus = 0;
+    hipError_t e = ftk::rate_launch_facts(&blocks, &cus);
+    if (e != hipSuccess) return hip_status(e, "ft_moe_measure_rates: launch facts");
+    const int mfma_blocks = 2 * cus;  // two 4-wave blocks per CU: two waves per SIMD
+    REQUIRE((size_t)mfma_blocks * 256 * 4 <= kRatesSink && (size_t)blocks * 16 <= kRatesSink, FT_E_UNSUPPORTED,
+            "%d compute units need more sink than the %zu bytes at the start of dev_buf", cus, kRatesSink);
+    uint8_t* base = (uint8_t*)dev_buf;
+    const long long dev_stream = (long long)((dev_bytes - kRatesSink) & ~(size_t)15);
+    const long long host_stream = (long long)(host_bytes & ~(size_t)15);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e != hipSuccess) {
+      if (e0) (void)hipEventDestroy(e0);
+      return hip_status(e, "ft_moe_measure_rates: event create");
+    }
+    // best (shortest) of reps timed launches after one untimed, in seconds; negative on a HIP error
+    auto best = [&](auto launch) -> double {
+      double t = 1e30;
+      for (int r = 0; r <= reps; ++r) {
+        if ((e = hipEventRecord(e0, stream)) != hipSuccess) return -1.0;
+        if ((e = launch()) != hipSuccess) return -1.0;
+        if ((e = hipEventRecord(e1, stream)) != hipSuccess) return -1.0;
+        if ((e = hipEventSynchronize(e1)) != hipSuccess) return -1.0;
+        float ms = 0.0f;
+        if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) return -1.0;
+        if (r > 0 && ms * 1e-3 < t) t = ms * 1e-3;
+      }
+      return t;
+    };
+    ft_moe_rates R{};
+    R.compute_units = cus;
+    R.stream_blocks = blocks;
+    double t = best([&] { return ftk::launch_stream_read(base + kRatesSink, dev_stream, blocks, (uint32_t*)base, stream); });
+    if (t > 0) R.hbm_read_gbs = (double)dev_stream / t / 1e9;
+    if (t > 0 && hv != nullptr) {
+      t = best([&] { return ftk::launch_stream_read(hv, host_stream, kFillBlocks, (uint32_t*)base, stream); });
+      if (t > 0) R.host_read_gbs = (double)host_stream / t / 1e9;
+    }
+    const double per_launch = (double)mfma_blocks * 4 * kRatesMfmaIters * 4;  // MFMA instructions
+    double* rate[3] = {&R.mfma_bf16_tflops, &R.mfma_fp8_tflops, &R.mfma_fp6_fp4_tflops};
+    const double flops[3] = {2.0 * 32 * 32 * 16, 2.0 * 32 * 32 * 64, 2.0 * 32 * 32 * 64};
+    for (int kind = 0; kind < 3 && t > 0; ++kind) {
+      t = best([&] { return ftk::launch_mfma_rate(kind, mfma_blocks, kRatesMfmaIters, (float*)base, stream); });
+      if (t > 0) *rate[kind] = per_launch * flops[kind] / t / 1e12;
+    }
+    // a bf16 32x32x16 MFMA occupies a SIMD for 32 cycles (1024 flops per SIMD and cycle)
+    R.mfma_clock_ghz = R.mfma_bf16_tflops * 1e12 / ((double)cus * 4 * 1024) / 1e9;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (t <= 0) return hip_status(e != hipSuccess ? e : hipErrorUnknown, "ft_moe_measure_rates");
+    *out = R;
+    return ok();
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_measure_rates: unexpected exception");
+  }
+}
+
 size_t ft_moe_layer_workspace(const ft_moe_bank* bank, int T, int E, int k, int shared_slot, int flags) {
   if (bank == nullptr || check_tek(T, E, k) != FT_OK || check_bank_shape(bank->fmt, bank->n_slots, bank->d, bank->I)) {
     g_err[0] = 0;

@@ -107,6 +107,15 @@ int residual_host(int fmt, int n_experts, int d, int I, const uint8_t* w13, cons
                   const int32_t* slot_of_expert, int T, int E, int k, float* out, int threads);
 hipError_t launch_residual_add(void* out, const float* res, long long n, bool out_bf16, hipStream_t s);
 
+// ---- start-up rate measurements (rates.hip)
+// every resident 256-thread block of the streaming-read kernel (per CU x CUs) and the CU count
+hipError_t rate_launch_facts(int* stream_blocks, int* cus);
+// reads `bytes` (a multiple of 16) at p with `blocks` blocks; sink: 4 words per block
+hipError_t launch_stream_read(const void* p, long long bytes, int blocks, uint32_t* sink, hipStream_t s);
+// kind 0: bf16 32x32x16, 1: e4m3 x e4m3 32x32x64, 2: e2m3 x e2m1 32x32x64; each of the `blocks`
+// 4-wave blocks issues iters x 4 MFMAs per wave; sink: 256 floats per block
+hipError_t launch_mfma_rate(int kind, int blocks, int iters, float* sink, hipStream_t s);
+
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* gather, int32_t* inv, void* ws, hipStream_t s);

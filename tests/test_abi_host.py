@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -66,6 +66,23 @@ def test_layer_noalloc_refuses_oversize_layers():
     _err(L.ft_moe_layer_noalloc(*args(4096, 8)), ft.FT_E_WORKSPACE, "static scratch")
     _err(L.ft_moe_layer_noalloc(*args(4, 0)), ft.FT_E_INVAL, "k must be")
     _err(L.ft_moe_layer_noalloc(*args(4, 8, 0x40)), ft.FT_E_INVAL, "unknown flags")
+
+
+def test_measure_rates_validation():
+    """Argument checks of the start-up rate call (before any HIP call)."""
+    L = ft.lib
+    r = ft.ft_moe_rates()
+    big, mib = 64 << 20, 1 << 20
+    call = lambda dev=A, nd=big, host=None, nh=0, reps=3, out=ctypes.byref(r): L.ft_moe_measure_rates(  # noqa: E731
+        dev, nd, host, nh, reps, out, None)
+    _err(call(out=None), ft.FT_E_INVAL, "out is null")
+    _err(call(dev=None), ft.FT_E_INVAL, "dev_buf is null")
+    _err(call(dev=ctypes.c_void_p(0x10010)), ft.FT_E_INVAL, "256-byte aligned")
+    _err(call(nd=big - 1), ft.FT_E_INVAL, "dev_bytes must be at least")
+    _err(call(reps=0), ft.FT_E_INVAL, "reps must be")
+    _err(call(reps=101), ft.FT_E_INVAL, "reps must be")
+    _err(call(host=MIS, nh=mib), ft.FT_E_INVAL, "host_buf is not 16-byte")
+    _err(call(host=A, nh=mib - 16), ft.FT_E_INVAL, "host_bytes must be at least")
 
 
 def test_cache_update_validation():
