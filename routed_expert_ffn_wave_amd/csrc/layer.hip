@@ -209,8 +209,14 @@ __device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int
   }
 }
 
+// The MXFP4 and NVFP4 instances, and Q4_0 with 8-wave blocks, are held to 128 VGPRs (four waves per
+// SIMD): they would otherwise take a few more, which leaves room for only one 8-wave block per CU
+// at d = 7168 (measured on mxfp4_shared at T = 16: 452 against 551 us per layer; nvfp4_decode 3 %
+// faster too).  The other instances fit four waves per SIMD as they are.
 template <int FMT, int WPB, int NT, int VPL, bool OUT_BF16>
-__global__ __launch_bounds__(WPB * 64) void layer_decode_kernel(LayerArgs L) {
+__global__ __launch_bounds__(WPB * 64)
+__attribute__((amdgpu_waves_per_eu(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || (FMT == FMT_Q4_0 && WPB == 8) ? 4 : 1)))
+void layer_decode_kernel(LayerArgs L) {
   const FfnArgs& a = L.f;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int T = a.T, E = a.E, k = a.k, n = T * k;
