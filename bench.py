@@ -267,6 +267,62 @@ def calibrate():
                       "compute_units": r["compute_units"], "stream_blocks": r["stream_blocks"]}), flush=True)
 
 
+def bench_layer_proj(w: synth.Workload, T: int, n_layers: int, steps: int, warmup: int):
+    """The decode layer from its activations (router projection + layer) over the workload's layers,
+    each way captured into a HIP graph and replayed: ft_moe_route_proj then ft_moe_layer (two
+    launches per layer), and ft_moe_layer_proj (the projection inside the one launch).  Own JSON
+    line: value = us per layer of the one-launch form."""
+    layers = build_layers(w, T, n_layers)
+    wrs = [synth.router_rows(w, l, device="cuda") for l in range(n_layers)]
+    xs = [x for _, _, x in layers]
+    lgs = [torch.empty(T, w.E, dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    rws = [torch.zeros(max(ft.ft_moe_route_proj_workspace(T), 16), dtype=torch.uint8, device="cuda")
+           for _ in range(n_layers)]
+    ids = torch.empty(T, w.k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, w.k, dtype=torch.float32, device="cuda")
+
+    def two():
+        for (layer, _, x), wr, lg, rw in zip(layers, wrs, lgs, rws):
+            ft.ft_moe_route_proj(x, wr, w.k, logits=lg, ids=ids, w=wt, ws=rw)
+            layer.forward(lg, x)
+
+    def one():
+        for (layer, _, x), wr in zip(layers, wrs):
+            layer.forward_proj(x, wr)
+
+    res = {}
+    for name, fn in (("route_proj_then_layer", two), ("layer_proj", one)):
+        for _ in range(max(warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / steps / n_layers * 1e6
+        check_status(layers, name)
+        del graph
+    log(f"layer from x: {res}")
+    print(json.dumps({"metric": "MoE-layer decode latency from the activations (router projection + layer)",
+                      "value": round(res["layer_proj"], 3), "unit": "us/layer", "n_gpus": 1, "steps": steps,
+                      "warmup": warmup, "higher_is_better": False, "vs_baseline": None, "data": "synthetic (seeded)",
+                      "config": {"workload": w.name, "T": T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
+                                 "bank_format": synth.FMT_NAMES[w.fmt], "layers_per_step": n_layers, "graph": True},
+                      "us_per_layer": {k: round(v, 3) for k, v in res.items()}}), flush=True)
+
+
 def bench_route_proj(w: synth.Workload, T: int, steps: int, warmup: int):
     """Router projection + route (ft_moe_route_proj) on the workload's shape: one call is one step;
     printed as its own JSON line (the step before the layer, not part of the layer's metric)."""
@@ -639,6 +695,9 @@ def main():
     ap.add_argument("--coexec", default=None, metavar="Q",
                     help="time co-executed steps: a fraction Q of each step's cold experts copied to the GPU, the rest "
                          "on the host ('auto': Q from the host link and host residual rates measured first)")
+    ap.add_argument("--layer-proj", action="store_true",
+                    help="time the decode layer from its activations: router projection + layer, in two launches "
+                         "and in one (ft_moe_layer_proj)")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the device's achievable rates (ft_moe_measure_rates) and print them as one JSON line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -661,6 +720,9 @@ def main():
     decode = T <= 64
     if args.calibrate:
         calibrate()
+        return
+    if args.layer_proj:
+        bench_layer_proj(w, T, n_layers, args.steps, args.warmup)
         return
     if args.route_proj:
         bench_route_proj(w, T, args.steps, args.warmup)

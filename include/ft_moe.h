@@ -242,6 +242,26 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
                  int flags, hipStream_t stream);
 
 /*
+ * The layer from the activations: the router projection of ft_moe_route_proj (logits[t][e] =
+ * x[t] . w_router[e], bf16 products summed in fp32, written to `logits` fp32 [T][E]), then
+ * ft_moe_layer on those logits, with every output of both.  Where ft_moe_layer runs its one-launch
+ * path and the T x E logits fit in a block's LDS, the projection runs inside that launch: a group of
+ * 8 blocks computes each token's logits (the experts dealt over their waves, each logit an fp32 sum
+ * in a fixed order: within the rounding bound of ft_moe_route_proj's), publishes them, and every
+ * block routes once all T rows are published; ids and w are exactly what ft_moe_route returns for the written
+ * logits.  Otherwise ft_moe_route_proj runs first.  w_router bf16 [E][d]; requires E <= 512 besides
+ * ft_moe_layer's conditions.  ws: ft_moe_layer_workspace(...) bytes (the same
+ * workspace serves both calls), zero-filled once by the caller.  The expert routing of a decode
+ * layer from its input in one launch: [walk-through] sections 一 and 五; [article]
+ * "为什么 MoE 模型适合做 CPU–GPU 协同？".
+ */
+int ft_moe_layer_proj(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot,
+                      const uint16_t* x, const uint16_t* w_router, int T, int E, int k, float* logits,
+                      int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* gather,
+                      int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
+                      uint32_t* residual_mask, void* ws, size_t ws_bytes, int flags, hipStream_t stream);
+
+/*
  * Scratch bytes of ft_moe_layer_noalloc: one static array per device that the library runs on,
  * held until the process ends.
  */

@@ -72,6 +72,7 @@ def _load():
         "ft_moe_layer_workspace": ([BP, i, i, i, i, i], sz),
         "ft_moe_layer": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
         "ft_moe_layer_noalloc": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i, P], i),
+        "ft_moe_layer_proj": ([BP, P, i, P, P, i, i, i, P, P, P, P, P, P, P, P, P, P, P, P, sz, i, P], i),
         "ft_moe_cache_update": ([P, i, i, i, ctypes.c_float, P, P, P, P, P, P, P, P, P], i),
         "ft_moe_cache_fill": ([BP, BP, P, P, i, P], i),
         "ft_moe_residual_host": ([BP, P, P, P, P, P, i, i, i, P, i], i),
@@ -92,7 +93,7 @@ EXPORTED = ("ft_moe_abi_version", "ft_moe_last_error", "ft_moe_route", "ft_moe_r
             "ft_moe_permute", "ft_moe_grouped_ffn_workspace", "ft_moe_grouped_ffn", "ft_moe_combine",
             "ft_moe_bank_bytes", "ft_moe_pack_bank", "ft_moe_dequant", "ft_moe_layer_workspace", "ft_moe_layer",
             "ft_moe_layer_noalloc", "ft_moe_cache_update", "ft_moe_cache_fill", "ft_moe_residual_host", "ft_moe_residual_add",
-            "ft_moe_measure_rates")
+            "ft_moe_measure_rates", "ft_moe_layer_proj")
 
 
 def _ptr(t: torch.Tensor | None):
@@ -399,6 +400,21 @@ class MoELayer:
                                         _ptr(self.y_shared), _ptr(self.out), _ptr(self.mask), _ptr(status),
                                         self.flags | self.out_flags, s))
         return self.out[: self.T], self.mask[: self.T]
+
+    def forward_proj(self, x: torch.Tensor, w_router: torch.Tensor, stream=None):
+        """The layer from the activations (ft_moe_layer_proj): the router logits x . w_router^T (bf16
+        [E][d] router rows) are computed into self.logits, then the layer runs on them.  Mode "layer"."""
+        if self.mode != "layer":
+            raise ValueError("forward_proj needs mode 'layer'")
+        T, E, k = self.T, self.E, self.k
+        if getattr(self, "logits", None) is None:
+            self.logits = torch.empty(max(T, 1), E, dtype=torch.float32, device=self.out.device)
+        _check(lib.ft_moe_layer_proj(self.bank.ref, _ptr(self.slot_of), self.shared_slot, _ptr(x), _ptr(w_router), T,
+                                     E, k, _ptr(self.logits), _ptr(self.ids), _ptr(self.w), _ptr(self.counts),
+                                     _ptr(self.offsets), _ptr(self.gather), _ptr(self.inv), _ptr(self.y_sorted),
+                                     _ptr(self.y_shared), _ptr(self.out), _ptr(self.mask), _ptr(self.ws),
+                                     self.ws.numel(), self.flags | self.out_flags, _stream(stream)))
+        return self.out[:T], self.mask[:T]
 
     def status_word(self) -> int:
         """The layer workspace's status word (non-zero: a wait of the fused kernel gave up; the

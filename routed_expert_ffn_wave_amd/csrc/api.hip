@@ -231,7 +231,7 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
 // queue counters (cleared by each unfused call), the h rows, the activation terms and the
 // permutation workspace of the unfused path.
 struct LayerWs {
-  size_t ctl, done13, cdone, zeroed, qctr, h, terms, perm, total;
+  size_t ctl, rproj, done13, cdone, zeroed, qctr, h, terms, perm, total;
   int n_rc;
 };
 
@@ -246,6 +246,10 @@ LayerWs layer_ws(const ft_moe_bank* b, int T, int E, int k, bool shared, bool fu
   size_t o = 0;
   L.ctl = o;
   o += round256((size_t)ftk::CTL_INTS * 4);
+  // ft_moe_layer_proj: the router projection's counters (zero between calls), also the per-token
+  // flags of the one-launch path's projection
+  L.rproj = o;
+  o += round256(ftk::route_proj_workspace_bytes(T > 0 ? T : 1));
   L.n_rc = fused ? ftk::layer_decode_rowchunks_upper(T, E, k, shared) : 0;
   L.done13 = o;
   o += round256((size_t)L.n_rc * ftk::CNT_STRIDE * 4);
@@ -740,11 +744,13 @@ namespace {
 
 // ft_moe_layer after its checks of T, E, k, the bank, the flags and shared_slot: the rest of the
 // validation and the launches, with the workspace `wsb` (ws_bytes long; null when missing).
+// w_router (ft_moe_layer_proj): the logits are first computed from x and the router rows into
+// `logits`, inside the one launch where that fits, else by the router projection kernel.
 int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const float* logits,
                   const uint16_t* x, int T, int E, int k, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                   int32_t* gather, int32_t* inv, uint16_t* y_sorted, uint16_t* y_shared, void* out,
                   uint32_t* residual_mask, uint8_t* wsb, size_t ws_bytes, int flags, hipStream_t stream,
-                  bool check_only = false) {
+                  bool check_only = false, const uint16_t* w_router = nullptr) {
   int rc;
   CHECK_PTR(counts, "counts");
   CHECK_PTR(offsets, "offsets");
@@ -770,8 +776,14 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   if (y_shared) CHECK_PTR(y_shared, "y_shared");
   CHECK_PTR(out, "out");
   if (residual_mask) CHECK_PTR(residual_mask, "residual_mask");
+  if (w_router) CHECK_PTR(w_router, "w_router");
   if (check_only) return FT_OK;
   const bool out_bf16 = (flags & FT_OUT_BF16) != 0;
+  const bool proj_fused = w_router && fused && ftk::layer_decode_fits(bank->fmt, T, E, k, bank->d, bank->I, true);
+  if (w_router && !proj_fused) {
+    hipError_t e = ftk::launch_route_proj(x, w_router, T, bank->d, E, k, (float*)logits, ids, w, wsb + W.rproj, stream);
+    if (e != hipSuccess) return hip_status(e, "ft_moe_layer_proj router projection launch");
+  }
   if (!fused) {
     hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_layer route launch");
@@ -823,6 +835,11 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   L.done13 = (int32_t*)(wsb + W.done13);
   L.n_rc = W.n_rc;
   L.cdone = (int32_t*)(wsb + W.cdone);
+  if (proj_fused) {
+    L.w_router = w_router;
+    L.proj_logits = (float*)logits;
+    L.pflag = (int32_t*)(wsb + W.rproj);
+  }
   return hip_status(ftk::launch_layer_decode(L, stream), "ft_moe_layer fused launch");
 }
 
@@ -857,6 +874,27 @@ int ft_moe_layer(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sha
                          y_sorted, y_shared, out, residual_mask, (uint8_t*)ws, ws_bytes, flags, stream);
   } catch (...) {
     return fail(FT_E_INTERNAL, "ft_moe_layer: unexpected exception");
+  }
+}
+
+int ft_moe_layer_proj(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
+                      const uint16_t* w_router, int T, int E, int k, float* logits, int32_t* ids, float* w,
+                      int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* inv, uint16_t* y_sorted,
+                      uint16_t* y_shared, void* out, uint32_t* residual_mask, void* ws, size_t ws_bytes, int flags,
+                      hipStream_t stream) {
+  try {
+    int rc = layer_args(bank, shared_slot, T, E, k, y_shared, flags);
+    if (rc) return rc;
+    REQUIRE(E <= 512, FT_E_INVAL, "E must be at most 512 for ft_moe_layer_proj (got %d)", E);
+    if (T > 0) {
+      CHECK_PTR(w_router, "w_router");
+      CHECK_PTR(logits, "logits");
+    }
+    return layer_checked(bank, slot_of_expert, shared_slot, logits, x, T, E, k, ids, w, counts, offsets, gather, inv,
+                         y_sorted, y_shared, out, residual_mask, (uint8_t*)ws, ws_bytes, flags, stream, false,
+                         T > 0 ? w_router : nullptr);
+  } catch (...) {
+    return fail(FT_E_INTERNAL, "ft_moe_layer_proj: unexpected exception");
   }
 }
 

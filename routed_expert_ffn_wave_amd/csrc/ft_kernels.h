@@ -159,6 +159,7 @@ constexpr int LAYER_RPL2 = 2;     // 64-row blocks per down item on the fused pa
 constexpr int CNT_STRIDE = 64;    // ints between two counters: one 256-byte line each, so polls and
                                   // updates of different counters never share a line
 constexpr int LAYER_NQ = 8;       // work queues of the fused FFN kernel (one per XCD)
+constexpr int LAYER_PG = 8;       // blocks that compute one token's router logits (ft_moe_layer_proj)
 constexpr int CTL_ERR = 0;        // control word: non-zero when a dependency wait gave up
 constexpr int CTL_QUEUE = CNT_STRIDE;  // queue q's next position at CTL_QUEUE + q * CNT_STRIDE
 constexpr int CTL_EXIT = CTL_QUEUE + LAYER_NQ * CNT_STRIDE;  // blocks that have finished
@@ -181,9 +182,14 @@ struct LayerArgs {
   int32_t* done13;           // [n_rc][CNT_STRIDE] finished gate/up items per row chunk
   int n_rc;                  // upper bound on row chunks (groups x token chunks)
   int32_t* cdone;            // [T][d/64][CNT_STRIDE] contributions made per (token, 64-column block)
+  // the router projection inside the launch (ft_moe_layer_proj), or w_router null: logits are an input
+  const uint16_t* w_router;  // bf16 [E][d]
+  float* proj_logits;        // fp32 [T][E]: the logits the launch computes (the same array as logits)
+  int32_t* pflag;            // [T]: tokens whose logits are published (zero at start, returned to zero)
 };
 hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s);
-bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I);  // its LDS fits one CU
+// its LDS fits one CU (proj: with the router projection's logits staged in LDS)
+bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I, bool proj = false);
 // upper bound on the row chunks (groups x chunks of LAYER_NT tokens) of a fused call
 inline int layer_decode_rowchunks_upper(int T, int E, int k, bool shared) {
   const int groups = (E < T * k ? E : T * k) + (shared ? 1 : 0);

@@ -213,7 +213,7 @@ __device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int
 // SIMD): they would otherwise take a few more, which leaves room for only one 8-wave block per CU
 // at d = 7168 (measured on mxfp4_shared at T = 16: 452 against 551 us per layer; nvfp4_decode 3 %
 // faster too).  The other instances fit four waves per SIMD as they are.
-template <int FMT, int WPB, int NT, int VPL, bool OUT_BF16>
+template <int FMT, int WPB, int NT, int VPL, bool OUT_BF16, bool PROJ>
 __global__ __launch_bounds__(WPB * 64)
 __attribute__((amdgpu_waves_per_eu(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || (FMT == FMT_Q4_0 && WPB == 8) ? 4 : 1)))
 void layer_decode_kernel(LayerArgs L) {
@@ -252,8 +252,72 @@ void layer_decode_kernel(LayerArgs L) {
     slot_reg[i] = e < E ? a.slot_of[e] : -1;
   }
 
+  // ---- the router projection (ft_moe_layer_proj): blocks LAYER_PG t .. LAYER_PG t + LAYER_PG - 1
+  // compute token t's logits.  Each wave takes experts (its block's rank in the token's group,
+  // its own index) plus multiples of LAYER_PG * WPB, four at a time with all their loads issued
+  // together: lane l takes the 16-byte pieces l, l + 64, ... of the row, and a butterfly over the
+  // wave adds the lanes' sums, the same order every run.  The logits go out with agent-scope
+  // stores, then each block adds one to the token's flag.  Every block waits until each of the T
+  // flags reaches LAYER_PG and copies the logits into LDS with agent-scope loads (another XCD's L2
+  // may hold stale lines of the array from an earlier call).  The computing blocks never wait
+  // before publishing and every block of the grid is resident, so every wait ends (bounded anyway,
+  // like the dependency waits).
+  const float* route_src = L.logits;
+  if constexpr (PROJ) {
+    const int d = a.d, npc = d / 8;
+    if ((int)blockIdx.x < T * LAYER_PG) {
+      const int t = blockIdx.x / LAYER_PG, gb = blockIdx.x % LAYER_PG;
+      const int stride = LAYER_PG * WPB;
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)t * d);
+      for (int e0 = gb * WPB + w; e0 < E; e0 += 4 * stride) {
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const u32x4* wr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wr[u] = (const u32x4*)(L.w_router + (size_t)min(e0 + u * stride, E - 1) * d);
+        for (int pc = lane; pc < npc; pc += 64) {
+          const u32x4 xv = xr[pc];
+          u32x4 rv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rv[u] = wr[u][pc];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[u] = dot2_bf16(xv[i], rv[u][i], sum[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) sum[u] += __shfl_xor(sum[u], o, 64);
+          const int e = e0 + u * stride;
+          if (lane == 0 && e < E)
+            __hip_atomic_store(L.proj_logits + (size_t)t * E + e, sum[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      wait_stores();  // this wave's logits have landed before the flag moves
+      __syncthreads();
+      if (tid == 0) atomic_add_agent(L.pflag + t, 1);
+    }
+    if (w == 0 && lane < T) {
+      int spins = 0;
+      while (atomic_load_agent(L.pflag + lane) < LAYER_PG) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins >= SPIN_LIMIT) {
+          atomic_add_agent(L.ctl + CTL_ERR, 1);
+          break;
+        }
+        if ((spins & 63) == 0 && atomic_load_agent(L.ctl + CTL_ERR) != 0) break;
+      }
+    }
+    __syncthreads();
+    float* s_lg = (float*)s_union;  // free until the first work item
+    for (int i = tid; i < T * E; i += WPB * 64)
+      s_lg[i] = __hip_atomic_load(L.proj_logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    route_src = s_lg;
+  }
+
   // ---- route (the same routine as the router kernel, so both give the same bits)
-  route_tokens<VPL>(L.logits, T, E, k, w, WPB, [&](int t, int j, int e, float wt) {
+  route_tokens<VPL>(route_src, T, E, k, w, WPB, [&](int t, int j, int e, float wt) {
     s_ids[t * k + j] = e;
     s_w[t * k + j] = wt;
   });
@@ -372,18 +436,26 @@ void layer_decode_kernel(LayerArgs L) {
   if (s_ctl[1]) {
     for (int q = tid; q < nq; q += WPB * 64) atomic_zero_agent(L.ctl + CTL_QUEUE + q * CNT_STRIDE);
     for (int i = tid; i < nrc; i += WPB * 64) atomic_zero_agent(L.done13 + i * CNT_STRIDE);
+    if (PROJ && tid < T) atomic_zero_agent(L.pflag + tid);
     for (int i = tid; i < T * ncb2; i += WPB * 64) atomic_zero_agent(L.cdone + i * CNT_STRIDE);
     if (tid == 0) atomic_zero_agent(L.ctl + CTL_EXIT);
   }
 }
 
-template <int FMT, int WPB, int VPL, bool OUT_BF16>
+// LDS of a fused launch: the bookkeeping, then the union of the GEMV items (which also holds the
+// router projection's logits before the first item)
+inline size_t layer_lds_bytes(int fmt, int T, int E, int k, int d, int I, int NT, int WPB, bool proj) {
+  size_t u = layer_union_bytes(fmt, d, I, NT, WPB);
+  if (proj && (size_t)T * E * 4 > u) u = (size_t)T * E * 4;
+  return ((layer_meta_ints(T, E, k, NT) * 4 + 15) & ~(size_t)15) + u;
+}
+
+template <int FMT, int WPB, int VPL, bool OUT_BF16, bool PROJ>
 static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   constexpr int NT = LAYER_NT;
-  auto kern = layer_decode_kernel<FMT, WPB, NT, VPL, OUT_BF16>;
+  auto kern = layer_decode_kernel<FMT, WPB, NT, VPL, OUT_BF16, PROJ>;
   const FfnArgs& a = L.f;
-  const size_t lds = ((layer_meta_ints(a.T, a.E, a.k, NT) * 4 + 15) & ~(size_t)15) +
-                     layer_union_bytes(FMT, a.d, a.I, NT, WPB);
+  const size_t lds = layer_lds_bytes(FMT, a.T, a.E, a.k, a.d, a.I, NT, WPB, PROJ);
   static LaunchCache cache;
   LaunchFacts f;
   if (cache.get((const void*)kern, WPB * 64, lds, &f) != hipSuccess) return hipGetLastError();
@@ -391,37 +463,45 @@ static hipError_t launch_layer_cfg(const LayerArgs& L, hipStream_t s) {
   const long long items = (long long)L.n_rc * (2 * a.I / 64 + a.d / (64 * LAYER_RPL2));
   long long blocks = (long long)f.per_cu * f.cus;
   if (blocks > items) blocks = items;
+  if (PROJ && blocks < (long long)a.T * LAYER_PG) blocks = (long long)a.T * LAYER_PG;  // the projection's blocks
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WPB * 64), lds, s, L);
   return hipGetLastError();
 }
 
-template <int FMT, int WPB, bool OUT_BF16>
+template <int FMT, int WPB, bool OUT_BF16, bool PROJ>
 static hipError_t launch_layer_vpl(const LayerArgs& L, hipStream_t s) {
   const int E = L.f.E;
-  if (E <= 64) return launch_layer_cfg<FMT, WPB, 1, OUT_BF16>(L, s);
-  if (E <= 128) return launch_layer_cfg<FMT, WPB, 2, OUT_BF16>(L, s);
-  if (E <= 256) return launch_layer_cfg<FMT, WPB, 4, OUT_BF16>(L, s);
-  if (E <= 512) return launch_layer_cfg<FMT, WPB, 8, OUT_BF16>(L, s);
-  return launch_layer_cfg<FMT, WPB, 16, OUT_BF16>(L, s);
+  if (E <= 64) return launch_layer_cfg<FMT, WPB, 1, OUT_BF16, PROJ>(L, s);
+  if (E <= 128) return launch_layer_cfg<FMT, WPB, 2, OUT_BF16, PROJ>(L, s);
+  if (E <= 256) return launch_layer_cfg<FMT, WPB, 4, OUT_BF16, PROJ>(L, s);
+  if (E <= 512) return launch_layer_cfg<FMT, WPB, 8, OUT_BF16, PROJ>(L, s);
+  if constexpr (PROJ)
+    return hipErrorInvalidValue;  // the router projection takes E <= 512
+  else
+    return launch_layer_cfg<FMT, WPB, 16, OUT_BF16, PROJ>(L, s);
+}
+
+template <int FMT, bool PROJ>
+static hipError_t launch_layer_proj(const LayerArgs& L, hipStream_t s) {
+  const int K = L.f.d > L.f.I ? L.f.d : L.f.I;
+  if (K <= 2048) {
+    if (L.out_bf16) return launch_layer_vpl<FMT, 4, true, PROJ>(L, s);
+    return launch_layer_vpl<FMT, 4, false, PROJ>(L, s);
+  }
+  if (L.out_bf16) return launch_layer_vpl<FMT, 8, true, PROJ>(L, s);
+  return launch_layer_vpl<FMT, 8, false, PROJ>(L, s);
 }
 
 template <int FMT>
 static hipError_t launch_layer_fmt(const LayerArgs& L, hipStream_t s) {
-  const int K = L.f.d > L.f.I ? L.f.d : L.f.I;
-  if (K <= 2048) {
-    if (L.out_bf16) return launch_layer_vpl<FMT, 4, true>(L, s);
-    return launch_layer_vpl<FMT, 4, false>(L, s);
-  }
-  if (L.out_bf16) return launch_layer_vpl<FMT, 8, true>(L, s);
-  return launch_layer_vpl<FMT, 8, false>(L, s);
+  if (L.w_router) return launch_layer_proj<FMT, true>(L, s);
+  return launch_layer_proj<FMT, false>(L, s);
 }
 
-bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I) {
+bool layer_decode_fits(int fmt, int T, int E, int k, int d, int I, bool proj) {
   const int WPB = (d > I ? d : I) <= 2048 ? 4 : 8;
-  const size_t lds = ((layer_meta_ints(T, E, k, LAYER_NT) * 4 + 15) & ~(size_t)15) +
-                     layer_union_bytes(fmt, d, I, LAYER_NT, WPB);
-  return lds <= 160 * 1024;
+  return layer_lds_bytes(fmt, T, E, k, d, I, LAYER_NT, WPB, proj) <= 160 * 1024;
 }
 
 hipError_t launch_layer_decode(const LayerArgs& L, hipStream_t s) {

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     out = subprocess.run(["nm", "-D", "--defined-only", ft.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(ft_moe_\w+)", out))
     assert set(names) <= exported, set(names) - exported
@@ -357,13 +357,27 @@ def test_layer_validation_and_workspace():
     unfused = L.ft_moe_layer_workspace(ctypes.byref(b), 8, 8, 2, -1, ft.FT_LAYER_UNFUSED)
     h = 8 * 2 * 512 * 2
     ctl = 10 * 64 * 4   # status word, a work-queue counter per XCD and the exit counter, each on its own line
+    rproj = lambda T: -(-((T + 15) // 16 * 64) // 256) * 256  # noqa: E731  (router-projection counters, 256-aligned)
     qctr = 4 * 8 * 16 * 4  # the four calls' work-queue counters (grouped FFN kernels)
-    assert unfused == ctl + qctr + h
+    assert unfused == ctl + rproj(8) + qctr + h
     assert fused > unfused
     big = L.ft_moe_layer_workspace(ctypes.byref(b), 4096, 8, 2, -1, 0)
-    assert big == ctl + qctr + 4096 * 2 * 512 * 2
+    assert big == ctl + rproj(4096) + qctr + 4096 * 2 * 512 * 2
     assert L.ft_moe_layer_workspace(ctypes.byref(b), 16, 8, 9, -1, 0) == 0
     assert L.ft_moe_layer_workspace(None, 16, 8, 2, -1, 0) == 0
+
+
+def test_layer_proj_validation():
+    """ft_moe_layer_proj's own checks, then those of ft_moe_layer (before any HIP call)."""
+    L = ft.lib
+    b = _bank(fmt=ft.FT_W_Q4_0, n=8, d=256, I=512)
+    call = lambda wr=A, lg=B, E=8, T=4, k=2, flags=0: L.ft_moe_layer_proj(  # noqa: E731
+        ctypes.byref(b), A, -1, A, wr, T, E, k, lg, A, A, A, A, A, A, A, None, A, None, A, 1 << 24, flags, None)
+    _err(call(E=513, k=2), ft.FT_E_INVAL, "E must be at most 512")
+    _err(call(wr=None), ft.FT_E_INVAL, "w_router is null")
+    _err(call(lg=None), ft.FT_E_INVAL, "logits is null")
+    _err(call(k=9), ft.FT_E_INVAL, "k must be")
+    _err(call(flags=0x40), ft.FT_E_INVAL, "unknown flags")
 
 
 def test_combine_validation():

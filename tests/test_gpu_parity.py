@@ -77,6 +77,61 @@ def test_route_proj(ft, T, d, E, k):
         assert not ws.any(), "the workspace must be left zero"
 
 
+# (workload, T, flags): the one-launch path with the projection inside (decode shapes, a shared expert,
+# partial residency, rows of 4096), and the two-launch path (T > 16, or the layer forced unfused)
+LAYER_PROJ_CASES = {
+    "q4_0_decode_T1": (synth.WORKLOADS["decode_q4_0"].replace(layers=1), 1, 0),
+    "q4_0_decode_T8": (synth.WORKLOADS["decode_q4_0"].replace(layers=1), 8, 0),
+    "tiny_bf16_T16": (synth.WORKLOADS["tiny_bf16"], 16, 0),
+    "mxfp4_shared_T5": (synth.WORKLOADS["mxfp4_shared"].replace(d=512, I=256, E=32, k=4), 5, 0),
+    "fp8_resident_T16": (synth.WORKLOADS["fp8_resident"].replace(d=512, I=256, E=32, k=4, n_resident=12), 16, 0),
+    "fp8_long_rows_T16": (synth.Workload("long_rows", 72, T=16, d=4096, E=16, k=4, I=256, fmt=synth.FMT_FP8_B128,
+                                         zipf=True), 16, 0),
+    "q4_0_T40_two_launches": (synth.WORKLOADS["decode_q4_0"].replace(layers=1, T=40, d=512, I=256, E=16, k=4), 40, 0),
+    "q4_0_T8_unfused": (synth.WORKLOADS["decode_q4_0"].replace(layers=1), 8, 8),
+}
+
+
+@pytest.mark.parametrize("name", list(LAYER_PROJ_CASES))
+def test_layer_proj(ft, name):
+    """ft_moe_layer_proj: the logits within the rounding bound of an fp32 sum of d products against
+    the oracle's fp64 router projection; routing, permutation and mask bit for bit and FFN rows and
+    outputs within the FFN tolerance against the oracle layer on the GPU's own logits; status word 0;
+    a second call (the same workspace) repeats every bit."""
+    w, T, flags = LAYER_PROJ_CASES[name]
+    li = synth.layer_inputs(w, layer=2, T=T)
+    wr = synth.router_rows(w, 2)
+    bank = device_bank(li.bank)
+    log(f"layer_proj {name}: T={T} d={w.d} E={w.E} k={w.k} flags={flags}")
+    layer = ft.MoELayer(bank, li.slot_of_expert.cuda(), w.k, T, shared_slot=w.shared_slot, flags=flags)
+    x, wr_d = li.x.cuda(), wr.cuda()
+    out, mask = layer.forward_proj(x, wr_d)
+    torch.cuda.synchronize()
+    assert layer.status_word() == 0, "a wait of the fused kernel gave up"
+    lg = layer.logits[:T].cpu()
+    ref = oracle.router_logits(li.x, wr)
+    xa = np.abs(oracle.bf16_to_f32(li.x)).astype(np.float64)
+    wa = np.abs(oracle.bf16_to_f32(wr)).astype(np.float64)
+    bound = w.d * 2.0 ** -24 * (xa @ wa.T) + 1e-30
+    err = np.abs(lg.numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), f"{name}: logit error {err.max()} over the bound"
+    n = T * w.k
+    g = dict(ids=layer.ids[:T].cpu().numpy(), w=layer.w[:T].cpu().numpy(), counts=layer.counts.cpu().numpy(),
+             offsets=layer.offsets.cpu().numpy(), gather=layer.gather[:n].cpu().numpy(),
+             inv=layer.inv[:n].cpu().numpy(), y_sorted=layer.y_sorted[:n],
+             y_shared=None if layer.y_shared is None else layer.y_shared[:T],
+             out=out.float().cpu().numpy(), mask=mask.cpu().numpy().astype(np.uint32))
+    li_gpu = synth.LayerInputs(w, 2, T, lg, li.x, li.slot_of_expert, li.bank)
+    compare_layer(li_gpu, g, label=f"layer_proj {name}")
+    first_out, first_lg = g["out"].copy(), lg.clone()
+    out2, _ = layer.forward_proj(x, wr_d)
+    torch.cuda.synchronize()
+    assert layer.status_word() == 0
+    assert torch.equal(layer.logits[:T].cpu(), first_lg), f"{name}: logits not repeatable"
+    assert np.array_equal(out2.float().cpu().numpy().view(np.uint32), first_out.view(np.uint32)), \
+        f"{name}: output not repeatable"
+
+
 ROUTE_CASES = [(1, 8, 2, "normal"), (37, 8, 2, "ties"), (64, 10, 4, "ties"), (300, 128, 8, "normal"),
                (513, 256, 8, "zipf"), (64, 1024, 32, "ties"), (5, 32, 32, "normal"), (33, 7, 1, "ties"),
                (20, 1, 1, "normal"), (100, 65, 8, "wide"), (16384, 256, 8, "zipf")]
