@@ -39,6 +39,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][WJ], uint8_t* stg_ba
   const int orow0 = (GATEUP || !shared) ? row0 + m0 : m0;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
+    if (hh == 1 && mrows <= 64) break;  // rows 64.. of the tile hold nothing to store
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * hh + ii;

@@ -31,6 +31,7 @@
 #include "ft_device.h"
 #include "ft_groups.h"
 #include "ft_kernels.h"
+#include "ft_queue.h"
 #include "ft_tile.h"
 
 namespace ftk {
@@ -414,9 +415,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
   const int a_rd0 = l32 * 64 + ((hi ^ xo) << 4);
   const int a_rd1 = l32 * 64 + (((2 + hi) ^ xo) << 4);
 
-  const int NB = gridDim.x;
-  const int lb = (NB % 8 == 0) ? (blockIdx.x % 8) * (NB / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int it = lb; it < nitems; it += NB) {
+  // Tiles come from the launch's work queues (claimed one tile ahead): a tile takes ~60 us at
+  // K = 2048, so a fixed stride over the tile list leaves the whole device waiting on the few blocks
+  // that drew one tile more than the rest, while queues let every block take the next tile as soon as
+  // it is free, which with tiles of unequal cost (the half tiles below) evens out the finish.
+  int* s_claim = s_tmp + 1;
+  int qoff = 0;
+  if (tid == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
+  __syncthreads();
+  int it = s_claim[0];
+  __syncthreads();
+  while (it >= 0 && it < nitems) {
+    int nxt = -1;
+    if (tid == 0) nxt = queue_claim(a.qctr, nitems, qoff);
     const int g = find_group(s_item0, gl.n, it);
     const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
     const int mt = local / ntiles, nt = local % ntiles;
@@ -427,98 +438,117 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
     const int m0 = mt * WBM;
     const int mrows = min(WBM, cnt - m0);
 
-    uint32_t aoff[DMA_A];
+    // A tile whose group has at most 64 rows left (a half tile) skips the MFMAs and LDS reads of
+    // its two empty 32-row fragments; its loads are the same as a full tile's (rows past the group
+    // repeat its last row), so the load counts the waits rely on do not change.  The two variants
+    // are separate copies of the whole tile, epilogue included, so neither carries the other's
+    // registers.
+    auto tile = [&](auto half) {
+      constexpr int MI = decltype(half)::value ? 2 : 4;  // 32-row fragments computed
+      uint32_t aoff[DMA_A];
 #pragma unroll
-    for (int q = 0; q < DMA_A; ++q) {
-      const int r = 16 * (DMA_A * wv + q) + (lane >> 2);
-      const int m = min(r, mrows - 1);
-      int src_row;
-      if (GATEUP)
-        src_row = shared ? (m0 + m) : a.gather[row0 + m0 + m] / a.k;
-      else
-        src_row = row0 + m0 + m;
-      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
-      aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
-    }
-    // A stage s (clamped to the last) into ring buffer `b`
-    auto issue_a = [&](int b, int s, int q) {
-      const int sc = min(s, nsteps - 1);
-      dma16(abase + (size_t)sc * (WBK * 2), aoff[q], ring_m0 + (uint32_t)b * A_BYTES + (DMA_A * wv + q) * 1024);
-    };
-    // This lane's B fragment j of substep u of step s (clamped): row 32 (j % 2) + l32 of block
-    // 8 nt + 2 wv + j / 2, chunk 4 s + 2 u + hi.
-    const uint8_t* bl = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K * 2 + (size_t)(8 * nt + 2 * wv) * nchunk * 1024 +
-                        (size_t)(hi * 1024 + l32 * 16);
-    auto load_b = [&](int s, int u, int j) -> bf16x8 {
-      const int sc = min(s, nsteps - 1);
-      return *(const bf16x8*)(bl + ((size_t)(j >> 1) * nchunk + 4 * sc + 2 * u) * 1024 + (j & 1) * 512);
-    };
+      for (int q = 0; q < DMA_A; ++q) {
+        const int r = 16 * (DMA_A * wv + q) + (lane >> 2);
+        const int m = min(r, mrows - 1);
+        int src_row;
+        if (GATEUP)
+          src_row = shared ? (m0 + m) : a.gather[row0 + m0 + m] / a.k;
+        else
+          src_row = row0 + m0 + m;
+        const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+        aoff[q] = (uint32_t)src_row * arow_bytes + (uint32_t)(c << 4);
+      }
+      // A stage s (clamped to the last) into ring buffer `b`
+      auto issue_a = [&](int b, int s, int q) {
+        const int sc = min(s, nsteps - 1);
+        dma16(abase + (size_t)sc * (WBK * 2), aoff[q], ring_m0 + (uint32_t)b * A_BYTES + (DMA_A * wv + q) * 1024);
+      };
+      // This lane's B fragment j of substep u of step s (clamped): row 32 (j % 2) + l32 of block
+      // 8 nt + 2 wv + j / 2, chunk 4 s + 2 u + hi.
+      const uint8_t* bl = (GATEUP ? a.w13 : a.w2) + (size_t)slot * ncols * K * 2 + (size_t)(8 * nt + 2 * wv) * nchunk * 1024 +
+                          (size_t)(hi * 1024 + l32 * 16);
+      auto load_b = [&](int s, int u, int j) -> bf16x8 {
+        const int sc = min(s, nsteps - 1);
+        return *(const bf16x8*)(bl + ((size_t)(j >> 1) * nchunk + 4 * sc + 2 * u) * 1024 + (j & 1) * 512);
+      };
 
-    f32x16 acc[4][4];
+      f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    bf16x8 fa0[4], fa1[4];   // A fragments of substeps 0 and 1
-    bf16x8 bq[4][2][4];      // B register sets: [step % 4][substep][fragment]
-    auto frag_a = [&](const uint8_t* st, int u, int i) -> bf16x8 {
-      return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + i * 2048);
-    };
-
-    // prologue: A stages 0..BD_NS-1, then B of steps 0..2 and substep 0 of step 3
-    for (int s = 0; s < BD_NS; ++s)
-#pragma unroll
-      for (int q = 0; q < DMA_A; ++q) issue_a(s, s, q);
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (st < 3 || u == 0) bq[st][u][j] = load_b(st, u, j);
-    wait_vm<2 * (BD_NS - 1) + BD_PRO_B>();  // A stage 0
-    lds_reads_done_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa0[i] = frag_a(ring, 0, i);
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      bf16x8 fa0[4], fa1[4];   // A fragments of substeps 0 and 1
+      bf16x8 bq[4][2][4];      // B register sets: [step % 4][substep][fragment]
+      auto frag_a = [&](const uint8_t* st, int u, int i) -> bf16x8 {
+        return *(const bf16x8*)(st + (u ? a_rd1 : a_rd0) + i * 2048);
+      };
 
-    int cb = 0;  // ring buffer of step s
-    auto step = [&](int s, auto kset) {
-      constexpr int k = decltype(kset)::value;
-      const uint8_t* st = ring + cb * A_BYTES;
-      const int nb = (cb + 1 == BD_NS) ? 0 : cb + 1;
-      const uint8_t* nst = ring + nb * A_BYTES;
+      // prologue: A stages 0..BD_NS-1, then B of steps 0..2 and substep 0 of step 3
+      for (int s = 0; s < BD_NS; ++s)
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[n >> 2], bq[k][0][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
-        if (n < 4) fa1[n] = frag_a(st, 1, n);
-        else if (n < 8) bq[(k + 3) & 3][1][n - 4] = load_b(s + 3, 1, n - 4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (s + 1 < nsteps) bd_wait_stage(s);
+        for (int q = 0; q < DMA_A; ++q) issue_a(s, s, q);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (st < 3 || u == 0) bq[st][u][j] = load_b(st, u, j);
+      wait_vm<2 * (BD_NS - 1) + BD_PRO_B>();  // A stage 0
       lds_reads_done_barrier();
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[n >> 2], bq[k][1][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
-        if (n < 4) fa0[n] = frag_a(nst, 0, n);  // past the last step: read but unused
-        else if (n < 6) issue_a(cb, s + BD_NS, n - 4);
-        else if (n < 10) bq[k][0][n - 6] = load_b(s + 4, 0, n - 6);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i) fa0[i] = frag_a(ring, 0, i);
+
+      int cb = 0;  // ring buffer of step s
+      auto step = [&](int s, auto kset) {
+        constexpr int k = decltype(kset)::value;
+        const uint8_t* st = ring + cb * A_BYTES;
+        const int nb = (cb + 1 == BD_NS) ? 0 : cb + 1;
+        const uint8_t* nst = ring + nb * A_BYTES;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          if ((n >> 2) < MI)
+            acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[n >> 2], bq[k][0][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
+          if (n < 4) {
+            if (n < MI) fa1[n] = frag_a(st, 1, n);
+          } else if (n < 8) bq[(k + 3) & 3][1][n - 4] = load_b(s + 3, 1, n - 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s + 1 < nsteps) bd_wait_stage(s);
+        lds_reads_done_barrier();
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          if ((n >> 2) < MI)
+            acc[n >> 2][n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[n >> 2], bq[k][1][n & 3], acc[n >> 2][n & 3], 0, 0, 0);
+          if (n < 4) {
+            if (n < MI) fa0[n] = frag_a(nst, 0, n);  // past the last step: read but unused
+          } else if (n < 6) issue_a(cb, s + BD_NS, n - 4);
+          else if (n < 10) bq[k][0][n - 6] = load_b(s + 4, 0, n - 6);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        cb = nb;
+      };
+      for (int s = 0; s < nsteps; s += 4) {
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
+        step(s + 2, std::integral_constant<int, 2>{});
+        step(s + 3, std::integral_constant<int, 3>{});
       }
-      cb = nb;
+      // The clamped loads past the end are still in flight: they land in ring buffers and registers
+      // that nothing reads, but the staging area is separate and the next tile's prologue loads
+      // complete after them (issue order), so no wait is needed here.
+      store_tile<GATEUP, 4>(acc, stg, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
     };
-    for (int s = 0; s < nsteps; s += 4) {
-      step(s, std::integral_constant<int, 0>{});
-      step(s + 1, std::integral_constant<int, 1>{});
-      step(s + 2, std::integral_constant<int, 2>{});
-      step(s + 3, std::integral_constant<int, 3>{});
-    }
-    // The clamped loads past the end are still in flight: they land in ring buffers and registers
-    // that nothing reads, but the staging area is separate and the next tile's prologue loads
-    // complete after them (issue order), so no wait is needed here.
-    store_tile<GATEUP, 4>(acc, stg, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
+    if (mrows <= WBM / 2)
+      tile(std::true_type{});
+    else
+      tile(std::false_type{});
+    if (tid == 0) s_claim[0] = nxt;
     lds_reads_done_barrier();  // staging slices and ring buffers are rewritten by the next tile
+    it = s_claim[0];
+    __syncthreads();  // every thread has read the claim before thread 0 writes the next one
   }
 }
 
