@@ -77,6 +77,16 @@ def test_decode_q4_0_full(ft, layer):
     _check(ft, li, device_bank(li.bank), n_sample=w.T, label=f"decode_q4_0 layer {layer}")
 
 
+@pytest.mark.parametrize("T", [10, 12])
+def test_decode_q4_0_batch_sizes(ft, T):
+    """The decode shape at batch sizes between the 8-token workload and the one-launch path's
+    limit (two segments of 64 routed pairs in its bookkeeping, 1400-1700 gate/up items, more than
+    the blocks resident at once); every token against the oracle."""
+    w = W["decode_q4_0"].replace(T=T)  # the recipe's tensors drawn for T tokens
+    li = _inputs(w, 3, T)
+    _check(ft, li, device_bank(li.bank), n_sample=T, label=f"decode_q4_0 T={T}")
+
+
 def test_prefill_bf16_zipf_full(ft):
     w = W["prefill_bf16_zipf"]
     li = _inputs(w, 0, w.T)
