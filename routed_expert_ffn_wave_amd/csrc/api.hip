@@ -117,11 +117,12 @@ size_t mx_ws_bytes(const ft_moe_bank* b, int T, int E, int k, bool shared, int f
 constexpr size_t kQctrBytes = (ftk::FFN_QCTR_INTS * 4 + 255) & ~(size_t)255;
 
 // FfnArgs for one grouped-FFN call and its launches (arguments already validated).  terms: the
-// mx_ws_bytes region (unused by the other formats); qctr: kQctrBytes of queue counters.
+// mx_ws_bytes region (unused by the other formats); qctr: kQctrBytes of queue counters, cleared
+// here unless the caller's permutation kernel already cleared them (qctr_zeroed).
 int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, int shared_slot, const uint16_t* x,
                        int T, int E, int k, const int32_t* offsets, const int32_t* gather, uint16_t* y_sorted,
                        uint16_t* y_shared, uint16_t* h, uint8_t* terms, int32_t* qctr, int flags,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool qctr_zeroed = false) {
   const int path = flags & FT_PATH_MASK;
   const bool shared = shared_slot >= 0;
   ftk::FfnArgs a{};
@@ -179,9 +180,12 @@ int launch_grouped_ffn(const ft_moe_bank* bank, const int32_t* slot_of_expert, i
   const bool mx = run_gemm && mx_path(bank, T, E, k, shared, flags);
   uint8_t* xterms = terms;
   uint8_t* hterms = mx ? terms + ftk::mx_term_bytes(bank->fmt, T, bank->d) : nullptr;
-  // every launch below takes its items from its own queue counters, cleared here
-  hipError_t e = ftk::launch_zero_ints(qctr, ftk::FFN_QCTR_INTS, stream);
-  if (e != hipSuccess) return hip_status(e, "grouped_ffn queue clear launch");
+  // every launch below takes its items from its own queue counters, cleared here (or already)
+  hipError_t e = hipSuccess;
+  if (!qctr_zeroed) {
+    e = ftk::launch_zero_ints(qctr, ftk::FFN_QCTR_INTS, stream);
+    if (e != hipSuccess) return hip_status(e, "grouped_ffn queue clear launch");
+  }
   constexpr int QL = ftk::FFN_QCTR_INTS / 4;  // counters of one launch
   if (run_gemv) {
     a.min_cnt = 1;
@@ -787,11 +791,13 @@ int layer_checked(const ft_moe_bank* bank, const int32_t* slot_of_expert, int sh
   if (!fused) {
     hipError_t e = ftk::launch_route(logits, T, E, k, ids, w, stream);
     if (e != hipSuccess) return hip_status(e, "ft_moe_layer route launch");
-    e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream);
+    // the permutation also clears the grouped FFN's queue counters (one launch fewer)
+    e = ftk::launch_permute(ids, T, E, k, counts, offsets, gather, inv, wsb + W.perm, stream, (int32_t*)(wsb + W.qctr),
+                            ftk::FFN_QCTR_INTS);
     if (e != hipSuccess) return hip_status(e, "ft_moe_layer permute launch");
     rc = launch_grouped_ffn(bank, slot_of_expert, shared_slot, x, T, E, k, offsets, gather, y_sorted, y_shared,
                             (uint16_t*)(wsb + W.h), wsb + W.terms, (int32_t*)(wsb + W.qctr),
-                            flags & (FT_PATH_MASK | FT_GEMM_WIDEN), stream);
+                            flags & (FT_PATH_MASK | FT_GEMM_WIDEN), stream, true);
     if (rc) return rc;
     return hip_status(ftk::launch_combine(y_sorted, y_shared, ids, w, inv, slot_of_expert, bank->n_slots, T, E, k,
                                           bank->d, out, residual_mask, out_bf16, stream),

@@ -117,8 +117,11 @@ hipError_t launch_stream_read(const void* p, long long bytes, int blocks, uint32
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, float* sink, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int k);
+// zero (optional): nzero ints the permutation also sets to zero, in its own kernel when it runs as
+// one block (so a caller can clear the next call's counters without a launch of their own)
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
-                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s);
+                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s, int32_t* zero = nullptr,
+                          int nzero = 0);
 
 hipError_t launch_combine(const uint16_t* y_sorted, const uint16_t* y_shared, const int32_t* ids, const float* w,
                           const int32_t* inv, const int32_t* slot_of, int n_slots, int T, int E, int k, int d,

@@ -75,7 +75,9 @@ __host__ __device__ inline size_t layer_union_bytes(int fmt, int d, int I, int N
 // contributions token t's combine waits for, the groups (resident experts with tokens in
 // ascending expert order, then the shared expert) with their first row chunk, g_tmp[0] = number
 // of groups; block 0 also writes gather, inv, counts, offsets and the residual mask.
-template <int NT, int VPL>
+// PART 0 (one wave): the per-pair positions and rows, then the per-token counts and mask; PART 1
+// (another wave, at the same time): counts, offsets and the group list.
+template <int NT, int VPL, int PART>
 __device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int* s_slot, const int* s_ids, int* s_gtok,
                                                    int* s_crow, int* s_tgt, int* g_slot, int* g_row0, int* g_cnt,
                                                    int* g_rc0, int* g_tmp, uint64_t* s_resb) {
@@ -113,99 +115,102 @@ __device__ __forceinline__ void decode_bookkeeping(const LayerArgs& L, const int
     return lt;
   };
 
-  // per pair: sorted position -> token, and the row its y will be in; s_resb[r]: which pairs of
-  // segment r have a resident expert
-  for (int r = 0; r < nseg; ++r) {
-    const int f = lane + 64 * r;
-    const int e = f < n ? s_ids[f] : -1;
-    const bool ok = f < n && (unsigned)e < (unsigned)E;
-    int p = 0;
+  if constexpr (PART == 0) {
+    // per pair: sorted position -> token, and the row its y will be in; s_resb[r]: which pairs of
+    // segment r have a resident expert
+    for (int r = 0; r < nseg; ++r) {
+      const int f = lane + 64 * r;
+      const int e = f < n ? s_ids[f] : -1;
+      const bool ok = f < n && (unsigned)e < (unsigned)E;
+      int p = 0;
+      for (int s = 0; s < nseg; ++s) {
+        const uint64_t valid = segment(s);
+        uint64_t eq;
+        const uint64_t lt = compare(ok ? e : 0, valid, eq);
+        p += __popcll(lt) + (s < r ? __popcll(eq) : s == r ? __popcll(eq & below) : 0);
+      }
+      const bool res = ok && resident(s_slot[e]);
+      const uint64_t rb = __ballot(res);
+      if (lane == 0) s_resb[r] = rb;
+      if (ok) {
+        s_gtok[p] = f / k;
+        s_crow[f] = res ? p : -1;
+        if (out) {
+          L.gather[p] = f;
+          L.inv[f] = p;
+        }
+      } else if (f < n) {
+        s_crow[f] = -1;  // an id outside [0, E) (a row of NaN logits): no y row, as in the combine kernel
+      }
+    }
+    // per token: the residual mask and the contributions its combine waits for, from the resident
+    // ballots (token t's k <= 32 pairs start at bit t*k and span at most two segments)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < T) {
+      const int b0 = lane * k, s0 = b0 >> 6, sh = b0 & 63;
+      uint64_t v = s_resb[s0] >> sh;
+      if (sh + k > 64) v |= s_resb[s0 + 1] << (64 - sh);
+      const uint32_t kmask = k == 32 ? 0xffffffffu : (1u << k) - 1u;
+      const uint32_t res = (uint32_t)v & kmask;
+      s_tgt[lane] = __popc(res) + (a.shared_slot >= 0 ? 1 : 0);
+      if (out && L.mask) L.mask[lane] = ~res & kmask;
+    }
+  } else {
+    int ex_lt[VPL], ex_eq[VPL];
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) ex_lt[u] = ex_eq[u] = 0;
+    int total = 0;
     for (int s = 0; s < nseg; ++s) {
       const uint64_t valid = segment(s);
-      uint64_t eq;
-      const uint64_t lt = compare(ok ? e : 0, valid, eq);
-      p += __popcll(lt) + (s < r ? __popcll(eq) : s == r ? __popcll(eq & below) : 0);
-    }
-    const bool res = ok && resident(s_slot[e]);
-    const uint64_t rb = __ballot(res);
-    if (lane == 0) s_resb[r] = rb;
-    if (ok) {
-      s_gtok[p] = f / k;
-      s_crow[f] = res ? p : -1;
-      if (out) {
-        L.gather[p] = f;
-        L.inv[f] = p;
-      }
-    } else if (f < n) {
-      s_crow[f] = -1;  // an id outside [0, E) (a row of NaN logits): no y row, as in the combine kernel
-    }
-  }
-  int ex_lt[VPL], ex_eq[VPL];
+      total += __popcll(valid);
 #pragma unroll
-  for (int u = 0; u < VPL; ++u) ex_lt[u] = ex_eq[u] = 0;
-  int total = 0;
-  for (int s = 0; s < nseg; ++s) {
-    const uint64_t valid = segment(s);
-    total += __popcll(valid);
+      for (int u = 0; u < VPL; ++u) {
+        uint64_t eq;
+        const uint64_t lt = compare(lane + 64 * u, valid, eq);
+        ex_lt[u] += __popcll(lt);
+        ex_eq[u] += __popcll(eq);
+      }
+    }
+    // per expert: counts, offsets; groups in ascending expert order with their first row chunk
+    int ng = 0, nrc = 0;
 #pragma unroll
     for (int u = 0; u < VPL; ++u) {
-      uint64_t eq;
-      const uint64_t lt = compare(lane + 64 * u, valid, eq);
-      ex_lt[u] += __popcll(lt);
-      ex_eq[u] += __popcll(eq);
+      const int e = lane + 64 * u;
+      if (64 * u >= E) break;
+      const int cnt = ex_eq[u], off = ex_lt[u];
+      if (out && e < E) {
+        L.counts[e] = cnt;
+        L.offsets[e] = off;
+      }
+      const int slot = e < E ? s_slot[e] : -1;
+      const bool keep = e < E && cnt > 0 && resident(slot);
+      const int items = keep ? (cnt + NT - 1) / NT : 0;
+      const uint64_t kb = __ballot(keep);
+      const int incl = wave_incl_scan(items);
+      if (keep) {
+        const int gi = ng + __popcll(kb & below);
+        g_slot[gi] = slot;
+        g_row0[gi] = off;
+        g_cnt[gi] = cnt;
+        g_rc0[gi] = nrc + incl - items;
+      }
+      ng += __popcll(kb);
+      nrc += __builtin_amdgcn_readlane(incl, 63);
     }
-  }
-  // per expert: counts, offsets; groups in ascending expert order with their first row chunk
-  int ng = 0, nrc = 0;
-#pragma unroll
-  for (int u = 0; u < VPL; ++u) {
-    const int e = lane + 64 * u;
-    if (64 * u >= E) break;
-    const int cnt = ex_eq[u], off = ex_lt[u];
-    if (out && e < E) {
-      L.counts[e] = cnt;
-      L.offsets[e] = off;
-    }
-    const int slot = e < E ? s_slot[e] : -1;
-    const bool keep = e < E && cnt > 0 && resident(slot);
-    const int items = keep ? (cnt + NT - 1) / NT : 0;
-    const uint64_t kb = __ballot(keep);
-    const int incl = wave_incl_scan(items);
-    if (keep) {
-      const int gi = ng + __popcll(kb & below);
-      g_slot[gi] = slot;
-      g_row0[gi] = off;
-      g_cnt[gi] = cnt;
-      g_rc0[gi] = nrc + incl - items;
-    }
-    ng += __popcll(kb);
-    nrc += __builtin_amdgcn_readlane(incl, 63);
-  }
-  if (lane == 0) {
-    if (out) L.offsets[E] = total;
-    if (resident(a.shared_slot)) {  // the shared expert: every token, rows T*k.. of h
-      g_slot[ng] = a.shared_slot;
-      g_row0[ng] = n;
-      g_cnt[ng] = T;
+    if (lane == 0) {
+      if (out) L.offsets[E] = total;
+      if (resident(a.shared_slot)) {  // the shared expert: every token, rows T*k.. of h
+        g_slot[ng] = a.shared_slot;
+        g_row0[ng] = n;
+        g_cnt[ng] = T;
+        g_rc0[ng] = nrc;
+        nrc += (T + NT - 1) / NT;
+        ++ng;
+      }
       g_rc0[ng] = nrc;
-      nrc += (T + NT - 1) / NT;
-      ++ng;
+      g_tmp[0] = ng;
     }
-    g_rc0[ng] = nrc;
-    g_tmp[0] = ng;
-  }
-  // per token: the residual mask and the contributions its combine waits for, from the resident
-  // ballots (token t's k <= 32 pairs start at bit t*k and span at most two segments)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  if (lane < T) {
-    const int b0 = lane * k, s0 = b0 >> 6, sh = b0 & 63;
-    uint64_t v = s_resb[s0] >> sh;
-    if (sh + k > 64) v |= s_resb[s0 + 1] << (64 - sh);
-    const uint32_t kmask = k == 32 ? 0xffffffffu : (1u << k) - 1u;
-    const uint32_t res = (uint32_t)v & kmask;
-    s_tgt[lane] = __popc(res) + (a.shared_slot >= 0 ? 1 : 0);
-    if (out && L.mask) L.mask[lane] = ~res & kmask;
   }
 }
 
@@ -328,9 +333,14 @@ void layer_decode_kernel(LayerArgs L) {
   }
   __syncthreads();
 
-  // ---- permutation, groups, per-pair rows and per-token counts: wave 0, in registers
+  // ---- permutation, per-pair rows and per-token counts (wave 0) and, at the same time, counts,
+  // offsets and the group list (wave 1), in registers
   if (w == 0)
-    decode_bookkeeping<NT, VPL>(L, s_slot, s_ids, s_gather, s_crow, s_tgt, g_slot, g_row0, g_cnt, g_rc0, g_tmp, s_resb);
+    decode_bookkeeping<NT, VPL, 0>(L, s_slot, s_ids, s_gather, s_crow, s_tgt, g_slot, g_row0, g_cnt, g_rc0, g_tmp,
+                                   s_resb);
+  else if (w == 1)
+    decode_bookkeeping<NT, VPL, 1>(L, s_slot, s_ids, s_gather, s_crow, s_tgt, g_slot, g_row0, g_cnt, g_rc0, g_tmp,
+                                   s_resb);
   __syncthreads();
   if (blockIdx.x == 0) {  // the routing outputs of the call, and zero rows for tokens with nothing to combine
     for (int f = tid; f < n; f += WPB * 64) {

@@ -12,7 +12,8 @@
 //      peers plus the segment's running base is its sorted position, so positions follow flat
 //      order exactly and never depend on the order atomics happen to take.
 // Up to 16 segments (T*k <= 16384) run as one block of 16 waves; larger inputs use three kernels
-// and a workspace of per-(expert, segment) counts.
+// and a workspace of per-(expert, segment) counts.  (One block over 32 segments, two per wave, took
+// 33-36 us at 4096 tokens of top-8 routing against 22 us for the three kernels on 8 blocks each.)
 #include "ft_device.h"
 #include "ft_kernels.h"
 #include "ft_permute.h"
@@ -67,24 +68,26 @@ __device__ int block_exclusive_scan(int* a, int E, int* tmp) {
   return total;
 }
 
-// One block of 1024 threads (16 waves), n <= 16 * SEG; ids may live in LDS or global memory.
-// lds: at least 17 * E + 32 ints.
+// One block of 1024 threads (16 waves), n <= SMALL_SEGS * SEG; segment s is wave s % 16's.
+// lds: at least (nseg + 1) * E + 32 ints, nseg = max(16, ceil(n / SEG)).
+constexpr int SMALL_SEGS = 16;
 __device__ void permute_block(const int32_t* ids, int n, int E, int id_bits, int* lds, int32_t* __restrict__ counts,
                               int32_t* __restrict__ offsets, int32_t* __restrict__ gather,
                               int32_t* __restrict__ inv) {
-  int* hist = lds;            // [16][E]: per-wave counts, then per-wave bases
-  int* off = lds + 16 * E;    // [E]
-  int* tmp = off + E;         // [32]
+  const int nseg = max(16, (n + SEG - 1) / SEG);
+  int* hist = lds;              // [nseg][E]: per-segment counts, then per-segment bases
+  int* off = lds + nseg * E;    // [E]
+  int* tmp = off + E;           // [32]
   const int tid = threadIdx.x, wv = tid >> 6;
-  for (int i = tid; i < 17 * E; i += 1024) lds[i] = 0;
+  for (int i = tid; i < (nseg + 1) * E; i += 1024) lds[i] = 0;
   __syncthreads();
-  count_segment(ids, n, E, wv * SEG, hist + wv * E);
+  for (int sg = wv; sg < nseg; sg += 16) count_segment(ids, n, E, sg * SEG, hist + sg * E);
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int s = 0; s < 16; ++s) {
-      int c = hist[s * E + e];
-      hist[s * E + e] = run;
+    for (int sg = 0; sg < nseg; ++sg) {
+      int c = hist[sg * E + e];
+      hist[sg * E + e] = run;
       run += c;
     }
     off[e] = run;
@@ -94,18 +97,31 @@ __device__ void permute_block(const int32_t* ids, int n, int E, int id_bits, int
   const int total = block_exclusive_scan(off, E, tmp);
   for (int e = tid; e < E; e += 1024) offsets[e] = off[e];
   if (tid == 0) offsets[E] = total;
-  for (int i = tid; i < 16 * E; i += 1024) hist[i] += off[i % E];
+  for (int i = tid; i < nseg * E; i += 1024) hist[i] += off[i % E];
   __syncthreads();
-  scatter_segment(ids, n, E, wv * SEG, id_bits, hist + wv * E, gather, inv);
+  for (int sg = wv; sg < nseg; sg += 16) scatter_segment(ids, n, E, sg * SEG, id_bits, hist + sg * E, gather, inv);
 }
 
+// zero[0 .. nzero) is set to zero as well (the layer's grouped-FFN queue counters, so that the layer
+// needs no kernel of its own for them)
 __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                               int id_bits, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ gather,
-                                                              int32_t* __restrict__ inv) {
+                                                              int32_t* __restrict__ inv, int32_t* __restrict__ zero,
+                                                              int nzero) {
   extern __shared__ int lds[];
+  for (int i = threadIdx.x; i < nzero; i += 1024) zero[i] = 0;
   permute_block(ids, n, E, id_bits, lds, counts, offsets, gather, inv);
+}
+
+// LDS bytes of the one-block path for n entries (at least 16 segments' rows)
+static size_t small_lds_bytes(long long n, int E) {
+  const long long nseg = (n + SEG - 1) / SEG;
+  return (size_t)(((nseg > 16 ? nseg : 16) + 1) * E + 32) * sizeof(int);
+}
+bool permute_one_block(long long n, int E) {
+  return n <= (long long)SMALL_SEGS * SEG && small_lds_bytes(n, E) <= 160 * 1024;
 }
 
 // ---- large path: blocks of 256 threads (4 waves), one segment per wave.
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
 
 size_t permute_workspace_bytes(int T, int E, int k) {
   long long n = (long long)T * k;
-  if (n <= 16LL * SEG) return 0;
+  if (permute_one_block(n, E)) return 0;
   long long nseg = (n + SEG - 1) / SEG;
   return (size_t)(nseg * E * 4);
 }
@@ -190,16 +206,20 @@ static int id_bits_for(int E) {
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
-                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s) {
+                          int32_t* gather, int32_t* inv, void* ws, hipStream_t s, int32_t* zero, int nzero) {
   const int n = T * k;
   const int bits = id_bits_for(E);
-  if (n <= 16 * SEG) {
-    size_t lds = (size_t)(17 * E + 32) * sizeof(int);
+  if (permute_one_block(n, E)) {
+    const size_t lds = small_lds_bytes(n, E);
     hipError_t e = allow_lds((const void*)permute_small_kernel, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, ids, n, E, bits, counts, offsets,
-                       gather, inv);
+                       gather, inv, zero, zero ? nzero : 0);
     return hipGetLastError();
+  }
+  if (zero && nzero > 0) {
+    hipError_t e = launch_zero_ints(zero, nzero, s);
+    if (e != hipSuccess) return e;
   }
   const int nseg = (n + SEG - 1) / SEG;
   const int nblk = (nseg + 3) / 4;

@@ -240,10 +240,11 @@ def test_permute_validation_and_workspace():
     assert L.ft_moe_permute_workspace(8, 128, 8) == 0           # single-block path
     assert L.ft_moe_permute_workspace(2048, 128, 8) == 0        # 16384 entries: still one block
     assert L.ft_moe_permute_workspace(4096, 128, 8) == 32 * 128 * 4
+    assert L.ft_moe_permute_workspace(8192, 128, 8) == 64 * 128 * 4
     assert L.ft_moe_permute_workspace(16384, 256, 8) == 128 * 256 * 4
-    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, None, 0, None), ft.FT_E_WORKSPACE, "needs 16384 bytes")
-    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, A, 100, None), ft.FT_E_WORKSPACE, "needs")
-    _err(L.ft_moe_permute(A, 4096, 128, 8, B, B, B, B, MIS, 1 << 20, None), ft.FT_E_INVAL, "ws is not")
+    _err(L.ft_moe_permute(A, 8192, 128, 8, B, B, B, B, None, 0, None), ft.FT_E_WORKSPACE, "needs 32768 bytes")
+    _err(L.ft_moe_permute(A, 8192, 128, 8, B, B, B, B, A, 100, None), ft.FT_E_WORKSPACE, "needs")
+    _err(L.ft_moe_permute(A, 8192, 128, 8, B, B, B, B, MIS, 1 << 20, None), ft.FT_E_INVAL, "ws is not")
     _err(L.ft_moe_permute(A, 4, 8, 2, None, B, B, B, None, 0, None), ft.FT_E_INVAL, "counts is null")
     _err(L.ft_moe_permute(None, 4, 8, 2, B, B, B, B, None, 0, None), ft.FT_E_INVAL, "ids is null")
     _err(L.ft_moe_permute(A, 4, 8, 2, B, B, MIS, B, None, 0, None), ft.FT_E_INVAL, "gather is not")
