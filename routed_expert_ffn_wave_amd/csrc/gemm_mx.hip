@@ -246,211 +246,223 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
     const int m0 = mt * MX_BM;
     const int mrows = min(MX_BM, cnt - m0);
 
-    // ---- this thread's share of the activation rows (rows past the group's end repeat its last
-    // row; their results are never stored): QN code pieces and a scale word (threads 128..255
-    // repeat rows 0..127: the same word to the same place).  32-bit offsets from the terms base.
-    auto src_row = [&](int r) -> uint32_t {
-      const int m = min(r, mrows - 1);
-      if (GATEUP) return shared ? (uint32_t)(m0 + m) : (uint32_t)(a.gather[row0 + m0 + m] / a.k);
-      return (uint32_t)(row0 + m0 + m);
-    };
-    uint32_t aoff[QN];
-    uint32_t adst[QN];
+    // A tile whose group has at most 64 rows left (a half tile) skips the MFMAs and LDS reads of its
+    // two empty 32-row tiles; it loads what a full tile loads (rows past the group repeat its last
+    // row), and its empty tiles' accumulators stay zero.  The two variants are separate copies of
+    // the whole tile, epilogue included, so neither carries the other's registers.
+    auto tile = [&](auto half) {
+      constexpr int MI = decltype(half)::value ? 2 : 4;  // 32-row tiles computed
+      // ---- this thread's share of the activation rows (rows past the group's end repeat its last
+      // row; their results are never stored): QN code pieces and a scale word (threads 128..255
+      // repeat rows 0..127: the same word to the same place).  32-bit offsets from the terms base.
+      auto src_row = [&](int r) -> uint32_t {
+        const int m = min(r, mrows - 1);
+        if (GATEUP) return shared ? (uint32_t)(m0 + m) : (uint32_t)(a.gather[row0 + m0 + m] / a.k);
+        return (uint32_t)(row0 + m0 + m);
+      };
+      uint32_t aoff[QN];
+      uint32_t adst[QN];
 #pragma unroll
-    for (int q = 0; q < QN; ++q) {
-      const int u = tid + 256 * q, r = u / UPR, pc = u % UPR;
-      aoff[q] = src_row(r) * (uint32_t)qpitch + (uint32_t)(pc * 16);
-      adst[q] = (uint32_t)(r * PITCH + pc * 16);
-    }
-    const uint32_t soff = src_row(tid & 127) * (uint32_t)(nblk * 2);
-    const uint32_t sdst = (uint32_t)((tid & 127) * PITCH + 2 * C::CB);
-    // two register sets (by step parity): a step's rows are loaded two steps before they are stored
-    u32x4 areg[2][QN];
-    uint32_t sreg[2];
-    auto load_a = [&](int set, int s) {  // step s's codes and scales (s clamped to the last step)
-      s = min(s, nsteps - 1);
-      const uint8_t* cb = qcodes + (size_t)s * 2 * C::CB;   // uniform
-      const uint8_t* sb = qscales + (size_t)s * 4;
+      for (int q = 0; q < QN; ++q) {
+        const int u = tid + 256 * q, r = u / UPR, pc = u % UPR;
+        aoff[q] = src_row(r) * (uint32_t)qpitch + (uint32_t)(pc * 16);
+        adst[q] = (uint32_t)(r * PITCH + pc * 16);
+      }
+      const uint32_t soff = src_row(tid & 127) * (uint32_t)(nblk * 2);
+      const uint32_t sdst = (uint32_t)((tid & 127) * PITCH + 2 * C::CB);
+      // two register sets (by step parity): a step's rows are loaded two steps before they are stored
+      u32x4 areg[2][QN];
+      uint32_t sreg[2];
+      auto load_a = [&](int set, int s) {  // step s's codes and scales (s clamped to the last step)
+        s = min(s, nsteps - 1);
+        const uint8_t* cb = qcodes + (size_t)s * 2 * C::CB;   // uniform
+        const uint8_t* sb = qscales + (size_t)s * 4;
 #pragma unroll
-      for (int q = 0; q < QN; ++q) areg[set][q] = *(const u32x4*)(cb + aoff[q]);
-      sreg[set] = *(const uint32_t*)(sb + soff);
-    };
-    auto store_a = [&](int set, int buf) {
-      uint8_t* b = abuf + buf * (MX_BM * PITCH);
+        for (int q = 0; q < QN; ++q) areg[set][q] = *(const u32x4*)(cb + aoff[q]);
+        sreg[set] = *(const uint32_t*)(sb + soff);
+      };
+      auto store_a = [&](int set, int buf) {
+        uint8_t* b = abuf + buf * (MX_BM * PITCH);
 #pragma unroll
-      for (int q = 0; q < QN; ++q) *(u32x4*)(b + adst[q]) = areg[set][q];
-      *(uint32_t*)(b + sdst) = sreg[set];
-    };
+        for (int q = 0; q < QN; ++q) *(u32x4*)(b + adst[q]) = areg[set][q];
+        *(uint32_t*)(b + sdst) = sreg[set];
+      };
 
-    // ---- this wave's weight rows: a uniform base per fragment, one 32-bit lane offset
-    const int nchunk = FP8 ? K / 16 : K / 32;  // 16-byte code chunks per weight row
-    const size_t mat_bytes = (size_t)ncols * nchunk * 16;
-    const uint8_t* wmat = (GATEUP ? a.w13 : a.w2) + (size_t)slot * mat_bytes;
-    const int blk0 = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;  // the wave's first 64-row device block
-    const uint8_t* wbase = wmat + (size_t)blk0 * nchunk * 1024;
-    const uint8_t* sbase = FP8 ? nullptr
-                               : (GATEUP ? a.s13 : a.s2) + (size_t)slot * ncols * nchunk + (size_t)blk0 * nchunk * 64;
-    const uint32_t blane = (uint32_t)(hi * 1024 + l32 * 16);  // chunk parity and row of this lane
-    const uint32_t slane = (uint32_t)(hi * 64 + l32);
-    // fragment j: rows 32 (j % 2) of device block blk0 + j / 2 (MXFP4); rows 32 j of blk0 (FP8)
-    auto frag_off = [&](int j) -> size_t {
-      return FP8 ? (size_t)j * 512 : (size_t)(j >> 1) * nchunk * 1024 + (size_t)(j & 1) * 512;
-    };
-    auto frag_soff = [&](int j) -> size_t { return (size_t)(j >> 1) * nchunk * 64 + (size_t)(j & 1) * 32; };
-    float bsc[WN];  // FP8: the current 128-K block's scale of each fragment's rows
-    int rb[WN];     // FP8: 128-row scale block of each fragment
-    const float* s32 = FP8 ? (const float*)(GATEUP ? a.s13 : a.s2) + (size_t)slot * (size_t)(ncols / 128) * (K / 128)
-                           : nullptr;
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      rb[j] = GATEUP ? (32 * blk0 + (j ? a.I : 0)) / 128 : (64 * blk0 + 32 * j) / 128;
-      bsc[j] = 1.0f;
-    }
-    u32x4 bq[MX_RING][WN][FP8 ? 2 : 1];
-    int bs[MX_RING][WN];
-    auto load_b = [&](auto SL, int s) {  // step s's weight operands into register set SL
-      constexpr int sl = decltype(SL)::value;
-      s = min(s, nsteps - 1);
+      // ---- this wave's weight rows: a uniform base per fragment, one 32-bit lane offset
+      const int nchunk = FP8 ? K / 16 : K / 32;  // 16-byte code chunks per weight row
+      const size_t mat_bytes = (size_t)ncols * nchunk * 16;
+      const uint8_t* wmat = (GATEUP ? a.w13 : a.w2) + (size_t)slot * mat_bytes;
+      const int blk0 = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;  // the wave's first 64-row device block
+      const uint8_t* wbase = wmat + (size_t)blk0 * nchunk * 1024;
+      const uint8_t* sbase = FP8 ? nullptr
+                                 : (GATEUP ? a.s13 : a.s2) + (size_t)slot * ncols * nchunk + (size_t)blk0 * nchunk * 64;
+      const uint32_t blane = (uint32_t)(hi * 1024 + l32 * 16);  // chunk parity and row of this lane
+      const uint32_t slane = (uint32_t)(hi * 64 + l32);
+      // fragment j: rows 32 (j % 2) of device block blk0 + j / 2 (MXFP4); rows 32 j of blk0 (FP8)
+      auto frag_off = [&](int j) -> size_t {
+        return FP8 ? (size_t)j * 512 : (size_t)(j >> 1) * nchunk * 1024 + (size_t)(j & 1) * 512;
+      };
+      auto frag_soff = [&](int j) -> size_t { return (size_t)(j >> 1) * nchunk * 64 + (size_t)(j & 1) * 32; };
+      float bsc[WN];  // FP8: the current 128-K block's scale of each fragment's rows
+      int rb[WN];     // FP8: 128-row scale block of each fragment
+      const float* s32 = FP8 ? (const float*)(GATEUP ? a.s13 : a.s2) + (size_t)slot * (size_t)(ncols / 128) * (K / 128)
+                             : nullptr;
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        if constexpr (FP8) {
-          const uint8_t* p0 = wbase + frag_off(j) + (size_t)(4 * s) * 1024;   // uniform
-          bq[sl][j][0] = *(const u32x4*)(p0 + blane);
-          bq[sl][j][FP8 ? 1 : 0] = *(const u32x4*)(p0 + 2048 + blane);
-          bs[sl][j] = unit_scale;
-        } else {
-          const uint8_t* p0 = wbase + frag_off(j) + (size_t)(2 * s) * 1024;
-          bq[sl][j][0] = *(const u32x4*)(p0 + blane);
-          bs[sl][j] = (int)*(sbase + frag_soff(j) + (size_t)(2 * s) * 64 + slane);
-        }
+        rb[j] = GATEUP ? (32 * blk0 + (j ? a.I : 0)) / 128 : (64 * blk0 + 32 * j) / 128;
+        bsc[j] = 1.0f;
       }
-    };
-
-    f32x16 acc[4][WN], part[4][WN];
+      u32x4 bq[MX_RING][WN][FP8 ? 2 : 1];
+      int bs[MX_RING][WN];
+      auto load_b = [&](auto SL, int s) {  // step s's weight operands into register set SL
+        constexpr int sl = decltype(SL)::value;
+        s = min(s, nsteps - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = part[i][j][r] = 0.0f;
-      }
-
-    // ---- prologue: step 0's activations in buffer 0, steps 1 and 2 in registers, weights of 0..2
-    load_a(0, 0);
-    store_a(0, 0);
-    load_a(1, 1);
-    load_a(0, 2);
-    load_b(std::integral_constant<int, 0>{}, 0);
-    load_b(std::integral_constant<int, 1>{}, 1);
-    load_b(std::integral_constant<int, 2>{}, 2);
-    __syncthreads();
-
-    // A fragment i of the buffer at `ab`: both terms and their scale bytes
-    struct AFrag {
-      i32x8 h, l;
-      int sh, sl;
-    };
-    auto read_a = [&](const uint8_t* ab, int i) -> AFrag {
-      const uint8_t* rp = ab + (32 * i + l32) * PITCH;
-      AFrag f;
-      if constexpr (FP8) {
-        const u32x4 h0 = *(const u32x4*)(rp + 16 * hi), h1 = *(const u32x4*)(rp + 64 + 16 * hi);
-        const u32x4 q0 = *(const u32x4*)(rp + 32 + 16 * hi), q1 = *(const u32x4*)(rp + 96 + 16 * hi);
-        f.h = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        f.l = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-      } else {
-        const u32x4 h0 = *(const u32x4*)(rp + 48 * hi);
-        const u32x2 h1 = *(const u32x2*)(rp + 48 * hi + 16);
-        const u32x2 q0 = *(const u32x2*)(rp + 48 * hi + 24);
-        const u32x4 q1 = *(const u32x4*)(rp + 48 * hi + 32);
-        f.h = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], 0, 0};
-        f.l = i32x8{(int)q0[0], (int)q0[1], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3], 0, 0};
-      }
-      const uint32_t sw = *(const uint16_t*)(rp + 2 * C::CB + 2 * hi);
-      f.sh = (int)(sw & 0xffu);
-      f.sl = (int)(sw >> 8);
-      return f;
-    };
-
-    auto step = [&](auto SL, int s) {
-      constexpr int sl = decltype(SL)::value;
-      load_b(std::integral_constant<int, (sl + 3) % MX_RING>{}, s + 3);
-      const uint8_t* ab = abuf + (sl & 1) * (MX_BM * PITCH);  // s and sl have the same parity
-      if constexpr (FP8) {
-        if ((sl & 1) == 0) {  // a new 128-K block: its scales
-          const int kb = s / 2;
-#pragma unroll
-          for (int j = 0; j < WN; ++j) bsc[j] = s32[(size_t)rb[j] * (K / 128) + kb];
-        }
-      }
-      i32x8 bv[WN];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const u32x4 c0 = bq[sl][j][0], c1 = bq[sl][j][FP8 ? 1 : 0];
-        bv[j] = FP8 ? i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]}
-                    : i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
-      }
-      AFrag cur = read_a(ab, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        AFrag nxt;
-        if (i < 3) nxt = read_a(ab, i + 1);  // the next row tile's reads go out before these MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-        // the hi terms of every fragment, then the lo terms: products into one accumulator are WN
-        // instructions apart
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int j = 0; j < WN; ++j) {
-            const i32x8& av = t ? cur.l : cur.h;
-            const int as = t ? cur.sl : cur.sh;
-            if constexpr (FP8) {
-              f32x16 p = part[i][j];
-              if (t == 0 && (sl & 1) == 0) p = f32x16{};  // the block's first product starts from zero
-              part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], p, C::ATYPE, C::BTYPE, 0, as, 0,
-                                                                           bs[sl][j]);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], C::ATYPE, C::BTYPE, 0,
-                                                                          as, 0, bs[sl][j]);
-            }
+        for (int j = 0; j < WN; ++j) {
+          if constexpr (FP8) {
+            const uint8_t* p0 = wbase + frag_off(j) + (size_t)(4 * s) * 1024;   // uniform
+            bq[sl][j][0] = *(const u32x4*)(p0 + blane);
+            bq[sl][j][FP8 ? 1 : 0] = *(const u32x4*)(p0 + 2048 + blane);
+            bs[sl][j] = unit_scale;
+          } else {
+            const uint8_t* p0 = wbase + frag_off(j) + (size_t)(2 * s) * 1024;
+            bq[sl][j][0] = *(const u32x4*)(p0 + blane);
+            bs[sl][j] = (int)*(sbase + frag_soff(j) + (size_t)(2 * s) * 64 + slane);
           }
         }
-        // FP8, last step of a 128-K block: row tile i - 1's block is complete (its MFMAs were
-        // issued a tile earlier): scale its partial sums into acc while tile i's MFMAs run
+      };
+
+      f32x16 acc[4][WN], part[4][WN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = part[i][j][r] = 0.0f;
+        }
+
+      // ---- prologue: step 0's activations in buffer 0, steps 1 and 2 in registers, weights of 0..2
+      load_a(0, 0);
+      store_a(0, 0);
+      load_a(1, 1);
+      load_a(0, 2);
+      load_b(std::integral_constant<int, 0>{}, 0);
+      load_b(std::integral_constant<int, 1>{}, 1);
+      load_b(std::integral_constant<int, 2>{}, 2);
+      __syncthreads();
+
+      // A fragment i of the buffer at `ab`: both terms and their scale bytes
+      struct AFrag {
+        i32x8 h, l;
+        int sh, sl;
+      };
+      auto read_a = [&](const uint8_t* ab, int i) -> AFrag {
+        const uint8_t* rp = ab + (32 * i + l32) * PITCH;
+        AFrag f;
         if constexpr (FP8) {
-          if ((sl & 1) == 1 && i > 0) {
+          const u32x4 h0 = *(const u32x4*)(rp + 16 * hi), h1 = *(const u32x4*)(rp + 64 + 16 * hi);
+          const u32x4 q0 = *(const u32x4*)(rp + 32 + 16 * hi), q1 = *(const u32x4*)(rp + 96 + 16 * hi);
+          f.h = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          f.l = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+        } else {
+          const u32x4 h0 = *(const u32x4*)(rp + 48 * hi);
+          const u32x2 h1 = *(const u32x2*)(rp + 48 * hi + 16);
+          const u32x2 q0 = *(const u32x2*)(rp + 48 * hi + 24);
+          const u32x4 q1 = *(const u32x4*)(rp + 48 * hi + 32);
+          f.h = i32x8{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], 0, 0};
+          f.l = i32x8{(int)q0[0], (int)q0[1], (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3], 0, 0};
+        }
+        const uint32_t sw = *(const uint16_t*)(rp + 2 * C::CB + 2 * hi);
+        f.sh = (int)(sw & 0xffu);
+        f.sl = (int)(sw >> 8);
+        return f;
+      };
+
+      auto step = [&](auto SL, int s) {
+        constexpr int sl = decltype(SL)::value;
+        load_b(std::integral_constant<int, (sl + 3) % MX_RING>{}, s + 3);
+        const uint8_t* ab = abuf + (sl & 1) * (MX_BM * PITCH);  // s and sl have the same parity
+        if constexpr (FP8) {
+          if ((sl & 1) == 0) {  // a new 128-K block: its scales
+            const int kb = s / 2;
+#pragma unroll
+            for (int j = 0; j < WN; ++j) bsc[j] = s32[(size_t)rb[j] * (K / 128) + kb];
+          }
+        }
+        i32x8 bv[WN];
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const u32x4 c0 = bq[sl][j][0], c1 = bq[sl][j][FP8 ? 1 : 0];
+          bv[j] = FP8 ? i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]}
+                      : i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], 0, 0, 0, 0};
+        }
+        AFrag cur = read_a(ab, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          AFrag nxt;
+          if (i < 3 && i + 1 < MI) nxt = read_a(ab, i + 1);  // the next row tile's reads go out before these MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          // the hi terms of every fragment, then the lo terms: products into one accumulator are WN
+          // instructions apart
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (i >= MI) break;
+#pragma unroll
+            for (int j = 0; j < WN; ++j) {
+              const i32x8& av = t ? cur.l : cur.h;
+              const int as = t ? cur.sl : cur.sh;
+              if constexpr (FP8) {
+                f32x16 p = part[i][j];
+                if (t == 0 && (sl & 1) == 0) p = f32x16{};  // the block's first product starts from zero
+                part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], p, C::ATYPE, C::BTYPE, 0, as, 0,
+                                                                             bs[sl][j]);
+              } else {
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], C::ATYPE, C::BTYPE, 0,
+                                                                            as, 0, bs[sl][j]);
+              }
+            }
+          }
+          // FP8, last step of a 128-K block: row tile i - 1's block is complete (its MFMAs were
+          // issued a tile earlier): scale its partial sums into acc while tile i's MFMAs run
+          if constexpr (FP8) {
+            if ((sl & 1) == 1 && i > 0) {
+#pragma unroll
+              for (int j = 0; j < WN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i - 1][j][r] = fmaf(part[i - 1][j][r], bsc[j], acc[i - 1][j][r]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < 3) cur = nxt;
+        }
+        if constexpr (FP8) {
+          if ((sl & 1) == 1) {
 #pragma unroll
             for (int j = 0; j < WN; ++j)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i - 1][j][r] = fmaf(part[i - 1][j][r], bsc[j], acc[i - 1][j][r]);
+              for (int r = 0; r < 16; ++r) acc[3][j][r] = fmaf(part[3][j][r], bsc[j], acc[3][j][r]);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (i < 3) cur = nxt;
+        // the next step's activations (loaded two steps ago) into the other buffer, then step s + 3's
+        store_a((sl + 1) & 1, (sl + 1) & 1);
+        load_a((sl + 1) & 1, s + 3);
+        __syncthreads();
+      };
+      for (int s = 0; s < nsteps; s += MX_RING) {
+        step(std::integral_constant<int, 0>{}, s);
+        step(std::integral_constant<int, 1>{}, s + 1);
+        step(std::integral_constant<int, 2>{}, s + 2);
+        step(std::integral_constant<int, 3>{}, s + 3);
       }
-      if constexpr (FP8) {
-        if ((sl & 1) == 1) {
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[3][j][r] = fmaf(part[3][j][r], bsc[j], acc[3][j][r]);
-        }
-      }
-      // the next step's activations (loaded two steps ago) into the other buffer, then step s + 3's
-      store_a((sl + 1) & 1, (sl + 1) & 1);
-      load_a((sl + 1) & 1, s + 3);
-      __syncthreads();
-    };
-    for (int s = 0; s < nsteps; s += MX_RING) {
-      step(std::integral_constant<int, 0>{}, s);
-      step(std::integral_constant<int, 1>{}, s + 1);
-      step(std::integral_constant<int, 2>{}, s + 2);
-      step(std::integral_constant<int, 3>{}, s + 3);
-    }
 
-    // ---- epilogue: staging slices over the activation buffers (every step has been read)
-    const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
-    store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
+      // ---- epilogue: staging slices over the activation buffers (every step has been read)
+      const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
+      store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
+    };
+    if (mrows <= MX_BM / 2)
+      tile(std::true_type{});
+    else
+      tile(std::false_type{});
     __syncthreads();  // the next tile's activations overwrite the staging slices
     if (tid == 0) s_claim[0] = nxt;
     __syncthreads();
