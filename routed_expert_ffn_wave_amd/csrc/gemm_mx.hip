@@ -246,12 +246,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
     const int m0 = mt * MX_BM;
     const int mrows = min(MX_BM, cnt - m0);
 
-    // A tile whose group has at most 64 rows left (a half tile) skips the MFMAs and LDS reads of its
-    // two empty 32-row tiles; it loads what a full tile loads (rows past the group repeat its last
-    // row), and its empty tiles' accumulators stay zero.  The two variants are separate copies of
-    // the whole tile, epilogue included, so neither carries the other's registers.
-    auto tile = [&](auto half) {
-      constexpr int MI = decltype(half)::value ? 2 : 4;  // 32-row tiles computed
+    // A tile whose group has at most 32 or 64 rows left (a partial tile) skips the MFMAs and LDS
+    // reads of its empty 32-row tiles; it loads what a full tile loads (rows past the group repeat
+    // its last row), and its empty tiles' accumulators stay zero.  The variants are separate copies
+    // of the whole tile, epilogue included, so none carries another's registers.
+    auto tile = [&](auto mi) {
+      constexpr int MI = decltype(mi)::value;  // 32-row tiles computed
       // ---- this thread's share of the activation rows (rows past the group's end repeat its last
       // row; their results are never stored): QN code pieces and a scale word (threads 128..255
       // repeat rows 0..127: the same word to the same place).  32-bit offsets from the terms base.
@@ -459,10 +459,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
       const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
       store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
     };
-    if (mrows <= MX_BM / 2)
-      tile(std::true_type{});
+    if (mrows <= MX_BM / 4)
+      tile(std::integral_constant<int, 1>{});
+    else if (mrows <= MX_BM / 2)
+      tile(std::integral_constant<int, 2>{});
     else
-      tile(std::false_type{});
+      tile(std::integral_constant<int, 4>{});
     __syncthreads();  // the next tile's activations overwrite the staging slices
     if (tid == 0) s_claim[0] = nxt;
     __syncthreads();

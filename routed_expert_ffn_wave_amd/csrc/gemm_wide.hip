@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
   // Tiles come from the launch's work queues (claimed one tile ahead): a tile takes ~60 us at
   // K = 2048, so a fixed stride over the tile list leaves the whole device waiting on the few blocks
   // that drew one tile more than the rest, while queues let every block take the next tile as soon as
-  // it is free, which with tiles of unequal cost (the half tiles below) evens out the finish.
+  // it is free, which with tiles of unequal cost (the partial tiles below) evens out the finish.
   int* s_claim = s_tmp + 1;
   int qoff = 0;
   if (tid == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
@@ -438,13 +438,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
     const int m0 = mt * WBM;
     const int mrows = min(WBM, cnt - m0);
 
-    // A tile whose group has at most 64 rows left (a half tile) skips the MFMAs and LDS reads of
-    // its two empty 32-row fragments; its loads are the same as a full tile's (rows past the group
-    // repeat its last row), so the load counts the waits rely on do not change.  The two variants
-    // are separate copies of the whole tile, epilogue included, so neither carries the other's
-    // registers.
-    auto tile = [&](auto half) {
-      constexpr int MI = decltype(half)::value ? 2 : 4;  // 32-row fragments computed
+    // A tile whose group has at most 32 or 64 rows left (a partial tile) skips the MFMAs and LDS
+    // reads of its empty 32-row fragments; its loads are the same as a full tile's (rows past the
+    // group repeat its last row), so the load counts the waits rely on do not change.  The variants
+    // are separate copies of the whole tile, epilogue included, so none carries another's registers.
+    auto tile = [&](auto mi) {
+      constexpr int MI = decltype(mi)::value;  // 32-row fragments computed
       uint32_t aoff[DMA_A];
 #pragma unroll
       for (int q = 0; q < DMA_A; ++q) {
@@ -541,10 +540,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
       // complete after them (issue order), so no wait is needed here.
       store_tile<GATEUP, 4>(acc, stg, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
     };
-    if (mrows <= WBM / 2)
-      tile(std::true_type{});
+    if (mrows <= WBM / 4)
+      tile(std::integral_constant<int, 1>{});
+    else if (mrows <= WBM / 2)
+      tile(std::integral_constant<int, 2>{});
     else
-      tile(std::false_type{});
+      tile(std::integral_constant<int, 4>{});
     if (tid == 0) s_claim[0] = nxt;
     lds_reads_done_barrier();  // staging slices and ring buffers are rewritten by the next tile
     it = s_claim[0];
