@@ -11,9 +11,9 @@
 //      expert find each other with ballots over the id bits; a lane's rank among its lower-numbered
 //      peers plus the segment's running base is its sorted position, so positions follow flat
 //      order exactly and never depend on the order atomics happen to take.
-// Up to 16 segments (T*k <= 16384) run as one block of 16 waves; larger inputs use three kernels
-// and a workspace of per-(expert, segment) counts.  (One block over 32 segments, two per wave, took
-// 33-36 us at 4096 tokens of top-8 routing against 22 us for the three kernels on 8 blocks each.)
+// Up to 16 segments (T*k <= 16384) run as one block of 16 waves; larger inputs use two kernels
+// (per-segment counts, then scan and scatter) and a workspace of per-(expert, segment) counts.  (One block over 32 segments, two per wave, took
+// 33-36 us at 4096 tokens of top-8 routing against 22 us for the kernels on 8 blocks each.)
 #include "ft_device.h"
 #include "ft_kernels.h"
 #include "ft_permute.h"
@@ -124,13 +124,17 @@ bool permute_one_block(long long n, int E) {
   return n <= (long long)SMALL_SEGS * SEG && small_lds_bytes(n, E) <= 160 * 1024;
 }
 
-// ---- large path: blocks of 256 threads (4 waves), one segment per wave.
+// ---- large path: blocks of 256 threads (4 waves), one segment per wave; two kernels.
 // seg_cnt layout [E][nseg] (expert major).
 
+// Per-segment expert counts; block 0 also sets zero[0 .. nzero) to zero.
 __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ ids, int n, int E, int nseg,
-                                                            int32_t* __restrict__ seg_cnt) {
+                                                            int32_t* __restrict__ seg_cnt, int32_t* __restrict__ zero,
+                                                            int nzero) {
   extern __shared__ int lds[];
   const int tid = threadIdx.x, wv = tid >> 6;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += 256) zero[i] = 0;
   for (int i = tid; i < 4 * E; i += 256) lds[i] = 0;
   __syncthreads();
   const int seg = blockIdx.x * 4 + wv;
@@ -142,32 +146,13 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
   }
 }
 
-// One wave per expert: exclusive prefix over segments in place; counts[e] = total.
-__global__ __launch_bounds__(256) void permute_segscan_kernel(int32_t* __restrict__ seg_cnt, int nseg, int E,
-                                                               int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  int32_t* row = seg_cnt + (size_t)e * nseg;
-  int carry = 0;
-  for (int s0 = 0; s0 < nseg; s0 += 64) {
-    int s = s0 + lane;
-    int v = (s < nseg) ? row[s] : 0;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (s < nseg) row[s] = carry + x - v;
-    carry += __shfl(x, 63, 64);
-  }
-  if (lane == 0) counts[e] = carry;
-}
-
+// Every block computes, for each expert, its total and the counts of the segments before its own
+// four (the same sums in the same order in every block, so all blocks agree), the offsets by a scan
+// over experts, and then scatters its segments; block 0 writes counts and offsets.  (A separate
+// scan kernel between the two cost a kernel boundary of a few microseconds plus its own run.)
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nseg,
-                                                               int id_bits, const int32_t* __restrict__ seg_base,
-                                                               const int32_t* __restrict__ counts,
+                                                               int id_bits, const int32_t* __restrict__ seg_cnt,
+                                                               int32_t* __restrict__ counts,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ gather,
                                                                int32_t* __restrict__ inv) {
@@ -176,19 +161,36 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
   int* base = lds + E;         // [4][E]
   int* tmp = base + 4 * E;     // [32]
   const int tid = threadIdx.x, wv = tid >> 6;
-  for (int e = tid; e < E; e += 256) off[e] = counts[e];
+  const int s0 = blockIdx.x * 4;  // this block's first segment
+  for (int e = tid; e < E; e += 256) {
+    const int32_t* row = seg_cnt + (size_t)e * nseg;
+    int run = 0, pre[4] = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < nseg; c0 += 32) {  // 32 independent loads at a time: one round trip each
+      int v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = c0 + u < nseg ? row[c0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c0 + u == s0 + q) pre[q] = run;
+        run += v[u];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) base[q * E + e] = pre[q];
+    off[e] = run;
+    if (blockIdx.x == 0) counts[e] = run;
+  }
   __syncthreads();
   const int total = block_exclusive_scan(off, E, tmp);
   if (blockIdx.x == 0) {
     for (int e = tid; e < E; e += 256) offsets[e] = off[e];
     if (tid == 0) offsets[E] = total;
   }
-  for (int i = tid; i < 4 * E; i += 256) {
-    int s = blockIdx.x * 4 + i / E, e = i % E;
-    base[i] = (s < nseg) ? off[e] + seg_base[(size_t)e * nseg + s] : 0;
-  }
+  for (int i = tid; i < 4 * E; i += 256) base[i] += off[i % E];
   __syncthreads();
-  const int seg = blockIdx.x * 4 + wv;
+  const int seg = s0 + wv;
   if (seg < nseg) scatter_segment(ids, n, E, seg * SEG, id_bits, base + wv * E, gather, inv);
 }
 
@@ -217,16 +219,11 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
                        gather, inv, zero, zero ? nzero : 0);
     return hipGetLastError();
   }
-  if (zero && nzero > 0) {
-    hipError_t e = launch_zero_ints(zero, nzero, s);
-    if (e != hipSuccess) return e;
-  }
   const int nseg = (n + SEG - 1) / SEG;
   const int nblk = (nseg + 3) / 4;
   int32_t* seg = (int32_t*)ws;
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(256), (size_t)4 * E * sizeof(int), s, ids, n, E, nseg,
-                     seg);
-  hipLaunchKernelGGL(permute_segscan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, seg, nseg, E, counts);
+                     seg, zero, zero ? nzero : 0);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(256), (size_t)(5 * E + 32) * sizeof(int), s, ids,
                      n, E, nseg, bits, seg, counts, offsets, gather, inv);
   return hipGetLastError();
