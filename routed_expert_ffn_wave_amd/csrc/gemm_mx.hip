@@ -44,6 +44,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int MX_BM = GEMM_BM;  // token rows per tile
 constexpr int MX_RING = 4;      // weight register sets (loads run 3 steps ahead)
+constexpr int MX_DEEP = 8;      // the same for tiles of at most 32 rows (loads run 7 steps ahead)
+
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void constexpr_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    constexpr_for<B + 1, E>(f);
+  }
+}
 
 template <bool FP8>
 struct MxCfg;
@@ -66,12 +76,19 @@ struct MxCfg<true> {                    // FP8-B128 weights, e4m3 activation ter
 template <bool FP8>
 constexpr int a_units() { return 2 * MxCfg<FP8>::CB / 16; }  // 16-byte pieces of codes per row and step
 
+constexpr int MX_KBMAX = 256;   // FP8: 128-K blocks per weight row held in LDS (K <= 32768)
+
 __host__ __device__ inline size_t mx_buf_off(int E) { return (group_lds_bytes(E) + 255) & ~(size_t)255; }
+// FP8: each wave's block scales ([wave][fragment][K / 128] fp32) follow the activation buffers
 template <bool FP8>
-__host__ __device__ inline size_t mx_lds_bytes(int E) {
+__host__ __device__ inline size_t mx_bsc_off(int E) {
   const size_t abuf = (size_t)2 * MX_BM * MxCfg<FP8>::PITCH;
   const size_t stg = FP8 ? (size_t)4 * 64 * (64 * 2 + 16) : (size_t)STG_BYTES;
   return mx_buf_off(E) + (abuf > stg ? abuf : stg);
+}
+template <bool FP8>
+__host__ __device__ inline size_t mx_lds_bytes(int E) {
+  return mx_bsc_off<FP8>(E) + (FP8 ? (size_t)4 * MxCfg<FP8>::WN * MX_KBMAX * 4 : 0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -250,41 +267,53 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
     // reads of its empty 32-row tiles; it loads what a full tile loads (rows past the group repeat
     // its last row), and its empty tiles' accumulators stay zero.  The variants are separate copies
     // of the whole tile, epilogue included, so none carries another's registers.
-    auto tile = [&](auto mi) {
-      constexpr int MI = decltype(mi)::value;  // 32-row tiles computed
+    auto tile = [&](auto mi, auto rg) {
+      constexpr int MI = decltype(mi)::value;    // 32-row tiles computed
+      constexpr int RING = decltype(rg)::value;  // weight register sets: loads run RING - 1 steps ahead
+      // A deep ring (more than MX_RING sets) also gives the activation terms one register set per
+      // step in flight, issued with the step's weights, so that waiting for a step's activations
+      // never waits for weights issued after them; such a tile stages only its MI row tiles.
+      constexpr bool DEEP = RING > MX_RING;
+      constexpr int AR = DEEP ? 32 * MI : MX_BM;  // activation rows staged per step
+      constexpr int NPC = AR * UPR;               // their 16-byte pieces per step
+      constexpr int QA = DEEP ? (NPC + 255) / 256 : QN;
+      constexpr int NSET = DEEP ? RING : 2;       // activation register sets
+      static_assert(DEEP || NPC == 256 * QN, "a full tile's pieces cover the threads exactly");
       // ---- this thread's share of the activation rows (rows past the group's end repeat its last
-      // row; their results are never stored): QN code pieces and a scale word (threads 128..255
-      // repeat rows 0..127: the same word to the same place).  32-bit offsets from the terms base.
+      // row; their results are never stored): QA code pieces and a scale word (threads past the
+      // staged rows repeat the first ones: the same words to the same places).  32-bit offsets from
+      // the terms base.
       auto src_row = [&](int r) -> uint32_t {
         const int m = min(r, mrows - 1);
         if (GATEUP) return shared ? (uint32_t)(m0 + m) : (uint32_t)(a.gather[row0 + m0 + m] / a.k);
         return (uint32_t)(row0 + m0 + m);
       };
-      uint32_t aoff[QN];
-      uint32_t adst[QN];
+      uint32_t aoff[QA];
+      uint32_t adst[QA];
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        const int u = tid + 256 * q, r = u / UPR, pc = u % UPR;
+      for (int q = 0; q < QA; ++q) {
+        const int u = (tid + 256 * q) % NPC, r = u / UPR, pc = u % UPR;
         aoff[q] = src_row(r) * (uint32_t)qpitch + (uint32_t)(pc * 16);
         adst[q] = (uint32_t)(r * PITCH + pc * 16);
       }
-      const uint32_t soff = src_row(tid & 127) * (uint32_t)(nblk * 2);
-      const uint32_t sdst = (uint32_t)((tid & 127) * PITCH + 2 * C::CB);
-      // two register sets (by step parity): a step's rows are loaded two steps before they are stored
-      u32x4 areg[2][QN];
-      uint32_t sreg[2];
+      const uint32_t soff = src_row(tid % AR) * (uint32_t)(nblk * 2);
+      const uint32_t sdst = (uint32_t)((tid % AR) * PITCH + 2 * C::CB);
+      // register sets of staged activations: by step parity (a step's rows are loaded two steps
+      // before they are stored), or one per ring slot (DEEP)
+      u32x4 areg[NSET][QA];
+      uint32_t sreg[NSET];
       auto load_a = [&](int set, int s) {  // step s's codes and scales (s clamped to the last step)
         s = min(s, nsteps - 1);
         const uint8_t* cb = qcodes + (size_t)s * 2 * C::CB;   // uniform
         const uint8_t* sb = qscales + (size_t)s * 4;
 #pragma unroll
-        for (int q = 0; q < QN; ++q) areg[set][q] = *(const u32x4*)(cb + aoff[q]);
+        for (int q = 0; q < QA; ++q) areg[set][q] = *(const u32x4*)(cb + aoff[q]);
         sreg[set] = *(const uint32_t*)(sb + soff);
       };
       auto store_a = [&](int set, int buf) {
         uint8_t* b = abuf + buf * (MX_BM * PITCH);
 #pragma unroll
-        for (int q = 0; q < QN; ++q) *(u32x4*)(b + adst[q]) = areg[set][q];
+        for (int q = 0; q < QA; ++q) *(u32x4*)(b + adst[q]) = areg[set][q];
         *(uint32_t*)(b + sdst) = sreg[set];
       };
 
@@ -305,6 +334,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
       auto frag_soff = [&](int j) -> size_t { return (size_t)(j >> 1) * nchunk * 64 + (size_t)(j & 1) * 32; };
       float bsc[WN];  // FP8: the current 128-K block's scale of each fragment's rows
       int rb[WN];     // FP8: 128-row scale block of each fragment
+      // FP8: this wave's block scales in LDS ([fragment][K / 128]), read a block at a time, so that
+      // no scale load in the K loop waits for the weights issued before it
+      float* s_bs = (float*)(lds + mx_bsc_off<FP8>(a.E)) + wv * WN * MX_KBMAX;
       const float* s32 = FP8 ? (const float*)(GATEUP ? a.s13 : a.s2) + (size_t)slot * (size_t)(ncols / 128) * (K / 128)
                              : nullptr;
 #pragma unroll
@@ -312,8 +344,21 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
         rb[j] = GATEUP ? (32 * blk0 + (j ? a.I : 0)) / 128 : (64 * blk0 + 32 * j) / 128;
         bsc[j] = 1.0f;
       }
-      u32x4 bq[MX_RING][WN][FP8 ? 2 : 1];
-      int bs[MX_RING][WN];
+      u32x4 bq[RING][WN][FP8 ? 2 : 1];
+      int bs[RING][WN];
+      // FP8: the wave's block scales, loaded before the prologue's loads and written to LDS after
+      // them (the wait for them leaves the prologue's loads in flight)
+      constexpr int BSN = FP8 ? MX_KBMAX / 64 : 1;
+      float bsl[WN][BSN];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int q = 0; q < BSN; ++q) {
+            const int kb = lane + 64 * q;
+            bsl[j][q] = kb < K / 128 ? s32[(size_t)rb[j] * (K / 128) + kb] : 0.0f;
+          }
+      }
       auto load_b = [&](auto SL, int s) {  // step s's weight operands into register set SL
         constexpr int sl = decltype(SL)::value;
         s = min(s, nsteps - 1);
@@ -341,14 +386,32 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
           for (int r = 0; r < 16; ++r) acc[i][j][r] = part[i][j][r] = 0.0f;
         }
 
-      // ---- prologue: step 0's activations in buffer 0, steps 1 and 2 in registers, weights of 0..2
-      load_a(0, 0);
-      store_a(0, 0);
-      load_a(1, 1);
-      load_a(0, 2);
-      load_b(std::integral_constant<int, 0>{}, 0);
-      load_b(std::integral_constant<int, 1>{}, 1);
-      load_b(std::integral_constant<int, 2>{}, 2);
+      // ---- prologue: step 0's activations in buffer 0; weights of steps 0 .. RING - 2, and the
+      // activations of steps 1 and 2 (DEEP: 1 .. RING - 2, each with its weights) in registers
+      if constexpr (DEEP) {
+        load_a(0, 0);
+        load_b(std::integral_constant<int, 0>{}, 0);
+        constexpr_for<1, RING - 1>([&](auto S) {
+          load_b(S, S);
+          load_a(S, S);
+        });
+        store_a(0, 0);
+      } else {
+        load_a(0, 0);
+        store_a(0, 0);
+        load_a(1, 1);
+        load_a(0, 2);
+        load_b(std::integral_constant<int, 0>{}, 0);
+        load_b(std::integral_constant<int, 1>{}, 1);
+        load_b(std::integral_constant<int, 2>{}, 2);
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int q = 0; q < BSN; ++q)
+            if (lane + 64 * q < K / 128) s_bs[j * MX_KBMAX + lane + 64 * q] = bsl[j][q];
+      }
       __syncthreads();
 
       // A fragment i of the buffer at `ab`: both terms and their scale bytes
@@ -380,13 +443,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
 
       auto step = [&](auto SL, int s) {
         constexpr int sl = decltype(SL)::value;
-        load_b(std::integral_constant<int, (sl + 3) % MX_RING>{}, s + 3);
+        load_b(std::integral_constant<int, (sl + RING - 1) % RING>{}, s + RING - 1);
+        if constexpr (DEEP) load_a((sl + RING - 1) % RING, s + RING - 1);
         const uint8_t* ab = abuf + (sl & 1) * (MX_BM * PITCH);  // s and sl have the same parity
         if constexpr (FP8) {
-          if ((sl & 1) == 0) {  // a new 128-K block: its scales
-            const int kb = s / 2;
+          if constexpr ((sl & 1) == 0) {  // a new 128-K block: its scales
 #pragma unroll
-            for (int j = 0; j < WN; ++j) bsc[j] = s32[(size_t)rb[j] * (K / 128) + kb];
+            for (int j = 0; j < WN; ++j) bsc[j] = s_bs[j * MX_KBMAX + s / 2];
           }
         }
         i32x8 bv[WN];
@@ -425,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
           // FP8, last step of a 128-K block: row tile i - 1's block is complete (its MFMAs were
           // issued a tile earlier): scale its partial sums into acc while tile i's MFMAs run
           if constexpr (FP8) {
-            if ((sl & 1) == 1 && i > 0) {
+            if ((sl & 1) == 1 && i > 0 && i - 1 < MI) {
 #pragma unroll
               for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -435,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
           __builtin_amdgcn_sched_barrier(0);
           if (i < 3) cur = nxt;
         }
-        if constexpr (FP8) {
+        if constexpr (FP8 && MI == 4) {
           if ((sl & 1) == 1) {
 #pragma unroll
             for (int j = 0; j < WN; ++j)
@@ -443,28 +506,40 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
               for (int r = 0; r < 16; ++r) acc[3][j][r] = fmaf(part[3][j][r], bsc[j], acc[3][j][r]);
           }
         }
-        // the next step's activations (loaded two steps ago) into the other buffer, then step s + 3's
-        store_a((sl + 1) & 1, (sl + 1) & 1);
-        load_a((sl + 1) & 1, s + 3);
+        // the next step's activations into the other buffer: DEEP, from the set loaded with its
+        // weights; else from the parity set loaded two steps ago, which then takes step s + 3's
+        if constexpr (DEEP) {
+          store_a((sl + 1) % RING, (sl + 1) & 1);
+        } else {
+          store_a((sl + 1) & 1, (sl + 1) & 1);
+          load_a((sl + 1) & 1, s + 3);
+        }
         __syncthreads();
       };
-      for (int s = 0; s < nsteps; s += MX_RING) {
-        step(std::integral_constant<int, 0>{}, s);
-        step(std::integral_constant<int, 1>{}, s + 1);
-        step(std::integral_constant<int, 2>{}, s + 2);
-        step(std::integral_constant<int, 3>{}, s + 3);
-      }
+      for (int s = 0; s < nsteps; s += RING)
+        constexpr_for<0, RING>([&](auto S) { step(S, s + S); });
 
       // ---- epilogue: staging slices over the activation buffers (every step has been read)
       const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
       store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
     };
-    if (mrows <= MX_BM / 4)
-      tile(std::integral_constant<int, 1>{});
+    // An FP8 tile of at most 32 rows is bound by its weight stream, not its MFMAs: it keeps
+    // MX_DEEP - 1 steps of loads in flight where the step count allows.  (The MXFP4 kernel has no
+    // registers to spare for it.)
+    bool deep = false;
+    if constexpr (FP8) {
+      if (mrows <= MX_BM / 4 && nsteps % MX_DEEP == 0) {
+        tile(std::integral_constant<int, 1>{}, std::integral_constant<int, MX_DEEP>{});
+        deep = true;
+      }
+    }
+    if (deep) {
+    } else if (mrows <= MX_BM / 4)
+      tile(std::integral_constant<int, 1>{}, std::integral_constant<int, MX_RING>{});
     else if (mrows <= MX_BM / 2)
-      tile(std::integral_constant<int, 2>{});
+      tile(std::integral_constant<int, 2>{}, std::integral_constant<int, MX_RING>{});
     else
-      tile(std::integral_constant<int, 4>{});
+      tile(std::integral_constant<int, 4>{}, std::integral_constant<int, MX_RING>{});
     __syncthreads();  // the next tile's activations overwrite the staging slices
     if (tid == 0) s_claim[0] = nxt;
     __syncthreads();
@@ -493,7 +568,8 @@ hipError_t launch_mx_cfg(const FfnArgs& a, const uint8_t* qcodes, const uint8_t*
 bool gemm_mx_fits(int fmt, int rows, int K, int E) {
   if (E > 512 || K % 256 != 0 || K < 256) return false;
   if (fmt == FMT_MXFP4) return rows % MxCfg<false>::BN == 0 && mx_lds_bytes<false>(E) <= 160 * 1024;
-  if (fmt == FMT_FP8_B128) return rows % MxCfg<true>::BN == 0 && mx_lds_bytes<true>(E) <= 160 * 1024;
+  if (fmt == FMT_FP8_B128)
+    return rows % MxCfg<true>::BN == 0 && K / 128 <= MX_KBMAX && mx_lds_bytes<true>(E) <= 160 * 1024;
   return false;
 }
 
