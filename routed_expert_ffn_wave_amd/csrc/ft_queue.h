@@ -29,4 +29,21 @@ __device__ __forceinline__ int queue_claim(int32_t* ctr, int nitems, int& qoff) 
   return -1;
 }
 
+// The same over an item list in two parts, [0, nA) and then [nA, nA + nB): each part is cut into
+// QN contiguous runs, and run q hands out its share of the first part before its share of the
+// second, so that every XCD takes its long items (tiles of many rows) before its short ones.
+__device__ __forceinline__ int queue_claim2(int32_t* ctr, int nA, int nB, int& qoff) {
+  const int runA = (nA + QN - 1) / QN, runB = (nB + QN - 1) / QN;
+  for (; qoff < QN; ++qoff) {
+    const int q = (int)((blockIdx.x + qoff) % QN);
+    const int loA = q * runA, lenA = max(0, min(nA, loA + runA) - loA);
+    const int loB = q * runB, lenB = max(0, min(nB, loB + runB) - loB);
+    if (lenA + lenB == 0) continue;
+    const int i = __hip_atomic_fetch_add(ctr + q * Q_STRIDE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < lenA) return loA + i;
+    if (i < lenA + lenB) return nA + loB + (i - lenA);
+  }
+  return -1;
+}
+
 }  // namespace ftk

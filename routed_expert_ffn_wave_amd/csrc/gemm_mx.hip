@@ -78,7 +78,10 @@ constexpr int a_units() { return 2 * MxCfg<FP8>::CB / 16; }  // 16-byte pieces o
 
 constexpr int MX_KBMAX = 256;   // FP8: 128-K blocks per weight row held in LDS (K <= 32768)
 
-__host__ __device__ inline size_t mx_buf_off(int E) { return (group_lds_bytes(E) + 255) & ~(size_t)255; }
+// LDS: the group list, each group's first partial-tile item ([E + 2] ints), then the buffers
+__host__ __device__ inline size_t mx_buf_off(int E) {
+  return (group_lds_bytes(E) + (size_t)(E + 2) * 4 + 255) & ~(size_t)255;
+}
 // FP8: each wave's block scales ([wave][fragment][K / 128] fp32) follow the activation buffers
 template <bool FP8>
 __host__ __device__ inline size_t mx_bsc_off(int E) {
@@ -219,6 +222,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   int* s_cnt = s_row0 + E2;
   int* s_item0 = s_cnt + E2;
   int* s_tmp = s_item0 + E2;
+  int* s_pitem0 = (int*)(lds + group_lds_bytes(a.E));
   uint8_t* abuf = lds + mx_buf_off(a.E);
 
   const int K = GATEUP ? a.d : a.I;
@@ -229,10 +233,29 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   const size_t qpitch = (size_t)nblk * C::CB;
   GroupSrc src{a.slot_of, a.offsets, a.E, a.T, a.k, a.shared_slot, a.min_cnt, a.max_cnt, a.n_slots};
   GroupList gl{s_slot, s_row0, s_cnt, s_item0, 0};
-  build_groups(src, gl, s_tmp, [&](int cnt) { return ((cnt + MX_BM - 1) / MX_BM) * ntiles; });
-  const int nitems = s_item0[gl.n];
-
+  // Items in two parts: the long tiles of every group (more than MX_BM / 2 rows: every full m-tile,
+  // and the last one if it holds more than half a tile; s_item0 prefix), then the short tile (the
+  // group's last m-tile with 1 .. MX_BM / 2 rows) of every group that has one (s_pitem0 prefix).  A
+  // long tile takes about twice as long as a short one, so each queue hands out its long tiles
+  // first and the launch ends on short ones.
+  build_groups(src, gl, s_tmp, [&](int cnt) { return (cnt / MX_BM + (cnt % MX_BM > MX_BM / 2)) * ntiles; });
   const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int carry = 0;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int i0 = 0; i0 < gl.n; i0 += 64) {
+      const int i = i0 + lane;
+      const int rem = i < gl.n ? s_cnt[i] % MX_BM : 0;
+      const uint64_t b = __ballot(rem > 0 && rem <= MX_BM / 2);
+      if (i < gl.n) s_pitem0[i] = (carry + __popcll(b & below)) * ntiles;
+      carry += __popcll(b);
+    }
+    if (lane == 0) s_pitem0[gl.n] = carry * ntiles;
+  }
+  __syncthreads();
+  const int nlong = s_item0[gl.n], nshort = s_pitem0[gl.n];
+  const int nitems = nlong + nshort;
+
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int TK = a.T * a.k;
@@ -246,19 +269,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   // others; a block that starts late takes fewer tiles (claimed one tile ahead)
   int* s_claim = s_tmp + 1;
   int qoff = 0;
-  if (tid == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
+  if (tid == 0) s_claim[0] = queue_claim2(a.qctr, nlong, nshort, qoff);
   __syncthreads();
   int it = s_claim[0];
   __syncthreads();
   for (; it >= 0 && it < nitems;) {
     int nxt = -1;
-    if (tid == 0) nxt = queue_claim(a.qctr, nitems, qoff);
-    const int g = find_group(s_item0, gl.n, it);
-    const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
-    const int mt = local / ntiles, nt = local % ntiles;
+    if (tid == 0) nxt = queue_claim2(a.qctr, nlong, nshort, qoff);
+    const bool full = it < nlong;  // a long tile
+    const int* pre = full ? s_item0 : s_pitem0;
+    const int v = full ? it : it - nlong;
+    const int g = find_group(pre, gl.n, v);
+    const int local = __builtin_amdgcn_readfirstlane(v - pre[g]);
     const int slot = __builtin_amdgcn_readfirstlane(s_slot[g]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_row0[g]);
     const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[g]);
+    const int mt = full ? local / ntiles : cnt / MX_BM, nt = full ? local % ntiles : local;
     const bool shared = row0 >= TK;
     const int m0 = mt * MX_BM;
     const int mrows = min(MX_BM, cnt - m0);
