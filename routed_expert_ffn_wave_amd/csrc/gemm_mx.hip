@@ -266,7 +266,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
 
   // tiles from the launch's work queues: block b serves the run of XCD b % 8 first (blocks go to
   // the XCDs round-robin, so tiles that share activation rows or weights share an L2), then the
-  // others; a block that starts late takes fewer tiles (claimed one tile ahead)
+  // others; a block that starts late takes fewer tiles (each claimed as the previous one's K loop
+  // ends)
   int* s_claim = s_tmp + 1;
   int qoff = 0;
   if (tid == 0) s_claim[0] = queue_claim2(a.qctr, nlong, nshort, qoff);
@@ -274,8 +275,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   int it = s_claim[0];
   __syncthreads();
   for (; it >= 0 && it < nitems;) {
-    int nxt = -1;
-    if (tid == 0) nxt = queue_claim2(a.qctr, nlong, nshort, qoff);
+    int nxt = -1;  // the next tile, claimed as this one's K loop ends
     const bool full = it < nlong;  // a long tile
     const int* pre = full ? s_item0 : s_pitem0;
     const int v = full ? it : it - nlong;
@@ -547,6 +547,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
 
       // ---- epilogue: staging slices over the activation buffers (every step has been read)
       const int dev_blk = FP8 ? 4 * nt + wv : 8 * nt + 2 * wv;
+      // the next tile is claimed only now (its latency hides behind the epilogue): claimed at the
+      // start of this tile, it would be bound to this block however late this block ends, and a
+      // block that drew a long tile would take a short one behind it while others sit idle
+      if (tid == 0) nxt = queue_claim2(a.qctr, nlong, nshort, qoff);
       store_tile<GATEUP, WN>(acc, abuf, a, lane, wv, dev_blk, shared, row0, m0, mrows);
     };
     // An FP8 tile of at most 32 rows is bound by its weight stream, not its MFMAs: it keeps

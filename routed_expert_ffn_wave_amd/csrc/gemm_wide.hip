@@ -415,10 +415,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
   const int a_rd0 = l32 * 64 + ((hi ^ xo) << 4);
   const int a_rd1 = l32 * 64 + (((2 + hi) ^ xo) << 4);
 
-  // Tiles come from the launch's work queues (claimed one tile ahead): a tile takes ~60 us at
-  // K = 2048, so a fixed stride over the tile list leaves the whole device waiting on the few blocks
-  // that drew one tile more than the rest, while queues let every block take the next tile as soon as
-  // it is free, which with tiles of unequal cost (the partial tiles below) evens out the finish.
+  // Tiles come from the launch's work queues (each claimed as the previous one's K loop ends): a
+  // tile takes ~60 us at K = 2048, so a fixed stride over the tile list leaves the whole device
+  // waiting on the few blocks that drew one tile more than the rest, while queues let every block
+  // take the next tile as soon as it is free, which with tiles of unequal cost (the partial tiles
+  // below) evens out the finish.
   int* s_claim = s_tmp + 1;
   int qoff = 0;
   if (tid == 0) s_claim[0] = queue_claim(a.qctr, nitems, qoff);
@@ -426,8 +427,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
   int it = s_claim[0];
   __syncthreads();
   while (it >= 0 && it < nitems) {
-    int nxt = -1;
-    if (tid == 0) nxt = queue_claim(a.qctr, nitems, qoff);
+    int nxt = -1;  // the next tile, claimed as this one's K loop ends
     const int g = find_group(s_item0, gl.n, it);
     const int local = __builtin_amdgcn_readfirstlane(it - s_item0[g]);
     const int mt = local / ntiles, nt = local % ntiles;
@@ -537,7 +537,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bd_kernel(FfnArgs a) {
       }
       // The clamped loads past the end are still in flight: they land in ring buffers and registers
       // that nothing reads, but the staging area is separate and the next tile's prologue loads
-      // complete after them (issue order), so no wait is needed here.
+      // complete after them (issue order), so no wait is needed here.  The next tile is claimed
+      // only now (its latency hides behind the epilogue), so that a block that ends late does not
+      // hold a tile that another block could have started.
+      if (tid == 0) nxt = queue_claim(a.qctr, nitems, qoff);
       store_tile<GATEUP, 4>(acc, stg, a, lane, wv, 8 * nt + 2 * wv, shared, row0, m0, mrows);
     };
     if (mrows <= WBM / 4)
