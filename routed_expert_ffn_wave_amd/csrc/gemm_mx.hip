@@ -78,7 +78,7 @@ constexpr int a_units() { return 2 * MxCfg<FP8>::CB / 16; }  // 16-byte pieces o
 
 constexpr int MX_KBMAX = 256;   // FP8: 128-K blocks per weight row held in LDS (K <= 32768)
 
-// LDS: the group list, each group's first partial-tile item ([E + 2] ints), then the buffers
+// LDS: the group list, each group's first short-tile item ([E + 2] ints), then the buffers
 __host__ __device__ inline size_t mx_buf_off(int E) {
   return (group_lds_bytes(E) + (size_t)(E + 2) * 4 + 255) & ~(size_t)255;
 }
@@ -266,8 +266,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
 
   // tiles from the launch's work queues: block b serves the run of XCD b % 8 first (blocks go to
   // the XCDs round-robin, so tiles that share activation rows or weights share an L2), then the
-  // others; a block that starts late takes fewer tiles (each claimed as the previous one's K loop
-  // ends)
+  // others, long tiles before short ones; a block that starts late takes fewer tiles (each is
+  // claimed as the previous one's K loop ends)
   int* s_claim = s_tmp + 1;
   int qoff = 0;
   if (tid == 0) s_claim[0] = queue_claim2(a.qctr, nlong, nshort, qoff);
@@ -276,15 +276,15 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_kernel(FfnArgs a, const uint8_
   __syncthreads();
   for (; it >= 0 && it < nitems;) {
     int nxt = -1;  // the next tile, claimed as this one's K loop ends
-    const bool full = it < nlong;  // a long tile
-    const int* pre = full ? s_item0 : s_pitem0;
-    const int v = full ? it : it - nlong;
+    const bool lng = it < nlong;  // a long tile
+    const int* pre = lng ? s_item0 : s_pitem0;
+    const int v = lng ? it : it - nlong;
     const int g = find_group(pre, gl.n, v);
     const int local = __builtin_amdgcn_readfirstlane(v - pre[g]);
     const int slot = __builtin_amdgcn_readfirstlane(s_slot[g]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_row0[g]);
     const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[g]);
-    const int mt = full ? local / ntiles : cnt / MX_BM, nt = full ? local % ntiles : local;
+    const int mt = lng ? local / ntiles : cnt / MX_BM, nt = lng ? local % ntiles : local;
     const bool shared = row0 >= TK;
     const int m0 = mt * MX_BM;
     const int mrows = min(MX_BM, cnt - m0);
